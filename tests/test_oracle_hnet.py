@@ -1,0 +1,167 @@
+"""Pins for the H-Net half of the oracle (route, quantile, compact, EMA dechunk)."""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy.spatial.distance import cosine as scipy_cosine_distance
+
+import oracle
+from synthdata import gen_c0, gen_c1
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def test_route_golden_hand_derived():
+    g = _gold("hnet_tiny.json")
+    p = oracle.route(np.array(g["q"]), np.array(g["k"]), np.array(g["offsets"]))
+    np.testing.assert_allclose(p, g["p_expected"], atol=1e-12)
+
+
+def test_route_matches_scipy_cosine_distance():
+    c = gen_c0()
+    p = oracle.route(c["q"], c["k"], c["offsets"])
+    off = c["offsets"]
+    for s in range(len(off) - 1):
+        assert p[off[s]] == 1.0
+        for t in range(off[s] + 1, off[s + 1], 7):
+            want = 0.5 * scipy_cosine_distance(c["q"][t].astype(np.float64), c["k"][t - 1].astype(np.float64))
+            assert abs(p[t] - want) < 1e-12
+
+
+def test_route_starts_and_range_ragged():
+    c = gen_c1(nseq=4, d=64, min_events=2, max_events=6)
+    p = oracle.route(c["q"], c["k"], c["offsets"])
+    assert np.all(p[c["offsets"][:-1]] == 1.0)
+    assert np.all((p >= 0) & (p <= 1))
+
+
+def test_route_zero_row_gives_half():
+    q = np.zeros((3, 4)); k = np.zeros((3, 4)); q[1] = 1.0
+    p = oracle.route(q, k, np.array([0, 3]))
+    assert p[1] == 0.5 and p[2] == 0.5
+
+
+def test_quantile_matches_numpy_lower():
+    rng = np.random.default_rng(3)
+    for n in (1, 2, 7, 1000, 4097):
+        p = rng.random(n)
+        assert oracle.stage_quantile(p, 0.75) == np.quantile(p, 0.75, method="lower")
+
+
+def test_quantile_keeps_about_a_quarter():
+    c = gen_c0(nseq=4, T=512)
+    p = oracle.route(c["q"], c["k"], c["offsets"])
+    tau = oracle.stage_quantile(p, 0.75)
+    b = oracle.boundary_mask(p, tau)
+    assert abs(b.mean() - 0.25) < 0.01
+
+
+def test_boundary_mask_fp32_decision_and_nan():
+    p = np.array([0.5, np.nextafter(0.5, 0), 0.7, np.nan])
+    b = oracle.boundary_mask(p, 0.5)
+    # nextafter(0.5, 0) in fp64 rounds to 0.5 in fp32: the decision is taken in fp32
+    assert list(b) == [True, True, True, False]
+
+
+def test_compact_scatter_recovers_rows_and_counts():
+    c = gen_c1(nseq=5, d=32, min_events=2, max_events=9)
+    p = oracle.route(c["q"], c["k"], c["offsets"])
+    b = oracle.boundary_mask(p, 0.5)
+    idx, coff, z, P = oracle.compact(b, p, c["h"], c["offsets"])
+    assert len(idx) == int(b.sum()) == len(z) == len(P)
+    back = np.zeros_like(c["h"])
+    back[idx] = z
+    assert np.array_equal(back[b], c["h"][b])
+    assert np.array_equal(np.asarray(P), p[b])
+    # chunk offsets by brute force per sequence
+    off = c["offsets"]
+    for s in range(len(off) - 1):
+        assert coff[s + 1] - coff[s] == sum(1 for t in range(off[s], off[s + 1]) if b[t])
+        assert idx[coff[s]] == off[s]  # every start is a boundary (p = 1)
+    assert np.all(np.diff(idx) > 0)
+
+
+def test_ema_golden_hand_derived():
+    g = _gold("hnet_tiny.json")
+    out = oracle.dechunk_ema(np.array(g["z"]), np.array(g["P"]), np.array(g["idx"]),
+                             np.array([0, 3]), np.array(g["ema_offsets"]))
+    np.testing.assert_allclose(out, g["ema_expected"], atol=1e-15)
+
+
+def _ragged_chunks(rng, lengths, d, first_p_one=True):
+    offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    N = offsets[-1]
+    b = rng.random(N) < 0.4
+    b[offsets[:-1]] = True
+    p = rng.random(N)
+    if first_p_one:
+        p[offsets[:-1]] = 1.0
+    rows = rng.standard_normal((N, d))
+    idx, coff, z, P = oracle.compact(b, p, rows, offsets)
+    return offsets, b, p, rows, idx, coff, z, P
+
+
+def test_ema_identity_when_every_byte_is_a_boundary_with_P1():
+    rng = np.random.default_rng(5)
+    offsets = np.array([0, 7, 20, 21])
+    rows = rng.standard_normal((21, 6)).astype(np.float32)
+    b = np.ones(21, bool); p = np.ones(21)
+    idx, coff, z, P = oracle.compact(b, p, rows, offsets)
+    out = oracle.dechunk_ema(z, P, idx, coff, offsets)
+    assert np.array_equal(out, rows.astype(np.float64))
+
+
+def test_ema_constant_z_is_fixed_point():
+    rng = np.random.default_rng(6)
+    offsets, b, p, rows, idx, coff, z, P = _ragged_chunks(rng, [30, 11, 50], 5)
+    v = rng.standard_normal(5)
+    out = oracle.dechunk_ema(np.tile(v, (len(z), 1)), P, idx, coff, offsets)
+    np.testing.assert_allclose(out, np.tile(v, (len(out), 1)), rtol=1e-14, atol=1e-14)
+
+
+def test_ema_constant_P_geometric_closed_form():
+    rng = np.random.default_rng(7)
+    M, d, a = 40, 3, 0.3
+    z = rng.standard_normal((M, d))
+    P = np.full(M, a); P[0] = 1.0
+    idx = np.arange(M); offsets = np.array([0, M]); coff = np.array([0, M])
+    out = oracle.dechunk_ema(z, P, idx, coff, offsets)
+    for c in range(M):
+        want = (1 - a) ** c * z[0] + sum(a * (1 - a) ** (c - j) * z[j] for j in range(1, c + 1))
+        np.testing.assert_allclose(out[c], want, rtol=1e-12, atol=1e-12)
+
+
+def test_ema_stays_in_convex_hull_and_is_linear():
+    rng = np.random.default_rng(8)
+    offsets, b, p, rows, idx, coff, z, P = _ragged_chunks(rng, [64, 9, 33], 4)
+    out = oracle.dechunk_ema(z, P, idx, coff, offsets)
+    for s in range(3):
+        for c in range(coff[s], coff[s + 1]):
+            lo = z[coff[s]:c + 1].min(0) - 1e-12
+            hi = z[coff[s]:c + 1].max(0) + 1e-12
+            assert np.all(out[idx[c]] >= lo) and np.all(out[idx[c]] <= hi)
+    z2 = rng.standard_normal(z.shape)
+    lin = oracle.dechunk_ema(2.0 * z - 3.0 * z2, P, idx, coff, offsets)
+    np.testing.assert_allclose(lin, 2.0 * out - 3.0 * oracle.dechunk_ema(z2, P, idx, coff, offsets), atol=1e-12)
+
+
+def test_ema_chunk_form_equals_per_byte_form():
+    """Per-byte scan zbar_t = P_t x_t + (1-P_t) zbar_{t-1} with P_t = p_t b_t
+    (zbar reset to 0 at a start) gives the same result as the chunk scan."""
+    rng = np.random.default_rng(9)
+    offsets, b, p, rows, idx, coff, z, P = _ragged_chunks(rng, [25, 40, 3], 6, first_p_one=False)
+    out = oracle.dechunk_ema(z, P, idx, coff, offsets)
+    ref = np.zeros_like(out)
+    for s in range(3):
+        zb = np.zeros(6)
+        for t in range(offsets[s], offsets[s + 1]):
+            Pt = p[t] * b[t]
+            zb = Pt * rows[t] + (1 - Pt) * zb if b[t] else zb
+            ref[t] = zb
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
