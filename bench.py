@@ -1,0 +1,381 @@
+"""Throughput of the dynamic-chunking layer on one MI355X.
+
+One step = one pass of the whole chunk layer over one batch of 32 byte
+streams of 8192 bytes each:
+  * H-Net two-stage hierarchy (the C2 workload at T = 8192): route with the
+    stage's 0.75 score quantile, compact, route + compact the stage-2 rows,
+    EMA-dechunk stage 2 back to stage-1 length, EMA-dechunk stage 1 back to
+    bytes (d_local 512, d_mid 768, bf16);
+  * ByteFlow layer (the C4 workload): coding rate Delta R (d 512, eps^2 0.5),
+    BOS + Top-(K-1) with K = 2048, gather of the K rows, 16-bin multi-linear
+    upsample from d_global 1536 with the residual (bf16).
+The random stand-ins around the layer (q/k projections, the stage-2 input
+projection, the projection back to d_local, the global map g = z W_g) are
+computed once before the timed region.  Inputs are resident in HBM when
+timing starts.  value = 32 * 8192 byte positions / step time.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-op", default=None, help="time only this op in a loop (for rocprofv3)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Workload:
+    """Device-resident inputs, stand-ins, outputs and workspaces of one step."""
+
+    def __init__(self):
+        import torch
+        import byte_level_lm_amd as B
+        from synthdata import gen_c2, gen_c4
+
+        self.B = B
+        self.torch = torch
+        bf = torch.bfloat16
+        dev = torch.device("cuda")
+        t0 = time.time()
+        c2 = gen_c2(fixed_T=8192)
+        c4 = gen_c4()
+        log(f"inputs generated in {time.time() - t0:.1f}s")
+        self.c2, self.c4 = c2, c4
+        T = 8192
+        self.nseq = 32
+        self.N = int(c2["offsets"][-1])
+        assert self.N == self.nseq * T
+        # ---------------- H-Net
+        self.off = torch.from_numpy(c2["offsets"]).to(dev)
+        self.h1 = torch.from_numpy(c2["h"]).to(dev, bf)
+        self.q1 = torch.from_numpy(c2["q"]).to(dev, bf)
+        self.k1 = torch.from_numpy(c2["k"]).to(dev, bf)
+        N = self.N
+        self.p1 = torch.empty(N, device=dev)
+        self.b1 = torch.empty(N, dtype=torch.uint8, device=dev)
+        self.tau1 = torch.empty(1, device=dev)
+        self.ws_route = torch.empty(B.route_workspace(N), dtype=torch.uint8, device=dev)
+        self.ws_compact = torch.empty(B.compact_workspace(N), dtype=torch.uint8, device=dev)
+        self.idx1 = torch.empty(N, dtype=torch.int32, device=dev)
+        self.coff1 = torch.empty(self.nseq + 1, dtype=torch.int64, device=dev)
+        self.z1 = torch.empty((N, 512), dtype=bf, device=dev)
+        self.P1 = torch.empty(N, device=dev)
+        self.st = torch.zeros(1, dtype=torch.int32, device=dev)
+        # untimed first pass of stage 1 to size stage 2 and build its stand-in inputs
+        self._stage1()
+        torch.cuda.synchronize()
+        self.M1 = int(self.coff1[-1].item())
+        M1 = self.M1
+        w_mid = torch.from_numpy(c2["w_mid"]).to(dev, torch.float32)
+        wq2 = torch.from_numpy(c2["wq2"]).to(dev, torch.float32)
+        wk2 = torch.from_numpy(c2["wk2"]).to(dev, torch.float32)
+        self.x2 = (self.z1[:M1].float() @ w_mid).to(bf)
+        self.q2 = (self.x2.float() @ wq2).to(bf)
+        self.k2 = (self.x2.float() @ wk2).to(bf)
+        self.p2 = torch.empty(M1, device=dev)
+        self.b2 = torch.empty(M1, dtype=torch.uint8, device=dev)
+        self.tau2 = torch.empty(1, device=dev)
+        self.idx2 = torch.empty(M1, dtype=torch.int32, device=dev)
+        self.coff2 = torch.empty(self.nseq + 1, dtype=torch.int64, device=dev)
+        self.z2 = torch.empty((M1, 768), dtype=bf, device=dev)
+        self.P2 = torch.empty(M1, device=dev)
+        self.y2 = torch.empty((M1, 768), dtype=bf, device=dev)
+        self.out1 = torch.empty((N, 512), dtype=bf, device=dev)
+        self.ws_dechunk = torch.empty(B.dechunk_workspace(768), dtype=torch.uint8, device=dev)
+        self._stage2()
+        self._dechunk2()
+        torch.cuda.synchronize()
+        self.M2 = int(self.coff2[-1].item())
+        w_back = torch.from_numpy(c2["w_back"]).to(dev, torch.float32)
+        self.y1 = (self.y2.float() @ w_back).to(bf)  # stand-in projection back to d_local
+        # ---------------- ByteFlow
+        self.K, self.nbins = c4["K"], c4["nbins"]
+        self.h4 = torch.from_numpy(c4["h"]).to(dev, bf)
+        self.off4 = torch.arange(self.nseq + 1, dtype=torch.int64, device=dev) * T
+        self.dR = torch.empty((self.nseq, T), device=dev)
+        self.ws_cr = torch.empty(B.coding_rate_workspace(self.nseq, T, 512), dtype=torch.uint8, device=dev)
+        self.idx4 = torch.empty((self.nseq, self.K), dtype=torch.int32, device=dev)
+        self.mask4 = torch.empty((self.nseq, T), dtype=torch.uint8, device=dev)
+        self.gidx4 = torch.empty(self.nseq * self.K, dtype=torch.int32, device=dev)
+        self.coff4 = torch.empty(self.nseq + 1, dtype=torch.int64, device=dev)
+        self.z4 = torch.empty((self.nseq * self.K, 512), dtype=bf, device=dev)
+        self.ws_compact4 = torch.empty(B.compact_workspace(self.N), dtype=torch.uint8, device=dev)
+        self.W = torch.from_numpy(c4["w_bin"]).to(dev, bf)
+        self.s4 = torch.empty_like(self.h4)
+        self.ws_up = torch.empty(B.upsample_workspace(self.nseq, T, self.K, 1536, 512, self.nbins),
+                                 dtype=torch.uint8, device=dev)
+        self._coding_rate(); self._topk(); self._gather()
+        torch.cuda.synchronize()
+        w_g = torch.from_numpy(c4["w_g"]).to(dev, torch.float32)
+        self.g4 = (self.z4.float() @ w_g).to(bf).view(self.nseq, self.K, 1536)  # global stand-in
+        self._upsample()
+        torch.cuda.synchronize()
+        log(f"setup done: M1={self.M1} ({self.M1 / N:.3f} N), M2={self.M2} ({self.M2 / N:.3f} N)")
+
+    # ------------------------------------------------------------ ops of one step
+    def _stage1(self):
+        B = self.B
+        B.route(self.q1, self.k1, self.off, quantile=0.75, p_out=self.p1, b_out=self.b1, tau_out=self.tau1,
+                ws=self.ws_route)
+        B.compact(self.b1, self.off, rows=self.h1, p=self.p1, capacity=self.N, idx_out=self.idx1,
+                  chunk_offsets_out=self.coff1, rows_out=self.z1, P_out=self.P1, status=self.st,
+                  ws=self.ws_compact)
+
+    def _stage2(self):
+        B = self.B
+        B.route(self.q2, self.k2, self.coff1, quantile=0.75, p_out=self.p2, b_out=self.b2,
+                tau_out=self.tau2, ws=self.ws_route)
+        B.compact(self.b2, self.coff1, rows=self.x2, p=self.p2, capacity=self.M1, idx_out=self.idx2,
+                  chunk_offsets_out=self.coff2, rows_out=self.z2, P_out=self.P2, status=self.st,
+                  ws=self.ws_compact)
+
+    def _dechunk2(self):
+        self.B.dechunk_ema(self.z2, self.P2, self.idx2, self.coff2, self.coff1, self.M1, out=self.y2,
+                           ws=self.ws_dechunk)
+
+    def _dechunk1(self):
+        self.B.dechunk_ema(self.y1, self.P1, self.idx1, self.coff1, self.off, self.N, out=self.out1,
+                           ws=self.ws_dechunk)
+
+    def _coding_rate(self):
+        self.B.coding_rate(self.h4, 0.5, dR_out=self.dR, status=self.st, ws=self.ws_cr)
+
+    def _topk(self):
+        self.B.topk_select(self.dR, self.K, idx_out=self.idx4, mask_out=self.mask4, status=self.st)
+
+    def _gather(self):
+        self.B.compact(self.mask4.view(-1), self.off4, rows=self.h4.view(-1, 512), capacity=self.nseq * self.K,
+                       idx_out=self.gidx4, chunk_offsets_out=self.coff4, rows_out=self.z4, status=self.st,
+                       ws=self.ws_compact4)
+
+    def _upsample(self):
+        self.B.upsample_bins(self.g4, self.W, self.idx4, self.h4, self.nbins, s_out=self.s4, ws=self.ws_up)
+
+    def ops(self):
+        return [("route+compact stage1", self._stage1), ("route+compact stage2", self._stage2),
+                ("dechunk stage2", self._dechunk2), ("dechunk stage1", self._dechunk1),
+                ("coding_rate", self._coding_rate), ("topk_select", self._topk),
+                ("gather", self._gather), ("upsample_bins", self._upsample)]
+
+    def step(self):
+        for _, f in self.ops():
+            f()
+
+    # ------------------------------------------------------------ algorithmic work
+    def algorithmic(self):
+        """Algorithmic HBM bytes / MFMA flops per op (what the method must touch)."""
+        N, M1, M2, nseq, K = self.N, self.M1, self.M2, self.nseq, self.K
+        e = 2
+        idx = self.idx4.cpu().numpy()
+        T = 8192
+        items = 0
+        for s in range(nseq):
+            L = np.diff(np.concatenate([idx[s], [T]]))
+            items += int(np.minimum(L, self.nbins).sum())
+        self.up_items = items
+        return {
+            "route+compact stage1": dict(bytes=N * (2 * 512 * e + 4 + 1) + N + M1 * (4 + 4 + 4 + 2 * 512 * e)),
+            "route+compact stage2": dict(bytes=M1 * (2 * 768 * e + 4 + 1) + M1 + M2 * (4 + 4 + 4 + 2 * 768 * e)),
+            "dechunk stage2": dict(bytes=M2 * (768 * e + 8) + M1 * 768 * e),
+            "dechunk stage1": dict(bytes=M1 * (512 * e + 8) + N * 512 * e),
+            "coding_rate": dict(flops=3 * T * 512 * 512 * nseq, bytes=N * 512 * e + N * 4),
+            "topk_select": dict(bytes=N * 4 + N + nseq * K * 4),
+            "gather": dict(bytes=N + nseq * K * (4 + 2 * 512 * e)),
+            "upsample_bins": dict(flops=2 * 1536 * 512 * items, bytes=2 * N * 512 * e + nseq * K * 1536 * e),
+        }
+
+
+def time_ops(wl, reps=5):
+    """Average duration of each op (HIP events on the stream the kernels run on)."""
+    torch = wl.torch
+    res = {}
+    for name, f in wl.ops():
+        f()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            f()
+        ev1.record()
+        torch.cuda.synchronize()
+        res[name] = ev0.elapsed_time(ev1) / reps
+    return res
+
+
+def cpu_baseline(wl):
+    """The oracle, as it stands, on a bounded sample of the same workload, one thread."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from synthdata import gen_c2_stage2_inputs, gen_c2_backproj, gen_c4_global
+
+    c2, c4 = wl.c2, wl.c4
+    T = 8192
+    with threadpool_limits(limits=1):
+        # H-Net two-stage layer on the first stream (8192 bytes)
+        t0 = time.perf_counter()
+        off = np.array([0, T], np.int64)
+        q, k, h = c2["q"][:T], c2["k"][:T], c2["h"][:T]
+        p1 = oracle.route(q, k, off)
+        tau1 = oracle.stage_quantile(p1, 0.75)
+        b1 = oracle.boundary_mask(p1, tau1)
+        i1, co1, z1, P1 = oracle.compact(b1, p1, h, off)
+        s2 = gen_c2_stage2_inputs(z1, c2)
+        t_standin = time.perf_counter()
+        p2 = oracle.route(s2["q2"], s2["k2"], co1)
+        t_standin = time.perf_counter() - t_standin
+        tau2 = oracle.stage_quantile(p2, 0.75)
+        b2 = oracle.boundary_mask(p2, tau2)
+        i2, co2, z2, P2 = oracle.compact(b2, p2, s2["x2"], co1)
+        y2 = oracle.dechunk_ema(z2, P2, i2, co2, co1)
+        y1 = gen_c2_backproj(y2, c2)
+        oracle.dechunk_ema(y1, P1, i1, co1, off)
+        t_hnet = time.perf_counter() - t0
+        # ByteFlow: Delta R on the first 768 positions of stream 0
+        npos = 768
+        t0 = time.perf_counter()
+        oracle.coding_rate_at(c4["h"][0].astype(np.float64), 0.5, np.arange(npos))
+        t_dr = time.perf_counter() - t0
+        dr = wl.dR[0:1].cpu().numpy()
+        t0 = time.perf_counter()
+        sel = oracle.topk_select(dr, wl.K)
+        z = oracle.gather(c4["h"][0:1], sel)
+        t_topk = time.perf_counter() - t0
+        g = gen_c4_global(z, c4)
+        nup = 2048
+        t0 = time.perf_counter()
+        oracle.upsample_bins(g, c4["w_bin"], sel, c4["h"][0:1, :], c4["nbins"]) if False else None
+        # upsample of the first nup positions of the stream (same per-position work)
+        cmap, bins = oracle.chunk_bins(sel[0], T, c4["nbins"])
+        hh = c4["h"][0].astype(np.float64)
+        W = c4["w_bin"].astype(np.float64)
+        gg = g[0].astype(np.float64)
+        for t in range(nup):
+            _ = hh[t] + gg[cmap[t]] @ W[bins[t]]
+        t_up = time.perf_counter() - t0
+    sec_per_byte = t_hnet / T + t_dr / npos + t_topk / T + t_up / nup
+    total = t_hnet + t_dr + t_topk + t_up
+    return {
+        "value": 1.0 / sec_per_byte,
+        "unit": "bytes/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"oracle fp64, 1 thread: H-Net two-stage layer on 1 of the 32 streams ({T} B, "
+                   f"{t_hnet:.1f}s incl. stand-ins), Delta R at the first {npos} positions of one stream "
+                   f"({t_dr:.1f}s), Top-K + gather of one stream ({t_topk:.2f}s), upsample of {nup} "
+                   f"positions ({t_up:.1f}s); per-byte costs summed, {total:.1f}s of CPU work"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    wl = Workload()
+    if args.profile_op:
+        f = dict(wl.ops())[args.profile_op]
+        for _ in range(args.steps):
+            f()
+        torch.cuda.synchronize()
+        log("profiled", args.profile_op, args.steps, "launches")
+        return
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        wl.step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f}s)")
+    per_op = time_ops(wl)
+    alg = wl.algorithmic()
+    breakdown = {}
+    for name, t in per_op.items():
+        a = alg[name]
+        d = {"ms": round(t, 4)}
+        if "bytes" in a:
+            d["hbm_GBps"] = round(a["bytes"] / (t * 1e-3) / 1e9, 1)
+        if "flops" in a:
+            d["TFLOPs"] = round(a["flops"] / (t * 1e-3) / 1e12, 2)
+        breakdown[name] = d
+    dom = max(per_op, key=per_op.get)
+    cr = alg["coding_rate"]
+    roof = {
+        "kernel": "bllm_coding_rate (cr_gram_prefix + cr_factor), fp32 MFMA",
+        "bound": "mfma",
+        "achieved": round(cr["flops"] / (per_op["coding_rate"] * 1e-3) / 1e12, 3),
+        "peak": FP32_MFMA_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "traffic": None,
+    }
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    hnet_ms = sum(per_op[n] for n in ("route+compact stage1", "route+compact stage2", "dechunk stage2", "dechunk stage1"))
+    hnet_bytes = sum(alg[n]["bytes"] for n in ("route+compact stage1", "route+compact stage2", "dechunk stage2", "dechunk stage1"))
+    out = {
+        "metric": "chunked bytes/sec at T=8192 (route+compact+dechunk, ΔR+TopK); % roofline",
+        "value": wl.N / (ms * 1e-3),
+        "unit": "bytes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hnet_2stage_T8192_B32 + byteflow_T8192_B32_K2048", "global_batch": 32,
+                   "seq_len": 8192, "hnet": {"d_local": 512, "d_mid": 768, "stage_quantile": 0.75,
+                                             "M1": wl.M1, "M2": wl.M2},
+                   "byteflow": {"d_local": 512, "d_global": 1536, "K": 2048, "bins": 16, "eps2": 0.5,
+                                "upsample_items": wl.up_items},
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "dominant_op": dom,
+        "breakdown": breakdown,
+        "hnet_layer": {"ms": round(hnet_ms, 4), "bytes_per_s": wl.N / (hnet_ms * 1e-3),
+                       "hbm_GBps": round(hnet_bytes / (hnet_ms * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(hnet_bytes / (hnet_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle baseline on the host")
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,11 @@
+"""MI355X-native dynamic-chunking layer for tokenizer-free hierarchical byte models.
+
+The compute path is the HIP library libbllm.so (C ABI in include/bllm.h);
+this package only marshals torch tensors (device memory and the current
+stream) into it.  See ``byte_level_lm_amd.ops``.
+"""
+from ._lib import lib, LIB_PATH, EXPORTS, BllmError  # noqa: F401
+from .ops import (  # noqa: F401
+    route, compact, dechunk_ema, coding_rate, topk_select, upsample_bins,
+    route_workspace, compact_workspace, dechunk_workspace, coding_rate_workspace, upsample_workspace,
+)

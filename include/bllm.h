@@ -1,0 +1,190 @@
+/*
+ * bllm.h -- C ABI of the dynamic-chunking layer of tokenizer-free hierarchical
+ * byte models, built for AMD Instinct MI355X (gfx950).
+ *
+ * Two downsamplers and two upsamplers sit between a byte-level local encoder
+ * and a global model:
+ *   H-Net style:   bllm_route -> bllm_compact -> ... -> bllm_dechunk_ema
+ *   ByteFlow:      bllm_coding_rate -> bllm_topk_select -> bllm_compact (gather)
+ *                  -> ... -> bllm_upsample_bins
+ *
+ * Sources of the operations (page titles; sections as on the page):
+ *   [BG]  "ByteGen: A Tokenizer-Free Generative Model for Orderbook Events in
+ *         Byte Space" analyst report, section 2.3 Methodology.
+ *   [BF2] "ByteFlow: Language Modeling through Adaptive Byte Compression
+ *         without a Tokenizer" paper notes, key designs 2 and 4.
+ *   [BF4] ByteFlow paper page (arXiv 2603.03583), "lossy coding rate"
+ *         prerequisite and "method step details" stages 2 and 4.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers to caller-owned memory.  The
+ *     library never allocates, frees or synchronises; every call only
+ *     enqueues kernels on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream) and returns.
+ *   - Scratch memory comes in through (ws, ws_bytes); its size is given by the
+ *     matching bllm_*_workspace() function.  Contents need not be initialised
+ *     and are clobbered.  Workspaces must not be shared by calls that may
+ *     run concurrently.
+ *   - Row-major, densely packed rows.  A ragged batch is packed rows of all
+ *     sequences back to back plus `offsets` (int64 [nseq+1], device,
+ *     offsets[0] = 0, non-decreasing, offsets[nseq] = total).
+ *   - dtype is BLLM_F32 or BLLM_BF16 (bf16 bit patterns, fp32 accumulation,
+ *     round-to-nearest-even on output).  Row pointers must be 16-byte aligned
+ *     and d * element size a multiple of 16 bytes.
+ *   - Return value: BLLM_OK or a negative BLLM_E_* code.  Argument errors are
+ *     detected on the host before anything is enqueued.  Data-dependent
+ *     conditions (capacity overflow, non-finite values) are reported through
+ *     an optional device int32 `status` word that the call ORs flags into
+ *     (BLLM_S_* bits); the caller zeroes it beforehand and reads it after its
+ *     own synchronisation.
+ */
+#ifndef BLLM_H
+#define BLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define BLLM_OK 0
+#define BLLM_E_INVAL (-1)  /* bad argument (null pointer, size out of range) */
+#define BLLM_E_NOTSUP (-2) /* valid but unsupported shape/dtype/alignment     */
+#define BLLM_E_WS (-3)     /* workspace too small                            */
+#define BLLM_E_HIP (-4)    /* the HIP runtime reported an error at launch    */
+
+/* device status flags (ORed into *status) */
+#define BLLM_S_CAPACITY 1  /* compaction produced more rows than `capacity`   */
+#define BLLM_S_NONFINITE 2 /* a NaN/Inf input or a non-positive pivot was met */
+
+/* dtypes */
+#define BLLM_F32 0
+#define BLLM_BF16 1
+
+int bllm_version(void);
+const char* bllm_status_string(int code);
+
+/*
+ * bllm_route -- H-Net boundary scoring ([BG] 2.3: boundary probability from
+ * the cosine similarity of adjacent byte representations).
+ *
+ *   p_t = (1 - cos(q_t, k_{t-1})) / 2, clamped to [0, 1];  p = 1 at every
+ *   sequence start (no pair crosses offsets).  cos = <q,k> / max(|q||k|, 1e-12).
+ *   b_t = [p_t >= tau] decided in fp32; NaN p gives b = 0.
+ *   tau = threshold when quantile < 0; otherwise tau is the order statistic
+ *   of rank floor(quantile * (total - 1)) (0-based, ascending, NaN last) of all
+ *   `total` scores of the batch (one threshold per call = per hierarchy stage).
+ *
+ * q, k     : [total x d] rows of dtype (the routing projections of h).
+ * offsets  : int64 [nseq+1] device.
+ * p_out    : fp32 [total]; b_out : uint8 [total] (0/1); tau_out : fp32 [1]
+ *            device, may be NULL.
+ * ws       : bllm_route_workspace(total) bytes (needed when quantile >= 0).
+ * Errors   : BLLM_E_INVAL for null q/k/offsets/p_out/b_out, d < 1, nseq < 1,
+ *            total < 0, quantile > 1; BLLM_E_NOTSUP for bad dtype/alignment.
+ */
+size_t bllm_route_workspace(int64_t total);
+int bllm_route(const void* q, const void* k, int dtype, int64_t d, const int64_t* offsets,
+               int64_t nseq, int64_t total, float threshold, double quantile, float* p_out,
+               uint8_t* b_out, float* tau_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bllm_compact -- keep the boundary positions of a ragged batch ([BG] 2.3
+ * chunking into a shorter sequence; also the gather z = [h_{s_1} .. h_{s_K}]
+ * of [BF4] stage 2 when `mask` is the Top-K mask).
+ *
+ *   idx_out[r]          = global position of the r-th set mask byte (ascending)
+ *   chunk_offsets_out[s]= number of set bytes before offsets[s]  (int64 [nseq+1];
+ *                         chunk_offsets_out[nseq] = M, the total count)
+ *   rows_out[r]         = rows[idx_out[r]]   (if rows != NULL)
+ *   P_out[r]            = p[idx_out[r]]      (if p != NULL)
+ * At most `capacity` entries are written; if M > capacity the
+ * BLLM_S_CAPACITY flag is set in *status (chunk_offsets still hold the true
+ * counts).  idx_out is int32 (total must be < 2^31).
+ * ws: bllm_compact_workspace(total) bytes.
+ */
+size_t bllm_compact_workspace(int64_t total);
+int bllm_compact(const uint8_t* mask, const float* p, const void* rows, int dtype, int64_t d,
+                 const int64_t* offsets, int64_t nseq, int64_t total, int64_t capacity,
+                 int32_t* idx_out, int64_t* chunk_offsets_out, void* rows_out, float* P_out,
+                 int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bllm_dechunk_ema -- EMA smoothing back to byte length ([BG] 2.3).
+ *
+ *   per sequence s, over its chunks c = chunk_offsets[s] .. chunk_offsets[s+1]-1:
+ *     zbar_c = P_c * z_c + (1 - P_c) * zbar_{c-1},  zbar before the first chunk = 0
+ *   out_t = zbar_{c(t)} for every position t of the sequence, c(t) the last chunk
+ *   with idx[c] <= t; positions before a sequence's first chunk get 0.
+ *
+ * z        : [>= M x d] dtype, P : fp32 [M], idx : int32 [M] (global positions,
+ *            ascending, inside their sequence), chunk_offsets : int64 [nseq+1]
+ *            device (M = chunk_offsets[nseq], read on the device).
+ * max_chunks: host upper bound on M (grid sizing; typically the compaction
+ *            capacity).  out : [total x d] dtype.
+ * ws       : bllm_dechunk_workspace(d) bytes.
+ */
+size_t bllm_dechunk_workspace(int64_t d);
+int bllm_dechunk_ema(const void* z, const float* P, int dtype, int64_t d, const int32_t* idx,
+                     const int64_t* chunk_offsets, const int64_t* offsets, int64_t nseq,
+                     int64_t total, int64_t max_chunks, void* out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * bllm_coding_rate -- marginal lossy coding rate ([BF4] prerequisite "lossy
+ * coding rate" and stage 2):
+ *   R(H) = 1/2 logdet(I + alpha H H^T) = 1/2 logdet(I_d + alpha H^T H),
+ *   alpha = d / eps2,  dR_t = R(h_1..t) - R(h_1..t-1)  for t = 0..T-1 (0-based;
+ *   dR_0 = R(h_1)).
+ * Computed exactly (up to fp32 rounding) as the logs of the Cholesky pivots of
+ * I_T + alpha H H^T, obtained block by block from the d x d prefix matrices
+ * (the incremental Sherman-Morrison-Woodbury route the [BF4] weakness
+ * analysis suggests).
+ *
+ * h : [nseq x T x d] dtype, dense.  dR_out : fp32 [nseq x T].
+ * status : optional device word (BLLM_S_NONFINITE on NaN/Inf or lost
+ *          positive definiteness).
+ * Limits : 1 <= d <= 640 (BLLM_E_NOTSUP beyond), T >= 1, eps2 > 0.
+ * ws     : bllm_coding_rate_workspace(nseq, T, d) bytes.
+ */
+size_t bllm_coding_rate_workspace(int64_t nseq, int64_t T, int64_t d);
+int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d, double eps2,
+                     float* dR_out, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * bllm_topk_select -- ByteFlow boundary set ([BF4] stage 2, [BF2] key design 2):
+ *   S = {0} U {the K-1 largest score_t, t = 1..T-1}, in increasing time order.
+ *   Ties go to the earlier position; NaN ranks below every number (and sets
+ *   BLLM_S_NONFINITE); -0.0 equals +0.0.
+ * score : fp32 [nseq x T].  idx_out : int32 [nseq x K] (positions inside the
+ * sequence, idx_out[s*K] = 0).  mask_out : uint8 [nseq x T] or NULL.
+ * Limits: 1 <= K <= T <= 16384 (the scores of one sequence live in LDS).
+ */
+int bllm_topk_select(const float* score, int64_t nseq, int64_t T, int64_t K, int32_t* idx_out,
+                     uint8_t* mask_out, int32_t* status, void* stream);
+
+/*
+ * bllm_upsample_bins -- multi-linear reconstruction with the large residual
+ * ([BF4] stage 4, [BF2] key design 4):
+ *   c(t)   = last i with idx[i] <= t,  L_c = idx[c+1] - idx[c] (idx[K] = T)
+ *   bin(t) = floor(nbins * (t - idx[c]) / L_c)          (relative position in chunk)
+ *   s_t    = h_t + g_{c(t)} W_{bin(t)}                  (row vectors)
+ * g : [nseq x K x d_global], W : [nbins x d_global x d_local],
+ * idx : int32 [nseq x K] (ascending, idx[s*K] = 0), h, s_out : [nseq x T x d_local].
+ * dtype must be BLLM_BF16 (bf16 MFMA, fp32 accumulate).
+ * Limits: nbins <= 64, d_global % 32 == 0, d_local % 8 == 0, nseq * T < 2^31.
+ * ws : bllm_upsample_workspace(nseq, T, K, d_global, d_local, nbins) bytes
+ *      (bin-bucketed work items and a transposed copy of W).
+ */
+size_t bllm_upsample_workspace(int64_t nseq, int64_t T, int64_t K, int64_t d_global,
+                               int64_t d_local, int64_t nbins);
+int bllm_upsample_bins(const void* g, const void* W, const int32_t* idx, const void* h, int dtype,
+                       int64_t nseq, int64_t T, int64_t K, int64_t d_global, int64_t d_local,
+                       int64_t nbins, void* s_out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BLLM_H */

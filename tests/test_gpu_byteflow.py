@@ -1,0 +1,206 @@
+"""GPU parity: ByteFlow coding rate, Top-K, gather and binned upsample against the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from synthdata import bf16_round, cluster_rows, gen_c0_dr_tiny, gen_c3, gen_c4, gen_c4_global
+from tests.helpers import oracle_dr_parallel, row_rel_err, say, to_dev, to_np, topk_band_compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    import byte_level_lm_amd as B
+    B.lib()
+    return B
+
+
+def _torch():
+    import torch
+    return torch
+
+
+# ------------------------------------------------------------------ Top-K
+
+def _topk_check(ops, sc, K):
+    idx, mask, st = ops.topk_select(to_dev(sc.astype(np.float32)), K)
+    want = oracle.topk_select(sc.astype(np.float32), K)
+    assert np.array_equal(to_np(idx), want)
+    assert np.array_equal(to_np(mask), oracle.topk_mask(want, sc.shape[1]))
+    return st
+
+
+def test_topk_bitexact_on_oracle_delta_r(ops):
+    rng = np.random.default_rng(1)
+    h = cluster_rows(rng, 2, 600, 16)
+    dr = oracle.coding_rate(h, 0.5).astype(np.float32)
+    for K in (1, 2, 3, 150, 599, 600):
+        _topk_check(ops, dr, K)
+
+
+def test_topk_ties_specials_and_ragged_sizes(ops):
+    rng = np.random.default_rng(2)
+    for T in (1, 2, 5, 1023, 1025, 3000, 16384):
+        sc = rng.integers(0, 5, size=(3, T)).astype(np.float32)
+        sc[0, ::7] = -0.0
+        sc[1, ::11] = np.inf
+        sc[2, ::13] = -np.inf
+        for K in sorted({1, min(T, 2), max(1, T // 3), T}):
+            _topk_check(ops, sc, K)
+    sc = rng.standard_normal((2, 100)).astype(np.float32)
+    sc[0, 5] = np.nan
+    st = _topk_check(ops, sc, 30)
+    assert int(to_np(st)[0]) & 2
+
+
+def test_topk_full_size_c3_shape(ops):
+    rng = np.random.default_rng(3)
+    sc = rng.standard_normal((8, 8192)).astype(np.float32)
+    _topk_check(ops, sc, 2048)
+
+
+# ------------------------------------------------------------------ coding rate
+
+def _dr(ops, h, eps2, dtype):
+    dR, st = ops.coding_rate(to_dev(h, dtype), eps2)
+    return to_np(dR), int(to_np(st)[0])
+
+
+def test_coding_rate_tiny_brute_force_case(ops):
+    torch = _torch()
+    c = gen_c0_dr_tiny()
+    g, st = _dr(ops, c["h"][None], c["eps2"], torch.float32)
+    o = oracle.coding_rate(c["h"], c["eps2"])
+    assert st == 0
+    assert np.max(np.abs(g[0] - o) / np.abs(o)) < 1e-4
+
+
+@pytest.mark.parametrize("T,d", [(700, 64), (1000, 256), (33, 8), (129, 40)])
+def test_coding_rate_fp32_vs_oracle(ops, T, d):
+    torch = _torch()
+    rng = np.random.default_rng(T + d)
+    h = cluster_rows(rng, 2, T, d).astype(np.float32)
+    say("coding_rate fp32 T", T, "d", d)
+    g, st = _dr(ops, h, 0.5, torch.float32)
+    assert st == 0
+    for s in range(2):
+        o = oracle.coding_rate(h[s], 0.5)
+        assert np.max(np.abs(g[s] - o) / np.abs(o)) < 1e-3
+
+
+def test_coding_rate_bf16_d512_vs_oracle(ops):
+    torch = _torch()
+    rng = np.random.default_rng(5)
+    h = bf16_round(cluster_rows(rng, 1, 600, 512))
+    say("coding_rate bf16 d=512 T=600")
+    g, st = _dr(ops, h, 0.5, torch.bfloat16)
+    o = oracle_dr_parallel(h[0].astype(np.float64), 0.5)
+    assert st == 0
+    assert np.max(np.abs(g[0] - o) / np.abs(o)) < 1e-3
+
+
+def test_coding_rate_nonfinite_sets_status(ops):
+    torch = _torch()
+    h = cluster_rows(np.random.default_rng(6), 1, 100, 16).astype(np.float32)
+    h[0, 50, 3] = np.nan
+    _, st = _dr(ops, h, 0.5, torch.float32)
+    assert st & 2
+
+
+def test_coding_rate_topk_full_size_c3(ops):
+    """C3 at full size: 8 x 8192 x 256 fp32.  Sampled Delta R against the oracle
+    in every sequence, then the Top-K set of one full sequence against the
+    oracle's, outside the 1e-5 band around the K-th value."""
+    torch = _torch()
+    c = gen_c3()
+    say("C3 generated")
+    g, st = _dr(ops, c["h"], c["eps2"], torch.float32)
+    assert st == 0
+    rng = np.random.default_rng(9)
+    for s in range(c["nseq"]):
+        pos = np.sort(rng.choice(c["T"], 24, replace=False))
+        o = oracle.coding_rate_at(c["h"][s], c["eps2"], pos)
+        assert np.max(np.abs(g[s, pos] - o) / np.abs(o)) < 1e-3
+    o0 = oracle_dr_parallel(c["h"][0].astype(np.float64), c["eps2"])
+    assert np.max(np.abs(g[0] - o0) / o0) < 1e-3
+    idx, mask, _ = ops.topk_select(to_dev(g), c["K"])
+    bad, nband = topk_band_compare(to_np(idx)[0], oracle.topk_select(o0, c["K"]), o0, c["K"])
+    say("C3 max abs err", np.max(np.abs(g[0] - o0)), "band size", nband)
+    assert len(bad) == 0, bad
+
+
+def test_coding_rate_full_size_c4_sampled(ops):
+    torch = _torch()
+    c = gen_c4()
+    say("C4 generated")
+    g, st = _dr(ops, c["h"], c["eps2"], torch.bfloat16)
+    assert st == 0
+    rng = np.random.default_rng(10)
+    for s in (0, 13, 31):
+        pos = np.sort(rng.choice(c["T"], 8, replace=False))
+        o = oracle.coding_rate_at(c["h"][s], c["eps2"], pos)
+        assert np.max(np.abs(g[s, pos] - o) / np.abs(o)) < 1e-3
+
+
+# ------------------------------------------------------------------ gather + upsample
+
+def test_gather_via_compact_on_topk_mask(ops):
+    torch = _torch()
+    rng = np.random.default_rng(11)
+    nseq, T, d, K = 3, 1000, 64, 100
+    h = bf16_round(rng.standard_normal((nseq, T, d)))
+    sc = rng.standard_normal((nseq, T)).astype(np.float32)
+    idx, mask, _ = ops.topk_select(to_dev(sc), K)
+    off = np.arange(nseq + 1, dtype=np.int64) * T
+    gi, coff, z, _, _ = ops.compact(mask.reshape(-1), to_dev(off), rows=to_dev(h.reshape(-1, d), torch.bfloat16))
+    want = (to_np(idx) + off[:-1, None]).reshape(-1)
+    assert np.array_equal(to_np(gi)[:nseq * K], want)
+    assert np.array_equal(to_np(coff), np.arange(nseq + 1) * K)
+    assert np.array_equal(to_np(z)[:nseq * K], oracle.gather(h, to_np(idx)).reshape(-1, d))
+
+
+def _random_idx(rng, nseq, T, K):
+    return np.stack([np.sort(np.concatenate([[0], rng.choice(np.arange(1, T), K - 1, replace=False)]))
+                     for _ in range(nseq)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("nseq,T,K,dg,dl,B", [(2, 300, 40, 64, 32, 16), (3, 1000, 37, 96, 136, 4),
+                                              (1, 64, 64, 32, 8, 16), (2, 500, 1, 64, 64, 16)])
+def test_upsample_vs_oracle(ops, nseq, T, K, dg, dl, B):
+    torch = _torch()
+    rng = np.random.default_rng(T + K)
+    idx = _random_idx(rng, nseq, T, K)
+    g = bf16_round(rng.standard_normal((nseq, K, dg)))
+    W = bf16_round(rng.standard_normal((B, dg, dl)) / np.sqrt(dg))
+    h = bf16_round(rng.standard_normal((nseq, T, dl)))
+    bf = torch.bfloat16
+    s = ops.upsample_bins(to_dev(g, bf), to_dev(W, bf), to_dev(idx), to_dev(h, bf), B)
+    ref = oracle.upsample_bins(g, W, idx, h, B)
+    assert row_rel_err(to_np(s), ref) < 2e-2
+
+
+def test_byteflow_chain_full_size_c4(ops):
+    """C4 at full size (the launch configuration of bench.py): Delta R, Top-K,
+    gather, global stand-in, 16-bin upsample + residual; upsample rows of two
+    sequences checked against the oracle."""
+    torch = _torch()
+    bf = torch.bfloat16
+    c = gen_c4()
+    nseq, T, K = c["nseq"], c["T"], c["K"]
+    h_t = to_dev(c["h"], bf)
+    dR, st = ops.coding_rate(h_t, c["eps2"])
+    idx, mask, _ = ops.topk_select(dR, K)
+    off = np.arange(nseq + 1, dtype=np.int64) * T
+    gi, coff, z, _, _ = ops.compact(mask.reshape(-1), to_dev(off), rows=h_t.reshape(-1, c["d_local"]),
+                                    capacity=nseq * K)
+    z_np = to_np(z).reshape(nseq, K, -1)
+    idx_np = to_np(idx)
+    assert np.array_equal(z_np, oracle.gather(c["h"], idx_np))
+    g = gen_c4_global(z_np, c)
+    s = ops.upsample_bins(to_dev(g, bf), to_dev(c["w_bin"], bf), idx, h_t, c["nbins"])
+    s_np = to_np(s)
+    for q in (0, 31):
+        ref = oracle.upsample_bins(g[q:q + 1], c["w_bin"], idx_np[q:q + 1], c["h"][q:q + 1], c["nbins"])
+        assert row_rel_err(s_np[q:q + 1], ref) < 2e-2
+    say("C4 chain ok")

@@ -1,0 +1,247 @@
+"""GPU parity: H-Net route / quantile / compact / EMA dechunk against the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from synthdata import gen_c0, gen_c1, gen_c2, gen_c2_stage2_inputs, gen_c2_backproj
+from tests.helpers import to_dev, to_np, row_rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    import byte_level_lm_amd as B
+    B.lib()
+    return B
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ragged(rng, lengths, d, dtype):
+    torch = _torch()
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    N = int(off[-1])
+    q = rng.standard_normal((N, d)).astype(np.float32)
+    k = rng.standard_normal((N, d)).astype(np.float32)
+    h = rng.standard_normal((N, d)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        from synthdata import bf16_round
+        q, k, h = bf16_round(q), bf16_round(k), bf16_round(h)
+    return off, q, k, h
+
+
+def _check_route(ops, q, k, off, dtype, threshold=0.5):
+    p, b, tau = ops.route(to_dev(q, dtype), to_dev(k, dtype), to_dev(off), threshold=threshold)
+    p_g, b_g = to_np(p), to_np(b).astype(bool)
+    p_o = oracle.route(q, k, off)
+    assert np.max(np.abs(p_g - p_o)) < 5e-6
+    assert np.all(p_g[off[:-1][np.diff(off) > 0]] == 1.0)
+    keep = np.abs(p_o - threshold) > 1e-5
+    assert np.array_equal(b_g[keep], oracle.boundary_mask(p_o, threshold)[keep])
+    assert float(to_np(tau)[0]) == np.float32(threshold)
+    return p_g, b_g
+
+
+def test_route_c0_fp32(ops):
+    torch = _torch()
+    c = gen_c0()
+    say("route C0 fp32", c["q"].shape)
+    _check_route(ops, c["q"], c["k"], c["offsets"], torch.float32)
+
+
+@pytest.mark.parametrize("d", [8, 64, 512, 768])
+def test_route_ragged_bf16(ops, d):
+    torch = _torch()
+    rng = np.random.default_rng(100 + d)
+    off, q, k, _ = _ragged(rng, [1, 0, 37, 300, 0, 1025, 2], d, torch.bfloat16)
+    say("route ragged bf16 d", d, "N", off[-1])
+    _check_route(ops, q, k, off, torch.bfloat16)
+
+
+def test_route_zero_rows_and_nan(ops):
+    torch = _torch()
+    q = np.zeros((6, 8), np.float32); k = np.zeros((6, 8), np.float32)
+    q[2] = 1.0; k[1] = 1.0                     # p_2: parallel -> 0
+    q[3, 0] = np.nan                           # NaN -> b = 0
+    off = np.array([0, 6], np.int64)
+    p, b, _ = ops.route(to_dev(q), to_dev(k), to_dev(off), threshold=0.5)
+    p, b = to_np(p), to_np(b)
+    assert p[0] == 1.0 and p[1] == 0.5 and p[2] == 0.0 and np.isnan(p[3]) and b[3] == 0
+    assert p[4] == 0.5 and b[4] == 1
+
+
+def test_route_quantile_c1(ops):
+    torch = _torch()
+    c = gen_c1(nseq=6, d=512, min_events=3, max_events=40)
+    say("route quantile C1 N", c["offsets"][-1])
+    p, b, tau = ops.route(to_dev(c["q"], torch.bfloat16), to_dev(c["k"], torch.bfloat16),
+                          to_dev(c["offsets"]), quantile=0.75)
+    p_g, b_g, tau_g = to_np(p), to_np(b).astype(bool), float(to_np(tau)[0])
+    n = len(p_g)
+    assert tau_g == np.sort(p_g)[int(np.floor(0.75 * (n - 1)))]  # exact order statistic
+    assert np.array_equal(b_g, p_g >= np.float32(tau_g))
+    p_o = oracle.route(c["q"], c["k"], c["offsets"])
+    assert abs(tau_g - oracle.stage_quantile(p_o, 0.75)) < 1e-5
+    assert abs(b_g.mean() - 0.25) < 0.01
+
+
+def test_route_quantile_extremes(ops):
+    torch = _torch()
+    rng = np.random.default_rng(7)
+    off, q, k, _ = _ragged(rng, [50, 70], 16, torch.float32)
+    for qt in (0.0, 1.0):
+        p, b, tau = ops.route(to_dev(q), to_dev(k), to_dev(off), quantile=qt)
+        p_g = to_np(p)
+        want = p_g.min() if qt == 0.0 else p_g.max()
+        assert float(to_np(tau)[0]) == want
+
+
+def _compact_check(ops, b, p, rows, off, dtype, capacity=None):
+    idx, coff, z, P, st = ops.compact(to_dev(b.astype(np.uint8)), to_dev(off), rows=to_dev(rows, dtype),
+                                      p=to_dev(p.astype(np.float32)), capacity=capacity)
+    i_o, c_o, z_o, P_o = oracle.compact(b, p.astype(np.float32), rows, off)
+    M = len(i_o)
+    cap = len(b) if capacity is None else capacity
+    m = min(M, cap)
+    assert np.array_equal(to_np(coff), c_o)
+    assert np.array_equal(to_np(idx)[:m], i_o[:m])
+    assert np.array_equal(to_np(z)[:m], z_o[:m])
+    assert np.array_equal(to_np(P)[:m], P_o[:m])
+    return idx, coff, z, P, st
+
+
+def test_compact_matches_oracle_bitexact(ops):
+    torch = _torch()
+    rng = np.random.default_rng(11)
+    off, q, k, h = _ragged(rng, [5000, 1, 0, 4096, 3, 8191, 17], 64, torch.bfloat16)
+    p, b = _check_route(ops, q, k, off, torch.bfloat16)
+    say("compact N", off[-1], "M", b.sum())
+    _, _, _, _, st = _compact_check(ops, b, p, h, off, torch.bfloat16)
+    assert int(to_np(st)[0]) == 0
+
+
+def test_compact_capacity_overflow_sets_status(ops):
+    torch = _torch()
+    rng = np.random.default_rng(12)
+    off = np.array([0, 300, 1000], np.int64)
+    b = rng.random(1000) < 0.5
+    p = rng.random(1000).astype(np.float32)
+    h = rng.standard_normal((1000, 16)).astype(np.float32)
+    cap = int(b.sum()) - 5
+    _, _, _, _, st = _compact_check(ops, b, p, h, off, torch.float32, capacity=cap)
+    assert int(to_np(st)[0]) & 1
+
+
+def test_compact_edges_no_start_boundary_and_empty(ops):
+    torch = _torch()
+    off = np.array([0, 0, 10, 10, 25, 25], np.int64)
+    b = np.zeros(25, bool); b[[3, 4, 12, 24]] = True  # sequence 1 has no boundary at its start
+    p = np.linspace(0, 1, 25).astype(np.float32)
+    h = np.arange(25 * 8, dtype=np.float32).reshape(25, 8)
+    _compact_check(ops, b, p, h, off, torch.float32)
+    # no boundary at all
+    _compact_check(ops, np.zeros(25, bool), p, h, off, torch.float32)
+
+
+def _dechunk_check(ops, z, P, idx, coff, off, dtype, tol):
+    N = int(off[-1])
+    out = ops.dechunk_ema(to_dev(z, dtype), to_dev(P.astype(np.float32)), to_dev(idx.astype(np.int32)),
+                          to_dev(coff), to_dev(off), N)
+    ref = oracle.dechunk_ema(z, P.astype(np.float32), idx, coff, off)
+    err = row_rel_err(to_np(out), ref)
+    assert err < tol, err
+    return out
+
+
+@pytest.mark.parametrize("dtname,d", [("f32", 64), ("bf16", 512), ("bf16", 768), ("f32", 8)])
+def test_dechunk_matches_oracle(ops, dtname, d):
+    torch = _torch()
+    dtype = torch.float32 if dtname == "f32" else torch.bfloat16
+    rng = np.random.default_rng(20 + d)
+    off, q, k, h = _ragged(rng, [3000, 1, 0, 5000, 64], d, dtype)
+    p, b = _check_route(ops, q, k, off, dtype)
+    idx, coff, z, P, _ = ops.compact(to_dev(b.astype(np.uint8)), to_dev(off), rows=to_dev(h, dtype),
+                                     p=to_dev(p))
+    M = int(to_np(coff)[-1])
+    say("dechunk", dtname, d, "N", off[-1], "M", M)
+    _dechunk_check(ops, to_np(z)[:M], to_np(P)[:M], to_np(idx)[:M].astype(np.int64), to_np(coff), off,
+                   dtype, 1e-4 if dtname == "f32" else 2e-2)
+
+
+def test_dechunk_identity_when_P_is_one(ops):
+    torch = _torch()
+    rng = np.random.default_rng(31)
+    for dtype in (torch.float32, torch.bfloat16):
+        off = np.array([0, 17, 17, 4000, 9001], np.int64)
+        N = 9001
+        rows = rng.standard_normal((N, 32)).astype(np.float32)
+        rows_t = to_dev(rows, dtype)
+        idx = np.arange(N, dtype=np.int32)
+        out = ops.dechunk_ema(rows_t, to_dev(np.ones(N, np.float32)), to_dev(idx), to_dev(off), to_dev(off), N)
+        assert torch.equal(out, rows_t)
+
+
+def test_dechunk_many_chunks_and_zero_prefix(ops):
+    torch = _torch()
+    rng = np.random.default_rng(32)
+    # > 4096 chunks so tiles hold several chunks; sequences that start without a boundary
+    off = np.array([0, 9000, 9000, 20000], np.int64)
+    b = rng.random(20000) < 0.6
+    b[0] = False; b[:5] = False; b[9000] = False; b[9000:9010] = False
+    P = rng.uniform(0.05, 1.0, 20000).astype(np.float32)
+    rows = rng.standard_normal((20000, 16)).astype(np.float32)
+    idx, coff, z, PP = oracle.compact(b, P, rows, off)
+    out = _dechunk_check(ops, z, PP, idx, coff, off, torch.float32, 1e-4)
+    assert np.all(to_np(out)[:5] == 0) and np.all(to_np(out)[9000:9010] == 0)
+    # no chunks at all: everything zero
+    e = np.zeros(0, np.int64)
+    o2 = ops.dechunk_ema(to_dev(np.zeros((1, 16), np.float32)), to_dev(np.zeros(1, np.float32)),
+                         to_dev(np.zeros(1, np.int32)), to_dev(np.zeros(4, np.int64)), to_dev(off), 20000)
+    assert float(o2.abs().max()) == 0.0
+
+
+def test_c2_two_stage_full_size(ops):
+    """The headline H-Net workload: 32 streams of 8192 bytes, two stages at the
+    0.75 score quantile each, both EMA scans back to full length (launch
+    configuration of bench.py)."""
+    torch = _torch()
+    bf = torch.bfloat16
+    c = gen_c2(fixed_T=8192)
+    off = c["offsets"]; N = int(off[-1])
+    say("C2@8192 generated N", N)
+    p1, b1, tau1 = ops.route(to_dev(c["q"], bf), to_dev(c["k"], bf), to_dev(off), quantile=0.75)
+    p1g, b1g = to_np(p1), to_np(b1).astype(bool)
+    p1o = oracle.route(c["q"], c["k"], off)
+    assert np.max(np.abs(p1g - p1o)) < 5e-6
+    tau1g = float(to_np(tau1)[0])
+    assert tau1g == np.sort(p1g)[int(np.floor(0.75 * (N - 1)))]
+    assert abs(tau1g - oracle.stage_quantile(p1o, 0.75)) < 1e-5
+    idx1, coff1, z1, P1, st = ops.compact(b1, to_dev(off), rows=to_dev(c["h"], bf), p=p1)
+    i1o, c1o, z1o, P1o = oracle.compact(b1g, p1g, c["h"], off)
+    M1 = len(i1o)
+    assert np.array_equal(to_np(coff1), c1o) and np.array_equal(to_np(idx1)[:M1], i1o)
+    assert np.array_equal(to_np(z1)[:M1], z1o) and np.array_equal(to_np(P1)[:M1], P1o)
+    say("stage 1 M1", M1, "ratio", M1 / N)
+    s2 = gen_c2_stage2_inputs(z1o, c)
+    p2, b2, tau2 = ops.route(to_dev(s2["q2"], bf), to_dev(s2["k2"], bf), coff1, quantile=0.75)
+    p2g, b2g = to_np(p2), to_np(b2).astype(bool)
+    p2o = oracle.route(s2["q2"], s2["k2"], c1o)
+    assert np.max(np.abs(p2g - p2o)) < 5e-6
+    idx2, coff2, z2, P2, _ = ops.compact(b2, coff1, rows=to_dev(s2["x2"], bf), p=p2)
+    i2o, c2o, z2o, P2o = oracle.compact(b2g, p2g, s2["x2"], c1o)
+    M2 = len(i2o)
+    assert np.array_equal(to_np(idx2)[:M2], i2o) and np.array_equal(to_np(z2)[:M2], z2o)
+    say("stage 2 M2", M2, "ratio", M2 / N)
+    assert 0.2 < M1 / N < 0.3 and 0.04 < M2 / N < 0.09
+    y2 = ops.dechunk_ema(z2, P2, idx2, coff2, coff1, M1)
+    y2o = oracle.dechunk_ema(z2o, P2o, i2o, c2o, c1o)
+    assert row_rel_err(to_np(y2), y2o) < 2e-2
+    y1 = gen_c2_backproj(to_np(y2), c)
+    out = ops.dechunk_ema(to_dev(y1, bf), P1, idx1, coff1, to_dev(off), N)
+    outo = oracle.dechunk_ema(y1, P1o, i1o, c1o, off)
+    assert row_rel_err(to_np(out), outo) < 2e-2
+    say("C2@8192 chain ok")
