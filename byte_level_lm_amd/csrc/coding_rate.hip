@@ -1,4 +1,4 @@
-// ByteFlow marginal coding rate Delta R_t on fp32 MFMA.
+// ByteFlow marginal coding rate Delta R_t on MFMA.
 //
 // ByteFlow paper page: "lossy coding rate" prerequisite, R(H) = 1/2 logdet(I +
 // (d/eps^2) H H^T); method step details, stage 2, Delta R_t = R(h_1..t) -
@@ -7,19 +7,26 @@
 // (scaled by sqrt(alpha)) and prefix matrix A_j = I_d + alpha sum_{i<j} H_i^T H_i,
 // the pivots of the block's rows are those of S_j = I_c + B_j A_j^{-1} B_j^T
 // (Woodbury; the incremental route the page's weakness analysis points to).
-// Every block is independent once A_j is known, so each gets one workgroup
-// that factors the (d'+c) x (d'+c) quasi-definite matrix
+// Every block is independent once A_j is known; each block matrix
 //     [ A_j   B_j^T ]            = L diag(+1 (d'), -1 (c)) L^T
 //     [ B_j   -I_c  ]
-// with a left-looking blocked signed Cholesky (32-wide panels): columns of the
-// A part subtract earlier panels as usual; columns of the S part add the A-part
-// panels and subtract the S-part panels.  The diagonal of the S part of L are
-// the pivots; Delta R = log(pivot).
+// is factored by a blocked signed Cholesky with 64-wide panels: columns of
+// the A part subtract earlier panels as usual; columns of the S part add the
+// A-part panels and subtract the S-part panels.  The diagonal of the S part
+// of L are the pivots; Delta R = log(pivot).
 //
-// Kernels: cr_gram_prefix (A_j for every block, one 32x32 tile per workgroup,
-// 4 waves split the rows), cr_factor (one workgroup per block matrix).
-// Workspace: nseq * nblk * ldm^2 fp32 (ldm = d' + c), the A part written by
-// the first kernel, the rest of L written by the second.
+// Launch sequence for a batch (all block matrices of all sequences at once):
+//   cr_gram_prefix  A_j for every block j (64x64 output tile per workgroup,
+//                   bf16 or fp32 MFMA over rows staged transposed in LDS)
+//   cr_init_sdiag   identity into the S-part diagonal tiles
+//   for each panel k:
+//     cr_diag       factor the (already updated) 64x64 diagonal tile, log of
+//                   the S-part pivots, explicit inverse of the tile's factor
+//     cr_panel      one workgroup per 64x64 tile below it (XCD-aware order):
+//                   left-looking update over the earlier panels, X = acc L_kk^-T,
+//                   then the right-looking update of that row's diagonal tile
+// Workspace: nmat = nseq * nblk matrices of ldm^2 fp32 (ldm = d' + c), plus a
+// 64x64 inverse slot per matrix.
 #include <cmath>
 
 #include "common.h"
@@ -28,213 +35,447 @@ namespace bllm {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int NB = 64;  // panel width
 
 __device__ inline floatx16 mfma32(float a, float b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// C/D layout of v_mfma_f32_32x32x2f32: lane l, register r holds element
+// C/D layout of the 32x32 MFMAs: lane l, register r holds element
 // (row 8*(r/4) + 4*(l/32) + r%4, column l%32).
 __device__ inline int crow(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+__device__ inline floatx16 zero16() {
+  floatx16 z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
 struct CRGeom {
-  int T, d, dp, c, nblk, ldm;
+  int T, d, dp, c, nblk, ldm, nmat;
 };
 
+__device__ inline int block_rows(const CRGeom& g, int j) { return min(g.c, g.T - j * g.c); }
+__device__ inline int block_n(const CRGeom& g, int j) {
+  return g.dp + ((block_rows(g, j) + NB - 1) / NB) * NB;
+}
+
+// ------------------------------------------------------------------ Gram prefix
+
+template <int DT> struct GramLds;
+template <> struct GramLds<BLLM_BF16> { typedef uint16_t T; static constexpr int LD = 40; };
+template <> struct GramLds<BLLM_F32> { typedef float T; static constexpr int LD = 36; };
+
+// rows [r0, r0+32) (those < rend) of feature strip [f0, f0+64) -> s[feature][row]
+template <int DT>
+__device__ inline void stage_strip(const void* h, int64_t hrow0, int d, int r0, int rend, int f0,
+                                   typename GramLds<DT>::T* s) {
+  constexpr int LD = GramLds<DT>::LD;
+  const int t = threadIdx.x;
+  if (DT == BLLM_BF16) {
+    const int row = t >> 3, fc = (t & 7) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + row < rend && f0 + fc < d)
+      v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(h) + (hrow0 + r0 + row) * d + f0 + fc);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint16_t* sb = reinterpret_cast<uint16_t*>(s);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sb[(fc + 2 * e) * LD + row] = static_cast<uint16_t>(w[e] & 0xFFFFu);
+      sb[(fc + 2 * e + 1) * LD + row] = static_cast<uint16_t>(w[e] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = (t >> 4) + 16 * hh, fc = (t & 15) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r0 + row < rend && f0 + fc < d)
+        v = *reinterpret_cast<const float4*>(static_cast<const float*>(h) + (hrow0 + r0 + row) * d + f0 + fc);
+      float* sf = reinterpret_cast<float*>(s);
+      sf[(fc + 0) * LD + row] = v.x;
+      sf[(fc + 1) * LD + row] = v.y;
+      sf[(fc + 2) * LD + row] = v.z;
+      sf[(fc + 3) * LD + row] = v.w;
+    }
+  }
+}
+
+template <int DT>
+__device__ inline floatx16 gram_chunk(const typename GramLds<DT>::T* sI, const typename GramLds<DT>::T* sJ,
+                                      int wm, int wn, int lane, floatx16 acc) {
+  constexpr int LD = GramLds<DT>::LD;
+  if (DT == BLLM_BF16) {
+#pragma unroll
+    for (int k0 = 0; k0 < 32; k0 += 16) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(sI) +
+                                                        (32 * wm + (lane & 31)) * LD + k0 + 8 * (lane >> 5));
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(sJ) +
+                                                        (32 * wn + (lane & 31)) * LD + k0 + 8 * (lane >> 5));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+  } else {
+    const float* pa = reinterpret_cast<const float*>(sI) + (32 * wm + (lane & 31)) * LD + 16 * (lane >> 5);
+    const float* pb = reinterpret_cast<const float*>(sJ) + (32 * wn + (lane & 31)) * LD + 16 * (lane >> 5);
+#pragma unroll
+    for (int st = 0; st < 16; ++st) acc = mfma32(pa[st], pb[st], acc);
+  }
+  return acc;
+}
+
+// One 64x64 tile (I >= J) of A_j for all blocks j of one sequence; wave
+// (wm, wn) owns the 32x32 quadrant and keeps its running sum in registers.
 template <int DT>
 __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h, float* __restrict__ ws,
                                                       CRGeom g, float alpha) {
-  __shared__ float red[4][16][64];
+  typedef typename GramLds<DT>::T E;
+  constexpr int LD = GramLds<DT>::LD;
+  __shared__ __attribute__((aligned(16))) E sI[64 * LD];
+  __shared__ __attribute__((aligned(16))) E sJ[64 * LD];
   const int s = blockIdx.y;
   int t = blockIdx.x, I = 0;
   while (t > I) { t -= I + 1; ++I; }
   const int J = t;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int colA = 32 * I + (lane & 31), colB = 32 * J + (lane & 31);
-  const bool okA = colA < g.d, okB = colB < g.d;
+  const int wm = w >> 1, wn = w & 1;
   const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
-  const int64_t hbase = static_cast<int64_t>(s) * g.T * g.d;
-  floatx16 acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int64_t hrow0 = static_cast<int64_t>(s) * g.T;
+  floatx16 acc = zero16();
   for (int j = 0; j < g.nblk; ++j) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[w][r][lane] = acc[r];
-    __syncthreads();
     float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 4 * w + q;
-      const float v = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
-      const int row = 32 * I + crow(r, lane), col = 32 * J + (lane & 31);
-      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * v;
+    for (int r = 0; r < 16; ++r) {
+      const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
+      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
     }
-    __syncthreads();
     if (j == g.nblk - 1) break;
     const int rbeg = j * g.c, rend = min(rbeg + g.c, g.T);
-    for (int r = rbeg + 2 * w; r < rend; r += 8) {
-      const int row = r + (lane >> 5);
-      float a = 0.f, b = 0.f;
-      if (row < rend) {
-        if (okA) a = load_elem(h, hbase + static_cast<int64_t>(row) * g.d + colA, DT);
-        if (okB) b = load_elem(h, hbase + static_cast<int64_t>(row) * g.d + colB, DT);
-      }
-      acc = mfma32(a, b, acc);
+    for (int r0 = rbeg; r0 < rend; r0 += 32) {
+      __syncthreads();
+      stage_strip<DT>(h, hrow0, g.d, r0, rend, 64 * I, sI);
+      if (I != J) stage_strip<DT>(h, hrow0, g.d, r0, rend, 64 * J, sJ);
+      __syncthreads();
+      acc = gram_chunk<DT>(sI, I != J ? sJ : sI, wm, wn, lane, acc);
     }
   }
 }
 
+// identity into the 64x64 diagonal tiles of the S part
+__global__ __launch_bounds__(256) void cr_init_sdiag(float* __restrict__ ws, CRGeom g) {
+  const int m = blockIdx.x;
+  float* Mx = ws + static_cast<int64_t>(m) * g.ldm * g.ldm;
+  for (int q = g.dp; q < g.ldm; q += NB)
+    for (int e = threadIdx.x; e < NB * NB; e += blockDim.x) {
+      const int r = e >> 6, cc = e & 63;
+      Mx[static_cast<int64_t>(q + r) * g.ldm + q + cc] = r == cc ? 1.f : 0.f;
+    }
+}
+
+// ------------------------------------------------------------------ diagonal tile
+
+// One wave per block matrix: Cholesky of the 64x64 diagonal tile of panel k,
+// the logs of its S-part pivots into dR, and the inverse of the tile's factor.
+// 2x2 blocks of 32: lane i holds row i (a = columns 0..31, b = columns 32..63).
+//   1. eliminate columns 0..31 over all 64 rows  -> L11 (lanes 0..31), L21 (lanes 32..63)
+//   2. D22 -= L21 L21^T                           (lanes 32..63, L21 rows from LDS)
+//   3. eliminate columns 32..63 of D22            -> L22 (lanes 32..63)
+//   4. inverse [[L11^-1, 0], [-L22^-1 L21 L11^-1, L22^-1]] by column solves
+// Pivots are broadcast with readlane; every loop has a fixed trip count of 32.
+__global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __restrict__ linv,
+                                              float* __restrict__ dR, int32_t* __restrict__ status,
+                                              CRGeom g, int k) {
+  __shared__ float sL[NB][33];   // rows of [L11; L21] (32 columns), later L22 in rows 32..63
+  __shared__ float sT[32][33];   // L11^-1 (row-major), then Z = L21 L11^-1
+  const int m = blockIdx.x;
+  const int s = m / g.nblk, j = m % g.nblk;
+  if (NB * k >= block_n(g, j)) return;
+  const int cj = block_rows(g, j);
+  const int i = threadIdx.x;
+  const bool hi = i >= 32;
+  const int ih = i & 31;
+  const float* D = ws + static_cast<int64_t>(m) * g.ldm * g.ldm + static_cast<int64_t>(NB * k) * g.ldm + NB * k;
+  float a[32], b[32];
+  {
+    const float* Dr = D + static_cast<int64_t>(i) * g.ldm;
+#pragma unroll
+    for (int q = 0; q < 32; q += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(Dr + q);
+      a[q] = v.x; a[q + 1] = v.y; a[q + 2] = v.z; a[q + 3] = v.w;
+      const float4 u = *reinterpret_cast<const float4*>(Dr + 32 + q);
+      b[q] = u.x; b[q + 1] = u.y; b[q + 2] = u.z; b[q + 3] = u.w;
+    }
+  }
+  bool bad = false;
+  float piv = 0.f;  // this lane's diagonal entry of L
+  // 1. columns 0..31 (rows i >= kk of lanes 0..31, all of lanes 32..63)
+#pragma unroll
+  for (int jj = 0; jj < 32; ++jj) {
+    const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[jj]), jj));
+    bad |= !(pv > 0.f);
+    const float l = sqrtf(pv);
+    if (i == jj) { a[jj] = l; piv = l; }
+    else if (i > jj) a[jj] = a[jj] / l;
+#pragma unroll
+    for (int kk = jj + 1; kk < 32; ++kk) {
+      const float lk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[jj]), kk));
+      if (i >= kk) a[kk] = fmaf(-a[jj], lk, a[kk]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 32; ++q) sL[i][q] = (hi || q <= i) ? a[q] : 0.f;
+  __syncthreads();
+  // 2. D22 -= L21 L21^T
+  if (hi) {
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      float acc = b[q];
+#pragma unroll
+      for (int p = 0; p < 32; ++p) acc = fmaf(-a[p], sL[32 + q][p], acc);
+      b[q] = acc;
+    }
+  }
+  // 3. columns 32..63 on lanes 32..63
+#pragma unroll
+  for (int jj = 0; jj < 32; ++jj) {
+    const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b[jj]), 32 + jj));
+    bad |= !(pv > 0.f);
+    const float l = sqrtf(pv);
+    if (ih == jj) { b[jj] = l; if (hi) piv = l; }
+    else if (ih > jj) b[jj] = b[jj] / l;
+#pragma unroll
+    for (int kk = jj + 1; kk < 32; ++kk) {
+      const float lk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b[jj]), 32 + kk));
+      if (ih >= kk) b[kk] = fmaf(-b[jj], lk, b[kk]);
+    }
+  }
+  if (bad && status && i == 0) atomicOr(status, BLLM_S_NONFINITE);
+  __syncthreads();
+  if (hi) {
+#pragma unroll
+    for (int q = 0; q < 32; ++q) sL[i][q] = q <= ih ? b[q] : 0.f;  // rows 32..63 now hold L22
+  }
+  // 4a. lanes 0..31: column i of L11^-1 -> sT[r][i]; lanes 32..63: column ih of L22^-1
+  float x[32];
+  {
+    const int base = hi ? 32 : 0;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      float acc = r == ih ? 1.f : 0.f;
+#pragma unroll
+      for (int p = 0; p < r; ++p) acc = fmaf(-sL[base + r][p], x[p], acc);
+      x[r] = acc / sL[base + r][r];
+    }
+  }
+  float* Li = linv + static_cast<int64_t>(m) * NB * NB;
+  if (!hi) {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      sT[r][i] = x[r];
+      Li[r * NB + i] = x[r];
+      Li[r * NB + 32 + i] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) Li[(32 + r) * NB + 32 + ih] = x[r];
+  }
+  __syncthreads();
+  // 4b. lanes 32..63: row ih of Z = L21 L11^-1 (L21 row still in a[])
+  float z[32];
+  if (hi) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      float acc = 0.f;
+#pragma unroll
+      for (int p = 0; p < 32; ++p) acc = fmaf(a[p], sT[p][c], acc);
+      z[c] = acc;
+    }
+  }
+  __syncthreads();
+  if (hi) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) sT[ih][c] = z[c];
+  }
+  __syncthreads();
+  // 4c. lanes 32..63: column ih of Y with L22 Y = -Z  -> Linv[32 + r][ih]
+  if (hi) {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      float acc = -sT[r][ih];
+#pragma unroll
+      for (int p = 0; p < r; ++p) acc = fmaf(-sL[32 + r][p], x[p], acc);
+      x[r] = acc / sL[32 + r][r];
+      Li[(32 + r) * NB + ih] = x[r];
+    }
+  }
+  // hardware log2 scaled by ln 2 (about 1 ulp); no out-of-line call
+  if (NB * k >= g.dp) {
+    const int rr = NB * k + i - g.dp;
+    if (rr < cj) dR[static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c + rr] = __logf(piv);
+  }
+}
+
+// ------------------------------------------------------------------ panel tiles
+
 template <int DT>
-__device__ inline float orig_elem(const void* h, const float* Mx, const CRGeom& g, int s, int r0,
-                                  int cj, float salpha, int row, int col) {
-  if (col >= g.dp) return row == col ? 1.f : 0.f;
+__device__ inline float orig_offdiag(const void* h, const float* Mx, const CRGeom& g, int64_t hrow0,
+                                     int cj, float salpha, int row, int col) {
+  if (col >= g.dp) return 0.f;  // S part below its diagonal tiles
   if (row < g.dp) return Mx[static_cast<int64_t>(row) * g.ldm + col];
   const int rr = row - g.dp;
   if (rr >= cj || col >= g.d) return 0.f;
-  return salpha * load_elem(h, (static_cast<int64_t>(s) * g.T + r0 + rr) * g.d + col, DT);
+  return salpha * load_elem(h, (hrow0 + rr) * g.d + col, DT);
 }
 
-// acc = orig(tile i, panel k) -/+ sum over earlier panels kk of L[i,kk] L[k,kk]^T
+constexpr int PLD = 36;  // LDS row stride (floats) of 32-column chunks
+constexpr int XLD = 68;  // LDS row stride of 64-column tiles
+
+// 64x64 tile (i, k), i > k, of every block matrix.  Grid: ceil(nmat/8)*8*ntk
+// blocks; block b runs on XCD b%8 and all tiles of one matrix share an XCD so
+// the panel rows L[k, :] they all read stay in that XCD's L2.
 template <int DT>
-__device__ inline floatx16 panel_update(const void* h, const float* Mx, const CRGeom& g, int s,
-                                        int r0, int cj, float salpha, int i, int k, int ntA,
-                                        int lane) {
+__global__ __launch_bounds__(256) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
+                                                const float* __restrict__ linv, CRGeom g, float salpha,
+                                                int k, int ntk) {
+  __shared__ __attribute__((aligned(16))) float smem[2 * 64 * XLD];
+  float* sA = smem;              // [64][PLD]  rows of tile i, current 32-column chunk
+  float* sB = smem + 64 * PLD;   // [64][PLD]  rows of tile k
+  float* sX = smem;              // [64][XLD]  reused after the update loop
+  float* sLi = smem + 64 * XLD;  // [64][XLD]
+  const int b = blockIdx.x;
+  const int xcd = b & 7, q = b >> 3;
+  const int m = (q / ntk) * 8 + xcd;
+  const int i = k + 1 + q % ntk;
+  if (m >= g.nmat) return;
+  const int j = m % g.nblk;
+  if (NB * i >= block_n(g, j)) return;
+  const int s = m / g.nblk;
+  const int cj = block_rows(g, j);
+  const int64_t hrow0 = static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c;
+  float* Mx = ws + static_cast<int64_t>(m) * g.ldm * g.ldm;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int wm = w >> 1, wn = w & 1;
+  const int row0 = NB * i + 32 * wm, col0 = NB * k + 32 * wn;
   floatx16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r)
-    acc[r] = orig_elem<DT>(h, Mx, g, s, r0, cj, salpha, 32 * i + crow(r, lane), 32 * k + (lane & 31));
-  const bool panelS = k >= ntA;
-  const float* ra = Mx + static_cast<int64_t>(32 * i + (lane & 31)) * g.ldm + 16 * (lane >> 5);
-  const float* rb = Mx + static_cast<int64_t>(32 * k + (lane & 31)) * g.ldm + 16 * (lane >> 5);
-  for (int kk = 0; kk < k; ++kk) {
-    const float sg = (panelS && kk < ntA) ? 1.f : -1.f;
-    float a[16], b[16];
+    acc[r] = orig_offdiag<DT>(h, Mx, g, hrow0, cj, salpha, row0 + crow(r, lane), col0 + (lane & 31));
+  const bool panelS = NB * k >= g.dp;
+  // left-looking update over the 2k earlier 32-column chunks, loads of chunk
+  // c+1 in flight while chunk c runs on the MFMAs
+  const int nch = 2 * k;
+  const int lr = tid >> 3, lc = (tid & 7) * 4;  // loader: rows lr, lr+32; columns lc..lc+3
+  const float* gA = Mx + static_cast<int64_t>(NB * i + lr) * g.ldm + lc;
+  const float* gB = Mx + static_cast<int64_t>(NB * k + lr) * g.ldm + lc;
+  const int64_t r32 = 32 * static_cast<int64_t>(g.ldm);
+  float4 pa0, pa1, pb0, pb1;
+  if (nch > 0) {
+    pa0 = *reinterpret_cast<const float4*>(gA);
+    pa1 = *reinterpret_cast<const float4*>(gA + r32);
+    pb0 = *reinterpret_cast<const float4*>(gB);
+    pb1 = *reinterpret_cast<const float4*>(gB + r32);
+  }
+  for (int ch = 0; ch < nch; ++ch) {
+    __syncthreads();
+    *reinterpret_cast<float4*>(sA + lr * PLD + lc) = pa0;
+    *reinterpret_cast<float4*>(sA + (lr + 32) * PLD + lc) = pa1;
+    *reinterpret_cast<float4*>(sB + lr * PLD + lc) = pb0;
+    *reinterpret_cast<float4*>(sB + (lr + 32) * PLD + lc) = pb1;
+    __syncthreads();
+    if (ch + 1 < nch) {
+      const int co = 32 * (ch + 1);
+      pa0 = *reinterpret_cast<const float4*>(gA + co);
+      pa1 = *reinterpret_cast<const float4*>(gA + r32 + co);
+      pb0 = *reinterpret_cast<const float4*>(gB + co);
+      pb1 = *reinterpret_cast<const float4*>(gB + r32 + co);
+    }
+    const float sg = (panelS && 32 * ch < g.dp) ? 1.f : -1.f;
+    const float* pa = sA + (32 * wm + (lane & 31)) * PLD + 16 * (lane >> 5);
+    const float* pb = sB + (32 * wn + (lane & 31)) * PLD + 16 * (lane >> 5);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float4 x = *reinterpret_cast<const float4*>(ra + 32 * kk + 4 * v);
-      const float4 y = *reinterpret_cast<const float4*>(rb + 32 * kk + 4 * v);
-      a[4 * v] = sg * x.x; a[4 * v + 1] = sg * x.y; a[4 * v + 2] = sg * x.z; a[4 * v + 3] = sg * x.w;
-      b[4 * v] = y.x; b[4 * v + 1] = y.y; b[4 * v + 2] = y.z; b[4 * v + 3] = y.w;
+    for (int st = 0; st < 16; ++st) acc = mfma32(sg * pa[st], pb[st], acc);
+  }
+  // X = acc * Linv^T
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sX[(32 * wm + crow(r, lane)) * XLD + 32 * wn + (lane & 31)] = acc[r];
+  const float* Li = linv + static_cast<int64_t>(m) * NB * NB;
+  for (int e = tid; e < NB * NB / 4; e += blockDim.x) {
+    const int r = e >> 4, cc = (e & 15) * 4;
+    *reinterpret_cast<float4*>(sLi + r * XLD + cc) = *reinterpret_cast<const float4*>(Li + r * NB + cc);
+  }
+  __syncthreads();
+  floatx16 x = zero16();
+#pragma unroll
+  for (int mb = 0; mb < NB; mb += 32) {
+    const float* pa = sX + (32 * wm + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
+    const float* pb = sLi + (32 * wn + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
+#pragma unroll
+    for (int st = 0; st < 16; ++st) x = mfma32(pa[st], pb[st], x);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    Mx[static_cast<int64_t>(row0 + crow(r, lane)) * g.ldm + col0 + (lane & 31)] = x[r];
+  // right-looking update of this row's diagonal tile: D_i -/+= X X^T
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sX[(32 * wm + crow(r, lane)) * XLD + 32 * wn + (lane & 31)] = x[r];
+  __syncthreads();
+  if (wm >= wn) {
+    const float sg = (NB * i >= g.dp && !panelS) ? 1.f : -1.f;
+    float* D = Mx + static_cast<int64_t>(NB * i + 32 * wm) * g.ldm + NB * i + 32 * wn;
+    floatx16 dd;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dd[r] = D[static_cast<int64_t>(crow(r, lane)) * g.ldm + (lane & 31)];
+#pragma unroll
+    for (int mb = 0; mb < NB; mb += 32) {
+      const float* pa = sX + (32 * wm + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
+      const float* pb = sX + (32 * wn + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
+#pragma unroll
+      for (int st = 0; st < 16; ++st) dd = mfma32(sg * pa[st], pb[st], dd);
     }
 #pragma unroll
-    for (int st = 0; st < 16; ++st) acc = mfma32(a[st], b[st], acc);
+    for (int r = 0; r < 16; ++r) D[static_cast<int64_t>(crow(r, lane)) * g.ldm + (lane & 31)] = dd[r];
   }
-  return acc;
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) void cr_factor(const void* __restrict__ h, float* __restrict__ ws,
-                                                 float* __restrict__ dR, int32_t* __restrict__ status,
-                                                 CRGeom g, float salpha) {
-  __shared__ float sdiag[32][33];
-  __shared__ float slinv[32][33];
-  __shared__ float sstage[4][32][33];
-  __shared__ int sbad;
-  const int j = blockIdx.x, s = blockIdx.y;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r0 = j * g.c;
-  const int cj = min(g.c, g.T - r0);
-  const int n = g.dp + ((cj + 31) & ~31);
-  const int nt = n >> 5, ntA = g.dp >> 5;
-  float* Mx = ws + (static_cast<int64_t>(s) * g.nblk + j) * static_cast<int64_t>(g.ldm) * g.ldm;
-  if (threadIdx.x == 0) sbad = 0;
-  for (int k = 0; k < nt; ++k) {
-    // phase A: wave w updates tile k + w (wave 0 holds the diagonal tile)
-    floatx16 acc0;
-    const int i0 = k + w;
-    if (i0 < nt) acc0 = panel_update<DT>(h, Mx, g, s, r0, cj, salpha, i0, k, ntA, lane);
-    if (w == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sdiag[crow(r, lane)][lane & 31] = acc0[r];
-    }
-    __syncthreads();
-    if (w == 0) {
-      // unblocked Cholesky of the 32x32 diagonal tile; lane i < 32 owns row i
-      float a[32];
-      const int me = lane & 31;
-#pragma unroll
-      for (int m = 0; m < 32; ++m) a[m] = m <= me ? sdiag[me][m] : 0.f;
-      bool bad = false;
-#pragma unroll
-      for (int jj = 0; jj < 32; ++jj) {
-        const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[jj]), jj));
-        bad |= !(pv > 0.f);
-        const float l = sqrtf(pv);
-        const float inv = 1.f / l;
-        if (me == jj) a[jj] = l;
-        else if (me > jj) a[jj] *= inv;
-#pragma unroll
-        for (int kk = jj + 1; kk < 32; ++kk) {
-          const float lk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[jj]), kk));
-          if (me >= kk) a[kk] = fmaf(-a[jj], lk, a[kk]);
-        }
-      }
-      if (lane < 32) {
-#pragma unroll
-        for (int m = 0; m < 32; ++m) sdiag[me][m] = m <= me ? a[m] : 0.f;
-        if (k >= ntA) {
-          const int rr = 32 * k + me - g.dp;
-          if (rr < cj) dR[static_cast<int64_t>(s) * g.T + r0 + rr] = logf(a[me]);
-        }
-      }
-      if (bad && lane == 0) sbad = 1;
-    }
-    __syncthreads();
-    if (w == 0 && lane < 32) {
-      // column `lane` of the inverse of the diagonal tile's factor
-      const int m = lane;
-      float x[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        float acc = (i == m) ? 1.f : 0.f;
-#pragma unroll
-        for (int p = 0; p < i; ++p) acc = fmaf(-sdiag[i][p], x[p], acc);
-        x[i] = acc / sdiag[i][i];
-      }
-#pragma unroll
-      for (int i = 0; i < 32; ++i) slinv[i][m] = x[i];
-    }
-    __syncthreads();
-    // phase B: X = acc * Linv^T for every tile below the diagonal
-#pragma unroll 1
-    for (int q = 0;; ++q) {
-      const int i = k + w + 4 * q;
-      if (i >= nt) break;
-      if (i == k) continue;
-      floatx16 acc = q == 0 ? acc0 : panel_update<DT>(h, Mx, g, s, r0, cj, salpha, i, k, ntA, lane);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sstage[w][crow(r, lane)][lane & 31] = acc[r];
-      float a[16], b[16];
-#pragma unroll
-      for (int st = 0; st < 16; ++st) {
-        a[st] = sstage[w][lane & 31][16 * (lane >> 5) + st];
-        b[st] = slinv[lane & 31][16 * (lane >> 5) + st];
-      }
-      floatx16 x;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = 0.f;
-#pragma unroll
-      for (int st = 0; st < 16; ++st) x = mfma32(a[st], b[st], x);
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        Mx[static_cast<int64_t>(32 * i + crow(r, lane)) * g.ldm + 32 * k + (lane & 31)] = x[r];
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0 && sbad && status) atomicOr(status, BLLM_S_NONFINITE);
-}
-
-CRGeom cr_geometry(int64_t T, int64_t d) {
+CRGeom cr_geometry(int64_t nseq, int64_t T, int64_t d) {
   CRGeom g;
   g.T = static_cast<int>(T);
   g.d = static_cast<int>(d);
-  g.dp = static_cast<int>((d + 31) / 32 * 32);
-  int c = (g.dp / 2 + 31) / 32 * 32;
-  c = c < 32 ? 32 : (c > 128 ? 128 : c);
+  g.dp = static_cast<int>((d + NB - 1) / NB * NB);
+  int c = (g.dp / 2 + NB - 1) / NB * NB;
+  c = c < NB ? NB : (c > 128 ? 128 : c);
   g.c = c;
   g.nblk = static_cast<int>((T + c - 1) / c);
   g.ldm = g.dp + c;
+  g.nmat = static_cast<int>(nseq) * g.nblk;
   return g;
+}
+
+size_t cr_ws_bytes(const CRGeom& g) {
+  return static_cast<size_t>(g.nmat) * (static_cast<size_t>(g.ldm) * g.ldm + NB * NB) * 4 + 256;
+}
+
+template <int DT>
+void cr_launch(const void* h, const CRGeom& g, int nseq, double alpha, float* dR, int32_t* status,
+               float* ws, hipStream_t st) {
+  float* linv = ws + static_cast<int64_t>(g.nmat) * g.ldm * g.ldm;
+  const int nt = g.dp / NB;
+  hipLaunchKernelGGL(cr_gram_prefix<DT>, dim3(nt * (nt + 1) / 2, nseq), dim3(256), 0, st, h, ws, g,
+                     static_cast<float>(alpha));
+  hipLaunchKernelGGL(cr_init_sdiag, dim3(g.nmat), dim3(256), 0, st, ws, g);
+  const int npan = g.ldm / NB;
+  const float salpha = static_cast<float>(std::sqrt(alpha));
+  for (int k = 0; k < npan; ++k) {
+    hipLaunchKernelGGL(cr_diag, dim3(g.nmat), dim3(64), 0, st, ws, linv, dR, status, g, k);
+    const int ntk = npan - k - 1;
+    if (ntk > 0) {
+      const unsigned grid = static_cast<unsigned>((g.nmat + 7) / 8 * 8 * ntk);
+      hipLaunchKernelGGL(cr_panel<DT>, dim3(grid), dim3(256), 0, st, h, ws, linv, g, salpha, k, ntk);
+    }
+  }
 }
 
 }  // namespace
@@ -244,8 +485,7 @@ using namespace bllm;
 
 extern "C" size_t bllm_coding_rate_workspace(int64_t nseq, int64_t T, int64_t d) {
   if (nseq < 1 || T < 1 || d < 1) return 0;
-  const CRGeom g = cr_geometry(T, d);
-  return static_cast<size_t>(nseq) * g.nblk * static_cast<size_t>(g.ldm) * g.ldm * 4 + 256;
+  return cr_ws_bytes(cr_geometry(nseq, T, d));
 }
 
 extern "C" int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d,
@@ -254,22 +494,15 @@ extern "C" int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t 
   if (!h || !dR_out || nseq < 1 || T < 1 || d < 1 || !(eps2 > 0.0)) return BLLM_E_INVAL;
   if (!valid_dtype(dtype)) return BLLM_E_NOTSUP;
   if (d > 640 || nseq > 65535 || T > (int64_t(1) << 24)) return BLLM_E_NOTSUP;
-  if (!ws || ws_bytes < bllm_coding_rate_workspace(nseq, T, d) || !aligned16(ws)) return BLLM_E_WS;
-  const CRGeom g = cr_geometry(T, d);
+  if ((d * elem_size(dtype)) % 16 != 0 || !aligned16(h)) return BLLM_E_NOTSUP;
+  const CRGeom g = cr_geometry(nseq, T, d);
+  if (static_cast<int64_t>(g.nmat) * g.nblk > (int64_t(1) << 31)) return BLLM_E_NOTSUP;
+  if (!ws || ws_bytes < cr_ws_bytes(g) || !aligned16(ws)) return BLLM_E_WS;
   const double alpha = static_cast<double>(d) / eps2;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int nt = g.dp / 32;
-  const dim3 ggrid(static_cast<unsigned>(nt * (nt + 1) / 2), static_cast<unsigned>(nseq));
-  const dim3 fgrid(static_cast<unsigned>(g.nblk), static_cast<unsigned>(nseq));
-  float* w = static_cast<float*>(ws);
-  if (dtype == BLLM_F32) {
-    hipLaunchKernelGGL(cr_gram_prefix<BLLM_F32>, ggrid, dim3(256), 0, st, h, w, g, static_cast<float>(alpha));
-    hipLaunchKernelGGL(cr_factor<BLLM_F32>, fgrid, dim3(256), 0, st, h, w, dR_out, status, g,
-                       static_cast<float>(std::sqrt(alpha)));
-  } else {
-    hipLaunchKernelGGL(cr_gram_prefix<BLLM_BF16>, ggrid, dim3(256), 0, st, h, w, g, static_cast<float>(alpha));
-    hipLaunchKernelGGL(cr_factor<BLLM_BF16>, fgrid, dim3(256), 0, st, h, w, dR_out, status, g,
-                       static_cast<float>(std::sqrt(alpha)));
-  }
+  if (dtype == BLLM_F32)
+    cr_launch<BLLM_F32>(h, g, static_cast<int>(nseq), alpha, dR_out, status, static_cast<float*>(ws), st);
+  else
+    cr_launch<BLLM_BF16>(h, g, static_cast<int>(nseq), alpha, dR_out, status, static_cast<float*>(ws), st);
   return launch_status();
 }
