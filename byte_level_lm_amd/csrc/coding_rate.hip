@@ -162,6 +162,82 @@ __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h
   }
 }
 
+// bf16 input: the same 64x64 prefix tiles, one whole block of c <= 128 rows
+// per iteration.  The next block's rows are in flight in registers while the
+// current one runs on the MFMAs; each thread owns 4 consecutive rows x 8
+// features and writes them transposed as one 8-byte LDS store per feature.
+__device__ inline uint2 pack4_bf16(uint4 r0, uint4 r1, uint4 r2, uint4 r3, int e) {
+  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r0);
+  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r1);
+  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r2);
+  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r3);
+  const int sh = 16 * (e & 1);
+  const uint32_t v0 = (w0[e >> 1] >> sh) & 0xFFFFu, v1 = (w1[e >> 1] >> sh) & 0xFFFFu;
+  const uint32_t v2 = (w2[e >> 1] >> sh) & 0xFFFFu, v3 = (w3[e >> 1] >> sh) & 0xFFFFu;
+  return make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+}
+
+__global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __restrict__ h,
+                                                           float* __restrict__ ws, CRGeom g, float alpha) {
+  constexpr int LDR = 136;  // 128 rows + 8 pad (bf16) per feature row
+  __shared__ __attribute__((aligned(16))) uint16_t sI[64 * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t sJ[64 * LDR];
+  const int s = blockIdx.y;
+  int tt = blockIdx.x, I = 0;
+  while (tt > I) { tt -= I + 1; ++I; }
+  const int J = tt;
+  const bool same = I == J;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int wm = w >> 1, wn = w & 1;
+  const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
+  const int rq = (tid >> 3) * 4, fc = (tid & 7) * 8;
+  const bool fiok = 64 * I + fc < g.d, fjok = 64 * J + fc < g.d;
+  const uint16_t* hI = h + static_cast<int64_t>(s) * g.T * g.d + 64 * I + fc;
+  const uint16_t* hJ = h + static_cast<int64_t>(s) * g.T * g.d + 64 * J + fc;
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  uint4 xi0, xi1, xi2, xi3, xj0, xj1, xj2, xj3;
+  auto fetch = [&](int j) {
+    const int r0 = j * g.c + rq, rend = min(j * g.c + g.c, g.T);
+    const int64_t o = static_cast<int64_t>(r0) * g.d;
+    const bool q0 = r0 < rend, q1 = r0 + 1 < rend, q2 = r0 + 2 < rend, q3 = r0 + 3 < rend;
+    xi0 = fiok && q0 ? *reinterpret_cast<const uint4*>(hI + o) : z4;
+    xi1 = fiok && q1 ? *reinterpret_cast<const uint4*>(hI + o + g.d) : z4;
+    xi2 = fiok && q2 ? *reinterpret_cast<const uint4*>(hI + o + 2 * g.d) : z4;
+    xi3 = fiok && q3 ? *reinterpret_cast<const uint4*>(hI + o + 3 * g.d) : z4;
+    if (!same) {
+      xj0 = fjok && q0 ? *reinterpret_cast<const uint4*>(hJ + o) : z4;
+      xj1 = fjok && q1 ? *reinterpret_cast<const uint4*>(hJ + o + g.d) : z4;
+      xj2 = fjok && q2 ? *reinterpret_cast<const uint4*>(hJ + o + 2 * g.d) : z4;
+      xj3 = fjok && q3 ? *reinterpret_cast<const uint4*>(hJ + o + 3 * g.d) : z4;
+    }
+  };
+  if (g.nblk > 1) fetch(0);
+  floatx16 acc = zero16();
+  const uint16_t* sJr = same ? sI : sJ;
+  for (int j = 0; j < g.nblk; ++j) {
+    float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
+      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
+    }
+    if (j == g.nblk - 1) break;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      *reinterpret_cast<uint2*>(sI + (fc + e) * LDR + rq) = pack4_bf16(xi0, xi1, xi2, xi3, e);
+      if (!same) *reinterpret_cast<uint2*>(sJ + (fc + e) * LDR + rq) = pack4_bf16(xj0, xj1, xj2, xj3, e);
+    }
+    __syncthreads();
+    if (j + 1 < g.nblk - 1) fetch(j + 1);
+    for (int k0 = 0; k0 < g.c; k0 += 16) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sI + (32 * wm + (lane & 31)) * LDR + k0 + 8 * (lane >> 5));
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(sJr + (32 * wn + (lane & 31)) * LDR + k0 + 8 * (lane >> 5));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+  }
+}
+
 // identity into the 64x64 diagonal tiles of the S part
 __global__ __launch_bounds__(256) void cr_init_sdiag(float* __restrict__ ws, CRGeom g) {
   const int m = blockIdx.x;
@@ -463,8 +539,12 @@ void cr_launch(const void* h, const CRGeom& g, int nseq, double alpha, float* dR
                float* ws, hipStream_t st) {
   float* linv = ws + static_cast<int64_t>(g.nmat) * g.ldm * g.ldm;
   const int nt = g.dp / NB;
-  hipLaunchKernelGGL(cr_gram_prefix<DT>, dim3(nt * (nt + 1) / 2, nseq), dim3(256), 0, st, h, ws, g,
-                     static_cast<float>(alpha));
+  if (DT == BLLM_BF16)
+    hipLaunchKernelGGL(cr_gram_prefix_bf16, dim3(nt * (nt + 1) / 2, nseq), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(h), ws, g, static_cast<float>(alpha));
+  else
+    hipLaunchKernelGGL(cr_gram_prefix<DT>, dim3(nt * (nt + 1) / 2, nseq), dim3(256), 0, st, h, ws, g,
+                       static_cast<float>(alpha));
   hipLaunchKernelGGL(cr_init_sdiag, dim3(g.nmat), dim3(256), 0, st, ws, g);
   const int npan = g.ldm / NB;
   const float salpha = static_cast<float>(std::sqrt(alpha));

@@ -9,10 +9,11 @@
 // Positions of one chunk that share a bin need the same product, so the work
 // items are the distinct (chunk, bin) pairs, each covering a run of
 // consecutive positions.  Items are bucketed by bin (counting sort with wave
-// ballots), then one grouped GEMM per bin on bf16 MFMA (v_mfma_f32_32x32x16_bf16):
-// A rows are gathered from g by chunk, B = W_b (transposed once into the
-// workspace so both operands are contiguous along the reduction), and the
-// epilogue adds h_t and writes every position of the item's run.
+// ballots; a deterministic order), then one grouped GEMM per bin on bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16): A rows are gathered from g by chunk, B = W_b
+// (transposed once into the workspace so both operands are contiguous along
+// the reduction), and the epilogue adds h_t and writes every position of the
+// item's run with 16-byte loads and stores.
 #include <algorithm>
 
 #include "common.h"
@@ -24,7 +25,11 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kChunksPerBlock = 256;
-constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLDK = kBK + 8;  // LDS row stride (bf16) of the operand tiles
+
+// row of element r held by `lane` in a 32x32 MFMA accumulator
+__device__ inline int crow_of(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 struct UpGeom {
   int nseq, T, K, dg, dl, nbins, nblk;
@@ -33,30 +38,24 @@ struct UpGeom {
 // first position offset of bin b in a chunk of length L: ceil(b L / B)
 __device__ inline int bin_lo(int b, int L, int B) { return (b * L + B - 1) / B; }
 
-__device__ inline uint64_t present_bins(int L, int B) {
-  uint64_t m = 0;
-  for (int b = 0; b < B; ++b)
-    if (bin_lo(b, L, B) < bin_lo(b + 1, L, B)) m |= uint64_t(1) << b;
-  return m;
-}
+__device__ inline bool bin_present(int b, int L, int B) { return bin_lo(b, L, B) < bin_lo(b + 1, L, B); }
 
 __device__ inline int chunk_len(const int32_t* idx, const UpGeom& g, int64_t cg) {
   const int i = static_cast<int>(cg % g.K);
-  const int64_t s = cg / g.K;
-  const int cur = idx[cg];
   const int nxt = i + 1 < g.K ? idx[cg + 1] : g.T;
-  (void)s;
-  return nxt - cur;
+  return nxt - idx[cg];
 }
 
+// per-block, per-bin item counts
 __global__ __launch_bounds__(kChunksPerBlock) void up_count(const int32_t* __restrict__ idx, UpGeom g,
                                                             int32_t* __restrict__ counts) {
   __shared__ int wc[4][64];
   const int64_t cg = static_cast<int64_t>(blockIdx.x) * kChunksPerBlock + threadIdx.x;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint64_t m = cg < static_cast<int64_t>(g.nseq) * g.K ? present_bins(chunk_len(idx, g, cg), g.nbins) : 0;
+  const bool valid = cg < static_cast<int64_t>(g.nseq) * g.K;
+  const int L = valid ? chunk_len(idx, g, cg) : 0;
   for (int b = 0; b < g.nbins; ++b) {
-    const uint64_t bal = __ballot((m >> b) & 1);
+    const uint64_t bal = __ballot(valid && bin_present(b, L, g.nbins));
     if (lane == 0) wc[w][b] = __popcll(bal);
   }
   __syncthreads();
@@ -65,19 +64,32 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_count(const int32_t* __res
         wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] + wc[3][threadIdx.x];
 }
 
-// single block: per-bin totals, item offsets, tile offsets, per-block bases
-__global__ __launch_bounds__(64) void up_offsets(const int32_t* __restrict__ counts, UpGeom g,
-                                                 int32_t* __restrict__ base, int32_t* __restrict__ bin_off,
-                                                 int32_t* __restrict__ bin_cnt, int32_t* __restrict__ tile_off) {
+// single block: per-bin running offsets of every count block, bin offsets and
+// tile offsets.  Counts are staged through LDS in chunks of 64 blocks.
+__global__ __launch_bounds__(256) void up_offsets(const int32_t* __restrict__ counts, UpGeom g,
+                                                  int32_t* __restrict__ base, int32_t* __restrict__ bin_off,
+                                                  int32_t* __restrict__ bin_cnt, int32_t* __restrict__ tile_off) {
+  constexpr int CB = 64;
+  __shared__ int sc[CB][65];
   __shared__ int tot[64];
-  const int b = threadIdx.x;
-  int sum = 0;
-  if (b < g.nbins) {
-    for (int k = 0; k < g.nblk; ++k) sum += counts[static_cast<int64_t>(k) * g.nbins + b];
-    tot[b] = sum;
+  const int tid = threadIdx.x;
+  int run = 0;
+  for (int k0 = 0; k0 < g.nblk; k0 += CB) {
+    const int nk = min(CB, g.nblk - k0);
+    __syncthreads();
+    for (int e = tid; e < nk * g.nbins; e += blockDim.x)
+      sc[e / g.nbins][e % g.nbins] = counts[static_cast<int64_t>(k0) * g.nbins + e];
+    __syncthreads();
+    if (tid < g.nbins) {
+      for (int k = 0; k < nk; ++k) {
+        base[static_cast<int64_t>(k0 + k) * g.nbins + tid] = run;
+        run += sc[k][tid];
+      }
+    }
   }
+  if (tid < g.nbins) tot[tid] = run;
   __syncthreads();
-  if (b == 0) {
+  if (tid == 0) {
     int io = 0, to = 0;
     for (int q = 0; q < g.nbins; ++q) {
       bin_off[q] = io;
@@ -89,15 +101,11 @@ __global__ __launch_bounds__(64) void up_offsets(const int32_t* __restrict__ cou
     tile_off[g.nbins] = to;
   }
   __syncthreads();
-  if (b < g.nbins) {
-    int run = bin_off[b];
-    for (int k = 0; k < g.nblk; ++k) {
-      base[static_cast<int64_t>(k) * g.nbins + b] = run;
-      run += counts[static_cast<int64_t>(k) * g.nbins + b];
-    }
-  }
+  for (int64_t e = tid; e < static_cast<int64_t>(g.nblk) * g.nbins; e += blockDim.x)
+    base[e] += bin_off[e % g.nbins];
 }
 
+// items grouped by bin, in chunk order inside each bin
 __global__ __launch_bounds__(kChunksPerBlock) void up_items(const int32_t* __restrict__ idx, UpGeom g,
                                                             const int32_t* __restrict__ base,
                                                             int4* __restrict__ items) {
@@ -106,20 +114,17 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_items(const int32_t* __res
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool valid = cg < static_cast<int64_t>(g.nseq) * g.K;
   const int L = valid ? chunk_len(idx, g, cg) : 0;
-  const uint64_t m = valid ? present_bins(L, g.nbins) : 0;
-  int below[64];
   for (int b = 0; b < g.nbins; ++b) {
-    const uint64_t bal = __ballot((m >> b) & 1);
-    below[b] = lanes_below(bal);
+    const uint64_t bal = __ballot(valid && bin_present(b, L, g.nbins));
     if (lane == 0) wc[w][b] = __popcll(bal);
   }
   __syncthreads();
-  if (!valid) return;
-  const int64_t s = cg / g.K;
-  const int64_t row0 = s * g.T + idx[cg];
+  const int64_t row0 = valid ? (cg / g.K) * g.T + idx[cg] : 0;
   for (int b = 0; b < g.nbins; ++b) {
-    if (!((m >> b) & 1)) continue;
-    int slot = base[static_cast<int64_t>(blockIdx.x) * g.nbins + b] + below[b];
+    const bool pres = valid && bin_present(b, L, g.nbins);
+    const uint64_t bal = __ballot(pres);
+    if (!pres) continue;
+    int slot = base[static_cast<int64_t>(blockIdx.x) * g.nbins + b] + lanes_below(bal);
     for (int q = 0; q < w; ++q) slot += wc[q][b];
     const int lo = bin_lo(b, L, g.nbins), hi = bin_lo(b + 1, L, g.nbins);
     items[slot] = make_int4(static_cast<int>(cg), static_cast<int>(row0 + lo), hi - lo, 0);
@@ -142,7 +147,8 @@ __global__ __launch_bounds__(256) void up_transpose(const uint16_t* __restrict__
     if (n0 + r < dl && k0 + tx < dg) dst[static_cast<int64_t>(n0 + r) * dg + k0 + tx] = t[tx][r];
 }
 
-// grouped gather-GEMM: one 128 x 128 output tile (items x d_local) per block
+// grouped gather-GEMM: one 128 x 128 output tile (items x d_local) per block;
+// four waves in 2 x 2, each a 64 x 64 quadrant of 2 x 2 MFMA 32x32 tiles.
 __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat,
                                                const uint16_t* __restrict__ Wt,
                                                const uint16_t* __restrict__ h, UpGeom g,
@@ -151,10 +157,12 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
                                                const int32_t* __restrict__ tile_off,
                                                const int4* __restrict__ items,
                                                uint16_t* __restrict__ out) {
-  constexpr int LDK = kBK + 8;  // padded row (bf16 elements)
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kBM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kBN * LDK];
+  constexpr int kOLD = kBN + 4;  // fp32 row stride of the epilogue staging area
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBM * kLDK];
   __shared__ int4 sItem[kBM];
+  uint16_t* sA = smem;
+  uint16_t* sB = smem + kBM * kLDK;
+  float* sO = reinterpret_cast<float*>(smem);  // [64][kOLD] fp32, reused after the K loop
   const int tau = blockIdx.x;
   if (tau >= tile_off[g.nbins]) return;
   int b = 0;
@@ -174,37 +182,56 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
-  // loader geometry: each thread moves 32 bytes (16 bf16) of A and of B per K step
-  const int lrow = tid >> 1, lhalf = tid & 1;
-  const bool arow_ok = lrow < mcount;
-  const uint16_t* arow = gmat + static_cast<int64_t>(sItem[lrow].x) * g.dg + 16 * lhalf;
-  const uint16_t* brow = Wt + (static_cast<int64_t>(b) * g.dl + n0 + lrow) * g.dg + 16 * lhalf;
-  const bool brow_ok = n0 + lrow < g.dl;
-  for (int k0 = 0; k0 < g.dg; k0 += kBK) {
-    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
-    if (arow_ok) {
-      a0 = *reinterpret_cast<const uint4*>(arow + k0);
-      a1 = *reinterpret_cast<const uint4*>(arow + k0 + 8);
-    }
-    if (brow_ok) {
-      b0 = *reinterpret_cast<const uint4*>(brow + k0);
-      b1 = *reinterpret_cast<const uint4*>(brow + k0 + 8);
-    }
+  // loader: thread moves rows lr + 32*q (q = 0..3), 16-byte column chunk lc;
+  // the next K step's operands are in flight in named registers during the MFMAs
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const uint16_t* ar0 = gmat + static_cast<int64_t>(sItem[lr].x) * g.dg + lc;
+  const uint16_t* ar1 = gmat + static_cast<int64_t>(sItem[lr + 32].x) * g.dg + lc;
+  const uint16_t* ar2 = gmat + static_cast<int64_t>(sItem[lr + 64].x) * g.dg + lc;
+  const uint16_t* ar3 = gmat + static_cast<int64_t>(sItem[lr + 96].x) * g.dg + lc;
+  const uint16_t* wb = Wt + static_cast<int64_t>(b) * g.dl * g.dg + lc;
+  const int nr0 = min(n0 + lr, g.dl - 1), nr1 = min(n0 + lr + 32, g.dl - 1);
+  const int nr2 = min(n0 + lr + 64, g.dl - 1), nr3 = min(n0 + lr + 96, g.dl - 1);
+  const uint16_t* br0 = wb + static_cast<int64_t>(nr0) * g.dg;
+  const uint16_t* br1 = wb + static_cast<int64_t>(nr1) * g.dg;
+  const uint16_t* br2 = wb + static_cast<int64_t>(nr2) * g.dg;
+  const uint16_t* br3 = wb + static_cast<int64_t>(nr3) * g.dg;
+  const bool a0 = lr < mcount, a1 = lr + 32 < mcount, a2 = lr + 64 < mcount, a3 = lr + 96 < mcount;
+  const bool b0 = n0 + lr < g.dl, b1 = n0 + lr + 32 < g.dl, b2 = n0 + lr + 64 < g.dl, b3 = n0 + lr + 96 < g.dl;
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  uint4 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;
+  auto fetch = [&](int ko) {
+    const bool kin = ko + lc < g.dg;
+    pa0 = a0 && kin ? *reinterpret_cast<const uint4*>(ar0 + ko) : z4;
+    pa1 = a1 && kin ? *reinterpret_cast<const uint4*>(ar1 + ko) : z4;
+    pa2 = a2 && kin ? *reinterpret_cast<const uint4*>(ar2 + ko) : z4;
+    pa3 = a3 && kin ? *reinterpret_cast<const uint4*>(ar3 + ko) : z4;
+    pb0 = b0 && kin ? *reinterpret_cast<const uint4*>(br0 + ko) : z4;
+    pb1 = b1 && kin ? *reinterpret_cast<const uint4*>(br1 + ko) : z4;
+    pb2 = b2 && kin ? *reinterpret_cast<const uint4*>(br2 + ko) : z4;
+    pb3 = b3 && kin ? *reinterpret_cast<const uint4*>(br3 + ko) : z4;
+  };
+  fetch(0);
+  const int nk = (g.dg + kBK - 1) / kBK;
+  for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();
-    *reinterpret_cast<uint4*>(sA + lrow * LDK + 16 * lhalf) = a0;
-    *reinterpret_cast<uint4*>(sA + lrow * LDK + 16 * lhalf + 8) = a1;
-    *reinterpret_cast<uint4*>(sB + lrow * LDK + 16 * lhalf) = b0;
-    *reinterpret_cast<uint4*>(sB + lrow * LDK + 16 * lhalf + 8) = b1;
+    *reinterpret_cast<uint4*>(sA + lr * kLDK + lc) = pa0;
+    *reinterpret_cast<uint4*>(sA + (lr + 32) * kLDK + lc) = pa1;
+    *reinterpret_cast<uint4*>(sA + (lr + 64) * kLDK + lc) = pa2;
+    *reinterpret_cast<uint4*>(sA + (lr + 96) * kLDK + lc) = pa3;
+    *reinterpret_cast<uint4*>(sB + lr * kLDK + lc) = pb0;
+    *reinterpret_cast<uint4*>(sB + (lr + 32) * kLDK + lc) = pb1;
+    *reinterpret_cast<uint4*>(sB + (lr + 64) * kLDK + lc) = pb2;
+    *reinterpret_cast<uint4*>(sB + (lr + 96) * kLDK + lc) = pb3;
     __syncthreads();
+    if (kt + 1 < nk) fetch((kt + 1) * kBK);
 #pragma unroll
     for (int ks = 0; ks < kBK; ks += 16) {
       bf16x8 af[2], bfr[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int ar = 64 * wm + 32 * t + (lane & 31);
-        const int br = 64 * wn + 32 * t + (lane & 31);
-        af[t] = *reinterpret_cast<const bf16x8*>(sA + ar * LDK + ks + 8 * (lane >> 5));
-        bfr[t] = *reinterpret_cast<const bf16x8*>(sB + br * LDK + ks + 8 * (lane >> 5));
+        af[t] = *reinterpret_cast<const bf16x8*>(sA + (64 * wm + 32 * t + (lane & 31)) * kLDK + ks + 8 * (lane >> 5));
+        bfr[t] = *reinterpret_cast<const bf16x8*>(sB + (64 * wn + 32 * t + (lane & 31)) * kLDK + ks + 8 * (lane >> 5));
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -213,22 +240,51 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
           acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[c], acc[a][c], 0, 0, 0);
     }
   }
-  // epilogue: s_t = h_t + acc for every position of the item's run
+  // epilogue, one pass per row half p (rows 64p..64p+63, written by the waves
+  // with wm == p): stage fp32 in LDS, then spread the (row, position of the
+  // item's run, 8-column chunk) units evenly over the block, so long runs of
+  // one chunk do not serialise on a few threads.  Each unit adds 8 values of h
+  // and writes 8 outputs with 16-byte accesses.
+  __shared__ int sPre[65];
+  for (int p = 0; p < 2; ++p) {
+    __syncthreads();
+    if (wm == p) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = 64 * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int n = n0 + 64 * wn + 32 * c + (lane & 31);
-        if (m >= mcount || n >= g.dl) continue;
-        const int4 it = sItem[m];
-        for (int e = 0; e < it.z; ++e) {
-          const int64_t o = static_cast<int64_t>(it.y + e) * g.dl + n;
-          out[o] = f32_to_bf16(acc[a][c][r] + bf16_to_f32(h[o]));
-        }
+          for (int r = 0; r < 16; ++r)
+            sO[(32 * a + crow_of(r, lane)) * kOLD + 64 * wn + 32 * c + (lane & 31)] = acc[a][c][r];
+    }
+    if (tid == 0) {
+      int run = 0;
+      for (int r = 0; r < 64; ++r) {
+        sPre[r] = run;
+        const int m = 64 * p + r;
+        run += m < mcount ? sItem[m].z : 0;
       }
+      sPre[64] = run;
+    }
+    __syncthreads();
+    const int nchunk = min(kBN, g.dl - n0) / 8;
+    const int nunits = sPre[64] * nchunk;
+    for (int u = tid; u < nunits; u += blockDim.x) {
+      const int qpos = u / nchunk, ch = u - qpos * nchunk;
+      int lo = 0, hi = 64;  // last row r with sPre[r] <= qpos
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sPre[mid] <= qpos) lo = mid; else hi = mid;
+      }
+      const int4 it = sItem[64 * p + lo];
+      const int64_t o = static_cast<int64_t>(it.y + (qpos - sPre[lo])) * g.dl + n0 + 8 * ch;
+      float hv[8], sv[8];
+      Vec<BLLM_BF16>::load(h, o, hv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = sO[lo * kOLD + 8 * ch + e] + hv[e];
+      Vec<BLLM_BF16>::store(out, o, sv);
+    }
+  }
 }
 
 struct UpWs {
@@ -279,7 +335,7 @@ extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* 
       d_local < 1 || nbins < 1)
     return BLLM_E_INVAL;
   if (dtype != BLLM_BF16) return BLLM_E_NOTSUP;
-  if (nbins > 64 || d_global % kBK != 0 || d_local % 8 != 0 || nseq * T >= (int64_t(1) << 31) ||
+  if (nbins > 64 || d_global % 8 != 0 || d_local % 8 != 0 || nseq * T >= (int64_t(1) << 31) ||
       !aligned16(gm) || !aligned16(W) || !aligned16(h) || !aligned16(s_out))
     return BLLM_E_NOTSUP;
   UpGeom g{static_cast<int>(nseq), static_cast<int>(T), static_cast<int>(K), static_cast<int>(d_global),
@@ -293,7 +349,7 @@ extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* 
                                         static_cast<unsigned>(nbins)),
                      dim3(256), 0, st, static_cast<const uint16_t*>(W), g.dg, g.dl, u.Wt);
   hipLaunchKernelGGL(up_count, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts);
-  hipLaunchKernelGGL(up_offsets, dim3(1), dim3(64), 0, st, u.counts, g, u.base, u.bin_off, u.bin_cnt,
+  hipLaunchKernelGGL(up_offsets, dim3(1), dim3(256), 0, st, u.counts, g, u.base, u.bin_off, u.bin_cnt,
                      u.tile_off);
   hipLaunchKernelGGL(up_items, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.base, u.items);
   const int64_t max_tiles = ceil_div(nseq * T, kBM) + nbins;

@@ -38,9 +38,11 @@ def say(*a):
 
 
 def _dr_range(args):
+    from threadpoolctl import threadpool_limits
     import oracle
     h, eps2, a, b = args
-    return oracle.coding_rate_at(h, eps2, np.arange(a, b))
+    with threadpool_limits(limits=1):  # one BLAS thread per worker process
+        return oracle.coding_rate_at(h, eps2, np.arange(a, b))
 
 
 def oracle_dr_parallel(h, eps2, nproc=None):

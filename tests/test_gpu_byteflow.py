@@ -141,6 +141,15 @@ def test_coding_rate_full_size_c4_sampled(ops):
         pos = np.sort(rng.choice(c["T"], 8, replace=False))
         o = oracle.coding_rate_at(c["h"][s], c["eps2"], pos)
         assert np.max(np.abs(g[s, pos] - o) / np.abs(o)) < 1e-3
+    # one whole sequence: every Delta R, then the Top-K set outside the 1e-5 band
+    s = 7
+    say("C4 oracle on one full sequence (parallel workers)")
+    o = oracle_dr_parallel(c["h"][s].astype(np.float64), c["eps2"])
+    assert np.max(np.abs(g[s] - o) / o) < 1e-3
+    idx, _, _ = ops.topk_select(to_dev(g[s:s + 1]), c["K"])
+    bad, nband = topk_band_compare(to_np(idx)[0], oracle.topk_select(o, c["K"]), o, c["K"])
+    say("C4 seq", s, "max abs err", np.max(np.abs(g[s] - o)), "band size", nband)
+    assert len(bad) == 0, bad
 
 
 # ------------------------------------------------------------------ gather + upsample
