@@ -18,13 +18,13 @@
 // Launch sequence for a batch (all block matrices of all sequences at once):
 //   cr_gram_prefix  A_j for every block j (64x64 output tile per workgroup,
 //                   bf16 or fp32 MFMA over rows staged transposed in LDS)
-//   cr_init_sdiag   identity into the S-part diagonal tiles
 //   for each panel k:
-//     cr_diag       factor the (already updated) 64x64 diagonal tile, log of
-//                   the S-part pivots, explicit inverse of the tile's factor
+//     cr_diag       one wave per matrix factors the 64x64 diagonal tile (k, k),
+//                   writes the S-part pivots' logs and the inverse of the factor
 //     cr_panel      one workgroup per 64x64 tile below it (XCD-aware order):
-//                   left-looking update over the earlier panels, X = acc L_kk^-T,
-//                   then the right-looking update of that row's diagonal tile
+//                   left-looking update over the earlier panels, X = acc L_kk^-T;
+//                   the workgroup of the next row tile also forms the next
+//                   diagonal tile from the same staged row chunks and writes it
 // Workspace: nmat = nseq * nblk matrices of ldm^2 fp32 (ldm = d' + c), plus a
 // 64x64 inverse slot per matrix.
 #include <cmath>
@@ -55,8 +55,19 @@ __device__ inline floatx16 zero16() {
 }
 
 struct CRGeom {
-  int T, d, dp, c, nblk, ldm, nmat;
+  int T, d, dp, c, nblk, ldm, nmat, nseq;
 };
+
+// Gram tiles: 1-D grid of ceil(nseq/8)*8 * ntp blocks.  Block b runs on XCD
+// b % 8; every tile of one sequence lands on the same XCD so the rows of h
+// they all stream are fetched into that XCD's L2 once.
+__device__ inline bool gram_tile_of_block(const CRGeom& g, int& s, int& t) {
+  const int ntile = g.dp / 64, ntp = ntile * (ntile + 1) / 2;
+  const int b = blockIdx.x, xcd = b & 7, q = b >> 3;
+  s = (q / ntp) * 8 + xcd;
+  t = q % ntp;
+  return s < g.nseq;
+}
 
 __device__ inline int block_rows(const CRGeom& g, int j) { return min(g.c, g.T - j * g.c); }
 __device__ inline int block_n(const CRGeom& g, int j) {
@@ -134,8 +145,9 @@ __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h
   constexpr int LD = GramLds<DT>::LD;
   __shared__ __attribute__((aligned(16))) E sI[64 * LD];
   __shared__ __attribute__((aligned(16))) E sJ[64 * LD];
-  const int s = blockIdx.y;
-  int t = blockIdx.x, I = 0;
+  int s, t;
+  if (!gram_tile_of_block(g, s, t)) return;
+  int I = 0;
   while (t > I) { t -= I + 1; ++I; }
   const int J = t;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -182,8 +194,9 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
   constexpr int LDR = 136;  // 128 rows + 8 pad (bf16) per feature row
   __shared__ __attribute__((aligned(16))) uint16_t sI[64 * LDR];
   __shared__ __attribute__((aligned(16))) uint16_t sJ[64 * LDR];
-  const int s = blockIdx.y;
-  int tt = blockIdx.x, I = 0;
+  int s, tt;
+  if (!gram_tile_of_block(g, s, tt)) return;
+  int I = 0;
   while (tt > I) { tt -= I + 1; ++I; }
   const int J = tt;
   const bool same = I == J;
@@ -238,158 +251,195 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
   }
 }
 
-// identity into the 64x64 diagonal tiles of the S part
-__global__ __launch_bounds__(256) void cr_init_sdiag(float* __restrict__ ws, CRGeom g) {
-  const int m = blockIdx.x;
-  float* Mx = ws + static_cast<int64_t>(m) * g.ldm * g.ldm;
-  for (int q = g.dp; q < g.ldm; q += NB)
-    for (int e = threadIdx.x; e < NB * NB; e += blockDim.x) {
-      const int r = e >> 6, cc = e & 63;
-      Mx[static_cast<int64_t>(q + r) * g.ldm + q + cc] = r == cc ? 1.f : 0.f;
-    }
-}
-
 // ------------------------------------------------------------------ diagonal tile
 
-// One wave per block matrix: Cholesky of the 64x64 diagonal tile of panel k,
-// the logs of its S-part pivots into dR, and the inverse of the tile's factor.
-// 2x2 blocks of 32: lane i holds row i (a = columns 0..31, b = columns 32..63).
+constexpr int PLD = 36;  // LDS row stride (floats) of 32-column chunks
+constexpr int XLD = 68;  // LDS row stride of 64-column tiles
+
+// Factor the 64x64 tile D (lower triangle; global, row stride ldd) with one wave:
+// the logs of its pivots that fall in the S part go to dR, the inverse of the
+// factor to Li (global, 64x64 row-major).  2x2 blocks of 32, lane i owns row i:
 //   1. eliminate columns 0..31 over all 64 rows  -> L11 (lanes 0..31), L21 (lanes 32..63)
-//   2. D22 -= L21 L21^T                           (lanes 32..63, L21 rows from LDS)
-//   3. eliminate columns 32..63 of D22            -> L22 (lanes 32..63)
-//   4. inverse [[L11^-1, 0], [-L22^-1 L21 L11^-1, L22^-1]] by column solves
-// Pivots are broadcast with readlane; every loop has a fixed trip count of 32.
-__global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __restrict__ linv,
-                                              float* __restrict__ dR, int32_t* __restrict__ status,
-                                              CRGeom g, int k) {
-  __shared__ float sL[NB][33];   // rows of [L11; L21] (32 columns), later L22 in rows 32..63
-  __shared__ float sT[32][33];   // L11^-1 (row-major), then Z = L21 L11^-1
-  const int m = blockIdx.x;
-  const int s = m / g.nblk, j = m % g.nblk;
-  if (NB * k >= block_n(g, j)) return;
-  const int cj = block_rows(g, j);
-  const int i = threadIdx.x;
+//   2. D22 - L21 L21^T, eliminate columns 32..63  -> L22 (lanes 32..63)
+//   3. columns of L11^-1 (lanes 0..31) and L22^-1 (lanes 32..63) by forward
+//      substitution that pushes each solved entry into the later ones
+//   4. Y = -L22^-1 (L21 L11^-1) as two plain products:
+//      Linv = [[L11^-1, 0], [Y, L22^-1]]
+// Each elimination step broadcasts the pivot with one readlane and the scaled
+// column through LDS; lanes above the diagonal also run the updates, on
+// entries of the upper triangle that are never read.  Reciprocal square roots
+// replace divisions; LDS rows are 16-byte aligned and read 4 floats at a time.
+// sW is LDS scratch of kFactorLds floats (16-byte aligned).
+constexpr int kF = 36;  // row stride of the 32-wide LDS blocks
+constexpr int kFactorLds = 64 + 64 + 64 * kF + 2 * 32 * kF;
+
+__device__ __forceinline__ void ld4(const float* p, float* dst) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+}
+
+__device__ __forceinline__ void factor64(const float* __restrict__ D, int64_t ldd, float* __restrict__ sW,
+                                         float* __restrict__ Li, float* __restrict__ dR_blk,
+                                         int rr0, int cj, int32_t* __restrict__ status) {
+  float* col = sW;                 // [64]    column broadcast
+  float* rinv = sW + 64;           // [64]    reciprocals of the diagonal of L
+  float* sL = sW + 128;            // [64][kF] rows of L11 (0..31) and L21 (32..63)
+  float* sT11 = sL + 64 * kF;      // [32][kF] L11^T, later L11^-1 (row-major)
+  float* sT22 = sT11 + 32 * kF;    // [32][kF] L22^T, later L22^-1 (row-major)
+  const int i = threadIdx.x & 63, ih = i & 31;
   const bool hi = i >= 32;
-  const int ih = i & 31;
-  const float* D = ws + static_cast<int64_t>(m) * g.ldm * g.ldm + static_cast<int64_t>(NB * k) * g.ldm + NB * k;
-  float a[32], b[32];
-  {
-    const float* Dr = D + static_cast<int64_t>(i) * g.ldm;
-#pragma unroll
-    for (int q = 0; q < 32; q += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(Dr + q);
-      a[q] = v.x; a[q + 1] = v.y; a[q + 2] = v.z; a[q + 3] = v.w;
-      const float4 u = *reinterpret_cast<const float4*>(Dr + 32 + q);
-      b[q] = u.x; b[q + 1] = u.y; b[q + 2] = u.z; b[q + 3] = u.w;
-    }
-  }
+  float piv = 1.f, rd = 1.f;
   bool bad = false;
-  float piv = 0.f;  // this lane's diagonal entry of L
-  // 1. columns 0..31 (rows i >= kk of lanes 0..31, all of lanes 32..63)
+  float a[32], cv[32];
+#pragma unroll
+  for (int q = 0; q < 32; q += 4) ld4(D + i * ldd + q, a + q);
 #pragma unroll
   for (int jj = 0; jj < 32; ++jj) {
     const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[jj]), jj));
     bad |= !(pv > 0.f);
-    const float l = sqrtf(pv);
-    if (i == jj) { a[jj] = l; piv = l; }
-    else if (i > jj) a[jj] = a[jj] / l;
+    const float r = __builtin_amdgcn_rsqf(pv);
+    const float l = pv * r;
+    if (i == jj) { piv = l; rd = r; }
+    a[jj] = i == jj ? l : a[jj] * r;
+    col[i] = a[jj];
 #pragma unroll
-    for (int kk = jj + 1; kk < 32; ++kk) {
-      const float lk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[jj]), kk));
-      if (i >= kk) a[kk] = fmaf(-a[jj], lk, a[kk]);
-    }
+    for (int v = (jj + 1) / 4; v < 8; ++v) ld4(col + 4 * v, cv + 4 * v);
+#pragma unroll
+    for (int kk = jj + 1; kk < 32; ++kk) a[kk] = fmaf(-a[jj], cv[kk], a[kk]);
   }
 #pragma unroll
-  for (int q = 0; q < 32; ++q) sL[i][q] = (hi || q <= i) ? a[q] : 0.f;
+  for (int q = 0; q < 32; q += 4)
+    *reinterpret_cast<float4*>(sL + i * kF + q) =
+        make_float4((hi || q <= i) ? a[q] : 0.f, (hi || q + 1 <= i) ? a[q + 1] : 0.f,
+                    (hi || q + 2 <= i) ? a[q + 2] : 0.f, (hi || q + 3 <= i) ? a[q + 3] : 0.f);
+  if (!hi) {
+#pragma unroll
+    for (int q = 0; q < 32; ++q) sT11[q * kF + i] = q <= i ? a[q] : 0.f;
+  }
   __syncthreads();
-  // 2. D22 -= L21 L21^T
+  float b[32];
+#pragma unroll
+  for (int q = 0; q < 32; q += 4) ld4(D + i * ldd + 32 + q, b + q);
   if (hi) {
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
+      float rw[32];
+#pragma unroll
+      for (int p = 0; p < 32; p += 4) ld4(sL + (32 + q) * kF + p, rw + p);
       float acc = b[q];
 #pragma unroll
-      for (int p = 0; p < 32; ++p) acc = fmaf(-a[p], sL[32 + q][p], acc);
+      for (int p = 0; p < 32; ++p) acc = fmaf(-a[p], rw[p], acc);
       b[q] = acc;
     }
   }
-  // 3. columns 32..63 on lanes 32..63
 #pragma unroll
   for (int jj = 0; jj < 32; ++jj) {
     const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b[jj]), 32 + jj));
     bad |= !(pv > 0.f);
-    const float l = sqrtf(pv);
-    if (ih == jj) { b[jj] = l; if (hi) piv = l; }
-    else if (ih > jj) b[jj] = b[jj] / l;
+    const float r = __builtin_amdgcn_rsqf(pv);
+    const float l = pv * r;
+    if (ih == jj && hi) { piv = l; rd = r; }
+    b[jj] = ih == jj ? l : b[jj] * r;
+    col[i] = b[jj];
 #pragma unroll
-    for (int kk = jj + 1; kk < 32; ++kk) {
-      const float lk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b[jj]), 32 + kk));
-      if (ih >= kk) b[kk] = fmaf(-b[jj], lk, b[kk]);
-    }
+    for (int v = (jj + 1) / 4; v < 8; ++v) ld4(col + 32 + 4 * v, cv + 4 * v);
+#pragma unroll
+    for (int kk = jj + 1; kk < 32; ++kk) b[kk] = fmaf(-b[jj], cv[kk], b[kk]);
   }
   if (bad && status && i == 0) atomicOr(status, BLLM_S_NONFINITE);
-  __syncthreads();
   if (hi) {
 #pragma unroll
-    for (int q = 0; q < 32; ++q) sL[i][q] = q <= ih ? b[q] : 0.f;  // rows 32..63 now hold L22
+    for (int q = 0; q < 32; ++q) sT22[q * kF + ih] = q <= ih ? b[q] : 0.f;
   }
-  // 4a. lanes 0..31: column i of L11^-1 -> sT[r][i]; lanes 32..63: column ih of L22^-1
+  rinv[i] = rd;
+  __syncthreads();
+  // 3. lane m < 32: column m of L11^-1; lane 32+m: column m of L22^-1.
+  // sT holds L^T, so column p of L is the contiguous row p of sT.
   float x[32];
   {
-    const int base = hi ? 32 : 0;
+    const float* Tm = hi ? sT22 : sT11;
+    float ri[32];
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      float acc = r == ih ? 1.f : 0.f;
+    for (int p = 0; p < 32; p += 4) ld4(rinv + (hi ? 32 : 0) + p, ri + p);
 #pragma unroll
-      for (int p = 0; p < r; ++p) acc = fmaf(-sL[base + r][p], x[p], acc);
-      x[r] = acc / sL[base + r][r];
+    for (int r = 0; r < 32; ++r) x[r] = r == ih ? 1.f : 0.f;
+#pragma unroll
+    for (int p = 0; p < 32; ++p) {
+      x[p] *= ri[p];
+#pragma unroll
+      for (int v = (p + 1) / 4; v < 8; ++v) ld4(Tm + p * kF + 4 * v, cv + 4 * v);
+#pragma unroll
+      for (int r = p + 1; r < 32; ++r) x[r] = fmaf(-cv[r], x[p], x[r]);
     }
-  }
-  float* Li = linv + static_cast<int64_t>(m) * NB * NB;
-  if (!hi) {
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      sT[r][i] = x[r];
-      Li[r * NB + i] = x[r];
-      Li[r * NB + 32 + i] = 0.f;
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 32; ++r) Li[(32 + r) * NB + 32 + ih] = x[r];
   }
   __syncthreads();
-  // 4b. lanes 32..63: row ih of Z = L21 L11^-1 (L21 row still in a[])
-  float z[32];
-  if (hi) {
+  {
+    // inverses to LDS (row-major, over the consumed transposes) and to Li
+    float* Tw = hi ? sT22 : sT11;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
+    for (int r = 0; r < 32; ++r) Tw[r * kF + ih] = x[r];
+    if (!hi) {
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        Li[r * NB + i] = x[r];
+        Li[r * NB + 32 + i] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 32; ++r) Li[(32 + r) * NB + 32 + ih] = x[r];
+    }
+  }
+  __syncthreads();
+  if (hi) {
+    // 4. lane 32+c: column c of Z = L21 L11^-1, then of Y = -L22^-1 Z
+#pragma unroll
+    for (int p = 0; p < 32; ++p) cv[p] = sT11[p * kF + ih];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      float rw[32];
+#pragma unroll
+      for (int p = 0; p < 32; p += 4) ld4(sL + (32 + q) * kF + p, rw + p);
       float acc = 0.f;
 #pragma unroll
-      for (int p = 0; p < 32; ++p) acc = fmaf(a[p], sT[p][c], acc);
-      z[c] = acc;
+      for (int p = 0; p < 32; ++p) acc = fmaf(rw[p], cv[p], acc);
+      x[q] = acc;
     }
-  }
-  __syncthreads();
-  if (hi) {
-#pragma unroll
-    for (int c = 0; c < 32; ++c) sT[ih][c] = z[c];
-  }
-  __syncthreads();
-  // 4c. lanes 32..63: column ih of Y with L22 Y = -Z  -> Linv[32 + r][ih]
-  if (hi) {
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
-      float acc = -sT[r][ih];
+      float rw[32];
 #pragma unroll
-      for (int p = 0; p < r; ++p) acc = fmaf(-sL[32 + r][p], x[p], acc);
-      x[r] = acc / sL[32 + r][r];
-      Li[(32 + r) * NB + ih] = x[r];
+      for (int q = 0; q < 32; q += 4) ld4(sT22 + r * kF + q, rw + q);
+      float acc = 0.f;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) acc = fmaf(rw[q], x[q], acc);
+      Li[(32 + r) * NB + ih] = -acc;
     }
   }
-  // hardware log2 scaled by ln 2 (about 1 ulp); no out-of-line call
-  if (NB * k >= g.dp) {
-    const int rr = NB * k + i - g.dp;
-    if (rr < cj) dR[static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c + rr] = __logf(piv);
+  if (dR_blk != nullptr) {
+    const int rr = rr0 + i;  // row of the block (S part)
+    if (rr >= 0 && rr < cj) dR_blk[rr] = __logf(piv);  // hardware log2 scaled by ln 2
   }
+}
+
+// Panel k, diagonal tile: one wave per block matrix factors the 64x64 tile
+// (k, k) of the workspace -- the Gram prefix for k = 0, the tile the previous
+// panel's lookahead workgroup updated otherwise -- and writes the inverse of
+// its factor and, in the S part, the logs of its pivots.
+__global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __restrict__ linv,
+                                              float* __restrict__ dR, int32_t* __restrict__ status,
+                                              CRGeom g, int k) {
+  __shared__ __attribute__((aligned(16))) float sW[kFactorLds];
+  const int m = blockIdx.x;
+  const int s = m / g.nblk, j = m % g.nblk;
+  if (NB * k >= block_n(g, j)) return;
+  const float* D = ws + static_cast<int64_t>(m) * g.ldm * g.ldm + static_cast<int64_t>(NB * k) * g.ldm + NB * k;
+  float* dRb = NB * k >= g.dp ? dR + static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c : nullptr;
+  factor64(D, g.ldm, sW, linv + static_cast<int64_t>(m) * NB * NB, dRb, NB * k - g.dp, block_rows(g, j), status);
+}
+
+// orig value of the diagonal tile (i, i): the A part from the Gram prefix, identity in the S part
+__device__ inline float orig_diag(const float* Mx, const CRGeom& g, int row, int col) {
+  return col >= g.dp ? (row == col ? 1.f : 0.f) : Mx[static_cast<int64_t>(row) * g.ldm + col];
 }
 
 // ------------------------------------------------------------------ panel tiles
@@ -404,16 +454,20 @@ __device__ inline float orig_offdiag(const void* h, const float* Mx, const CRGeo
   return salpha * load_elem(h, (hrow0 + rr) * g.d + col, DT);
 }
 
-constexpr int PLD = 36;  // LDS row stride (floats) of 32-column chunks
-constexpr int XLD = 68;  // LDS row stride of 64-column tiles
-
-// 64x64 tile (i, k), i > k, of every block matrix.  Grid: ceil(nmat/8)*8*ntk
-// blocks; block b runs on XCD b%8 and all tiles of one matrix share an XCD so
-// the panel rows L[k, :] they all read stay in that XCD's L2.
+// Panel k: one workgroup per 64x64 tile (i, k), i > k, of every block matrix.
+//   X = (orig(i,k) -/+ sum_{kk<k} L[i,kk] L[k,kk]^T) Linv_k^T      (left-looking)
+// The workgroup of tile i = k+1 (the lookahead tile) also forms the next
+// diagonal tile D = orig(i,i) -/+ sum_{kk<=k} L[i,kk] L[i,kk]^T from the same
+// staged row chunks, factors it and writes Linv_{k+1} and the pivots, so the
+// next panel needs no separate diagonal launch.
+// Grid: 8 * ceil(nmat/8) * ntk blocks; block b runs on XCD b % 8 and all tiles
+// of one matrix share an XCD (the panel rows L[k, :] stay in its L2).  The
+// lookahead tiles of all matrices come first so their serial tail overlaps
+// the rest of the launch.
 template <int DT>
 __global__ __launch_bounds__(256) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
-                                                const float* __restrict__ linv, CRGeom g, float salpha,
-                                                int k, int ntk) {
+                                                const float* __restrict__ linv, CRGeom g,
+                                                float salpha, int k, int ntk) {
   __shared__ __attribute__((aligned(16))) float smem[2 * 64 * XLD];
   float* sA = smem;              // [64][PLD]  rows of tile i, current 32-column chunk
   float* sB = smem + 64 * PLD;   // [64][PLD]  rows of tile k
@@ -421,11 +475,16 @@ __global__ __launch_bounds__(256) void cr_panel(const void* __restrict__ h, floa
   float* sLi = smem + 64 * XLD;  // [64][XLD]
   const int b = blockIdx.x;
   const int xcd = b & 7, q = b >> 3;
-  const int m = (q / ntk) * 8 + xcd;
-  const int i = k + 1 + q % ntk;
+  const int m8 = (g.nmat + 7) / 8;
+  int m, t;
+  if (q < m8) { m = q * 8 + xcd; t = 0; }
+  else { const int q2 = q - m8; m = (q2 / (ntk - 1)) * 8 + xcd; t = 1 + q2 % (ntk - 1); }
   if (m >= g.nmat) return;
+  const int i = k + 1 + t;
   const int j = m % g.nblk;
-  if (NB * i >= block_n(g, j)) return;
+  const int nbn = block_n(g, j);
+  if (NB * i >= nbn) return;
+  const bool look = t == 0;
   const int s = m / g.nblk;
   const int cj = block_rows(g, j);
   const int64_t hrow0 = static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c;
@@ -433,11 +492,17 @@ __global__ __launch_bounds__(256) void cr_panel(const void* __restrict__ h, floa
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int wm = w >> 1, wn = w & 1;
   const int row0 = NB * i + 32 * wm, col0 = NB * k + 32 * wn;
-  floatx16 acc;
+  floatx16 acc, accD;
 #pragma unroll
   for (int r = 0; r < 16; ++r)
     acc[r] = orig_offdiag<DT>(h, Mx, g, hrow0, cj, salpha, row0 + crow(r, lane), col0 + (lane & 31));
+  if (look) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      accD[r] = orig_diag(Mx, g, row0 + crow(r, lane), NB * i + 32 * wn + (lane & 31));
+  }
   const bool panelS = NB * k >= g.dp;
+  const bool rowS = NB * i >= g.dp;
   // left-looking update over the 2k earlier 32-column chunks, loads of chunk
   // c+1 in flight while chunk c runs on the MFMAs
   const int nch = 2 * k;
@@ -466,13 +531,20 @@ __global__ __launch_bounds__(256) void cr_panel(const void* __restrict__ h, floa
       pb0 = *reinterpret_cast<const float4*>(gB + co);
       pb1 = *reinterpret_cast<const float4*>(gB + r32 + co);
     }
-    const float sg = (panelS && 32 * ch < g.dp) ? 1.f : -1.f;
+    const bool chA = 32 * ch < g.dp;
+    const float sg = (panelS && chA) ? 1.f : -1.f;
     const float* pa = sA + (32 * wm + (lane & 31)) * PLD + 16 * (lane >> 5);
     const float* pb = sB + (32 * wn + (lane & 31)) * PLD + 16 * (lane >> 5);
 #pragma unroll
     for (int st = 0; st < 16; ++st) acc = mfma32(sg * pa[st], pb[st], acc);
+    if (look && wm >= wn) {
+      const float sd = (rowS && chA) ? 1.f : -1.f;
+      const float* pc = sA + (32 * wn + (lane & 31)) * PLD + 16 * (lane >> 5);
+#pragma unroll
+      for (int st = 0; st < 16; ++st) accD = mfma32(sd * pa[st], pc[st], accD);
+    }
   }
-  // X = acc * Linv^T
+  // X = acc * Linv_k^T
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 16; ++r) sX[(32 * wm + crow(r, lane)) * XLD + 32 * wn + (lane & 31)] = acc[r];
@@ -493,26 +565,25 @@ __global__ __launch_bounds__(256) void cr_panel(const void* __restrict__ h, floa
 #pragma unroll
   for (int r = 0; r < 16; ++r)
     Mx[static_cast<int64_t>(row0 + crow(r, lane)) * g.ldm + col0 + (lane & 31)] = x[r];
-  // right-looking update of this row's diagonal tile: D_i -/+= X X^T
+  if (!look) return;
+  // lookahead: D -/+= X X^T, written over the diagonal tile (i, i) for the next
+  // panel's diagonal kernel (lower quadrants only)
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 16; ++r) sX[(32 * wm + crow(r, lane)) * XLD + 32 * wn + (lane & 31)] = x[r];
   __syncthreads();
   if (wm >= wn) {
-    const float sg = (NB * i >= g.dp && !panelS) ? 1.f : -1.f;
-    float* D = Mx + static_cast<int64_t>(NB * i + 32 * wm) * g.ldm + NB * i + 32 * wn;
-    floatx16 dd;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dd[r] = D[static_cast<int64_t>(crow(r, lane)) * g.ldm + (lane & 31)];
+    const float sd = (rowS && !panelS) ? 1.f : -1.f;
 #pragma unroll
     for (int mb = 0; mb < NB; mb += 32) {
       const float* pa = sX + (32 * wm + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
-      const float* pb = sX + (32 * wn + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
+      const float* pc = sX + (32 * wn + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
 #pragma unroll
-      for (int st = 0; st < 16; ++st) dd = mfma32(sg * pa[st], pb[st], dd);
+      for (int st = 0; st < 16; ++st) accD = mfma32(sd * pa[st], pc[st], accD);
     }
+    float* Dt = Mx + static_cast<int64_t>(NB * i + 32 * wm) * g.ldm + NB * i + 32 * wn;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) D[static_cast<int64_t>(crow(r, lane)) * g.ldm + (lane & 31)] = dd[r];
+    for (int r = 0; r < 16; ++r) Dt[static_cast<int64_t>(crow(r, lane)) * g.ldm + (lane & 31)] = accD[r];
   }
 }
 
@@ -527,6 +598,7 @@ CRGeom cr_geometry(int64_t nseq, int64_t T, int64_t d) {
   g.nblk = static_cast<int>((T + c - 1) / c);
   g.ldm = g.dp + c;
   g.nmat = static_cast<int>(nseq) * g.nblk;
+  g.nseq = static_cast<int>(nseq);
   return g;
 }
 
@@ -539,13 +611,12 @@ void cr_launch(const void* h, const CRGeom& g, int nseq, double alpha, float* dR
                float* ws, hipStream_t st) {
   float* linv = ws + static_cast<int64_t>(g.nmat) * g.ldm * g.ldm;
   const int nt = g.dp / NB;
+  const unsigned ggrid = static_cast<unsigned>((nseq + 7) / 8 * 8 * (nt * (nt + 1) / 2));
   if (DT == BLLM_BF16)
-    hipLaunchKernelGGL(cr_gram_prefix_bf16, dim3(nt * (nt + 1) / 2, nseq), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(h), ws, g, static_cast<float>(alpha));
-  else
-    hipLaunchKernelGGL(cr_gram_prefix<DT>, dim3(nt * (nt + 1) / 2, nseq), dim3(256), 0, st, h, ws, g,
+    hipLaunchKernelGGL(cr_gram_prefix_bf16, dim3(ggrid), dim3(256), 0, st, static_cast<const uint16_t*>(h), ws, g,
                        static_cast<float>(alpha));
-  hipLaunchKernelGGL(cr_init_sdiag, dim3(g.nmat), dim3(256), 0, st, ws, g);
+  else
+    hipLaunchKernelGGL(cr_gram_prefix<DT>, dim3(ggrid), dim3(256), 0, st, h, ws, g, static_cast<float>(alpha));
   const int npan = g.ldm / NB;
   const float salpha = static_cast<float>(std::sqrt(alpha));
   for (int k = 0; k < npan; ++k) {
