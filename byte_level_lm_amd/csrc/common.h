@@ -95,9 +95,21 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// sum over aligned groups of `g` lanes (g a power of two <= 64)
-__device__ inline float group_sum(float v, int g) {
-  for (int off = g >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+// sum over aligned groups of G lanes, every lane of a group gets the sum:
+// DPP quad permutes and row mirrors inside a row of 16 lanes, then swizzle
+// and permute across rows
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int G>
+__device__ inline float group_sum(float v) {
+  if (G >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  if (G >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  if (G >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if (G >= 16) v += dpp_f<0x140>(v); // row_mirror
+  if (G >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // xor 16
+  if (G >= 64) v += __shfl_xor(v, 32, kWave);
   return v;
 }
 

@@ -80,12 +80,21 @@ __global__ __launch_bounds__(256) void ema_tile_carry(const float* __restrict__ 
   constexpr int per = kNT / 256;
   const int f0 = blockIdx.x * 4;
   const int j = threadIdx.x;
-  float A = 1.f;
-  float4 U = make_float4(0.f, 0.f, 0.f, 0.f);
+  // this thread's tiles, all loads in flight at once
+  float ta[per];
+  float4 tu[per];
+#pragma unroll
   for (int q = 0; q < per; ++q) {
     const int64_t i = static_cast<int64_t>(j) * per + q;
-    const float a = Aagg[i];
-    const float4 u = *reinterpret_cast<const float4*>(Uagg + i * d + f0);
+    ta[q] = Aagg[i];
+    tu[q] = *reinterpret_cast<const float4*>(Uagg + i * d + f0);
+  }
+  float A = 1.f;
+  float4 U = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int q = 0; q < per; ++q) {
+    const float a = ta[q];
+    const float4 u = tu[q];
     U = make_float4(fmaf(a, U.x, u.x), fmaf(a, U.y, u.y), fmaf(a, U.z, u.z), fmaf(a, U.w, u.w));
     A *= a;
   }
@@ -108,11 +117,12 @@ __global__ __launch_bounds__(256) void ema_tile_carry(const float* __restrict__ 
     __syncthreads();
   }
   float4 cv = j > 0 ? shU[j - 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
   for (int q = 0; q < per; ++q) {
     const int64_t i = static_cast<int64_t>(j) * per + q;
     *reinterpret_cast<float4*>(carry + i * d + f0) = cv;
-    const float a = Aagg[i];
-    const float4 u = *reinterpret_cast<const float4*>(Uagg + i * d + f0);
+    const float a = ta[q];
+    const float4 u = tu[q];
     cv = make_float4(fmaf(a, cv.x, u.x), fmaf(a, cv.y, u.y), fmaf(a, cv.z, u.z), fmaf(a, cv.w, u.w));
   }
 }
