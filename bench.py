@@ -29,6 +29,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -298,6 +299,15 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.profile_op == "copy":
+        # plain device copy of a known size: the calibration for the HBM byte counters
+        src = torch.ones(COPY_BYTES // 4, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("profiled copy of", COPY_BYTES, "bytes,", args.steps, "launches")
+        return
     wl = Workload()
     if args.profile_op:
         f = dict(wl.ops())[args.profile_op]

@@ -21,10 +21,9 @@
 //   for each panel k:
 //     cr_diag       one wave per matrix factors the 64x64 diagonal tile (k, k),
 //                   writes the S-part pivots' logs and the inverse of the factor
-//     cr_panel      one workgroup per 64x64 tile below it (XCD-aware order):
-//                   left-looking update over the earlier panels, X = acc L_kk^-T;
-//                   the workgroup of the next row tile also forms the next
-//                   diagonal tile from the same staged row chunks and writes it
+//     cr_panel      one workgroup per matrix: every tile below the diagonal of
+//                   panel k (left-looking update over the earlier panels, then
+//                   X = acc L_kk^-T) and the next diagonal tile
 // Workspace: nmat = nseq * nblk matrices of ldm^2 fp32 (ldm = d' + c), plus a
 // 64x64 inverse slot per matrix.
 #include <cmath>
@@ -253,12 +252,10 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
 
 // ------------------------------------------------------------------ diagonal tile
 
-constexpr int PLD = 36;  // LDS row stride (floats) of 32-column chunks
-constexpr int XLD = 68;  // LDS row stride of 64-column tiles
 
-// Factor the 64x64 tile D (lower triangle; global, row stride ldd) with one wave:
-// the logs of its pivots that fall in the S part go to dR, the inverse of the
-// factor to Li (global, 64x64 row-major).  2x2 blocks of 32, lane i owns row i:
+// Factor the 64x64 tile D (lower triangle; LDS, row stride ldd) with one wave
+// of a larger workgroup: the logs of its pivots that fall in the S part go to
+// dR, the inverse of the factor to Li (LDS, row stride lip).  2x2 blocks of 32, lane i owns row i:
 //   1. eliminate columns 0..31 over all 64 rows  -> L11 (lanes 0..31), L21 (lanes 32..63)
 //   2. D22 - L21 L21^T, eliminate columns 32..63  -> L22 (lanes 32..63)
 //   3. columns of L11^-1 (lanes 0..31) and L22^-1 (lanes 32..63) by forward
@@ -278,8 +275,12 @@ __device__ __forceinline__ void ld4(const float* p, float* dst) {
   dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
 }
 
-__device__ __forceinline__ void factor64(const float* __restrict__ D, int64_t ldd, float* __restrict__ sW,
-                                         float* __restrict__ Li, float* __restrict__ dR_blk,
+// LDS ordering among the lanes of the one wave running factor64 (no barrier:
+// the other waves of the workgroup do not take part)
+__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup"); }
+
+__device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, float* __restrict__ sW,
+                                         float* __restrict__ Li, int lip, float* __restrict__ dR_blk,
                                          int rr0, int cj, int32_t* __restrict__ status) {
   float* col = sW;                 // [64]    column broadcast
   float* rinv = sW + 64;           // [64]    reciprocals of the diagonal of L
@@ -316,7 +317,7 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int64_t ld
 #pragma unroll
     for (int q = 0; q < 32; ++q) sT11[q * kF + i] = q <= i ? a[q] : 0.f;
   }
-  __syncthreads();
+  wave_lds_sync();
   float b[32];
 #pragma unroll
   for (int q = 0; q < 32; q += 4) ld4(D + i * ldd + 32 + q, b + q);
@@ -352,7 +353,7 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int64_t ld
     for (int q = 0; q < 32; ++q) sT22[q * kF + ih] = q <= ih ? b[q] : 0.f;
   }
   rinv[i] = rd;
-  __syncthreads();
+  wave_lds_sync();
   // 3. lane m < 32: column m of L11^-1; lane 32+m: column m of L22^-1.
   // sT holds L^T, so column p of L is the contiguous row p of sT.
   float x[32];
@@ -372,7 +373,7 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int64_t ld
       for (int r = p + 1; r < 32; ++r) x[r] = fmaf(-cv[r], x[p], x[r]);
     }
   }
-  __syncthreads();
+  wave_lds_sync();
   {
     // inverses to LDS (row-major, over the consumed transposes) and to Li
     float* Tw = hi ? sT22 : sT11;
@@ -381,15 +382,15 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int64_t ld
     if (!hi) {
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
-        Li[r * NB + i] = x[r];
-        Li[r * NB + 32 + i] = 0.f;
+        Li[r * lip + i] = x[r];
+        Li[r * lip + 32 + i] = 0.f;
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 32; ++r) Li[(32 + r) * NB + 32 + ih] = x[r];
+      for (int r = 0; r < 32; ++r) Li[(32 + r) * lip + 32 + ih] = x[r];
     }
   }
-  __syncthreads();
+  wave_lds_sync();
   if (hi) {
     // 4. lane 32+c: column c of Z = L21 L11^-1, then of Y = -L22^-1 Z
 #pragma unroll
@@ -412,7 +413,7 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int64_t ld
       float acc = 0.f;
 #pragma unroll
       for (int q = 0; q < 32; ++q) acc = fmaf(rw[q], x[q], acc);
-      Li[(32 + r) * NB + ih] = -acc;
+      Li[(32 + r) * lip + ih] = -acc;
     }
   }
   if (dR_blk != nullptr) {
@@ -421,10 +422,71 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int64_t ld
   }
 }
 
-// Panel k, diagonal tile: one wave per block matrix factors the 64x64 tile
-// (k, k) of the workspace -- the Gram prefix for k = 0, the tile the previous
-// panel's lookahead workgroup updated otherwise -- and writes the inverse of
-// its factor and, in the S part, the logs of its pivots.
+// ------------------------------------------------------------------ factorization
+// Left-looking by 64-column panels, two launches per panel over all block
+// matrices at once:
+//   cr_diag(k)   one wave per matrix factors the diagonal tile D_k (the Gram
+//                prefix for k = 0, else written by cr_panel(k-1)), stores
+//                Linv_k and, in the S part, the logs of the pivots
+//   cr_panel(k)  one workgroup per matrix builds every tile below the diagonal
+//                of panel k, in passes of kPassTiles tiles:
+//                  ACC_i = orig(i, k) -/+ sum_{cols < 64k} L[i, :] L[k, :]^T
+//                  L[i, k] = ACC_i Linv_k^T                            (TRSM)
+//                from row strips of L staged through LDS kChunk columns at a
+//                time (the panel's rows once per pass, every other strip row
+//                once), and the next diagonal tile
+//                  D_{k+1} = orig -/+ sum_{cols <= 64k+63} L[k+1, :] L[k+1, :]^T
+// Waves hold ACC_i^T (panel columns x tile rows), so the TRSM is
+// Linv_k * ACC_i^T with the accumulator registers as the MFMA B operand: with
+// the k index of MFMA step st taken as crow(st, lane), register st of a C/D
+// tile is exactly the B element that lane supplies.
+constexpr int kChunk = 16;                      // columns per staged strip chunk
+constexpr int kWaitVmcnt0 = 0x0F70;             // s_waitcnt vmcnt(0), other counters unconstrained
+constexpr int kSP = 20;                         // LDS row pitch of a strip chunk (floats)
+constexpr int kPassTiles = 2;                   // tiles below the diagonal per pass
+constexpr int kSlots = kPassTiles / 2;          // pass tiles per wave
+constexpr int kStripRows = 64 * (kPassTiles + 1);
+constexpr int kXP = 68;                         // LDS row pitch of 64x64 tiles
+constexpr int kStripFloats = 2 * kStripRows * kSP;
+constexpr int kPanelFloats = kStripFloats + 64 * kXP;
+static_assert(64 * kXP <= kStripFloats, "X staging must fit in the strip buffers");
+static_assert(kPassTiles == 2, "the strip loader below issues kPassTiles + 1 = 3 loads per set");
+
+// elements (row, col .. col+3), col % 4 == 0; a group lies wholly in one part
+template <int DT>
+__device__ inline float4 orig4(const void* h, const float* Mx, const CRGeom& g, int64_t hrow0, int cj,
+                               float salpha, int row, int col) {
+  if (col >= g.dp)
+    return make_float4(row == col ? 1.f : 0.f, row == col + 1 ? 1.f : 0.f, row == col + 2 ? 1.f : 0.f,
+                       row == col + 3 ? 1.f : 0.f);
+  if (row < g.dp) return *reinterpret_cast<const float4*>(Mx + static_cast<int64_t>(row) * g.ldm + col);
+  const int rr = row - g.dp;
+  if (rr >= cj || col >= g.d) return make_float4(0.f, 0.f, 0.f, 0.f);
+  const int64_t e = (hrow0 + rr) * g.d + col;
+  if (DT == BLLM_F32) {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(h) + e);
+    return make_float4(salpha * v.x, salpha * v.y, salpha * v.z, salpha * v.w);
+  }
+  const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(h) + e);
+  return make_float4(salpha * bf16_to_f32(static_cast<uint16_t>(v.x & 0xFFFFu)),
+                     salpha * bf16_to_f32(static_cast<uint16_t>(v.x >> 16)),
+                     salpha * bf16_to_f32(static_cast<uint16_t>(v.y & 0xFFFFu)),
+                     salpha * bf16_to_f32(static_cast<uint16_t>(v.y >> 16)));
+}
+
+// C/D tile registers of one lane from the row segments orig(row, col0 + crow(q, lane))
+template <int DT>
+__device__ inline floatx16 orig_tile_t(const void* h, const float* Mx, const CRGeom& g, int64_t hrow0,
+                                       int cj, float salpha, int row, int col0, int hh) {
+  floatx16 a;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const float4 v = orig4<DT>(h, Mx, g, hrow0, cj, salpha, row, col0 + 8 * q4 + 4 * hh);
+    a[4 * q4] = v.x; a[4 * q4 + 1] = v.y; a[4 * q4 + 2] = v.z; a[4 * q4 + 3] = v.w;
+  }
+  return a;
+}
+
 __global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __restrict__ linv,
                                               float* __restrict__ dR, int32_t* __restrict__ status,
                                               CRGeom g, int k) {
@@ -434,157 +496,211 @@ __global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __r
   if (NB * k >= block_n(g, j)) return;
   const float* D = ws + static_cast<int64_t>(m) * g.ldm * g.ldm + static_cast<int64_t>(NB * k) * g.ldm + NB * k;
   float* dRb = NB * k >= g.dp ? dR + static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c : nullptr;
-  factor64(D, g.ldm, sW, linv + static_cast<int64_t>(m) * NB * NB, dRb, NB * k - g.dp, block_rows(g, j), status);
+  factor64(D, g.ldm, sW, linv + static_cast<int64_t>(m) * NB * NB, NB, dRb, NB * k - g.dp,
+           block_rows(g, j), status);
 }
-
-// orig value of the diagonal tile (i, i): the A part from the Gram prefix, identity in the S part
-__device__ inline float orig_diag(const float* Mx, const CRGeom& g, int row, int col) {
-  return col >= g.dp ? (row == col ? 1.f : 0.f) : Mx[static_cast<int64_t>(row) * g.ldm + col];
-}
-
-// ------------------------------------------------------------------ panel tiles
 
 template <int DT>
-__device__ inline float orig_offdiag(const void* h, const float* Mx, const CRGeom& g, int64_t hrow0,
-                                     int cj, float salpha, int row, int col) {
-  if (col >= g.dp) return 0.f;  // S part below its diagonal tiles
-  if (row < g.dp) return Mx[static_cast<int64_t>(row) * g.ldm + col];
-  const int rr = row - g.dp;
-  if (rr >= cj || col >= g.d) return 0.f;
-  return salpha * load_elem(h, (hrow0 + rr) * g.d + col, DT);
-}
-
-// Panel k: one workgroup per 64x64 tile (i, k), i > k, of every block matrix.
-//   X = (orig(i,k) -/+ sum_{kk<k} L[i,kk] L[k,kk]^T) Linv_k^T      (left-looking)
-// The workgroup of tile i = k+1 (the lookahead tile) also forms the next
-// diagonal tile D = orig(i,i) -/+ sum_{kk<=k} L[i,kk] L[i,kk]^T from the same
-// staged row chunks, factors it and writes Linv_{k+1} and the pivots, so the
-// next panel needs no separate diagonal launch.
-// Grid: 8 * ceil(nmat/8) * ntk blocks; block b runs on XCD b % 8 and all tiles
-// of one matrix share an XCD (the panel rows L[k, :] stay in its L2).  The
-// lookahead tiles of all matrices come first so their serial tail overlaps
-// the rest of the launch.
-template <int DT>
-__global__ __launch_bounds__(256) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
-                                                const float* __restrict__ linv, CRGeom g,
-                                                float salpha, int k, int ntk) {
-  __shared__ __attribute__((aligned(16))) float smem[2 * 64 * XLD];
-  float* sA = smem;              // [64][PLD]  rows of tile i, current 32-column chunk
-  float* sB = smem + 64 * PLD;   // [64][PLD]  rows of tile k
-  float* sX = smem;              // [64][XLD]  reused after the update loop
-  float* sLi = smem + 64 * XLD;  // [64][XLD]
-  const int b = blockIdx.x;
-  const int xcd = b & 7, q = b >> 3;
-  const int m8 = (g.nmat + 7) / 8;
-  int m, t;
-  if (q < m8) { m = q * 8 + xcd; t = 0; }
-  else { const int q2 = q - m8; m = (q2 / (ntk - 1)) * 8 + xcd; t = 1 + q2 % (ntk - 1); }
-  if (m >= g.nmat) return;
-  const int i = k + 1 + t;
-  const int j = m % g.nblk;
-  const int nbn = block_n(g, j);
-  if (NB * i >= nbn) return;
-  const bool look = t == 0;
-  const int s = m / g.nblk;
+__global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
+                                                   const float* __restrict__ linv, CRGeom g,
+                                                   float salpha, int k) {
+  __shared__ __attribute__((aligned(16))) float lds[kPanelFloats];
+  float* sLi = lds + kStripFloats;      // Linv_k
+  float* sX = lds;                      // X_{k+1} (over the strip buffers)
+  const int m = blockIdx.x;
+  const int s = m / g.nblk, j = m % g.nblk;
+  const int npan = block_n(g, j) / NB;
+  if (k + 1 >= npan) return;
   const int cj = block_rows(g, j);
   const int64_t hrow0 = static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c;
   float* Mx = ws + static_cast<int64_t>(m) * g.ldm * g.ldm;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int wm = w >> 1, wn = w & 1;
-  const int row0 = NB * i + 32 * wm, col0 = NB * k + 32 * wn;
-  floatx16 acc, accD;
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-    acc[r] = orig_offdiag<DT>(h, Mx, g, hrow0, cj, salpha, row0 + crow(r, lane), col0 + (lane & 31));
-  if (look) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      accD[r] = orig_diag(Mx, g, row0 + crow(r, lane), NB * i + 32 * wn + (lane & 31));
-  }
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wp = w >> 1, wn = w & 1;  // pass tiles u = wp + 2 sl; tile-row half wn
+  const int dm = w >> 1, dn = w & 1;  // block of the lookahead tile
   const bool panelS = NB * k >= g.dp;
-  const bool rowS = NB * i >= g.dp;
-  // left-looking update over the 2k earlier 32-column chunks, loads of chunk
-  // c+1 in flight while chunk c runs on the MFMAs
-  const int nch = 2 * k;
-  const int lr = tid >> 3, lc = (tid & 7) * 4;  // loader: rows lr, lr+32; columns lc..lc+3
-  const float* gA = Mx + static_cast<int64_t>(NB * i + lr) * g.ldm + lc;
-  const float* gB = Mx + static_cast<int64_t>(NB * k + lr) * g.ldm + lc;
-  const int64_t r32 = 32 * static_cast<int64_t>(g.ldm);
-  float4 pa0, pa1, pb0, pb1;
-  if (nch > 0) {
-    pa0 = *reinterpret_cast<const float4*>(gA);
-    pa1 = *reinterpret_cast<const float4*>(gA + r32);
-    pb0 = *reinterpret_cast<const float4*>(gB);
-    pb1 = *reinterpret_cast<const float4*>(gB + r32);
-  }
-  for (int ch = 0; ch < nch; ++ch) {
-    __syncthreads();
-    *reinterpret_cast<float4*>(sA + lr * PLD + lc) = pa0;
-    *reinterpret_cast<float4*>(sA + (lr + 32) * PLD + lc) = pa1;
-    *reinterpret_cast<float4*>(sB + lr * PLD + lc) = pb0;
-    *reinterpret_cast<float4*>(sB + (lr + 32) * PLD + lc) = pb1;
-    __syncthreads();
-    if (ch + 1 < nch) {
-      const int co = 32 * (ch + 1);
-      pa0 = *reinterpret_cast<const float4*>(gA + co);
-      pa1 = *reinterpret_cast<const float4*>(gA + r32 + co);
-      pb0 = *reinterpret_cast<const float4*>(gB + co);
-      pb1 = *reinterpret_cast<const float4*>(gB + r32 + co);
-    }
-    const bool chA = 32 * ch < g.dp;
-    const float sg = (panelS && chA) ? 1.f : -1.f;
-    const float* pa = sA + (32 * wm + (lane & 31)) * PLD + 16 * (lane >> 5);
-    const float* pb = sB + (32 * wn + (lane & 31)) * PLD + 16 * (lane >> 5);
-#pragma unroll
-    for (int st = 0; st < 16; ++st) acc = mfma32(sg * pa[st], pb[st], acc);
-    if (look && wm >= wn) {
-      const float sd = (rowS && chA) ? 1.f : -1.f;
-      const float* pc = sA + (32 * wn + (lane & 31)) * PLD + 16 * (lane >> 5);
-#pragma unroll
-      for (int st = 0; st < 16; ++st) accD = mfma32(sd * pa[st], pc[st], accD);
+  const bool rowS1 = NB * (k + 1) >= g.dp;
+  const int nt = npan - k - 1;
+  const int nch = NB * k / kChunk;
+  {
+    const float* Li = linv + static_cast<int64_t>(m) * NB * NB;
+    for (int e = tid; e < NB * NB / 4; e += 256) {
+      const int r = e >> 4, cc = (e & 15) * 4;
+      *reinterpret_cast<float4*>(sLi + r * kXP + cc) = *reinterpret_cast<const float4*>(Li + r * NB + cc);
     }
   }
-  // X = acc * Linv_k^T
-  __syncthreads();
+  // lookahead tile, symmetric: read orig transposed for row-contiguous loads
+  floatx16 accD = orig_tile_t<DT>(h, Mx, g, hrow0, cj, salpha, NB * (k + 1) + 32 * dn + l32,
+                                  NB * (k + 1) + 32 * dm, hh);
+  for (int t0 = 0; t0 < nt; t0 += kPassTiles) {
+    const int npt = min(kPassTiles, nt - t0);
+    const bool first = t0 == 0;
+    floatx16 acc[kSlots][2];  // [slot][panel-column half]
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sX[(32 * wm + crow(r, lane)) * XLD + 32 * wn + (lane & 31)] = acc[r];
-  const float* Li = linv + static_cast<int64_t>(m) * NB * NB;
-  for (int e = tid; e < NB * NB / 4; e += blockDim.x) {
-    const int r = e >> 4, cc = (e & 15) * 4;
-    *reinterpret_cast<float4*>(sLi + r * XLD + cc) = *reinterpret_cast<const float4*>(Li + r * NB + cc);
-  }
-  __syncthreads();
-  floatx16 x = zero16();
+    for (int sl = 0; sl < kSlots; ++sl) {
+      const int u = wp + 2 * sl;
+      const int row = NB * (k + 1 + t0 + u) + 32 * wn + l32;
 #pragma unroll
-  for (int mb = 0; mb < NB; mb += 32) {
-    const float* pa = sX + (32 * wm + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
-    const float* pb = sLi + (32 * wn + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
-#pragma unroll
-    for (int st = 0; st < 16; ++st) x = mfma32(pa[st], pb[st], x);
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-    Mx[static_cast<int64_t>(row0 + crow(r, lane)) * g.ldm + col0 + (lane & 31)] = x[r];
-  if (!look) return;
-  // lookahead: D -/+= X X^T, written over the diagonal tile (i, i) for the next
-  // panel's diagonal kernel (lower quadrants only)
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sX[(32 * wm + crow(r, lane)) * XLD + 32 * wn + (lane & 31)] = x[r];
-  __syncthreads();
-  if (wm >= wn) {
-    const float sd = (rowS && !panelS) ? 1.f : -1.f;
-#pragma unroll
-    for (int mb = 0; mb < NB; mb += 32) {
-      const float* pa = sX + (32 * wm + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
-      const float* pc = sX + (32 * wn + (lane & 31)) * XLD + mb + 16 * (lane >> 5);
-#pragma unroll
-      for (int st = 0; st < 16; ++st) accD = mfma32(sd * pa[st], pc[st], accD);
+      for (int mb = 0; mb < 2; ++mb)
+        acc[sl][mb] = u < npt ? orig_tile_t<DT>(h, Mx, g, hrow0, cj, salpha, row, NB * k + 32 * mb, hh)
+                              : zero16();
     }
-    float* Dt = Mx + static_cast<int64_t>(NB * i + 32 * wm) * g.ldm + NB * i + 32 * wn;
+    // strip rows: the panel's 64 rows, then the pass tiles' rows.  Two sets of
+    // named prefetch registers: chunk ch + 2 is loaded while chunk ch is
+    // staged and multiplied.  Rows past the pass load a valid panel row
+    // instead and chunks past the end load the panel's own columns (inside
+    // the row, never staged), so the loads are unconditional and the wait
+    // counts static.
+    const int nrows = NB * (npt + 1);
+    const int lr = tid >> 2, lc = (tid & 3) * 4;
+    int go[3];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Dt[static_cast<int64_t>(crow(r, lane)) * g.ldm + (lane & 31)] = accD[r];
+    for (int it = 0; it < 3; ++it) {
+      const int r = lr + 64 * it;
+      const int grow = r < NB ? NB * k + r : (r < nrows ? NB * (k + 1 + t0) + (r - NB) : NB * k + (r & 63));
+      go[it] = grow * g.ldm + lc;
+    }
+    float4 qa0, qa1, qa2, qb0, qb1, qb2;
+    auto ldq = [&](int it, int co) { return *reinterpret_cast<const float4*>(Mx + go[it] + co); };
+    auto fetch_a = [&](int ch) {
+      const int co = ch * kChunk;
+      qa0 = ldq(0, co); qa1 = ldq(1, co); qa2 = ldq(2, co);
+    };
+    auto fetch_b = [&](int ch) {
+      const int co = ch * kChunk;
+      qb0 = ldq(0, co); qb1 = ldq(1, co); qb2 = ldq(2, co);
+    };
+    auto stash = [&](float* sb, const float4& v0, const float4& v1, const float4& v2) {
+      *reinterpret_cast<float4*>(sb + lr * kSP + lc) = v0;
+      *reinterpret_cast<float4*>(sb + (lr + 64) * kSP + lc) = v1;
+      *reinterpret_cast<float4*>(sb + (lr + 128) * kSP + lc) = v2;
+    };
+    auto compute = [&](const float* sb, int ch) {
+      const bool chA = ch * kChunk < g.dp;
+      const float sg = (panelS && chA) ? 1.f : -1.f;
+      float a0[8], a1[8];
+      ld4(sb + l32 * kSP + 8 * hh, a0);
+      ld4(sb + l32 * kSP + 8 * hh + 4, a0 + 4);
+      ld4(sb + (32 + l32) * kSP + 8 * hh, a1);
+      ld4(sb + (32 + l32) * kSP + 8 * hh + 4, a1 + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { a0[e] *= sg; a1[e] *= sg; }
+#pragma unroll
+      for (int sl = 0; sl < kSlots; ++sl) {
+        const int u = wp + 2 * sl;
+        if (u < npt) {
+          float b[8];
+          const float* pb = sb + (NB + NB * u + 32 * wn + l32) * kSP + 8 * hh;
+          ld4(pb, b);
+          ld4(pb + 4, b + 4);
+#pragma unroll
+          for (int st = 0; st < 8; ++st) {
+            acc[sl][0] = mfma32(a0[st], b[st], acc[sl][0]);
+            acc[sl][1] = mfma32(a1[st], b[st], acc[sl][1]);
+          }
+        }
+      }
+      if (first) {
+        const float sd = (rowS1 && chA) ? 1.f : -1.f;
+        float da[8], db[8];
+        ld4(sb + (NB + 32 * dm + l32) * kSP + 8 * hh, da);
+        ld4(sb + (NB + 32 * dm + l32) * kSP + 8 * hh + 4, da + 4);
+        ld4(sb + (NB + 32 * dn + l32) * kSP + 8 * hh, db);
+        ld4(sb + (NB + 32 * dn + l32) * kSP + 8 * hh + 4, db + 4);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) accD = mfma32(sd * da[st], db[st], accD);
+      }
+    };
+    float* sb0 = lds;
+    float* sb1 = lds + kStripRows * kSP;
+    // the accumulators were loaded from memory: wait here once, so that the
+    // loop's only outstanding loads are the prefetches
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (nch > 0) {
+      fetch_a(0);
+      fetch_b(1);
+    }
+    // one LDS-only barrier per chunk (the prefetches stay in flight): a buffer
+    // is restaged only after every wave has passed the barrier of the chunk
+    // staged in between
+    for (int ch = 0; ch < nch; ch += 2) {
+      stash(sb0, qa0, qa1, qa2);
+      lds_barrier();
+      fetch_a(ch + 2);
+      compute(sb0, ch);
+      if (ch + 1 < nch) {
+        stash(sb1, qb0, qb1, qb2);
+        lds_barrier();
+        fetch_b(ch + 3);
+        compute(sb1, ch + 1);
+      }
+    }
+    __syncthreads();  // strip buffers free (sX lives there); sLi staged
+    // TRSM: X_u^T = Linv_k * ACC_u^T, written as rows of L
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) {
+      const int u = wp + 2 * sl;
+      if (u < npt) {
+        floatx16 x0 = zero16(), x1 = zero16();
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float l00[4], l10[4], l11[4];
+          const int kc = 8 * q4 + 4 * hh;  // crow(4*q4 + e, lane) = kc + e
+          ld4(sLi + l32 * kXP + kc, l00);
+          ld4(sLi + (32 + l32) * kXP + kc, l10);
+          ld4(sLi + (32 + l32) * kXP + 32 + kc, l11);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int st = 4 * q4 + e;
+            x0 = mfma32(l00[e], acc[sl][0][st], x0);
+            x1 = mfma32(l10[e], acc[sl][0][st], x1);
+            x1 = mfma32(l11[e], acc[sl][1][st], x1);
+          }
+        }
+        const int row = NB * (k + 1 + t0 + u) + 32 * wn + l32;
+        float* Lr = Mx + static_cast<int64_t>(row) * g.ldm + NB * k;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int kc = 8 * q4 + 4 * hh;
+          *reinterpret_cast<float4*>(Lr + kc) =
+              make_float4(x0[4 * q4], x0[4 * q4 + 1], x0[4 * q4 + 2], x0[4 * q4 + 3]);
+          *reinterpret_cast<float4*>(Lr + 32 + kc) =
+              make_float4(x1[4 * q4], x1[4 * q4 + 1], x1[4 * q4 + 2], x1[4 * q4 + 3]);
+        }
+        if (first && u == 0) {
+          float* xr = sX + (32 * wn + l32) * kXP;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int kc = 8 * q4 + 4 * hh;
+            *reinterpret_cast<float4*>(xr + kc) =
+                make_float4(x0[4 * q4], x0[4 * q4 + 1], x0[4 * q4 + 2], x0[4 * q4 + 3]);
+            *reinterpret_cast<float4*>(xr + 32 + kc) =
+                make_float4(x1[4 * q4], x1[4 * q4 + 1], x1[4 * q4 + 2], x1[4 * q4 + 3]);
+          }
+        }
+      }
+    }
+    if (first) {
+      // D_{k+1} -/+= X_{k+1} X_{k+1}^T over the panel's columns
+      __syncthreads();
+      const float sd = (rowS1 && !panelS) ? 1.f : -1.f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float da[16], db[16];
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+          ld4(sX + (32 * dm + l32) * kXP + 32 * half + 16 * hh + e, da + e);
+          ld4(sX + (32 * dn + l32) * kXP + 32 * half + 16 * hh + e, db + e);
+        }
+#pragma unroll
+        for (int st = 0; st < 16; ++st) accD = mfma32(sd * da[st], db[st], accD);
+      }
+    }
+    __syncthreads();  // sX and the strip buffers are reused next
   }
+  // D_{k+1} over the diagonal tile (k+1, k+1), whose original is consumed
+  float* Dt = Mx + static_cast<int64_t>(NB * (k + 1) + 32 * dm) * g.ldm + NB * (k + 1) + 32 * dn;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) Dt[static_cast<int64_t>(crow(q, lane)) * g.ldm + l32] = accD[q];
 }
 
 CRGeom cr_geometry(int64_t nseq, int64_t T, int64_t d) {
@@ -609,7 +725,6 @@ size_t cr_ws_bytes(const CRGeom& g) {
 template <int DT>
 void cr_launch(const void* h, const CRGeom& g, int nseq, double alpha, float* dR, int32_t* status,
                float* ws, hipStream_t st) {
-  float* linv = ws + static_cast<int64_t>(g.nmat) * g.ldm * g.ldm;
   const int nt = g.dp / NB;
   const unsigned ggrid = static_cast<unsigned>((nseq + 7) / 8 * 8 * (nt * (nt + 1) / 2));
   if (DT == BLLM_BF16)
@@ -617,15 +732,13 @@ void cr_launch(const void* h, const CRGeom& g, int nseq, double alpha, float* dR
                        static_cast<float>(alpha));
   else
     hipLaunchKernelGGL(cr_gram_prefix<DT>, dim3(ggrid), dim3(256), 0, st, h, ws, g, static_cast<float>(alpha));
+  float* linv = ws + static_cast<int64_t>(g.nmat) * g.ldm * g.ldm;
   const int npan = g.ldm / NB;
   const float salpha = static_cast<float>(std::sqrt(alpha));
   for (int k = 0; k < npan; ++k) {
     hipLaunchKernelGGL(cr_diag, dim3(g.nmat), dim3(64), 0, st, ws, linv, dR, status, g, k);
-    const int ntk = npan - k - 1;
-    if (ntk > 0) {
-      const unsigned grid = static_cast<unsigned>((g.nmat + 7) / 8 * 8 * ntk);
-      hipLaunchKernelGGL(cr_panel<DT>, dim3(grid), dim3(256), 0, st, h, ws, linv, g, salpha, k, ntk);
-    }
+    if (k + 1 < npan)
+      hipLaunchKernelGGL(cr_panel<DT>, dim3(g.nmat), dim3(256), 0, st, h, ws, linv, g, salpha, k);
   }
 }
 

@@ -115,6 +115,15 @@ __device__ inline float group_sum(float v) {
 
 __device__ inline int lane_id() { return __lane_id(); }
 
+// Workgroup barrier that orders LDS only: unlike __syncthreads it does not
+// wait for this wave's outstanding global loads, so prefetches stay in flight
+// across it.  Global stores are not made visible by it.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // number of set bits of `mask` in lanes below this one
 __device__ inline int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
