@@ -173,10 +173,11 @@ __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h
   }
 }
 
-// bf16 input: the same 64x64 prefix tiles, one whole block of c <= 128 rows
-// per iteration.  The next block's rows are in flight in registers while the
-// current one runs on the MFMAs; each thread owns 4 consecutive rows x 8
-// features and writes them transposed as one 8-byte LDS store per feature.
+// bf16 input: the same 64x64 prefix tiles, rows taken in sub-chunks of R = 128
+// rows (64 when c is not a multiple of 128), so a block holds c / R of them.
+// The next sub-chunk's rows are in flight in registers while the current one
+// runs on the MFMAs; each thread owns 4 consecutive rows x 8 features and
+// writes them transposed as one 8-byte LDS store per feature.
 __device__ inline uint2 pack4_bf16(uint4 r0, uint4 r1, uint4 r2, uint4 r3, int e) {
   const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r0);
   const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r1);
@@ -202,14 +203,17 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int wm = w >> 1, wn = w & 1;
   const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
+  const int R = g.c % 128 == 0 ? 128 : 64;
+  const int spb = g.c / R;                // sub-chunks per block
+  const int nq = (g.nblk - 1) * spb;      // sub-chunks that feed some prefix
   const int rq = (tid >> 3) * 4, fc = (tid & 7) * 8;
   const bool fiok = 64 * I + fc < g.d, fjok = 64 * J + fc < g.d;
   const uint16_t* hI = h + static_cast<int64_t>(s) * g.T * g.d + 64 * I + fc;
   const uint16_t* hJ = h + static_cast<int64_t>(s) * g.T * g.d + 64 * J + fc;
   const uint4 z4 = make_uint4(0, 0, 0, 0);
   uint4 xi0, xi1, xi2, xi3, xj0, xj1, xj2, xj3;
-  auto fetch = [&](int j) {
-    const int r0 = j * g.c + rq, rend = min(j * g.c + g.c, g.T);
+  auto fetch = [&](int q) {
+    const int r0 = q * R + rq, rend = min(q * R + R, g.T);
     const int64_t o = static_cast<int64_t>(r0) * g.d;
     const bool q0 = r0 < rend, q1 = r0 + 1 < rend, q2 = r0 + 2 < rend, q3 = r0 + 3 < rend;
     xi0 = fiok && q0 ? *reinterpret_cast<const uint4*>(hI + o) : z4;
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       xj3 = fjok && q3 ? *reinterpret_cast<const uint4*>(hJ + o + 3 * g.d) : z4;
     }
   };
-  if (g.nblk > 1) fetch(0);
+  if (nq > 0) fetch(0);
   floatx16 acc = zero16();
   const uint16_t* sJr = same ? sI : sJ;
   for (int j = 0; j < g.nblk; ++j) {
@@ -234,18 +238,21 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
     }
     if (j == g.nblk - 1) break;
-    __syncthreads();
+    for (int sq = 0; sq < spb; ++sq) {
+      const int q = j * spb + sq;
+      __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      *reinterpret_cast<uint2*>(sI + (fc + e) * LDR + rq) = pack4_bf16(xi0, xi1, xi2, xi3, e);
-      if (!same) *reinterpret_cast<uint2*>(sJ + (fc + e) * LDR + rq) = pack4_bf16(xj0, xj1, xj2, xj3, e);
-    }
-    __syncthreads();
-    if (j + 1 < g.nblk - 1) fetch(j + 1);
-    for (int k0 = 0; k0 < g.c; k0 += 16) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sI + (32 * wm + (lane & 31)) * LDR + k0 + 8 * (lane >> 5));
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(sJr + (32 * wn + (lane & 31)) * LDR + k0 + 8 * (lane >> 5));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      for (int e = 0; e < 8; ++e) {
+        *reinterpret_cast<uint2*>(sI + (fc + e) * LDR + rq) = pack4_bf16(xi0, xi1, xi2, xi3, e);
+        if (!same) *reinterpret_cast<uint2*>(sJ + (fc + e) * LDR + rq) = pack4_bf16(xj0, xj1, xj2, xj3, e);
+      }
+      __syncthreads();
+      if (q + 1 < nq) fetch(q + 1);
+      for (int k0 = 0; k0 < R; k0 += 16) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sI + (32 * wm + (lane & 31)) * LDR + k0 + 8 * (lane >> 5));
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(sJr + (32 * wn + (lane & 31)) * LDR + k0 + 8 * (lane >> 5));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      }
     }
   }
 }
@@ -708,8 +715,9 @@ CRGeom cr_geometry(int64_t nseq, int64_t T, int64_t d) {
   g.T = static_cast<int>(T);
   g.d = static_cast<int>(d);
   g.dp = static_cast<int>((d + NB - 1) / NB * NB);
+  // c near d/2 minimises the factorization flops per row, (d' + c)^3 / (3c)
   int c = (g.dp / 2 + NB - 1) / NB * NB;
-  c = c < NB ? NB : (c > 128 ? 128 : c);
+  c = c < NB ? NB : (c > 256 ? 256 : c);
   g.c = c;
   g.nblk = static_cast<int>((T + c - 1) / c);
   g.ldm = g.dp + c;

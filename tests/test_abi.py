@@ -43,7 +43,9 @@ def test_workspace_sizes(L):
     assert L.bllm_compact_workspace(10**6) >= (10**6 // 4096) * 4
     assert L.bllm_dechunk_workspace(512) >= 2 * 4096 * 512 * 4
     # nseq * nblk * ldm^2 fp32 with ldm = d' + c: d=512 -> c=128, ldm=640, nblk=64
-    assert L.bllm_coding_rate_workspace(32, 8192, 512) >= 32 * 64 * 640 * 640 * 4
+    # d = 512: blocks of c = 256 rows, 32 blocks per sequence, block matrices of
+    # (512 + 256)^2 fp32 plus a 64 x 64 inverse slot each
+    assert L.bllm_coding_rate_workspace(32, 8192, 512) == 32 * 32 * (768 * 768 + 64 * 64) * 4 + 256
     assert L.bllm_coding_rate_workspace(0, 8192, 512) == 0
     assert L.bllm_upsample_workspace(32, 8192, 2048, 1536, 512, 16) >= 16 * 1536 * 512 * 2
 
