@@ -2,11 +2,11 @@
 
 One step = one pass of the whole chunk layer over one batch of 32 byte
 streams of 8192 bytes each:
-  * H-Net two-stage hierarchy (the C2 workload at T = 8192): route with the
+  * H-Net two-stage hierarchy (32 event streams of 8192 bytes): route with the
     stage's 0.75 score quantile, compact, route + compact the stage-2 rows,
     EMA-dechunk stage 2 back to stage-1 length, EMA-dechunk stage 1 back to
     bytes (d_local 512, d_mid 768, bf16);
-  * ByteFlow layer (the C4 workload): coding rate Delta R (d 512, eps^2 0.5),
+  * ByteFlow layer (32 x 8192 x 512): coding rate Delta R (d 512, eps^2 0.5),
     BOS + Top-(K-1) with K = 2048, gather of the K rows, 16-bin multi-linear
     upsample from d_global 1536 with the residual (bf16).
 The random stand-ins around the layer (q/k projections, the stage-2 input
@@ -52,26 +52,26 @@ class Workload:
     def __init__(self):
         import torch
         import byte_level_lm_amd as B
-        from synthdata import gen_c2, gen_c4
+        from synthdata import gen_hnet_two_stage, gen_byteflow_layer
 
         self.B = B
         self.torch = torch
         bf = torch.bfloat16
         dev = torch.device("cuda")
         t0 = time.time()
-        c2 = gen_c2(fixed_T=8192)
-        c4 = gen_c4()
+        hn = gen_hnet_two_stage(fixed_T=8192)
+        bfl = gen_byteflow_layer()
         log(f"inputs generated in {time.time() - t0:.1f}s")
-        self.c2, self.c4 = c2, c4
+        self.hn, self.bfl = hn, bfl
         T = 8192
         self.nseq = 32
-        self.N = int(c2["offsets"][-1])
+        self.N = int(hn["offsets"][-1])
         assert self.N == self.nseq * T
         # ---------------- H-Net
-        self.off = torch.from_numpy(c2["offsets"]).to(dev)
-        self.h1 = torch.from_numpy(c2["h"]).to(dev, bf)
-        self.q1 = torch.from_numpy(c2["q"]).to(dev, bf)
-        self.k1 = torch.from_numpy(c2["k"]).to(dev, bf)
+        self.off = torch.from_numpy(hn["offsets"]).to(dev)
+        self.h1 = torch.from_numpy(hn["h"]).to(dev, bf)
+        self.q1 = torch.from_numpy(hn["q"]).to(dev, bf)
+        self.k1 = torch.from_numpy(hn["k"]).to(dev, bf)
         N = self.N
         self.p1 = torch.empty(N, device=dev)
         self.b1 = torch.empty(N, dtype=torch.uint8, device=dev)
@@ -88,9 +88,9 @@ class Workload:
         torch.cuda.synchronize()
         self.M1 = int(self.coff1[-1].item())
         M1 = self.M1
-        w_mid = torch.from_numpy(c2["w_mid"]).to(dev, torch.float32)
-        wq2 = torch.from_numpy(c2["wq2"]).to(dev, torch.float32)
-        wk2 = torch.from_numpy(c2["wk2"]).to(dev, torch.float32)
+        w_mid = torch.from_numpy(hn["w_mid"]).to(dev, torch.float32)
+        wq2 = torch.from_numpy(hn["wq2"]).to(dev, torch.float32)
+        wk2 = torch.from_numpy(hn["wk2"]).to(dev, torch.float32)
         self.x2 = (self.z1[:M1].float() @ w_mid).to(bf)
         self.q2 = (self.x2.float() @ wq2).to(bf)
         self.k2 = (self.x2.float() @ wk2).to(bf)
@@ -108,11 +108,11 @@ class Workload:
         self._dechunk2()
         torch.cuda.synchronize()
         self.M2 = int(self.coff2[-1].item())
-        w_back = torch.from_numpy(c2["w_back"]).to(dev, torch.float32)
+        w_back = torch.from_numpy(hn["w_back"]).to(dev, torch.float32)
         self.y1 = (self.y2.float() @ w_back).to(bf)  # stand-in projection back to d_local
         # ---------------- ByteFlow
-        self.K, self.nbins = c4["K"], c4["nbins"]
-        self.h4 = torch.from_numpy(c4["h"]).to(dev, bf)
+        self.K, self.nbins = bfl["K"], bfl["nbins"]
+        self.h4 = torch.from_numpy(bfl["h"]).to(dev, bf)
         self.off4 = torch.arange(self.nseq + 1, dtype=torch.int64, device=dev) * T
         self.dR = torch.empty((self.nseq, T), device=dev)
         self.ws_cr = torch.empty(B.coding_rate_workspace(self.nseq, T, 512), dtype=torch.uint8, device=dev)
@@ -122,13 +122,13 @@ class Workload:
         self.coff4 = torch.empty(self.nseq + 1, dtype=torch.int64, device=dev)
         self.z4 = torch.empty((self.nseq * self.K, 512), dtype=bf, device=dev)
         self.ws_compact4 = torch.empty(B.compact_workspace(self.N), dtype=torch.uint8, device=dev)
-        self.W = torch.from_numpy(c4["w_bin"]).to(dev, bf)
+        self.W = torch.from_numpy(bfl["w_bin"]).to(dev, bf)
         self.s4 = torch.empty_like(self.h4)
         self.ws_up = torch.empty(B.upsample_workspace(self.nseq, T, self.K, 1536, 512, self.nbins),
                                  dtype=torch.uint8, device=dev)
         self._coding_rate(); self._topk(); self._gather()
         torch.cuda.synchronize()
-        w_g = torch.from_numpy(c4["w_g"]).to(dev, torch.float32)
+        w_g = torch.from_numpy(bfl["w_g"]).to(dev, torch.float32)
         self.g4 = (self.z4.float() @ w_g).to(bf).view(self.nseq, self.K, 1536)  # global stand-in
         self._upsample()
         torch.cuda.synchronize()
@@ -207,6 +207,22 @@ class Workload:
         }
 
 
+def coding_rate_traffic():
+    """HBM bytes per bllm_coding_rate call from the committed rocprofv3 counter
+    summary, or None when it is missing or its sources have changed since."""
+    import re
+    from byte_level_lm_amd.profsum import sources_sha256
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "coding_rate_bf16_32x8192x512.md")
+    try:
+        text = open(path).read()
+        block = json.loads(re.findall(r"```json\n(.*?)\n```", text, re.S)[-1])
+    except (OSError, IndexError, ValueError):
+        return None
+    if block.get("sources_sha256") != sources_sha256("coding_rate") or "hbm_bytes_per_call" not in block:
+        return None
+    return block["hbm_bytes_per_call"]
+
+
 def time_ops(wl, reps=5):
     """Average duration of each op (HIP events on the stream the kernels run on)."""
     torch = wl.torch
@@ -229,20 +245,20 @@ def cpu_baseline(wl):
     """The oracle, as it stands, on a bounded sample of the same workload, one thread."""
     from threadpoolctl import threadpool_limits
     import oracle
-    from synthdata import gen_c2_stage2_inputs, gen_c2_backproj, gen_c4_global
+    from synthdata import gen_stage2_inputs, gen_stage2_backproj, gen_global_standin
 
-    c2, c4 = wl.c2, wl.c4
+    hn, bfl = wl.hn, wl.bfl
     T = 8192
     with threadpool_limits(limits=1):
         # H-Net two-stage layer on the first stream (8192 bytes)
         t0 = time.perf_counter()
         off = np.array([0, T], np.int64)
-        q, k, h = c2["q"][:T], c2["k"][:T], c2["h"][:T]
+        q, k, h = hn["q"][:T], hn["k"][:T], hn["h"][:T]
         p1 = oracle.route(q, k, off)
         tau1 = oracle.stage_quantile(p1, 0.75)
         b1 = oracle.boundary_mask(p1, tau1)
         i1, co1, z1, P1 = oracle.compact(b1, p1, h, off)
-        s2 = gen_c2_stage2_inputs(z1, c2)
+        s2 = gen_stage2_inputs(z1, hn)
         t_standin = time.perf_counter()
         p2 = oracle.route(s2["q2"], s2["k2"], co1)
         t_standin = time.perf_counter() - t_standin
@@ -250,27 +266,26 @@ def cpu_baseline(wl):
         b2 = oracle.boundary_mask(p2, tau2)
         i2, co2, z2, P2 = oracle.compact(b2, p2, s2["x2"], co1)
         y2 = oracle.dechunk_ema(z2, P2, i2, co2, co1)
-        y1 = gen_c2_backproj(y2, c2)
+        y1 = gen_stage2_backproj(y2, hn)
         oracle.dechunk_ema(y1, P1, i1, co1, off)
         t_hnet = time.perf_counter() - t0
         # ByteFlow: Delta R on the first 768 positions of stream 0
         npos = 768
         t0 = time.perf_counter()
-        oracle.coding_rate_at(c4["h"][0].astype(np.float64), 0.5, np.arange(npos))
+        oracle.coding_rate_at(bfl["h"][0].astype(np.float64), 0.5, np.arange(npos))
         t_dr = time.perf_counter() - t0
         dr = wl.dR[0:1].cpu().numpy()
         t0 = time.perf_counter()
         sel = oracle.topk_select(dr, wl.K)
-        z = oracle.gather(c4["h"][0:1], sel)
+        z = oracle.gather(bfl["h"][0:1], sel)
         t_topk = time.perf_counter() - t0
-        g = gen_c4_global(z, c4)
+        g = gen_global_standin(z, bfl)
         nup = 2048
         t0 = time.perf_counter()
-        oracle.upsample_bins(g, c4["w_bin"], sel, c4["h"][0:1, :], c4["nbins"]) if False else None
         # upsample of the first nup positions of the stream (same per-position work)
-        cmap, bins = oracle.chunk_bins(sel[0], T, c4["nbins"])
-        hh = c4["h"][0].astype(np.float64)
-        W = c4["w_bin"].astype(np.float64)
+        cmap, bins = oracle.chunk_bins(sel[0], T, bfl["nbins"])
+        hh = bfl["h"][0].astype(np.float64)
+        W = bfl["w_bin"].astype(np.float64)
         gg = g[0].astype(np.float64)
         for t in range(nup):
             _ = hh[t] + gg[cmap[t]] @ W[bins[t]]
@@ -320,16 +335,28 @@ def main():
         wl.step()
     torch.cuda.synchronize()
     log("warmup done")
+    # the dominant op is bracketed by events of its own inside the timed steps
+    # (all ops run on torch's current stream)
+    dom_name = "coding_rate"
+    dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     t0 = time.perf_counter()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record()
     for i in range(args.steps):
-        wl.step()
+        for name, f in wl.ops():
+            if name == dom_name:
+                dom_ev[i][0].record()
+                f()
+                dom_ev[i][1].record()
+            else:
+                f()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
+    dom_ms = sum(a.elapsed_time(b) for a, b in dom_ev) / args.steps
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f}s)")
     per_op = time_ops(wl)
     alg = wl.algorithmic()
@@ -342,17 +369,21 @@ def main():
         if "flops" in a:
             d["TFLOPs"] = round(a["flops"] / (t * 1e-3) / 1e12, 2)
         breakdown[name] = d
-    dom = max(per_op, key=per_op.get)
     cr = alg["coding_rate"]
     roof = {
-        "kernel": "bllm_coding_rate (cr_gram_prefix + cr_factor), fp32 MFMA",
+        "kernel": "one bllm_coding_rate call: cr_gram_prefix_bf16 + 12 cr_diag + 11 cr_panel, fp32 MFMA",
         "bound": "mfma",
-        "achieved": round(cr["flops"] / (per_op["coding_rate"] * 1e-3) / 1e12, 3),
+        "achieved": round(cr["flops"] / (dom_ms * 1e-3) / 1e12, 3),
         "peak": FP32_MFMA_PEAK_TFLOPS,
         "unit": "TFLOP/s",
-        "traffic": None,
+        "traffic": coding_rate_traffic(),
     }
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    # the Gram's 2d^2 of the 3d^2 flops per row are exact in bf16: mixed ideal time
+    ideal_ms = (2 * cr["flops"] / 3 / (BF16_MFMA_PEAK_TFLOPS * 1e12) + cr["flops"] / 3 / (FP32_MFMA_PEAK_TFLOPS * 1e12)) * 1e3
+    roof["op_ms"] = round(dom_ms, 4)
+    roof["mixed_precision_ideal_ms"] = round(ideal_ms, 4)
+    roof["mixed_precision_frac"] = round(ideal_ms / dom_ms, 4)
     hnet_ms = sum(per_op[n] for n in ("route+compact stage1", "route+compact stage2", "dechunk stage2", "dechunk stage1"))
     hnet_bytes = sum(alg[n]["bytes"] for n in ("route+compact stage1", "route+compact stage2", "dechunk stage2", "dechunk stage1"))
     out = {
@@ -375,7 +406,7 @@ def main():
                                 "upsample_items": wl.up_items},
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "dominant_op": dom,
+        "dominant_op": dom_name,
         "breakdown": breakdown,
         "hnet_layer": {"ms": round(hnet_ms, 4), "bytes_per_s": wl.N / (hnet_ms * 1e-3),
                        "hbm_GBps": round(hnet_bytes / (hnet_ms * 1e-3) / 1e9, 1),

@@ -1,0 +1,185 @@
+"""Summaries of rocprofv3 runs of bench.py, written as short markdown files.
+
+    python -m byte_level_lm_amd.profsum --op coding_rate --trace DIR \
+        [--fetch DIR --write DIR --copy-fetch DIR --copy-write DIR] \
+        --cmd "the rocprofv3 commands" --workload "..." --out profiles/NAME.md
+    python -m byte_level_lm_amd.profsum --op step --trace DIR --cmd ... --workload ... --out ...
+
+DIR is a rocprofv3 ``--output-format csv`` directory.  ``--trace`` holds a
+``--kernel-trace --stats`` run; ``--fetch``/``--write`` hold ``--pmc FETCH_SIZE``
+and ``--pmc WRITE_SIZE`` runs of the same op; ``--copy-*`` the same counters
+for ``bench.py --profile-op copy`` (a device copy of ``bench.COPY_BYTES``),
+which calibrates KiB-per-dispatch counter values into bytes.
+
+The summary ends with a JSON block (op, per-call duration, HBM bytes per call,
+SHA-256 of the op's sources) that bench.py reads for its roofline traffic; it
+ignores the block once the sources have changed.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+# kernels that make up one call of each C-ABI op, and the sources they come from
+OPS = {
+    "coding_rate": (("cr_gram_prefix", "cr_diag", "cr_panel"), ("coding_rate.hip", "common.h")),
+    "upsample_bins": (("up_count", "up_offsets", "up_items", "up_transpose", "up_gemm"),
+                      ("upsample.hip", "common.h")),
+}
+
+
+def sources_sha256(op: str) -> str:
+    h = hashlib.sha256()
+    for name in OPS[op][1]:
+        with open(os.path.join(HERE, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _short(name: str) -> str:
+    n = name.split("(anonymous namespace)::", 1)[1] if "(anonymous namespace)::" in name else name
+    return n.split("(")[0].replace("void ", "").strip()
+
+
+def _one(d: str, pattern: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no {pattern} under {d}")
+    return hits[0]
+
+
+def _of_op(op: str, name: str) -> bool:
+    return any(_short(name).startswith(p) for p in OPS[op][0])
+
+
+def trace_calls(op: str, d: str):
+    """Kernel dispatches of the op grouped into calls (a call starts at its first kernel)."""
+    rows = list(csv.DictReader(open(_one(d, "*kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    first = OPS[op][0][0]
+    calls = []
+    for r in rows:
+        if not _of_op(op, r["Kernel_Name"]):
+            continue
+        if _short(r["Kernel_Name"]).startswith(first) or not calls:
+            calls.append([])
+        calls[-1].append(r)
+    return calls
+
+
+def counter_last_call(op: str, d: str, counter: str) -> float:
+    """Sum of a counter (KiB) over the kernels of the op's last call in a --pmc run."""
+    rows = list(csv.DictReader(open(_one(d, "*counter_collection.csv"))))
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = int(r["Dispatch_Id"])
+        per.setdefault(key, [r["Kernel_Name"], 0.0])
+        per[key][1] += float(r["Counter_Value"])
+    disp = sorted(per.items())
+    first = OPS[op][0][0]
+    starts = [i for i, (_, (n, _)) in enumerate(disp) if _short(n).startswith(first)]
+    if not starts:
+        raise ValueError(f"no {first} dispatch in {d}")
+    return sum(v for _, (n, v) in disp[starts[-1]:] if _of_op(op, n))
+
+
+def counter_copy(d: str, counter: str) -> float:
+    rows = list(csv.DictReader(open(_one(d, "*counter_collection.csv"))))
+    vals = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]:
+            vals[int(r["Dispatch_Id"])] = vals.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise ValueError(f"no copy dispatch with {counter} in {d}")
+    return vals[max(vals)]
+
+
+def step_summary(d: str, cmd: str, workload: str, out: str, top: int = 25):
+    """Per-kernel table of a whole run (kernel_stats.csv), longest total first."""
+    rows = list(csv.DictReader(open(_one(d, "*kernel_stats.csv"))))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# rocprofv3 summary: {workload}", "", "Command (run from the repository root on the GPU host):", "",
+             "```", cmd, "```", "", "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
+    for r in rows[:top]:
+        lines.append(f"| {_short(r['Name'])[:60]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--op", required=True, choices=sorted(OPS) + ["step"])
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--cmd", required=True, help="the full commands that produced the runs")
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--out", required=True)
+    a = ap.parse_args()
+    if a.op == "step":
+        step_summary(a.trace, a.cmd, a.workload, a.out)
+        return
+
+    calls = trace_calls(a.op, a.trace)
+    timed = calls[1:] if len(calls) > 1 else calls  # the first call is bench.py's set-up pass
+    per_kernel = {}
+    for c in timed:
+        for r in c:
+            per_kernel.setdefault(_short(r["Kernel_Name"]), []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    call_ns = [sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in c) for c in timed]
+    span_ns = [int(c[-1]["End_Timestamp"]) - int(c[0]["Start_Timestamp"]) for c in timed]
+
+    lines = [f"# rocprofv3 summary: {a.op}, {a.workload}", "", "Commands (run from the repository root on the GPU host):", "",
+             "```", a.cmd, "```", "",
+             f"Calls profiled: {len(timed)} (after the set-up call).  Kernel time per call "
+             f"(sum of its kernels): {statistics.mean(call_ns) / 1e3:.1f} us; first-to-last span "
+             f"{statistics.mean(span_ns) / 1e3:.1f} us.", "",
+             "| kernel | launches per call | avg us | total us per call |", "|---|---|---|---|"]
+    for k, v in sorted(per_kernel.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {k} | {len(v) / len(timed):g} | {statistics.mean(v) / 1e3:.1f} | "
+                     f"{sum(v) / len(timed) / 1e3:.1f} |")
+    block = {"op": a.op, "workload": a.workload, "kernel_us_per_call": round(statistics.mean(call_ns) / 1e3, 2),
+             "sources_sha256": sources_sha256(a.op)}
+    if a.fetch and a.write and a.copy_fetch and a.copy_write:
+        f_kib = counter_last_call(a.op, a.fetch, "FETCH_SIZE")
+        w_kib = counter_last_call(a.op, a.write, "WRITE_SIZE")
+        cf_kib = counter_copy(a.copy_fetch, "FETCH_SIZE")
+        cw_kib = counter_copy(a.copy_write, "WRITE_SIZE")
+        f_scale = a.copy_bytes / (cf_kib * 1024)
+        w_scale = a.copy_bytes / (cw_kib * 1024)
+        fetch_b = f_kib * 1024 * f_scale
+        write_b = w_kib * 1024 * w_scale
+        lines += ["", "HBM traffic per call (FETCH_SIZE and WRITE_SIZE, KiB summed over the call's "
+                  "dispatches, scaled by a device copy of known size):", "",
+                  f"- copy of {a.copy_bytes} B: FETCH_SIZE {cf_kib:.0f} KiB (scale {f_scale:.3f}), "
+                  f"WRITE_SIZE {cw_kib:.0f} KiB (scale {w_scale:.3f})",
+                  f"- {a.op}: FETCH_SIZE {f_kib:.0f} KiB -> {fetch_b / 1e9:.3f} GB read; "
+                  f"WRITE_SIZE {w_kib:.0f} KiB -> {write_b / 1e9:.3f} GB written"]
+        block.update({"fetch_bytes_per_call": round(fetch_b), "write_bytes_per_call": round(write_b),
+                      "hbm_bytes_per_call": round(fetch_b + write_b),
+                      "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)})
+    lines += ["", "```json", json.dumps(block), "```", ""]
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()

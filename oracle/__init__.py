@@ -23,10 +23,10 @@ Sources (page titles; sections named as on the page):
         Sherman-Morrison-Woodbury evaluation suggested).
 
 Where the pages are silent the reading taken is stated in the docstring of
-the function concerned; the formulas the pages do not print for H-Net routing
-(p_t = (1 - cos(q_t, k_{t-1}))/2 with p = 1 at a sequence start, b_t = p_t >= tau)
-and for the EMA (zbar_t = P_t z_t + (1 - P_t) zbar_{t-1}) follow the task
-statement of this chunk layer.
+the function concerned.  [BG] describes H-Net routing and the EMA only in
+words; the formulas used are the plainest ones that description supports:
+p_t = (1 - cos(q_t, k_{t-1}))/2 with p = 1 at a sequence start, b_t = p_t >= tau,
+and zbar_t = P_t z_t + (1 - P_t) zbar_{t-1}.
 
 Every function here is pinned by tests against something other than itself
 (closed forms, brute force on tiny inputs, library routines, invariants);

@@ -6,16 +6,16 @@ consumes in bf16 are rounded here once (round-to-nearest-even) and returned as
 float32 arrays holding exactly representable bf16 values.
 
 Workloads (the shapes the pages' own training runs use, synthetic content):
-  * C0  tiny H-Net layer, fp32, 2 x 256 bytes, d=64, piecewise-constant h;
+  * tiny H-Net layer, fp32, 2 x 256 bytes, d=64, piecewise-constant h;
         plus a 32 x 8 coding-rate case for brute force.
-  * C1  ByteGen-style byte streams: 32-byte packed order-book events
+  * ByteGen-style byte streams: 32-byte packed order-book events
         (ByteGen report, section 2.3 "data preprocessing" and its Fig. 1),
         ragged 32 x U{32..256} events, batch 16, bf16 activations.
-  * C2  the C1 streams at batch 32 (optionally every sequence 8192 bytes)
+  * two-stage H-Net input: those streams at batch 32 (optionally every sequence 8192 bytes)
         driving a two-stage H-Net hierarchy, d 512 -> 768.
-  * C3  ByteFlow coding-rate chunking input: unit-norm rows drawn from a
+  * ByteFlow coding-rate chunking input: unit-norm rows drawn from a
         mixture of 32 Gaussian clusters with random cluster switches, fp32.
-  * C4  the C3 rows at d=512 in bf16 with a 1536-wide global stand-in and
+  * full ByteFlow layer input: those rows at d=512 in bf16 with a 1536-wide global stand-in and
         16 bin matrices for the multi-linear upsampling.
 """
 from __future__ import annotations
@@ -24,7 +24,12 @@ from dataclasses import dataclass
 
 import numpy as np
 
-CONFIG_SEED = [20260000 + i for i in range(5)]
+# one seeded stream per workload
+SEED_HNET_TINY = 20260000
+SEED_EVENT_STREAMS = 20260001
+SEED_HNET_TWO_STAGE = 20260002
+SEED_CODING_RATE_FP32 = 20260003
+SEED_BYTEFLOW_LAYER = 20260004
 
 # --------------------------------------------------------------------------
 # bf16 helpers (input rounding only)
@@ -79,11 +84,11 @@ def _matmul_rows(x, w, chunk=32768):
 
 
 # --------------------------------------------------------------------------
-# C0: tiny piecewise-constant activations
+# tiny piecewise-constant activations
 # --------------------------------------------------------------------------
 
 
-def gen_c0(seed: int = CONFIG_SEED[0], nseq: int = 2, T: int = 256, d: int = 64):
+def gen_hnet_tiny(seed: int = SEED_HNET_TINY, nseq: int = 2, T: int = 256, d: int = 64):
     """Piecewise-constant N(0,I) segments (lengths U{3..12}) plus noise of
     variance 0.05; Wq, Wk ~ N(0, 1/d).  q = h Wq and k = h Wk (row vectors)."""
     rng = np.random.default_rng(seed)
@@ -124,14 +129,14 @@ def cluster_rows(rng, nseq: int, T: int, d: int, ncl: int = 32, sigma: float = 0
     return out
 
 
-def gen_c0_dr_tiny(seed: int = CONFIG_SEED[0] + 100, T: int = 32, d: int = 8, eps2: float = 0.5):
+def gen_coding_rate_tiny(seed: int = SEED_HNET_TINY + 100, T: int = 32, d: int = 8, eps2: float = 0.5):
     rng = np.random.default_rng(seed)
     h = cluster_rows(rng, 1, T, d, ncl=4)[0]
     return dict(h=h.astype(np.float32), T=T, d=d, eps2=eps2)
 
 
 # --------------------------------------------------------------------------
-# C1/C2: 32-byte packed order-book events
+# 32-byte packed order-book events
 # --------------------------------------------------------------------------
 
 EPOCH_NS = 1_730_793_600_000_000_000  # 2024-11-05 08:00 UTC
@@ -198,7 +203,7 @@ def _embed_conv(rng, x_bytes, offsets, d):
     return h
 
 
-def gen_c1(seed: int = CONFIG_SEED[1], nseq: int = 16, d: int = 512, min_events: int = 32,
+def gen_event_streams(seed: int = SEED_EVENT_STREAMS, nseq: int = 16, d: int = 512, min_events: int = 32,
            max_events: int = 256, fixed_events=None):
     """ByteGen-style streams -> h = conv(embed(bytes)); q = h Wq, k = h Wk,
     Wq, Wk ~ N(0, 1/d); h, q, k rounded to bf16."""
@@ -212,13 +217,13 @@ def gen_c1(seed: int = CONFIG_SEED[1], nseq: int = 16, d: int = 512, min_events:
     return dict(bytes=xb, offsets=off, h=bf16_round(h), q=q, k=k, d=d, threshold=0.5, dtype="bf16")
 
 
-def gen_c2(seed: int = CONFIG_SEED[2], nseq: int = 32, d_local: int = 512, d_mid: int = 768,
+def gen_hnet_two_stage(seed: int = SEED_HNET_TWO_STAGE, nseq: int = 32, d_local: int = 512, d_mid: int = 768,
            fixed_T=None, min_events: int = 32, max_events: int = 256):
-    """Two-stage hierarchy on C1-style streams.  ``fixed_T`` (multiple of 32)
+    """Two-stage hierarchy on the event streams.  ``fixed_T`` (multiple of 32)
     makes every sequence that long (8192 for the headline workload).
     Stage thresholds come from the 0.75 score quantile of each stage."""
     fixed_events = None if fixed_T is None else fixed_T // 32
-    base = gen_c1(seed, nseq=nseq, d=d_local, min_events=min_events, max_events=max_events,
+    base = gen_event_streams(seed, nseq=nseq, d=d_local, min_events=min_events, max_events=max_events,
                   fixed_events=fixed_events)
     rng = np.random.default_rng(seed + 7919)
     base["w_mid"] = rng.standard_normal((d_local, d_mid)) / np.sqrt(d_local)
@@ -229,7 +234,7 @@ def gen_c2(seed: int = CONFIG_SEED[2], nseq: int = 32, d_local: int = 512, d_mid
     return base
 
 
-def gen_c2_stage2_inputs(z1, cfg):
+def gen_stage2_inputs(z1, cfg):
     """Stand-in for the stage-1 main network's input projection: x2 = z1 W_mid,
     q2 = x2 Wq2, k2 = x2 Wk2 (all rounded to bf16)."""
     x2 = bf16_round(_matmul_rows(z1, cfg["w_mid"]))
@@ -237,24 +242,24 @@ def gen_c2_stage2_inputs(z1, cfg):
                 k2=bf16_round(_matmul_rows(x2, cfg["wk2"])))
 
 
-def gen_c2_backproj(y2, cfg):
+def gen_stage2_backproj(y2, cfg):
     """Stand-in projection of the stage-2 result back to d_local (bf16)."""
     return bf16_round(_matmul_rows(y2, cfg["w_back"]))
 
 
 # --------------------------------------------------------------------------
-# C3/C4: ByteFlow coding-rate inputs
+# ByteFlow coding-rate inputs
 # --------------------------------------------------------------------------
 
 
-def gen_c3(seed: int = CONFIG_SEED[3], nseq: int = 8, T: int = 8192, d: int = 256,
+def gen_coding_rate_fp32(seed: int = SEED_CODING_RATE_FP32, nseq: int = 8, T: int = 8192, d: int = 256,
            eps2: float = 0.5, K: int = 2048):
     rng = np.random.default_rng(seed)
     h = cluster_rows(rng, nseq, T, d).astype(np.float32)
     return dict(h=h, nseq=nseq, T=T, d=d, eps2=eps2, K=K, dtype="f32")
 
 
-def gen_c4(seed: int = CONFIG_SEED[4], nseq: int = 32, T: int = 8192, d_local: int = 512,
+def gen_byteflow_layer(seed: int = SEED_BYTEFLOW_LAYER, nseq: int = 32, T: int = 8192, d_local: int = 512,
            d_global: int = 1536, K: int = 2048, nbins: int = 16, eps2: float = 0.5):
     rng = np.random.default_rng(seed)
     h = bf16_round(cluster_rows(rng, nseq, T, d_local))
@@ -264,7 +269,7 @@ def gen_c4(seed: int = CONFIG_SEED[4], nseq: int = 32, T: int = 8192, d_local: i
                 K=K, nbins=nbins, eps2=eps2, dtype="bf16")
 
 
-def gen_c4_global(z, cfg):
+def gen_global_standin(z, cfg):
     """Stand-in for W_proj followed by the global Transformer: g = z W_g (bf16)."""
     zz = np.asarray(z).reshape(-1, z.shape[-1])
     return bf16_round(_matmul_rows(zz, cfg["w_g"])).reshape(z.shape[:-1] + (cfg["w_g"].shape[1],))

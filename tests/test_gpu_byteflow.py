@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synthdata import bf16_round, cluster_rows, gen_c0_dr_tiny, gen_c3, gen_c4, gen_c4_global
+from synthdata import bf16_round, cluster_rows, gen_coding_rate_tiny, gen_coding_rate_fp32, gen_byteflow_layer, gen_global_standin
 from tests.helpers import oracle_dr_parallel, row_rel_err, say, to_dev, to_np, topk_band_compare
 
 pytestmark = pytest.mark.gpu
@@ -69,7 +69,7 @@ def _dr(ops, h, eps2, dtype):
 
 def test_coding_rate_tiny_brute_force_case(ops):
     torch = _torch()
-    c = gen_c0_dr_tiny()
+    c = gen_coding_rate_tiny()
     g, st = _dr(ops, c["h"][None], c["eps2"], torch.float32)
     o = oracle.coding_rate(c["h"], c["eps2"])
     assert st == 0
@@ -108,13 +108,13 @@ def test_coding_rate_nonfinite_sets_status(ops):
     assert st & 2
 
 
-def test_coding_rate_topk_full_size_c3(ops):
-    """C3 at full size: 8 x 8192 x 256 fp32.  Sampled Delta R against the oracle
+def test_coding_rate_topk_full_size_fp32_8x8192x256(ops):
+    """Full size: 8 x 8192 x 256 fp32.  Sampled Delta R against the oracle
     in every sequence, then the Top-K set of one full sequence against the
     oracle's, outside the 1e-5 band around the K-th value."""
     torch = _torch()
-    c = gen_c3()
-    say("C3 generated")
+    c = gen_coding_rate_fp32()
+    say("fp32 8 x 8192 x 256 generated")
     g, st = _dr(ops, c["h"], c["eps2"], torch.float32)
     assert st == 0
     rng = np.random.default_rng(9)
@@ -126,14 +126,14 @@ def test_coding_rate_topk_full_size_c3(ops):
     assert np.max(np.abs(g[0] - o0) / o0) < 1e-3
     idx, mask, _ = ops.topk_select(to_dev(g), c["K"])
     bad, nband = topk_band_compare(to_np(idx)[0], oracle.topk_select(o0, c["K"]), o0, c["K"])
-    say("C3 max abs err", np.max(np.abs(g[0] - o0)), "band size", nband)
+    say("fp32 max abs err", np.max(np.abs(g[0] - o0)), "band size", nband)
     assert len(bad) == 0, bad
 
 
-def test_coding_rate_full_size_c4_sampled(ops):
+def test_coding_rate_full_size_bf16_32x8192x512_sampled(ops):
     torch = _torch()
-    c = gen_c4()
-    say("C4 generated")
+    c = gen_byteflow_layer()
+    say("bf16 32 x 8192 x 512 generated")
     g, st = _dr(ops, c["h"], c["eps2"], torch.bfloat16)
     assert st == 0
     rng = np.random.default_rng(10)
@@ -143,12 +143,12 @@ def test_coding_rate_full_size_c4_sampled(ops):
         assert np.max(np.abs(g[s, pos] - o) / np.abs(o)) < 1e-3
     # one whole sequence: every Delta R, then the Top-K set outside the 1e-5 band
     s = 7
-    say("C4 oracle on one full sequence (parallel workers)")
+    say("oracle on one full sequence (parallel workers)")
     o = oracle_dr_parallel(c["h"][s].astype(np.float64), c["eps2"])
     assert np.max(np.abs(g[s] - o) / o) < 1e-3
     idx, _, _ = ops.topk_select(to_dev(g[s:s + 1]), c["K"])
     bad, nband = topk_band_compare(to_np(idx)[0], oracle.topk_select(o, c["K"]), o, c["K"])
-    say("C4 seq", s, "max abs err", np.max(np.abs(g[s] - o)), "band size", nband)
+    say("bf16 seq", s, "max abs err", np.max(np.abs(g[s] - o)), "band size", nband)
     assert len(bad) == 0, bad
 
 
@@ -189,13 +189,13 @@ def test_upsample_vs_oracle(ops, nseq, T, K, dg, dl, B):
     assert row_rel_err(to_np(s), ref) < 2e-2
 
 
-def test_byteflow_chain_full_size_c4(ops):
-    """C4 at full size (the launch configuration of bench.py): Delta R, Top-K,
+def test_byteflow_chain_full_size_bf16_32x8192(ops):
+    """32 x 8192 x 512 bf16 at full size (the launch configuration of bench.py): Delta R, Top-K,
     gather, global stand-in, 16-bin upsample + residual; upsample rows of two
     sequences checked against the oracle."""
     torch = _torch()
     bf = torch.bfloat16
-    c = gen_c4()
+    c = gen_byteflow_layer()
     nseq, T, K = c["nseq"], c["T"], c["K"]
     h_t = to_dev(c["h"], bf)
     dR, st = ops.coding_rate(h_t, c["eps2"])
@@ -206,10 +206,10 @@ def test_byteflow_chain_full_size_c4(ops):
     z_np = to_np(z).reshape(nseq, K, -1)
     idx_np = to_np(idx)
     assert np.array_equal(z_np, oracle.gather(c["h"], idx_np))
-    g = gen_c4_global(z_np, c)
+    g = gen_global_standin(z_np, c)
     s = ops.upsample_bins(to_dev(g, bf), to_dev(c["w_bin"], bf), idx, h_t, c["nbins"])
     s_np = to_np(s)
     for q in (0, 31):
         ref = oracle.upsample_bins(g[q:q + 1], c["w_bin"], idx_np[q:q + 1], c["h"][q:q + 1], c["nbins"])
         assert row_rel_err(s_np[q:q + 1], ref) < 2e-2
-    say("C4 chain ok")
+    say("ByteFlow chain ok")

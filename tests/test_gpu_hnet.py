@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synthdata import gen_c0, gen_c1, gen_c2, gen_c2_stage2_inputs, gen_c2_backproj
+from synthdata import gen_hnet_tiny, gen_event_streams, gen_hnet_two_stage, gen_stage2_inputs, gen_stage2_backproj
 from tests.helpers import to_dev, to_np, row_rel_err, say
 
 pytestmark = pytest.mark.gpu
@@ -48,8 +48,8 @@ def _check_route(ops, q, k, off, dtype, threshold=0.5):
 
 def test_route_c0_fp32(ops):
     torch = _torch()
-    c = gen_c0()
-    say("route C0 fp32", c["q"].shape)
+    c = gen_hnet_tiny()
+    say("route tiny fp32", c["q"].shape)
     _check_route(ops, c["q"], c["k"], c["offsets"], torch.float32)
 
 
@@ -74,10 +74,10 @@ def test_route_zero_rows_and_nan(ops):
     assert p[4] == 0.5 and b[4] == 1
 
 
-def test_route_quantile_c1(ops):
+def test_route_quantile_event_streams(ops):
     torch = _torch()
-    c = gen_c1(nseq=6, d=512, min_events=3, max_events=40)
-    say("route quantile C1 N", c["offsets"][-1])
+    c = gen_event_streams(nseq=6, d=512, min_events=3, max_events=40)
+    say("route quantile event streams N", c["offsets"][-1])
     p, b, tau = ops.route(to_dev(c["q"], torch.bfloat16), to_dev(c["k"], torch.bfloat16),
                           to_dev(c["offsets"]), quantile=0.75)
     p_g, b_g, tau_g = to_np(p), to_np(b).astype(bool), float(to_np(tau)[0])
@@ -210,9 +210,9 @@ def test_c2_two_stage_full_size(ops):
     configuration of bench.py)."""
     torch = _torch()
     bf = torch.bfloat16
-    c = gen_c2(fixed_T=8192)
+    c = gen_hnet_two_stage(fixed_T=8192)
     off = c["offsets"]; N = int(off[-1])
-    say("C2@8192 generated N", N)
+    say("two-stage 32 x 8192 generated N", N)
     p1, b1, tau1 = ops.route(to_dev(c["q"], bf), to_dev(c["k"], bf), to_dev(off), quantile=0.75)
     p1g, b1g = to_np(p1), to_np(b1).astype(bool)
     p1o = oracle.route(c["q"], c["k"], off)
@@ -226,7 +226,7 @@ def test_c2_two_stage_full_size(ops):
     assert np.array_equal(to_np(coff1), c1o) and np.array_equal(to_np(idx1)[:M1], i1o)
     assert np.array_equal(to_np(z1)[:M1], z1o) and np.array_equal(to_np(P1)[:M1], P1o)
     say("stage 1 M1", M1, "ratio", M1 / N)
-    s2 = gen_c2_stage2_inputs(z1o, c)
+    s2 = gen_stage2_inputs(z1o, c)
     p2, b2, tau2 = ops.route(to_dev(s2["q2"], bf), to_dev(s2["k2"], bf), coff1, quantile=0.75)
     p2g, b2g = to_np(p2), to_np(b2).astype(bool)
     p2o = oracle.route(s2["q2"], s2["k2"], c1o)
@@ -240,8 +240,8 @@ def test_c2_two_stage_full_size(ops):
     y2 = ops.dechunk_ema(z2, P2, idx2, coff2, coff1, M1)
     y2o = oracle.dechunk_ema(z2o, P2o, i2o, c2o, c1o)
     assert row_rel_err(to_np(y2), y2o) < 2e-2
-    y1 = gen_c2_backproj(to_np(y2), c)
+    y1 = gen_stage2_backproj(to_np(y2), c)
     out = ops.dechunk_ema(to_dev(y1, bf), P1, idx1, coff1, to_dev(off), N)
     outo = oracle.dechunk_ema(y1, P1o, i1o, c1o, off)
     assert row_rel_err(to_np(out), outo) < 2e-2
-    say("C2@8192 chain ok")
+    say("two-stage chain ok")

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synthdata import cluster_rows, gen_c0_dr_tiny
+from synthdata import cluster_rows, gen_coding_rate_tiny
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -27,7 +27,7 @@ def test_coding_rate_golden_hand_derived():
 
 def test_coding_rate_brute_force_txt_form():
     """Against the pages' own T x T form: R(h_1..t) = 1/2 slogdet(I_t + alpha H H^T)."""
-    c = gen_c0_dr_tiny()
+    c = gen_coding_rate_tiny()
     h = c["h"].astype(np.float64)
     a = c["d"] / c["eps2"]
     dr = oracle.coding_rate(h, c["eps2"])

@@ -7,7 +7,7 @@ import pytest
 from scipy.spatial.distance import cosine as scipy_cosine_distance
 
 import oracle
-from synthdata import gen_c0, gen_c1
+from synthdata import gen_hnet_tiny, gen_event_streams
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -24,7 +24,7 @@ def test_route_golden_hand_derived():
 
 
 def test_route_matches_scipy_cosine_distance():
-    c = gen_c0()
+    c = gen_hnet_tiny()
     p = oracle.route(c["q"], c["k"], c["offsets"])
     off = c["offsets"]
     for s in range(len(off) - 1):
@@ -35,7 +35,7 @@ def test_route_matches_scipy_cosine_distance():
 
 
 def test_route_starts_and_range_ragged():
-    c = gen_c1(nseq=4, d=64, min_events=2, max_events=6)
+    c = gen_event_streams(nseq=4, d=64, min_events=2, max_events=6)
     p = oracle.route(c["q"], c["k"], c["offsets"])
     assert np.all(p[c["offsets"][:-1]] == 1.0)
     assert np.all((p >= 0) & (p <= 1))
@@ -55,7 +55,7 @@ def test_quantile_matches_numpy_lower():
 
 
 def test_quantile_keeps_about_a_quarter():
-    c = gen_c0(nseq=4, T=512)
+    c = gen_hnet_tiny(nseq=4, T=512)
     p = oracle.route(c["q"], c["k"], c["offsets"])
     tau = oracle.stage_quantile(p, 0.75)
     b = oracle.boundary_mask(p, tau)
@@ -70,7 +70,7 @@ def test_boundary_mask_fp32_decision_and_nan():
 
 
 def test_compact_scatter_recovers_rows_and_counts():
-    c = gen_c1(nseq=5, d=32, min_events=2, max_events=9)
+    c = gen_event_streams(nseq=5, d=32, min_events=2, max_events=9)
     p = oracle.route(c["q"], c["k"], c["offsets"])
     b = oracle.boundary_mask(p, 0.5)
     idx, coff, z, P = oracle.compact(b, p, c["h"], c["offsets"])

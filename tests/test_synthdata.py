@@ -2,7 +2,7 @@
 import numpy as np
 import torch
 
-from synthdata import bf16_round, bf16_bits, event_bytes, gen_c0, gen_c1, gen_c3, cluster_rows
+from synthdata import bf16_round, bf16_bits, event_bytes, gen_hnet_tiny, gen_event_streams, gen_coding_rate_fp32, cluster_rows
 
 
 def test_bf16_round_matches_torch_rne():
@@ -15,10 +15,10 @@ def test_bf16_round_matches_torch_rne():
 
 
 def test_generators_are_deterministic():
-    a, b = gen_c1(nseq=3, d=16, max_events=40), gen_c1(nseq=3, d=16, max_events=40)
+    a, b = gen_event_streams(nseq=3, d=16, max_events=40), gen_event_streams(nseq=3, d=16, max_events=40)
     assert np.array_equal(a["bytes"], b["bytes"]) and np.array_equal(a["q"], b["q"])
-    assert np.array_equal(gen_c0()["q"], gen_c0()["q"])
-    assert np.array_equal(gen_c3(nseq=1, T=64, d=16)["h"], gen_c3(nseq=1, T=64, d=16)["h"])
+    assert np.array_equal(gen_hnet_tiny()["q"], gen_hnet_tiny()["q"])
+    assert np.array_equal(gen_coding_rate_fp32(nseq=1, T=64, d=16)["h"], gen_coding_rate_fp32(nseq=1, T=64, d=16)["h"])
 
 
 def test_event_layout():
@@ -40,7 +40,7 @@ def test_event_layout():
 
 
 def test_c1_offsets_and_ragged_lengths():
-    c = gen_c1(nseq=6, d=8)
+    c = gen_event_streams(nseq=6, d=8)
     L = np.diff(c["offsets"])
     assert np.all(L % 32 == 0) and np.all((L >= 32 * 32) & (L <= 32 * 256))
     assert c["h"].shape == (c["offsets"][-1], 8)
