@@ -8,7 +8,9 @@
 //
 // Positions of one chunk that share a bin need the same product, so the work
 // items are the distinct (chunk, bin) pairs, each covering a run of
-// consecutive positions.  Items are bucketed by bin (counting sort with wave
+// consecutive positions; runs longer than kMaxRun positions (long chunks) are
+// split into several items, so no GEMM tile's epilogue carries much more than
+// 128 * kMaxRun positions.  Items are bucketed by bin (counting sort with wave
 // ballots; a deterministic order), then one grouped GEMM per bin on bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16): A rows are gathered from g by chunk, B = W_b
 // (transposed once into the workspace so both operands are contiguous along
@@ -25,6 +27,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kChunksPerBlock = 256;
+constexpr int kMaxRun = 16;
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kLDK = kBK + 8;  // LDS row stride (bf16) of the operand tiles
 
@@ -38,12 +41,32 @@ struct UpGeom {
 // first position offset of bin b in a chunk of length L: ceil(b L / B)
 __device__ inline int bin_lo(int b, int L, int B) { return (b * L + B - 1) / B; }
 
-__device__ inline bool bin_present(int b, int L, int B) { return bin_lo(b, L, B) < bin_lo(b + 1, L, B); }
 
 __device__ inline int chunk_len(const int32_t* idx, const UpGeom& g, int64_t cg) {
   const int i = static_cast<int>(cg % g.K);
   const int nxt = i + 1 < g.K ? idx[cg + 1] : g.T;
   return nxt - idx[cg];
+}
+
+// items of bin b of a chunk of length L: its run split into pieces of at most kMaxRun
+__device__ inline int bin_pieces(int b, int L, int B) {
+  return (bin_lo(b + 1, L, B) - bin_lo(b, L, B) + kMaxRun - 1) / kMaxRun;
+}
+
+__device__ inline int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ inline int wave_excl_i(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x - v;
 }
 
 // per-block, per-bin item counts
@@ -55,8 +78,8 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_count(const int32_t* __res
   const bool valid = cg < static_cast<int64_t>(g.nseq) * g.K;
   const int L = valid ? chunk_len(idx, g, cg) : 0;
   for (int b = 0; b < g.nbins; ++b) {
-    const uint64_t bal = __ballot(valid && bin_present(b, L, g.nbins));
-    if (lane == 0) wc[w][b] = __popcll(bal);
+    const int n = wave_sum_i(valid ? bin_pieces(b, L, g.nbins) : 0);
+    if (lane == 0) wc[w][b] = n;
   }
   __syncthreads();
   if (threadIdx.x < g.nbins)
@@ -115,19 +138,20 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_items(const int32_t* __res
   const bool valid = cg < static_cast<int64_t>(g.nseq) * g.K;
   const int L = valid ? chunk_len(idx, g, cg) : 0;
   for (int b = 0; b < g.nbins; ++b) {
-    const uint64_t bal = __ballot(valid && bin_present(b, L, g.nbins));
-    if (lane == 0) wc[w][b] = __popcll(bal);
+    const int n = wave_sum_i(valid ? bin_pieces(b, L, g.nbins) : 0);
+    if (lane == 0) wc[w][b] = n;
   }
   __syncthreads();
   const int64_t row0 = valid ? (cg / g.K) * g.T + idx[cg] : 0;
   for (int b = 0; b < g.nbins; ++b) {
-    const bool pres = valid && bin_present(b, L, g.nbins);
-    const uint64_t bal = __ballot(pres);
-    if (!pres) continue;
-    int slot = base[static_cast<int64_t>(blockIdx.x) * g.nbins + b] + lanes_below(bal);
+    const int np = valid ? bin_pieces(b, L, g.nbins) : 0;
+    int slot = base[static_cast<int64_t>(blockIdx.x) * g.nbins + b] + wave_excl_i(np, lane);
     for (int q = 0; q < w; ++q) slot += wc[q][b];
     const int lo = bin_lo(b, L, g.nbins), hi = bin_lo(b + 1, L, g.nbins);
-    items[slot] = make_int4(static_cast<int>(cg), static_cast<int>(row0 + lo), hi - lo, 0);
+    for (int e = 0; e < np; ++e) {
+      const int a = lo + e * kMaxRun;
+      items[slot + e] = make_int4(static_cast<int>(cg), static_cast<int>(row0 + a), min(kMaxRun, hi - a), 0);
+    }
   }
 }
 
@@ -293,6 +317,12 @@ struct UpWs {
   uint16_t* Wt;
 };
 
+// items per chunk <= min(L, B) + L / kMaxRun (one per present bin, one more
+// per kMaxRun positions of its run), so per sequence <= T + T / kMaxRun
+size_t up_max_items(const UpGeom& g) {
+  return static_cast<size_t>(g.nseq) * (static_cast<size_t>(g.T) + g.T / kMaxRun + 1);
+}
+
 UpWs up_carve(void* ws, const UpGeom& g) {
   char* p = static_cast<char*>(ws);
   UpWs u;
@@ -302,14 +332,14 @@ UpWs up_carve(void* ws, const UpGeom& g) {
   u.bin_off = reinterpret_cast<int32_t*>(p); p += 256;
   u.bin_cnt = reinterpret_cast<int32_t*>(p); p += 256;
   u.tile_off = reinterpret_cast<int32_t*>(p); p += 512;
-  u.items = reinterpret_cast<int4*>(p); p += align_up(static_cast<size_t>(g.nseq) * g.T * 16, 256);
+  u.items = reinterpret_cast<int4*>(p); p += align_up(up_max_items(g) * 16, 256);
   u.Wt = reinterpret_cast<uint16_t*>(p);
   return u;
 }
 
 size_t up_ws_bytes(const UpGeom& g) {
   const size_t cb = align_up(static_cast<size_t>(g.nblk) * g.nbins * 4, 256);
-  return 2 * cb + 1024 + align_up(static_cast<size_t>(g.nseq) * g.T * 16, 256) +
+  return 2 * cb + 1024 + align_up(up_max_items(g) * 16, 256) +
          static_cast<size_t>(g.nbins) * g.dg * g.dl * 2 + 256;
 }
 
@@ -352,7 +382,7 @@ extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* 
   hipLaunchKernelGGL(up_offsets, dim3(1), dim3(256), 0, st, u.counts, g, u.base, u.bin_off, u.bin_cnt,
                      u.tile_off);
   hipLaunchKernelGGL(up_items, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.base, u.items);
-  const int64_t max_tiles = ceil_div(nseq * T, kBM) + nbins;
+  const int64_t max_tiles = ceil_div(static_cast<int64_t>(up_max_items(g)), kBM) + nbins;
   hipLaunchKernelGGL(up_gemm, dim3(static_cast<unsigned>(max_tiles), static_cast<unsigned>(ceil_div(d_local, kBN))),
                      dim3(256), 0, st, static_cast<const uint16_t*>(gm), u.Wt,
                      static_cast<const uint16_t*>(h), g, u.bin_off, u.bin_cnt, u.tile_off, u.items,
