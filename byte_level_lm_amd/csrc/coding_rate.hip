@@ -175,25 +175,30 @@ __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h
 
 // bf16 input: the same 64x64 prefix tiles, rows taken in sub-chunks of R = 128
 // rows (64 when c is not a multiple of 128), so a block holds c / R of them.
-// The next sub-chunk's rows are in flight in registers while the current one
-// runs on the MFMAs; each thread owns 4 consecutive rows x 8 features and
-// writes them transposed as one 8-byte LDS store per feature.
-__device__ inline uint2 pack4_bf16(uint4 r0, uint4 r1, uint4 r2, uint4 r3, int e) {
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r0);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r1);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r2);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r3);
-  const int sh = 16 * (e & 1);
-  const uint32_t v0 = (w0[e >> 1] >> sh) & 0xFFFFu, v1 = (w1[e >> 1] >> sh) & 0xFFFFu;
-  const uint32_t v2 = (w2[e >> 1] >> sh) & 0xFFFFu, v3 = (w3[e >> 1] >> sh) & 0xFFFFu;
-  return make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+// Rows are staged row-major in LDS with plain 16-byte stores; the MFMA
+// operands (8 consecutive rows of one feature per lane) are read with the
+// gfx950 transposing LDS read ds_read_b64_tr_b16: within each 16-lane group,
+// lane j points at row j/4 and features 4 (j % 4) .. +3, and lane i receives
+// feature i of those 4 rows.  Registers hold the next sub-chunk's rows; the
+// barriers around the single LDS stage order LDS only, so those loads stay in
+// flight across them.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+__device__ inline bf16x8 tr_frag(const uint16_t* s, int row, int col, int pitch) {
+  typedef __attribute__((address_space(3))) shortx4 lds_s4;
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(s + row * pitch + col));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(s + (row + 4) * pitch + col));
+  bf16x8 v;
+  __builtin_memcpy(&v, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&v) + 8, &hi, 8);
+  return v;
 }
 
 __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __restrict__ h,
                                                            float* __restrict__ ws, CRGeom g, float alpha) {
-  constexpr int LDR = 136;  // 128 rows + 8 pad (bf16) per feature row
-  __shared__ __attribute__((aligned(16))) uint16_t sI[64 * LDR];
-  __shared__ __attribute__((aligned(16))) uint16_t sJ[64 * LDR];
+  constexpr int GP = 72;  // LDS pitch (bf16) of a staged row: 64 features + 8 pad
+  __shared__ __attribute__((aligned(16))) uint16_t sI[128 * GP];
+  __shared__ __attribute__((aligned(16))) uint16_t sJ[128 * GP];
   int s, tt;
   if (!gram_tile_of_block(g, s, tt)) return;
   int I = 0;
@@ -206,30 +211,53 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
   const int R = g.c % 128 == 0 ? 128 : 64;
   const int spb = g.c / R;                // sub-chunks per block
   const int nq = (g.nblk - 1) * spb;      // sub-chunks that feed some prefix
-  const int rq = (tid >> 3) * 4, fc = (tid & 7) * 8;
-  const bool fiok = 64 * I + fc < g.d, fjok = 64 * J + fc < g.d;
-  const uint16_t* hI = h + static_cast<int64_t>(s) * g.T * g.d + 64 * I + fc;
-  const uint16_t* hJ = h + static_cast<int64_t>(s) * g.T * g.d + 64 * J + fc;
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-  uint4 xi0, xi1, xi2, xi3, xj0, xj1, xj2, xj3;
-  auto fetch = [&](int q) {
-    const int r0 = q * R + rq, rend = min(q * R + R, g.T);
-    const int64_t o = static_cast<int64_t>(r0) * g.d;
-    const bool q0 = r0 < rend, q1 = r0 + 1 < rend, q2 = r0 + 2 < rend, q3 = r0 + 3 < rend;
-    xi0 = fiok && q0 ? *reinterpret_cast<const uint4*>(hI + o) : z4;
-    xi1 = fiok && q1 ? *reinterpret_cast<const uint4*>(hI + o + g.d) : z4;
-    xi2 = fiok && q2 ? *reinterpret_cast<const uint4*>(hI + o + 2 * g.d) : z4;
-    xi3 = fiok && q3 ? *reinterpret_cast<const uint4*>(hI + o + 3 * g.d) : z4;
+  const int lr = tid >> 3, lc = (tid & 7) * 8;  // rows lr + 32 q, features lc .. lc + 7
+  const bool fiok = 64 * I + lc < g.d, fjok = 64 * J + lc < g.d;
+  const uint16_t* hI = h + static_cast<int64_t>(s) * g.T * g.d + 64 * I + lc;
+  const uint16_t* hJ = h + static_cast<int64_t>(s) * g.T * g.d + 64 * J + lc;
+  // one sub-chunk: rows q R + lr + 32 e; rows past the sequence or features
+  // past d read row 0 / feature 0 and are masked to zero (unconditional loads)
+  auto ld = [&](const uint16_t* base, bool fok, int q, int e) {
+    const int r = q * R + lr + 32 * e;
+    const bool ok = fok && r < g.T && lr + 32 * e < R;
+    uint4 v = *reinterpret_cast<const uint4*>(base - (fok ? 0 : lc) + static_cast<int64_t>(ok ? r : 0) * g.d);
+    const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+    v.x &= m; v.y &= m; v.z &= m; v.w &= m;
+    return v;
+  };
+  uint4 ai0, ai1, ai2, ai3, aj0, aj1, aj2, aj3;
+  auto fetch_a = [&](int q) {
+    ai0 = ld(hI, fiok, q, 0); ai1 = ld(hI, fiok, q, 1); ai2 = ld(hI, fiok, q, 2); ai3 = ld(hI, fiok, q, 3);
+    if (!same) { aj0 = ld(hJ, fjok, q, 0); aj1 = ld(hJ, fjok, q, 1); aj2 = ld(hJ, fjok, q, 2); aj3 = ld(hJ, fjok, q, 3); }
+  };
+  auto stash = [&](const uint4& x0, const uint4& x1, const uint4& x2, const uint4& x3, const uint4& y0,
+                   const uint4& y1, const uint4& y2, const uint4& y3) {
+    *reinterpret_cast<uint4*>(sI + lr * GP + lc) = x0;
+    *reinterpret_cast<uint4*>(sI + (lr + 32) * GP + lc) = x1;
+    *reinterpret_cast<uint4*>(sI + (lr + 64) * GP + lc) = x2;
+    *reinterpret_cast<uint4*>(sI + (lr + 96) * GP + lc) = x3;
     if (!same) {
-      xj0 = fjok && q0 ? *reinterpret_cast<const uint4*>(hJ + o) : z4;
-      xj1 = fjok && q1 ? *reinterpret_cast<const uint4*>(hJ + o + g.d) : z4;
-      xj2 = fjok && q2 ? *reinterpret_cast<const uint4*>(hJ + o + 2 * g.d) : z4;
-      xj3 = fjok && q3 ? *reinterpret_cast<const uint4*>(hJ + o + 3 * g.d) : z4;
+      *reinterpret_cast<uint4*>(sJ + lr * GP + lc) = y0;
+      *reinterpret_cast<uint4*>(sJ + (lr + 32) * GP + lc) = y1;
+      *reinterpret_cast<uint4*>(sJ + (lr + 64) * GP + lc) = y2;
+      *reinterpret_cast<uint4*>(sJ + (lr + 96) * GP + lc) = y3;
     }
   };
-  if (nq > 0) fetch(0);
   floatx16 acc = zero16();
   const uint16_t* sJr = same ? sI : sJ;
+  const int j16 = lane & 15;
+  const int frow = 8 * (lane >> 5) + (j16 >> 2);                  // + k0
+  const int fcolA = 32 * wm + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+  const int fcolB = 32 * wn + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+  auto compute = [&]() {
+    for (int k0 = 0; k0 < R; k0 += 16) {
+      const bf16x8 a = tr_frag(sI, k0 + frow, fcolA, GP);
+      const bf16x8 b = tr_frag(sJr, k0 + frow, fcolB, GP);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+  };
+  if (nq > 0) fetch_a(0);
+  int q = 0;
   for (int j = 0; j < g.nblk; ++j) {
     float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
 #pragma unroll
@@ -238,21 +266,12 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
     }
     if (j == g.nblk - 1) break;
-    for (int sq = 0; sq < spb; ++sq) {
-      const int q = j * spb + sq;
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        *reinterpret_cast<uint2*>(sI + (fc + e) * LDR + rq) = pack4_bf16(xi0, xi1, xi2, xi3, e);
-        if (!same) *reinterpret_cast<uint2*>(sJ + (fc + e) * LDR + rq) = pack4_bf16(xj0, xj1, xj2, xj3, e);
-      }
-      __syncthreads();
-      if (q + 1 < nq) fetch(q + 1);
-      for (int k0 = 0; k0 < R; k0 += 16) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sI + (32 * wm + (lane & 31)) * LDR + k0 + 8 * (lane >> 5));
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(sJr + (32 * wn + (lane & 31)) * LDR + k0 + 8 * (lane >> 5));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-      }
+    for (int sq = 0; sq < spb; ++sq, ++q) {
+      lds_barrier();
+      stash(ai0, ai1, ai2, ai3, aj0, aj1, aj2, aj3);
+      lds_barrier();
+      fetch_a(q + 1);
+      compute();
     }
   }
 }
