@@ -473,7 +473,8 @@ constexpr int kPassTiles = 2;                   // tiles below the diagonal per 
 constexpr int kSlots = kPassTiles / 2;          // pass tiles per wave
 constexpr int kStripRows = 64 * (kPassTiles + 1);
 constexpr int kXP = 68;                         // LDS row pitch of 64x64 tiles
-constexpr int kStripFloats = 2 * kStripRows * kSP;
+// one strip stage, also large enough for the staged X_{k+1} tile
+constexpr int kStripFloats = kStripRows * kSP > 64 * kXP ? kStripRows * kSP : 64 * kXP;
 constexpr int kPanelFloats = kStripFloats + 64 * kXP;
 static_assert(64 * kXP <= kStripFloats, "X staging must fit in the strip buffers");
 static_assert(kPassTiles == 2, "the strip loader below issues kPassTiles + 1 = 3 loads per set");
@@ -527,7 +528,7 @@ __global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __r
 }
 
 template <int DT>
-__global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
+__global__ __launch_bounds__(256, 4) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
                                                    const float* __restrict__ linv, CRGeom g,
                                                    float salpha, int k) {
   __shared__ __attribute__((aligned(16))) float lds[kPanelFloats];
@@ -636,8 +637,6 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
         for (int st = 0; st < 8; ++st) accD = mfma32(sd * da[st], db[st], accD);
       }
     };
-    float* sb0 = lds;
-    float* sb1 = lds + kStripRows * kSP;
     // the accumulators were loaded from memory: wait here once, so that the
     // loop's only outstanding loads are the prefetches
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -645,19 +644,20 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
       fetch_a(0);
       fetch_b(1);
     }
-    // one LDS-only barrier per chunk (the prefetches stay in flight): a buffer
-    // is restaged only after every wave has passed the barrier of the chunk
-    // staged in between
+    // one LDS stage, two LDS-only barriers per chunk (the prefetches stay in
+    // flight across them)
     for (int ch = 0; ch < nch; ch += 2) {
-      stash(sb0, qa0, qa1, qa2);
+      lds_barrier();
+      stash(lds, qa0, qa1, qa2);
       lds_barrier();
       fetch_a(ch + 2);
-      compute(sb0, ch);
+      compute(lds, ch);
       if (ch + 1 < nch) {
-        stash(sb1, qb0, qb1, qb2);
+        lds_barrier();
+        stash(lds, qb0, qb1, qb2);
         lds_barrier();
         fetch_b(ch + 3);
-        compute(sb1, ch + 1);
+        compute(lds, ch + 1);
       }
     }
     __syncthreads();  // strip buffers free (sX lives there); sLi staged
