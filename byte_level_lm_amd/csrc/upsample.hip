@@ -265,11 +265,8 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
     }
   }
   // epilogue, one pass per row half p (rows 64p..64p+63, written by the waves
-  // with wm == p): stage fp32 in LDS, then spread the (row, position of the
-  // item's run, 8-column chunk) units evenly over the block, so long runs of
-  // one chunk do not serialise on a few threads.  Each unit adds 8 values of h
-  // and writes 8 outputs with 16-byte accesses.
-  __shared__ int sPre[65];
+  // with wm == p): stage the fp32 accumulators in LDS, then add h and write
+  // every position of each item's run with 16-byte accesses.
   for (int p = 0; p < 2; ++p) {
     __syncthreads();
     if (wm == p) {
@@ -281,32 +278,40 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
           for (int r = 0; r < 16; ++r)
             sO[(32 * a + crow_of(r, lane)) * kOLD + 64 * wn + 32 * c + (lane & 31)] = acc[a][c][r];
     }
-    if (tid == 0) {
-      int run = 0;
-      for (int r = 0; r < 64; ++r) {
-        sPre[r] = run;
-        const int m = 64 * p + r;
-        run += m < mcount ? sItem[m].z : 0;
-      }
-      sPre[64] = run;
-    }
     __syncthreads();
+    // one (item row, 8-column chunk) pair per thread and round: the pair's
+    // 8 accumulator values are read once and its run (at most kMaxRun
+    // positions) is written four positions at a time, all four h loads
+    // issued before any is used
     const int nchunk = min(kBN, g.dl - n0) / 8;
-    const int nunits = sPre[64] * nchunk;
-    for (int u = tid; u < nunits; u += blockDim.x) {
-      const int qpos = u / nchunk, ch = u - qpos * nchunk;
-      int lo = 0, hi = 64;  // last row r with sPre[r] <= qpos
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (sPre[mid] <= qpos) lo = mid; else hi = mid;
-      }
-      const int4 it = sItem[64 * p + lo];
-      const int64_t o = static_cast<int64_t>(it.y + (qpos - sPre[lo])) * g.dl + n0 + 8 * ch;
-      float hv[8], sv[8];
-      Vec<BLLM_BF16>::load(h, o, hv);
+    const int rows = min(64, max(0, mcount - 64 * p));
+    for (int v = tid; v < rows * nchunk; v += 256) {
+      const int r = v / nchunk, ch = v - r * nchunk;
+      const int4 it = sItem[64 * p + r];
+      float acc8[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = sO[lo * kOLD + 8 * ch + e] + hv[e];
-      Vec<BLLM_BF16>::store(out, o, sv);
+      for (int e = 0; e < 8; ++e) acc8[e] = sO[r * kOLD + 8 * ch + e];
+      const int64_t o0 = static_cast<int64_t>(it.y) * g.dl + n0 + 8 * ch;
+      for (int q0 = 0; q0 < it.z; q0 += 4) {
+        uint4 hv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q = min(q0 + e, it.z - 1);  // past the run: reload its last position
+          hv[e] = *reinterpret_cast<const uint4*>(h + o0 + static_cast<int64_t>(q) * g.dl);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (q0 + e >= it.z) break;
+          const uint32_t wv[4] = {hv[e].x, hv[e].y, hv[e].z, hv[e].w};
+          float sv[8];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            sv[2 * c] = acc8[2 * c] + bf16_to_f32(static_cast<uint16_t>(wv[c] & 0xFFFFu));
+            sv[2 * c + 1] = acc8[2 * c + 1] + bf16_to_f32(static_cast<uint16_t>(wv[c] >> 16));
+          }
+          Vec<BLLM_BF16>::store(out, o0 + static_cast<int64_t>(q0 + e) * g.dl, sv);
+        }
+      }
     }
   }
 }
