@@ -9,6 +9,7 @@
 //
 // Memory layout: q, k packed rows [total x d]; p fp32 [total]; b uint8 [total].
 // HBM-bound: 2*d*e bytes read and 5 bytes written per position.
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -20,125 +21,93 @@ namespace {
 // Select the key of 0-based rank r (ascending) among the fp32 bit patterns of
 // p.  Every score is >= +0 or the canonical NaN 0x7FC00000, so bit 31 is 0 and
 // the unsigned bit order is the value order with NaN last.  Three digits:
-// bits [20, 31), [10, 20), [0, 10), most significant first, one pass over p
-// each.  A pass runs one workgroup per 4096 scores: every workgroup adds to
-// one global histogram and takes a completion ticket, and these same-address
-// device atomics serialize, so the pass time grows with the workgroup count
-// (measured optimum near 64 workgroups at 2^18 scores).  The last workgroup
-// of each pass turns the histogram into the next digit and clears it for the
-// following pass.  The scoring kernel's first workgroup initialises the state.
+// bits [20, 31), [10, 20), [0, 10), most significant first.
+//
+// One launch of G <= kSelMaxBlocks workgroups runs all three digits and the
+// threshold.  A workgroup holds one tile of 4096 scores in
+// registers (with more tiles than workgroups, each digit re-reads them), adds
+// its LDS histogram of the digit to a global one with device atomics, and
+// after a grid barrier every workgroup reads the whole histogram and narrows
+// the prefix itself, so all of them reach the same digit without a further
+// exchange.  Same-address device atomics serialize, so the flush grows with
+// G (measured optimum near 64 workgroups at 2^18 scores).  Last, each
+// workgroup writes b = [p >= tau] for its own scores.  The scoring kernel's
+// first workgroup zeroes the histograms and barrier counters beforehand.
 
 constexpr int kSelBins = 2048;
 constexpr int kSelThreads = 256;
 constexpr int kSelPerThread = 16;
+constexpr int kSelTile = kSelThreads * kSelPerThread;
+constexpr int kSelMaxBlocks = 64;
+constexpr int kSelDigits = 3;
+// The grid barriers need all G workgroups resident at once.  A workgroup
+// takes 256 threads, 64 VGPRs and 8 KB of LDS, so eight CUs already hold 64
+// of them, and the launch follows the scoring kernel on the same stream.
+// The spin bound (each round sleeps ~100 clocks, ~1 s in all) is never
+// reached in that case; if it were, tau comes out NaN and the kernel ends.
+constexpr uint32_t kSelSpinLimit = 1u << 22;
+constexpr uint32_t kNoKey = 0xFFFFFFFFu;  // past the end: bit 31 set, never selected
+
 struct SelectState {
-  uint32_t prefix;
-  uint32_t mask;
-  uint32_t rank;
-  uint32_t ticket;
-  float tau;
-  uint32_t pad[3];
-  uint32_t hist[kSelBins];
+  uint32_t arrive[kSelDigits];  // grid-barrier arrivals, one counter per digit
+  uint32_t pad[8 - kSelDigits];
+  uint32_t hist[kSelDigits][kSelBins];
 };
 
 // called by every thread of the scoring kernel's first workgroup
-__device__ inline void select_init(SelectState* st, uint32_t rank) {
-  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) st->hist[i] = 0;
+__device__ inline void select_init(SelectState* st) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(st);
+  constexpr int nw = static_cast<int>(sizeof(SelectState) / 4);
+  for (int i = threadIdx.x; i < nw; i += blockDim.x) w[i] = 0;
+}
+
+// Every workgroup of the grid arrives once at `arrive`; false if not all
+// nblocks arrived within the spin limit.  What the workgroups publish before
+// it (the histogram) is written with device-scope atomics only, so the
+// release needs no L2 write-back: each wave waits until its atomics are
+// acknowledged (vmcnt 0) before the arrival is counted.
+__device__ bool grid_barrier(uint32_t* arrive, uint32_t nblocks) {
+  __shared__ int all_in;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
   if (threadIdx.x == 0) {
-    st->prefix = 0;
-    st->mask = 0;
-    st->rank = rank;
-    st->ticket = 0;
-  }
-}
-
-// Add this workgroup's LDS histogram `lh` (nb bins, nb in {1024, 2048}) to the
-// global one; the last workgroup of the grid then picks the digit holding the
-// remaining rank, narrows prefix/mask/rank (and at shift 0 stores tau), and
-// clears the histogram and ticket.  All kSelThreads threads call this; the
-// digit search runs on the first 256.
-__device__ void select_flush_and_digit(SelectState* st, const uint32_t* lh, uint32_t nb,
-                                       int shift, float* tau_out, uint32_t* scan) {
-  __shared__ int is_last;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < static_cast<int>(nb); i += kSelThreads)
-    if (lh[i]) atomicAdd(&st->hist[i], lh[i]);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = (atomicAdd(&st->ticket, 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  // thread j < 256 owns bins [j*per, (j+1)*per)
-  const int per = static_cast<int>(nb) / 256;
-  uint32_t cnt[8];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    cnt[b] = 0;
-    if (tid < 256 && b < per)
-      cnt[b] = __hip_atomic_load(&st->hist[tid * per + b], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-    mine += cnt[b];
-  }
-  if (tid < 256) scan[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const uint32_t v = tid < 256 && tid >= off ? scan[tid - off] : 0u;
-    __syncthreads();
-    if (tid < 256) scan[tid] += v;
-    __syncthreads();
-  }
-  const uint32_t rank = st->rank, prefix = st->prefix, mask = st->mask;
-  const uint32_t incl = tid < 256 ? scan[tid] : 0u;
-  uint32_t cum = incl - mine;
-  __syncthreads();  // every thread has read rank/prefix/mask before one rewrites them
-  if (tid < 256 && cum <= rank && rank < incl) {
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      if (b < per && rank >= cum && rank < cum + cnt[b]) {
-        const uint32_t bin = tid * per + b;
-        st->rank = rank - cum;
-        st->prefix = prefix | (bin << shift);
-        st->mask = mask | ((nb - 1) << shift);
-        if (shift == 0) {
-          st->tau = __uint_as_float(prefix | bin);
-          if (tau_out) *tau_out = st->tau;
-        }
+    atomicAdd(arrive, 1u);
+    int done = 0;
+    for (uint32_t spin = 0; spin < kSelSpinLimit; ++spin) {
+      if (__hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= nblocks) {
+        done = 1;
+        break;
       }
-      cum += b < per ? cnt[b] : 0u;
+      __builtin_amdgcn_s_sleep(2);
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    all_in = done;
   }
   __syncthreads();
-  for (int i = tid; i < static_cast<int>(nb); i += kSelThreads) st->hist[i] = 0;
-  if (tid == 0) st->ticket = 0;
+  return all_in != 0;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_pass(const float* __restrict__ p, int64_t n,
-                                                           SelectState* st, int shift, int bits,
-                                                           float* tau_out) {
-  __shared__ uint32_t lh[kSelBins];
-  __shared__ uint32_t scan[256];
-  const uint32_t nb = 1u << bits;
-  for (int i = threadIdx.x; i < static_cast<int>(nb); i += kSelThreads) lh[i] = 0;
-  __syncthreads();
-  const uint32_t prefix = st->prefix, mask = st->mask;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSelThreads * kSelPerThread;
-  uint32_t key[kSelPerThread];
+__device__ inline void sel_load(const float* __restrict__ p, int64_t n, int64_t tile,
+                                uint32_t (&key)[kSelPerThread]) {
+  const int64_t base = tile * kSelTile + threadIdx.x;
 #pragma unroll
   for (int e = 0; e < kSelPerThread; ++e) {
-    const int64_t i = base + static_cast<int64_t>(e) * kSelThreads + threadIdx.x;
-    key[e] = i < n ? __float_as_uint(p[i]) : 0xFFFFFFFFu;  // never matches: bit 31 set
+    const int64_t i = base + static_cast<int64_t>(e) * kSelThreads;
+    key[e] = i < n ? __float_as_uint(p[i]) : kNoKey;
   }
-  // Scores often crowd into one or two bins of a digit; same-address LDS
-  // atomics of one wave serialize, so each wave first peels off up to two
-  // bins with one aggregated add each (ballot + popcount).
-  constexpr uint32_t kNone = 0xFFFFFFFFu;
+}
+
+// Add the keys under (prefix, mask) to the LDS histogram of the digit at
+// `shift`.  Scores often crowd into one or two bins of a digit and
+// same-address LDS atomics of one wave serialize, so each wave first peels
+// off up to two bins with one aggregated add each (ballot + popcount).
+__device__ inline void sel_count(const uint32_t (&key)[kSelPerThread], uint32_t prefix,
+                                 uint32_t mask, int shift, uint32_t nb, uint32_t* lh) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int e = 0; e < kSelPerThread; ++e) {
-    uint32_t bin = (key[e] & mask) == prefix && key[e] != kNone ? (key[e] >> shift) & (nb - 1) : kNone;
-    uint64_t active = __ballot(bin != kNone);
+    uint32_t bin = (key[e] & mask) == prefix && key[e] != kNoKey ? (key[e] >> shift) & (nb - 1) : kNoKey;
+    uint64_t active = __ballot(bin != kNoKey);
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
       if (active == 0) break;
@@ -146,35 +115,124 @@ __global__ __launch_bounds__(kSelThreads) void select_pass(const float* __restri
       const uint32_t lb = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
       const uint64_t same = __ballot(bin == lb);
       if (lane == leader) atomicAdd(&lh[lb], static_cast<uint32_t>(__popcll(same)));
-      if (bin == lb) bin = kNone;
+      if (bin == lb) bin = kNoKey;
       active &= ~same;
     }
-    if (bin != kNone) atomicAdd(&lh[bin], 1u);
+    if (bin != kNoKey) atomicAdd(&lh[bin], 1u);
   }
-  __syncthreads();
-  select_flush_and_digit(st, lh, nb, shift, tau_out, scan);
 }
 
-__global__ __launch_bounds__(256) void threshold_kernel(const float* __restrict__ p, int64_t n,
-                                                        const SelectState* st,
-                                                        uint8_t* __restrict__ b) {
-  const float tau = st->tau;
-  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+__device__ inline void sel_mark(const uint32_t (&key)[kSelPerThread], int64_t n, int64_t tile,
+                                float tau, uint8_t* __restrict__ b) {
+  const int64_t base = tile * kSelTile + threadIdx.x;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (i0 + e < n) b[i0 + e] = static_cast<uint8_t>(p[i0 + e] >= tau);
+  for (int e = 0; e < kSelPerThread; ++e) {
+    const int64_t i = base + static_cast<int64_t>(e) * kSelThreads;
+    if (i < n) b[i] = static_cast<uint8_t>(__uint_as_float(key[e]) >= tau);
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ p, int64_t n,
+                                                             uint32_t rank, SelectState* st,
+                                                             float* __restrict__ tau_out,
+                                                             uint8_t* __restrict__ b) {
+  __shared__ uint32_t lh[kSelBins];
+  __shared__ uint32_t wtot[kSelThreads / kWave];
+  __shared__ uint32_t found[2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const uint32_t G = gridDim.x;
+  const int64_t ntiles = (n + kSelTile - 1) / kSelTile;
+  const bool resident = ntiles <= static_cast<int64_t>(G);  // then G == ntiles
+  uint32_t key[kSelPerThread];
+  if (resident) sel_load(p, n, blockIdx.x, key);
+  uint32_t prefix = 0, mask = 0;
+  bool ok = true;
+  for (int dg = 0; dg < kSelDigits; ++dg) {
+    const int shift = dg == 0 ? 20 : (dg == 1 ? 10 : 0);
+    const uint32_t nb = dg == 0 ? 2048u : 1024u;
+    for (int i = tid; i < static_cast<int>(nb); i += kSelThreads) lh[i] = 0;
+    __syncthreads();
+    if (resident) {
+      sel_count(key, prefix, mask, shift, nb, lh);
+    } else {
+      for (int64_t t = blockIdx.x; t < ntiles; t += G) {
+        uint32_t kk[kSelPerThread];
+        sel_load(p, n, t, kk);
+        sel_count(kk, prefix, mask, shift, nb, lh);
+      }
+    }
+    __syncthreads();
+    uint32_t* gh = st->hist[dg];
+    for (int i = tid; i < static_cast<int>(nb); i += kSelThreads)
+      if (lh[i]) atomicAdd(&gh[i], lh[i]);
+    ok = grid_barrier(&st->arrive[dg], G) && ok;
+    // every workgroup: thread j owns bins [j*per, (j+1)*per); find the bin
+    // in which the remaining rank falls
+    const int per = static_cast<int>(nb) / kSelThreads;
+    uint32_t cnt[kSelBins / kSelThreads];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < kSelBins / kSelThreads; ++q) {
+      cnt[q] = q < per ? __hip_atomic_load(&gh[tid * per + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      mine += cnt[q];
+    }
+    uint32_t incl = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t t = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += t;
+    }
+    if (lane == kWave - 1) wtot[wv] = incl;
+    __syncthreads();
+    for (int w = 0; w < wv; ++w) incl += wtot[w];
+    const uint32_t cum = incl - mine;
+    if (cum <= rank && rank < incl) {
+      uint32_t c = cum;
+#pragma unroll
+      for (int q = 0; q < kSelBins / kSelThreads; ++q) {
+        if (q < per && rank >= c && rank < c + cnt[q]) {
+          found[0] = rank - c;
+          found[1] = static_cast<uint32_t>(tid * per + q);
+        }
+        c += cnt[q];
+      }
+    }
+    __syncthreads();
+    rank = found[0];
+    prefix |= found[1] << shift;
+    mask |= (nb - 1) << shift;
+    __syncthreads();  // found, wtot and lh are rewritten by the next digit
+  }
+  const float tau = ok ? __uint_as_float(prefix) : __builtin_nanf("");
+  if (blockIdx.x == 0 && tid == 0 && tau_out != nullptr) *tau_out = tau;
+  if (resident) {
+    sel_mark(key, n, blockIdx.x, tau, b);
+  } else {
+    for (int64_t t = blockIdx.x; t < ntiles; t += G) {
+      uint32_t kk[kSelPerThread];
+      sel_load(p, n, t, kk);
+      sel_mark(kk, n, t, tau, b);
+    }
+  }
 }
 
 // ------------------------------------------------------------- scoring
 // One group of G lanes per row (G a power of two, at most 8; each lane
 // covers `iters` of the row's 16-byte vectors).  A group scores kRows
 // consecutive rows at a time with every q/k load of those rows issued before
-// the reductions, and a block walks kPasses such row sets.  The sequence
+// the reductions, and a block walks `passes` (at most kPasses) such row sets,
+// as few as keep the grid at kRouteBlocks workgroups or more.  The sequence
 // starts inside a block's row range are marked in LDS once per block, from a
 // block-uniform (scalar) search of the offsets.  With a select state the
 // first block initialises it for the select passes that follow.
 constexpr int kRows = 2;
 constexpr int kPasses = 8;
+#ifndef BLLM_ROUTE_BLOCKS
+#define BLLM_ROUTE_BLOCKS 1024
+#endif
+constexpr int kRouteBlocks = BLLM_ROUTE_BLOCKS;
 constexpr int kRouteMaxRows = 256 * kRows * kPasses;
 
 // first s in [0, n) with a[s] >= x (n if none)
@@ -191,16 +249,17 @@ template <int DT, int GS>
 __global__ __launch_bounds__(256) void route_kernel(const void* __restrict__ q,
                                                     const void* __restrict__ k, int d,
                                                     const int64_t* __restrict__ offsets, int nseq,
-                                                    int64_t total, int iters, float threshold,
+                                                    int64_t total, int iters, int passes,
+                                                    float threshold,
                                                     float* __restrict__ p_out,
                                                     uint8_t* __restrict__ b_out,
                                                     float* __restrict__ tau_out,
-                                                    SelectState* sel, uint32_t rank) {
+                                                    SelectState* sel) {
   using V = Vec<DT>;
   __shared__ uint8_t sstart[kRouteMaxRows];
   constexpr int G = 1 << GS;
   constexpr int ngroups = 256 >> GS;
-  const int rows_per_block = ngroups * kRows * kPasses;
+  const int rows_per_block = ngroups * kRows * passes;
   const int tid = threadIdx.x;
   const int g = tid & (G - 1);
   const int grp = tid >> GS;
@@ -208,7 +267,7 @@ __global__ __launch_bounds__(256) void route_kernel(const void* __restrict__ q,
   const int64_t re = rb + rows_per_block < total ? rb + rows_per_block : total;
   const bool write_mask = sel == nullptr;
   if (write_mask && tau_out != nullptr && blockIdx.x == 0 && tid == 0) *tau_out = threshold;
-  if (!write_mask && blockIdx.x == 0) select_init(sel, rank);
+  if (!write_mask && blockIdx.x == 0) select_init(sel);
   for (int i = tid; i < rows_per_block; i += 256) sstart[i] = 0;
   __syncthreads();
   {
@@ -218,7 +277,7 @@ __global__ __launch_bounds__(256) void route_kernel(const void* __restrict__ q,
   }
   __syncthreads();
   const int nvec = d / V::N;
-  for (int ps = 0; ps < kPasses; ++ps) {
+  for (int ps = 0; ps < passes; ++ps) {
     const int64_t t0 = rb + static_cast<int64_t>(ps * ngroups + grp) * kRows;
     if (t0 >= re) break;
     // rows past the end are clamped to the last row and not written; a
@@ -291,13 +350,13 @@ __global__ __launch_bounds__(256) void route_kernel(const void* __restrict__ q,
 
 template <int DT>
 void launch_route(int gshift, dim3 grid, hipStream_t st, const void* q, const void* k, int d,
-                  const int64_t* offsets, int nseq, int64_t total, int iters, float threshold,
-                  float* p_out, uint8_t* b_out, float* tau_out, SelectState* sel,
-                  uint32_t rank) {
+                  const int64_t* offsets, int nseq, int64_t total, int iters, int passes,
+                  float threshold,
+                  float* p_out, uint8_t* b_out, float* tau_out, SelectState* sel) {
 #define BLLM_ROUTE_CASE(GS)                                                                      \
   case GS:                                                                                       \
     hipLaunchKernelGGL((route_kernel<DT, GS>), grid, dim3(256), 0, st, q, k, d, offsets, nseq,  \
-                       total, iters, threshold, p_out, b_out, tau_out, sel, rank);               \
+                       total, iters, passes, threshold, p_out, b_out, tau_out, sel);             \
     break;
   switch (gshift) {
     BLLM_ROUTE_CASE(0) BLLM_ROUTE_CASE(1) BLLM_ROUTE_CASE(2) BLLM_ROUTE_CASE(3)
@@ -339,26 +398,25 @@ extern "C" int bllm_route(const void* q, const void* k, int dtype, int64_t d,
   int gshift = 0;
   while ((1 << gshift) < nvec && gshift < 3) ++gshift;
   const int iters = static_cast<int>(ceil_div(nvec, 1 << gshift));
-  const int rows_per_block = (256 >> gshift) * kRows * kPasses;
+  const int64_t rows_per_pass = (256 >> gshift) * kRows;
+  const int passes = static_cast<int>(
+      std::min<int64_t>(kPasses, std::max<int64_t>(1, total / (rows_per_pass * kRouteBlocks))));
+  const int64_t rows_per_block = rows_per_pass * passes;
   const dim3 grid(static_cast<unsigned>(ceil_div(total, rows_per_block)));
   SelectState* sst = use_q ? static_cast<SelectState*>(ws) : nullptr;
-  const uint32_t rank =
-      use_q ? static_cast<uint32_t>(std::floor(quantile * static_cast<double>(total - 1))) : 0u;
   if (dtype == BLLM_F32)
     launch_route<BLLM_F32>(gshift, grid, st, q, k, static_cast<int>(d), offsets,
-                           static_cast<int>(nseq), total, iters, threshold, p_out, b_out, tau_out,
-                           sst, rank);
+                           static_cast<int>(nseq), total, iters, passes, threshold, p_out, b_out, tau_out,
+                           sst);
   else
     launch_route<BLLM_BF16>(gshift, grid, st, q, k, static_cast<int>(d), offsets,
-                            static_cast<int>(nseq), total, iters, threshold, p_out, b_out, tau_out,
-                            sst, rank);
+                            static_cast<int>(nseq), total, iters, passes, threshold, p_out, b_out, tau_out,
+                            sst);
   if (!use_q) return launch_status();
-  const unsigned nblk = static_cast<unsigned>(ceil_div(total, kSelThreads * kSelPerThread));
-  const dim3 sb(kSelThreads);
-  hipLaunchKernelGGL(select_pass, dim3(nblk), sb, 0, st, p_out, total, sst, 20, 11, tau_out);
-  hipLaunchKernelGGL(select_pass, dim3(nblk), sb, 0, st, p_out, total, sst, 10, 10, tau_out);
-  hipLaunchKernelGGL(select_pass, dim3(nblk), sb, 0, st, p_out, total, sst, 0, 10, tau_out);
-  hipLaunchKernelGGL(threshold_kernel, dim3(static_cast<unsigned>(ceil_div(total, 1024))),
-                     dim3(256), 0, st, p_out, total, sst, b_out);
+  if (launch_status() != BLLM_OK) return BLLM_E_HIP;
+  const uint32_t rank = static_cast<uint32_t>(std::floor(quantile * static_cast<double>(total - 1)));
+  const unsigned nblk = static_cast<unsigned>(std::min<int64_t>(kSelMaxBlocks, ceil_div(total, kSelTile)));
+  hipLaunchKernelGGL(select_kernel, dim3(nblk), dim3(kSelThreads), 0, st, p_out, total, rank, sst,
+                     tau_out, b_out);
   return launch_status();
 }

@@ -100,6 +100,52 @@ def test_route_quantile_extremes(ops):
         assert float(to_np(tau)[0]) == want
 
 
+def _check_quantile(p, b, tau, qt):
+    """tau is the exact order statistic of the returned scores (NaN last) and b = [p >= tau]."""
+    p_g, b_g, tau_g = to_np(p), to_np(b).astype(bool), float(to_np(tau)[0])
+    n = len(p_g)
+    want = np.sort(p_g)[int(np.floor(qt * (n - 1)))]
+    assert tau_g == want or (np.isnan(tau_g) and np.isnan(want))
+    assert np.array_equal(b_g, p_g >= np.float32(tau_g))
+    return p_g, tau_g
+
+
+def test_route_quantile_more_tiles_than_workgroups(ops):
+    """Over 2^18 scores the select kernel re-reads its tiles on every digit;
+    NaN scores sort last and are never kept."""
+    torch = _torch()
+    rng = np.random.default_rng(11)
+    off, q, k, _ = _ragged(rng, [150_000, 1, 150_000, 37_123], 8, torch.float32)
+    say("route quantile many tiles N", off[-1])
+    p_o = oracle.route(q, k, off)
+    for qt in (0.1, 0.75):
+        p, b, tau = ops.route(to_dev(q), to_dev(k), to_dev(off), quantile=qt)
+        _, tau_g = _check_quantile(p, b, tau, qt)
+        assert abs(tau_g - oracle.stage_quantile(p_o, qt)) < 1e-5
+    q[rng.integers(1, len(q), 100)] = np.nan
+    p, b, tau = ops.route(to_dev(q), to_dev(k), to_dev(off), quantile=0.999)
+    p_g, tau_g = _check_quantile(p, b, tau, 0.999)
+    assert np.isnan(p_g).sum() > 50 and not np.isnan(tau_g)
+
+
+def test_route_quantile_crowded_scores(ops):
+    """Every non-start score is exactly 1/2 (q_t orthogonal to k_{t-1}), so
+    all keys share one bin on every digit; a rank among the NaN scores gives
+    tau = NaN and b = 0."""
+    N, d = 70_000, 16
+    q = np.zeros((N, d), np.float32); q[:, 0] = 1.0
+    k = np.zeros((N, d), np.float32); k[:, 1] = 3.0
+    off = np.array([0, 30_000, N], np.int64)
+    for qt in (0.0, 0.5, 1.0):
+        p, b, tau = ops.route(to_dev(q), to_dev(k), to_dev(off), quantile=qt)
+        p_g, tau_g = _check_quantile(p, b, tau, qt)
+        assert tau_g == (1.0 if qt == 1.0 else 0.5)
+    q[5:] = np.nan
+    p, b, tau = ops.route(to_dev(q), to_dev(k), to_dev(off), quantile=1.0)
+    _, tau_g = _check_quantile(p, b, tau, 1.0)
+    assert np.isnan(tau_g) and not to_np(b).any()
+
+
 def _compact_check(ops, b, p, rows, off, dtype, capacity=None):
     idx, coff, z, P, st = ops.compact(to_dev(b.astype(np.uint8)), to_dev(off), rows=to_dev(rows, dtype),
                                       p=to_dev(p.astype(np.float32)), capacity=capacity)
