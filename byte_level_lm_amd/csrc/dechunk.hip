@@ -9,17 +9,72 @@
 // chunk of a sequence; u_c = P_c z_c) is a linear recurrence, scanned in three
 // passes over a fixed grid of kNT tiles of consecutive chunks (flat over the
 // packed batch; the a = 0 resets keep sequences independent):
-//   1. per tile: its affine aggregate (A = prod a, U = scan end from 0)
-//   2. per 4-feature slice: scan of the kNT aggregates -> carry into each tile
+//   1. per tile: its affine aggregate (A = prod a, U = scan end from 0); the
+//      same launch zeroes the rows of each sequence before its first chunk
+//   2. per 32-feature column block: scan of the kNT aggregates -> carry into
+//      each tile
 //   3. per tile: rescan from the carry and write every byte row of each chunk
+// A wave owns one (tile, feature slice).  It first reads the metadata of up
+// to 64 chunks at once, one chunk per lane (P, first row, last row, whether
+// the chunk starts its sequence), so that the serial loop over the chunks only
+// waits on the z rows, which it loads kUnroll chunks at a time.
 // HBM-bound: z is read twice, the [total x d] output is written once
-// (nontemporal); the tile aggregates add 2 * kNT * d * 4 bytes.
+// (nontemporal); the tile aggregates and carries add 3 * kNT * d * 4 bytes.
 #include "common.h"
 
 namespace bllm {
 namespace {
 
-constexpr int kNT = 4096;
+constexpr int kNT = 2048;      // tiles of consecutive chunks
+constexpr int kLaneBytes = 8;  // bytes of a row per lane
+constexpr int kUnroll = 4;     // z rows in flight per wave
+constexpr int kCarryCols = 8;                   // float4 columns per carry block
+constexpr int kCarryThreads = 1024;
+constexpr int kCarryGroups = kCarryThreads / kCarryCols;
+constexpr int kCarryPer = kNT / kCarryGroups;   // tiles per carry thread
+static_assert(kNT % kCarryGroups == 0, "tile count must split over the carry groups");
+
+// kLaneBytes of one row per lane (2, 4 or 8 elements), unpacked to fp32
+template <int DT> struct Lane {
+  static constexpr int E = DT == BLLM_F32 ? 4 : 2;
+  static constexpr int N = kLaneBytes / E;
+  static constexpr int W = kLaneBytes / 4;  // 32-bit words
+  __device__ static inline void load(const void* base, int64_t elem, float* x) {
+    const char* p = static_cast<const char*>(base) + elem * E;
+    uint32_t w[W];
+    if constexpr (W == 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (W == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      if constexpr (DT == BLLM_F32) {
+        x[i] = __uint_as_float(w[i]);
+      } else {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
+  }
+  __device__ static inline void store_nt(void* base, int64_t elem, const float* x) {
+    uint32_t* p = reinterpret_cast<uint32_t*>(static_cast<char*>(base) + elem * E);
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      uint32_t w;
+      if constexpr (DT == BLLM_F32)
+        w = __float_as_uint(x[i]);
+      else
+        w = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) |
+            (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+      __builtin_nontemporal_store(w, p + i);
+    }
+  }
+};
 
 struct Tile {
   int64_t c0, c1;
@@ -27,106 +82,221 @@ struct Tile {
 
 __device__ inline Tile tile_range(int64_t M, int64_t i) {
   const int64_t L = (M + kNT - 1) / kNT;
-  const int64_t c0 = i * L;
+  const int64_t c0 = i * L < M ? i * L : M;
   return {c0, c0 + L < M ? c0 + L : M};
 }
 
+// Metadata of chunk c = cb + lane (cb .. ce-1, ce - cb <= 64), one per lane:
+// the multiplier a_c, P_c, the first and one-past-last row of the chunk.
+// The sequences overlapping the range are walked with wave-uniform loads.
+struct ChunkMeta {
+  float a, P;
+  int64_t t0, t1;
+};
+
+__device__ inline ChunkMeta chunk_meta(const float* __restrict__ P, const int32_t* __restrict__ idx,
+                                       const int64_t* __restrict__ chunk_offsets,
+                                       const int64_t* __restrict__ offsets, int nseq, int64_t M,
+                                       int64_t cb, int64_t ce, int lane) {
+  const int64_t c = cb + lane < ce ? cb + lane : ce - 1;
+  ChunkMeta m;
+  m.P = P[c];
+  m.t0 = idx[c];
+  const int64_t cn = c + 1 < M ? c + 1 : c;
+  int64_t t1 = idx[cn];
+  bool start = false;
+  int s = upper_seq(chunk_offsets, nseq, cb);  // the sequence holding chunk cb
+  for (;;) {
+    const int64_t cs = chunk_offsets[s], ce_s = chunk_offsets[s + 1];
+    if (cs < ce_s) {  // empty sequences own no chunk
+      if (c == cs) start = true;
+      if (c == ce_s - 1) t1 = offsets[s + 1];
+    }
+    if (ce_s >= ce || s + 1 >= nseq) break;
+    ++s;
+  }
+  m.a = start ? 0.f : 1.f - m.P;
+  m.t1 = t1;
+  return m;
+}
+
+__device__ inline float lane_f(float v, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+}
+__device__ inline int64_t lane_i64(int64_t v, int j) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u & 0xFFFFFFFFu), j));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), j));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Pass 1.  Grid: (kNT/4 + nzero, nslices) blocks of 4 waves; blocks past the
+// tiles zero the rows before each sequence's first chunk (slice 0 only).
 template <int DT>
 __global__ __launch_bounds__(256) void ema_tile_aggregate(const void* __restrict__ z,
                                                           const float* __restrict__ P, int d,
+                                                          const int32_t* __restrict__ idx,
                                                           const int64_t* __restrict__ chunk_offsets,
+                                                          const int64_t* __restrict__ offsets,
                                                           int nseq, float* __restrict__ Aagg,
-                                                          float* __restrict__ Uagg) {
-  using V = Vec<DT>;
+                                                          float* __restrict__ Uagg,
+                                                          void* __restrict__ out) {
+  using V = Lane<DT>;
   const int lane = threadIdx.x & 63;
+  const int nvec = d / V::N;
+  if (blockIdx.x >= kNT / 4) {
+    if (blockIdx.y != 0) return;
+    float zero[V::N];
+#pragma unroll
+    for (int e = 0; e < V::N; ++e) zero[e] = 0.f;
+    const int nzb = gridDim.x - kNT / 4;
+    for (int s = blockIdx.x - kNT / 4; s < nseq; s += nzb) {
+      const int64_t cf = chunk_offsets[s];
+      const int64_t first = cf < chunk_offsets[s + 1] ? static_cast<int64_t>(idx[cf]) : offsets[s + 1];
+      const int64_t t0 = offsets[s];
+      const int64_t n = (first - t0) * nvec;
+      for (int64_t w = threadIdx.x; w < n; w += blockDim.x) {
+        const int64_t t = t0 + w / nvec;
+        const int v = static_cast<int>(w % nvec);
+        V::store_nt(out, t * d + static_cast<int64_t>(v) * V::N, zero);
+      }
+    }
+    return;
+  }
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int v = blockIdx.y * 64 + lane;
-  const bool active = v < d / V::N;
+  const int vc = v < nvec ? v : nvec - 1;  // clamped: every lane loads, the tail lanes do not store
   const int64_t M = chunk_offsets[nseq];
   const Tile tr = tile_range(M, i);
   float x[V::N];
 #pragma unroll
   for (int e = 0; e < V::N; ++e) x[e] = 0.f;
   float A = 1.f;
-  if (tr.c0 < tr.c1) {
-    int s = upper_seq(chunk_offsets, nseq, tr.c0);
-    for (int64_t c = tr.c0; c < tr.c1; ++c) {
-      while (chunk_offsets[s + 1] <= c) ++s;
-      const float Pc = P[c];
-      const float a = c == chunk_offsets[s] ? 0.f : 1.f - Pc;
-      if (active) {
-        float zz[V::N];
-        V::load(z, c * d + v * V::N, zz);
+  for (int64_t cb = tr.c0; cb < tr.c1; cb += 64) {
+    const int64_t ce = cb + 64 < tr.c1 ? cb + 64 : tr.c1;
+    const ChunkMeta m = chunk_meta(P, idx, chunk_offsets, offsets, nseq, M, cb, ce, lane);
+    const int n = static_cast<int>(ce - cb);
+    for (int j = 0; j < n; j += kUnroll) {
+      float zz[kUnroll][V::N];
 #pragma unroll
-        for (int e = 0; e < V::N; ++e) x[e] = fmaf(a, x[e], Pc * zz[e]);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t c = cb + (j + u < n ? j + u : n - 1);
+        V::load(z, c * d + static_cast<int64_t>(vc) * V::N, zz[u]);
       }
-      A *= a;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (j + u < n) {
+          const float a = lane_f(m.a, j + u);
+          const float Pc = lane_f(m.P, j + u);
+#pragma unroll
+          for (int e = 0; e < V::N; ++e) x[e] = fmaf(a, x[e], Pc * zz[u][e]);
+          A *= a;
+        }
+      }
     }
   }
-  if (active) {
-    float* u = Uagg + i * d + v * V::N;
+  if (v < nvec) {
+    float* u = Uagg + i * d + static_cast<int64_t>(v) * V::N;
 #pragma unroll
-    for (int e = 0; e < V::N; e += 4) *reinterpret_cast<float4*>(u + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+    for (int e = 0; e < V::N; ++e) u[e] = x[e];
   }
   if (blockIdx.y == 0 && lane == 0) Aagg[i] = A;
 }
 
-// one block per 4 features; thread j owns tiles [16j, 16j+16)
-__global__ __launch_bounds__(256) void ema_tile_carry(const float* __restrict__ Aagg,
-                                                      const float* __restrict__ Uagg, int d,
-                                                      float* __restrict__ carry) {
-  __shared__ float shA[256];
-  __shared__ float4 shU[256];
-  constexpr int per = kNT / 256;
-  const int f0 = blockIdx.x * 4;
-  const int j = threadIdx.x;
-  // this thread's tiles, all loads in flight at once
-  float ta[per];
-  float4 tu[per];
-#pragma unroll
-  for (int q = 0; q < per; ++q) {
-    const int64_t i = static_cast<int64_t>(j) * per + q;
-    ta[q] = Aagg[i];
-    tu[q] = *reinterpret_cast<const float4*>(Uagg + i * d + f0);
-  }
+// affine maps x -> A x + U composed in order: first (a1, u1), then (a2, u2)
+__device__ inline void compose(float a1, float4 u1, float a2, float4 u2, float& a, float4& u) {
+  a = a2 * a1;
+  u = make_float4(fmaf(a2, u1.x, u2.x), fmaf(a2, u1.y, u2.y), fmaf(a2, u1.z, u2.z), fmaf(a2, u1.w, u2.w));
+}
+
+__device__ inline float4 shfl_up4(float4 v, int off) {
+  return make_float4(__shfl_up(v.x, off, kWave), __shfl_up(v.y, off, kWave), __shfl_up(v.z, off, kWave),
+                     __shfl_up(v.w, off, kWave));
+}
+
+// Pass 2.  One block per 32 features (whole 128-byte lines of the aggregate
+// rows, so no two blocks share a line); thread (group g, column col) owns
+// tiles [g*kCarryPer, (g+1)*kCarryPer) of its float4 column.  Group scans:
+// within the wave by shuffles (8 groups per wave), across the 16 waves
+// through LDS.  Writes the carry into every tile (the scan value before it).
+// The tile values are read in batches of at most 16 (twice: for the group
+// fold and for the carries) to stay within 128 VGPRs at 1024 threads.
+__global__ __launch_bounds__(kCarryThreads) void ema_tile_carry(const float* __restrict__ Aagg,
+                                                                const float* __restrict__ Uagg, int d,
+                                                                float* __restrict__ carry) {
+  __shared__ float shA[kCarryThreads / kWave][kCarryCols];
+  __shared__ float4 shU[kCarryThreads / kWave][kCarryCols];
+  const int tid = threadIdx.x;
+  const int col = tid & (kCarryCols - 1);
+  const int g = tid >> 3;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int f = blockIdx.x * (kCarryCols * 4) + col * 4;
+  const bool active = f < d;
+  const int fc = active ? f : d - 4;
+  constexpr int kBatch = kCarryPer < 16 ? kCarryPer : 16;
   float A = 1.f;
   float4 U = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 1
+  for (int q0 = 0; q0 < kCarryPer; q0 += kBatch) {
+    float ta[kBatch];
+    float4 tu[kBatch];
 #pragma unroll
-  for (int q = 0; q < per; ++q) {
-    const float a = ta[q];
-    const float4 u = tu[q];
-    U = make_float4(fmaf(a, U.x, u.x), fmaf(a, U.y, u.y), fmaf(a, U.z, u.z), fmaf(a, U.w, u.w));
-    A *= a;
-  }
-  shA[j] = A;
-  shU[j] = U;
-  __syncthreads();
-  // inclusive Hillis-Steele scan with the (ordered) affine composition
-  for (int off = 1; off < 256; off <<= 1) {
-    float pa = 1.f;
-    float4 pu = make_float4(0.f, 0.f, 0.f, 0.f);
-    const bool has = j >= off;
-    if (has) { pa = shA[j - off]; pu = shU[j - off]; }
-    __syncthreads();
-    if (has) {
-      const float a = shA[j];
-      const float4 u = shU[j];
-      shA[j] = a * pa;
-      shU[j] = make_float4(fmaf(a, pu.x, u.x), fmaf(a, pu.y, u.y), fmaf(a, pu.z, u.z), fmaf(a, pu.w, u.w));
+    for (int q = 0; q < kBatch; ++q) {
+      const int64_t i = static_cast<int64_t>(g) * kCarryPer + q0 + q;
+      ta[q] = Aagg[i];
+      tu[q] = *reinterpret_cast<const float4*>(Uagg + i * d + fc);
     }
-    __syncthreads();
-  }
-  float4 cv = j > 0 ? shU[j - 1] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int q = 0; q < per; ++q) {
-    const int64_t i = static_cast<int64_t>(j) * per + q;
-    *reinterpret_cast<float4*>(carry + i * d + f0) = cv;
-    const float a = ta[q];
-    const float4 u = tu[q];
-    cv = make_float4(fmaf(a, cv.x, u.x), fmaf(a, cv.y, u.y), fmaf(a, cv.z, u.z), fmaf(a, cv.w, u.w));
+    for (int q = 0; q < kBatch; ++q) compose(A, U, ta[q], tu[q], A, U);
+  }
+  // inclusive scan over the 8 groups of this wave (lanes 8 apart)
+#pragma unroll
+  for (int off = kCarryCols; off < kWave; off <<= 1) {
+    const float pa = __shfl_up(A, off, kWave);
+    const float4 pu = shfl_up4(U, off);
+    if (lane >= off) compose(pa, pu, A, U, A, U);
+  }
+  if (lane >= kWave - kCarryCols) {
+    shA[wv][col] = A;
+    shU[wv][col] = U;
+  }
+  // exclusive value of this group: previous group of the wave, after the
+  // totals of the earlier waves
+  float ea = __shfl_up(A, kCarryCols, kWave);
+  float4 eu = shfl_up4(U, kCarryCols);
+  if (lane < kCarryCols) {
+    ea = 1.f;
+    eu = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+  float pa = 1.f;
+  float4 pu = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int w = 0; w < wv; ++w) compose(pa, pu, shA[w][col], shU[w][col], pa, pu);
+  float cva;
+  float4 cv;
+  compose(pa, pu, ea, eu, cva, cv);
+  if (!active) return;
+#pragma unroll 1
+  for (int q0 = 0; q0 < kCarryPer; q0 += kBatch) {
+    float ta[kBatch];
+    float4 tu[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int64_t i = static_cast<int64_t>(g) * kCarryPer + q0 + q;
+      ta[q] = Aagg[i];
+      tu[q] = *reinterpret_cast<const float4*>(Uagg + i * d + fc);
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int64_t i = static_cast<int64_t>(g) * kCarryPer + q0 + q;
+      *reinterpret_cast<float4*>(carry + i * d + f) = cv;
+      compose(cva, cv, ta[q], tu[q], cva, cv);
+    }
   }
 }
 
+// Pass 3.  Same grid as pass 1 without the zeroing blocks.
 template <int DT>
 __global__ __launch_bounds__(256) void ema_tile_expand(const void* __restrict__ z,
                                                        const float* __restrict__ P, int d,
@@ -135,60 +305,47 @@ __global__ __launch_bounds__(256) void ema_tile_expand(const void* __restrict__ 
                                                        const int64_t* __restrict__ offsets, int nseq,
                                                        const float* __restrict__ carry,
                                                        void* __restrict__ out) {
-  using V = Vec<DT>;
+  using V = Lane<DT>;
   const int lane = threadIdx.x & 63;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int nvec = d / V::N;
   const int v = blockIdx.y * 64 + lane;
-  const bool active = v < d / V::N;
+  const bool active = v < nvec;
+  const int vc = active ? v : nvec - 1;
   const int64_t M = chunk_offsets[nseq];
   const Tile tr = tile_range(M, i);
   if (tr.c0 >= tr.c1) return;
   float x[V::N];
-  if (active) {
-    const float* cp = carry + i * d + v * V::N;
+  {
+    const float* cp = carry + i * d + static_cast<int64_t>(vc) * V::N;
 #pragma unroll
-    for (int e = 0; e < V::N; e += 4) {
-      const float4 t = *reinterpret_cast<const float4*>(cp + e);
-      x[e] = t.x; x[e + 1] = t.y; x[e + 2] = t.z; x[e + 3] = t.w;
-    }
+    for (int e = 0; e < V::N; ++e) x[e] = cp[e];
   }
-  int s = upper_seq(chunk_offsets, nseq, tr.c0);
-  for (int64_t c = tr.c0; c < tr.c1; ++c) {
-    while (chunk_offsets[s + 1] <= c) ++s;
-    const float Pc = P[c];
-    const float a = c == chunk_offsets[s] ? 0.f : 1.f - Pc;
-    const int64_t t0 = idx[c];
-    const int64_t t1 = c + 1 < chunk_offsets[s + 1] ? static_cast<int64_t>(idx[c + 1]) : offsets[s + 1];
-    if (active) {
-      float zz[V::N];
-      V::load(z, c * d + v * V::N, zz);
+  for (int64_t cb = tr.c0; cb < tr.c1; cb += 64) {
+    const int64_t ce = cb + 64 < tr.c1 ? cb + 64 : tr.c1;
+    const ChunkMeta m = chunk_meta(P, idx, chunk_offsets, offsets, nseq, M, cb, ce, lane);
+    const int n = static_cast<int>(ce - cb);
+    for (int j = 0; j < n; j += kUnroll) {
+      float zz[kUnroll][V::N];
 #pragma unroll
-      for (int e = 0; e < V::N; ++e) x[e] = fmaf(a, x[e], Pc * zz[e]);
-      for (int64_t t = t0; t < t1; ++t) V::store_nt(out, t * d + v * V::N, x);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t c = cb + (j + u < n ? j + u : n - 1);
+        V::load(z, c * d + static_cast<int64_t>(vc) * V::N, zz[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (j + u < n) {
+          const float a = lane_f(m.a, j + u);
+          const float Pc = lane_f(m.P, j + u);
+          const int64_t t0 = lane_i64(m.t0, j + u);
+          const int64_t t1 = lane_i64(m.t1, j + u);
+#pragma unroll
+          for (int e = 0; e < V::N; ++e) x[e] = fmaf(a, x[e], Pc * zz[u][e]);
+          if (active)
+            for (int64_t t = t0; t < t1; ++t) V::store_nt(out, t * d + static_cast<int64_t>(v) * V::N, x);
+        }
+      }
     }
-  }
-}
-
-// rows of a sequence before its first chunk (or all rows if it has none) are 0
-template <int DT>
-__global__ __launch_bounds__(256) void ema_zero_prefix(const int32_t* __restrict__ idx,
-                                                       const int64_t* __restrict__ chunk_offsets,
-                                                       const int64_t* __restrict__ offsets, int d,
-                                                       void* __restrict__ out) {
-  using V = Vec<DT>;
-  const int s = blockIdx.x;
-  const int64_t cf = chunk_offsets[s];
-  const int64_t first = cf < chunk_offsets[s + 1] ? static_cast<int64_t>(idx[cf]) : offsets[s + 1];
-  const int64_t t0 = offsets[s];
-  const int nvec = d / V::N;
-  const int64_t n = (first - t0) * nvec;
-  float zero[V::N];
-#pragma unroll
-  for (int e = 0; e < V::N; ++e) zero[e] = 0.f;
-  for (int64_t w = threadIdx.x; w < n; w += blockDim.x) {
-    const int64_t t = t0 + w / nvec;
-    const int v = static_cast<int>(w % nvec);
-    V::store(out, t * d + v * V::N, zero);
   }
 }
 
@@ -196,17 +353,18 @@ template <int DT>
 void launch_dechunk(const void* z, const float* P, int d, const int32_t* idx,
                     const int64_t* chunk_offsets, const int64_t* offsets, int nseq, void* out,
                     float* ws, hipStream_t st) {
-  constexpr int N = Vec<DT>::N;
+  constexpr int N = Lane<DT>::N;
   float* Aagg = ws;
   float* Uagg = ws + kNT;
   float* carry = Uagg + static_cast<int64_t>(kNT) * d;
   const int nslices = (d / N + 63) / 64;
-  const dim3 grid(kNT / 4, nslices);
-  hipLaunchKernelGGL(ema_zero_prefix<DT>, dim3(nseq), dim3(256), 0, st, idx, chunk_offsets, offsets, d, out);
-  hipLaunchKernelGGL(ema_tile_aggregate<DT>, grid, dim3(256), 0, st, z, P, d, chunk_offsets, nseq, Aagg, Uagg);
-  hipLaunchKernelGGL(ema_tile_carry, dim3(d / 4), dim3(256), 0, st, Aagg, Uagg, d, carry);
-  hipLaunchKernelGGL(ema_tile_expand<DT>, grid, dim3(256), 0, st, z, P, d, idx, chunk_offsets,
-                     offsets, nseq, carry, out);
+  const int nzero = nseq < 256 ? nseq : 256;
+  hipLaunchKernelGGL(ema_tile_aggregate<DT>, dim3(kNT / 4 + nzero, nslices), dim3(256), 0, st, z, P, d,
+                     idx, chunk_offsets, offsets, nseq, Aagg, Uagg, out);
+  hipLaunchKernelGGL(ema_tile_carry, dim3((d + kCarryCols * 4 - 1) / (kCarryCols * 4)),
+                     dim3(kCarryThreads), 0, st, Aagg, Uagg, d, carry);
+  hipLaunchKernelGGL(ema_tile_expand<DT>, dim3(kNT / 4, nslices), dim3(256), 0, st, z, P, d, idx,
+                     chunk_offsets, offsets, nseq, carry, out);
 }
 
 }  // namespace

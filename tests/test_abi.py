@@ -41,8 +41,10 @@ def test_version_and_status_strings(L):
 def test_workspace_sizes(L):
     assert L.bllm_route_workspace(1000) > 2048 * 4
     assert L.bllm_compact_workspace(10**6) >= (10**6 // 4096) * 4
-    assert L.bllm_dechunk_workspace(512) >= 2 * 4096 * 512 * 4
-    # nseq * nblk * ldm^2 fp32 with ldm = d' + c: d=512 -> c=128, ldm=640, nblk=64
+    # per tile: one fp32 product plus d fp32 aggregate and d fp32 carry values
+    w512, w768 = L.bllm_dechunk_workspace(512), L.bllm_dechunk_workspace(768)
+    tiles = (w768 - w512) // (2 * 256 * 4)
+    assert tiles >= 256 and w512 >= tiles * (1 + 2 * 512) * 4
     # d = 512: blocks of c = 256 rows, 32 blocks per sequence, block matrices of
     # (512 + 256)^2 fp32 plus a 64 x 64 inverse slot each
     assert L.bllm_coding_rate_workspace(32, 8192, 512) == 32 * 32 * (768 * 768 + 64 * 64) * 4 + 256

@@ -250,6 +250,26 @@ def test_dechunk_many_chunks_and_zero_prefix(ops):
     assert float(o2.abs().max()) == 0.0
 
 
+def test_dechunk_many_short_sequences(ops):
+    """700 ragged sequences (some empty, some without a boundary at their
+    start): resets inside most scan units, many sequences per zeroing block."""
+    torch = _torch()
+    rng = np.random.default_rng(33)
+    lengths = rng.integers(0, 41, 700)
+    lengths[::7] = 0
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    N = int(off[-1])
+    b = rng.random(N) < 0.3
+    starts = off[:-1][lengths > 0]
+    b[starts[::2]] = True
+    P = rng.uniform(0.0, 1.0, N).astype(np.float32)
+    rows = rng.standard_normal((N, 24)).astype(np.float32)
+    idx, coff, z, PP = oracle.compact(b, P, rows, off)
+    say("dechunk many short sequences N", N, "M", len(idx))
+    for dtype in (torch.float32, torch.bfloat16):
+        _dechunk_check(ops, z, PP, idx, coff, off, dtype, 1e-4 if dtype == torch.float32 else 2e-2)
+
+
 def test_c2_two_stage_full_size(ops):
     """The headline H-Net workload: 32 streams of 8192 bytes, two stages at the
     0.75 score quantile each, both EMA scans back to full length (launch
