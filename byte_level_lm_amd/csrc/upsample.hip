@@ -13,9 +13,9 @@
 // 128 * kMaxRun positions.  Items are bucketed by bin (counting sort with wave
 // ballots; a deterministic order), then one grouped GEMM per bin on bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16): A rows are gathered from g by chunk, B = W_b
-// (transposed once into the workspace so both operands are contiguous along
-// the reduction), and the epilogue adds h_t and writes every position of the
-// item's run with 16-byte loads and stores.
+// as stored (read down its columns with the transposing LDS read), and the
+// epilogue adds h_t and writes every position of the item's run with 16-byte
+// loads and stores.
 #include <algorithm>
 
 #include "common.h"
@@ -29,7 +29,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kChunksPerBlock = 256;
 constexpr int kMaxRun = 16;
 constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLDK = kBK + 8;  // LDS row stride (bf16) of the operand tiles
+constexpr int kPA = kBK + 8;   // LDS pitch (bf16) of the A tile [kBM][kBK]
+constexpr int kPB = kBN + 16;  // LDS pitch (bf16) of the B tile [kBK][kBN]: rows 8 banks apart
 
 // row of element r held by `lane` in a 32x32 MFMA accumulator
 __device__ inline int crow_of(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
@@ -155,45 +156,58 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_items(const int32_t* __res
   }
 }
 
-// Wt[b][n][k] = W[b][k][n], 32x32 tiles through LDS
-__global__ __launch_bounds__(256) void up_transpose(const uint16_t* __restrict__ W, int dg, int dl,
-                                                    uint16_t* __restrict__ Wt) {
-  __shared__ uint16_t t[32][33];
-  const int b = blockIdx.z;
-  const int k0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
-  const uint16_t* src = W + static_cast<int64_t>(b) * dg * dl;
-  uint16_t* dst = Wt + static_cast<int64_t>(b) * dg * dl;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int r = ty; r < 32; r += 8)
-    if (k0 + r < dg && n0 + tx < dl) t[r][tx] = src[static_cast<int64_t>(k0 + r) * dl + n0 + tx];
-  __syncthreads();
-  for (int r = ty; r < 32; r += 8)
-    if (n0 + r < dl && k0 + tx < dg) dst[static_cast<int64_t>(n0 + r) * dg + k0 + tx] = t[tx][r];
+// Two transposing LDS reads (ds_read_b64_tr_b16) give a lane the MFMA B
+// operand of a [k][n] tile: 8 consecutive k of one column n.  Within each
+// 16-lane group, lane j addresses row k + j/4 (and k + 4 + j/4), columns
+// col + 4 (j % 4) .. +3, and lane i receives column i of those 4 rows; with
+// row = 8 (lane / 32) + (lane % 16) / 4 and col = 16 ((lane / 16) % 2) +
+// 4 (lane % 4) added to the tile origin, lane l gets column l % 32 and
+// rows 8 (l / 32) .. +7.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+__device__ inline uint4 and4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
+
+__device__ inline bf16x8 tr_frag(const uint16_t* s, int row, int col, int pitch) {
+  typedef __attribute__((address_space(3))) shortx4 lds_s4;
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(s + row * pitch + col));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(s + (row + 4) * pitch + col));
+  bf16x8 v;
+  __builtin_memcpy(&v, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&v) + 8, &hi, 8);
+  return v;
 }
 
 // grouped gather-GEMM: one 128 x 128 output tile (items x d_local) per block;
 // four waves in 2 x 2, each a 64 x 64 quadrant of 2 x 2 MFMA 32x32 tiles.
+// A rows are gathered from g by chunk; B is W_b in its stored [k][n] layout,
+// staged row-major and read with the transposing LDS read.
+// Block numbering: workgroup L runs on XCD L % 8, so the column tiles of one
+// row tile are given ids 8 apart inside a group of 8 * ncol consecutive ids.
+// They then run at about the same time on the same XCD and the gathered g
+// rows of the row tile come from HBM into that XCD's L2 once.
 __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat,
-                                               const uint16_t* __restrict__ Wt,
+                                               const uint16_t* __restrict__ W,
                                                const uint16_t* __restrict__ h, UpGeom g,
                                                const int32_t* __restrict__ bin_off,
                                                const int32_t* __restrict__ bin_cnt,
                                                const int32_t* __restrict__ tile_off,
-                                               const int4* __restrict__ items,
+                                               const int4* __restrict__ items, int ncol,
                                                uint16_t* __restrict__ out) {
   constexpr int kOLD = kBN + 4;  // fp32 row stride of the epilogue staging area
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBM * kLDK];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kBM * kPA + kBK * kPB];
   __shared__ int4 sItem[kBM];
   uint16_t* sA = smem;
-  uint16_t* sB = smem + kBM * kLDK;
+  uint16_t* sB = smem + kBM * kPA;
   float* sO = reinterpret_cast<float*>(smem);  // [64][kOLD] fp32, reused after the K loop
-  const int tau = blockIdx.x;
+  static_assert(64 * kOLD * 4 <= (kBM * kPA + kBK * kPB) * 2, "epilogue staging must fit");
+  const int grp = blockIdx.x / (8 * ncol), rem = blockIdx.x % (8 * ncol);
+  const int tau = 8 * grp + (rem & 7);
   if (tau >= tile_off[g.nbins]) return;
   int b = 0;
   while (tile_off[b + 1] <= tau) ++b;
   const int first = (tau - tile_off[b]) * kBM;
   const int mcount = min(kBM, bin_cnt[b] - first);
-  const int n0 = blockIdx.y * kBN;
+  const int n0 = (rem >> 3) * kBN;
   const int tid = threadIdx.x;
   if (tid < kBM) sItem[tid] = tid < mcount ? items[bin_off[b] + first + tid] : make_int4(0, 0, 0, 0);
   __syncthreads();
@@ -206,47 +220,54 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
-  // loader: thread moves rows lr + 32*q (q = 0..3), 16-byte column chunk lc;
+  // A loader: thread moves rows lr + 32*q (q = 0..3), 16-byte column chunk lc;
+  // B loader: K rows kr + 16*q of W_b, 16-byte column chunk nc (columns past
+  // d_local read a valid column, their results are not written);
   // the next K step's operands are in flight in named registers during the MFMAs
   const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const int kr = tid >> 4, nc = (tid & 15) * 8;
   const uint16_t* ar0 = gmat + static_cast<int64_t>(sItem[lr].x) * g.dg + lc;
   const uint16_t* ar1 = gmat + static_cast<int64_t>(sItem[lr + 32].x) * g.dg + lc;
   const uint16_t* ar2 = gmat + static_cast<int64_t>(sItem[lr + 64].x) * g.dg + lc;
   const uint16_t* ar3 = gmat + static_cast<int64_t>(sItem[lr + 96].x) * g.dg + lc;
-  const uint16_t* wb = Wt + static_cast<int64_t>(b) * g.dl * g.dg + lc;
-  const int nr0 = min(n0 + lr, g.dl - 1), nr1 = min(n0 + lr + 32, g.dl - 1);
-  const int nr2 = min(n0 + lr + 64, g.dl - 1), nr3 = min(n0 + lr + 96, g.dl - 1);
-  const uint16_t* br0 = wb + static_cast<int64_t>(nr0) * g.dg;
-  const uint16_t* br1 = wb + static_cast<int64_t>(nr1) * g.dg;
-  const uint16_t* br2 = wb + static_cast<int64_t>(nr2) * g.dg;
-  const uint16_t* br3 = wb + static_cast<int64_t>(nr3) * g.dg;
-  const bool a0 = lr < mcount, a1 = lr + 32 < mcount, a2 = lr + 64 < mcount, a3 = lr + 96 < mcount;
-  const bool b0 = n0 + lr < g.dl, b1 = n0 + lr + 32 < g.dl, b2 = n0 + lr + 64 < g.dl, b3 = n0 + lr + 96 < g.dl;
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  const uint16_t* wb = W + static_cast<int64_t>(b) * g.dg * g.dl + min(n0 + nc, g.dl - 8);
   uint4 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;
+  // Every load is issued (rows past the items read chunk 0's g row, whose
+  // results are not written); K past d_global, only in a last partial step,
+  // is masked to zero.
   auto fetch = [&](int ko) {
     const bool kin = ko + lc < g.dg;
-    pa0 = a0 && kin ? *reinterpret_cast<const uint4*>(ar0 + ko) : z4;
-    pa1 = a1 && kin ? *reinterpret_cast<const uint4*>(ar1 + ko) : z4;
-    pa2 = a2 && kin ? *reinterpret_cast<const uint4*>(ar2 + ko) : z4;
-    pa3 = a3 && kin ? *reinterpret_cast<const uint4*>(ar3 + ko) : z4;
-    pb0 = b0 && kin ? *reinterpret_cast<const uint4*>(br0 + ko) : z4;
-    pb1 = b1 && kin ? *reinterpret_cast<const uint4*>(br1 + ko) : z4;
-    pb2 = b2 && kin ? *reinterpret_cast<const uint4*>(br2 + ko) : z4;
-    pb3 = b3 && kin ? *reinterpret_cast<const uint4*>(br3 + ko) : z4;
+    const uint32_t ma = kin ? 0xFFFFFFFFu : 0u;
+    const int koa = kin ? ko : 0;
+    pa0 = and4(*reinterpret_cast<const uint4*>(ar0 + koa), ma);
+    pa1 = and4(*reinterpret_cast<const uint4*>(ar1 + koa), ma);
+    pa2 = and4(*reinterpret_cast<const uint4*>(ar2 + koa), ma);
+    pa3 = and4(*reinterpret_cast<const uint4*>(ar3 + koa), ma);
+    const int k0 = ko + kr, k1 = k0 + 16, k2 = k0 + 32, k3 = k0 + 48;
+    pb0 = and4(*reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k0 < g.dg ? k0 : 0) * g.dl),
+               k0 < g.dg ? 0xFFFFFFFFu : 0u);
+    pb1 = and4(*reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k1 < g.dg ? k1 : 0) * g.dl),
+               k1 < g.dg ? 0xFFFFFFFFu : 0u);
+    pb2 = and4(*reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k2 < g.dg ? k2 : 0) * g.dl),
+               k2 < g.dg ? 0xFFFFFFFFu : 0u);
+    pb3 = and4(*reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k3 < g.dg ? k3 : 0) * g.dl),
+               k3 < g.dg ? 0xFFFFFFFFu : 0u);
   };
+  const int j16 = lane & 15;
+  const int frow = 8 * (lane >> 5) + (j16 >> 2);
+  const int fcol = 64 * wn + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
   fetch(0);
   const int nk = (g.dg + kBK - 1) / kBK;
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();
-    *reinterpret_cast<uint4*>(sA + lr * kLDK + lc) = pa0;
-    *reinterpret_cast<uint4*>(sA + (lr + 32) * kLDK + lc) = pa1;
-    *reinterpret_cast<uint4*>(sA + (lr + 64) * kLDK + lc) = pa2;
-    *reinterpret_cast<uint4*>(sA + (lr + 96) * kLDK + lc) = pa3;
-    *reinterpret_cast<uint4*>(sB + lr * kLDK + lc) = pb0;
-    *reinterpret_cast<uint4*>(sB + (lr + 32) * kLDK + lc) = pb1;
-    *reinterpret_cast<uint4*>(sB + (lr + 64) * kLDK + lc) = pb2;
-    *reinterpret_cast<uint4*>(sB + (lr + 96) * kLDK + lc) = pb3;
+    *reinterpret_cast<uint4*>(sA + lr * kPA + lc) = pa0;
+    *reinterpret_cast<uint4*>(sA + (lr + 32) * kPA + lc) = pa1;
+    *reinterpret_cast<uint4*>(sA + (lr + 64) * kPA + lc) = pa2;
+    *reinterpret_cast<uint4*>(sA + (lr + 96) * kPA + lc) = pa3;
+    *reinterpret_cast<uint4*>(sB + kr * kPB + nc) = pb0;
+    *reinterpret_cast<uint4*>(sB + (kr + 16) * kPB + nc) = pb1;
+    *reinterpret_cast<uint4*>(sB + (kr + 32) * kPB + nc) = pb2;
+    *reinterpret_cast<uint4*>(sB + (kr + 48) * kPB + nc) = pb3;
     __syncthreads();
     if (kt + 1 < nk) fetch((kt + 1) * kBK);
 #pragma unroll
@@ -254,8 +275,8 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
       bf16x8 af[2], bfr[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        af[t] = *reinterpret_cast<const bf16x8*>(sA + (64 * wm + 32 * t + (lane & 31)) * kLDK + ks + 8 * (lane >> 5));
-        bfr[t] = *reinterpret_cast<const bf16x8*>(sB + (64 * wn + 32 * t + (lane & 31)) * kLDK + ks + 8 * (lane >> 5));
+        af[t] = *reinterpret_cast<const bf16x8*>(sA + (64 * wm + 32 * t + (lane & 31)) * kPA + ks + 8 * (lane >> 5));
+        bfr[t] = tr_frag(sB, ks + frow, fcol + 32 * t, kPB);
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
@@ -319,7 +340,6 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
 struct UpWs {
   int32_t *counts, *base, *bin_off, *bin_cnt, *tile_off;
   int4* items;
-  uint16_t* Wt;
 };
 
 // items per chunk <= min(L, B) + L / kMaxRun (one per present bin, one more
@@ -337,15 +357,13 @@ UpWs up_carve(void* ws, const UpGeom& g) {
   u.bin_off = reinterpret_cast<int32_t*>(p); p += 256;
   u.bin_cnt = reinterpret_cast<int32_t*>(p); p += 256;
   u.tile_off = reinterpret_cast<int32_t*>(p); p += 512;
-  u.items = reinterpret_cast<int4*>(p); p += align_up(up_max_items(g) * 16, 256);
-  u.Wt = reinterpret_cast<uint16_t*>(p);
+  u.items = reinterpret_cast<int4*>(p);
   return u;
 }
 
 size_t up_ws_bytes(const UpGeom& g) {
   const size_t cb = align_up(static_cast<size_t>(g.nblk) * g.nbins * 4, 256);
-  return 2 * cb + 1024 + align_up(up_max_items(g) * 16, 256) +
-         static_cast<size_t>(g.nbins) * g.dg * g.dl * 2 + 256;
+  return 2 * cb + 1024 + align_up(up_max_items(g) * 16, 256) + 256;
 }
 
 }  // namespace
@@ -379,18 +397,16 @@ extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* 
   if (!ws || ws_bytes < up_ws_bytes(g) || !aligned16(ws)) return BLLM_E_WS;
   hipStream_t st = static_cast<hipStream_t>(stream);
   UpWs u = up_carve(ws, g);
-  hipLaunchKernelGGL(up_transpose, dim3(static_cast<unsigned>(ceil_div(d_local, 32)),
-                                        static_cast<unsigned>(ceil_div(d_global, 32)),
-                                        static_cast<unsigned>(nbins)),
-                     dim3(256), 0, st, static_cast<const uint16_t*>(W), g.dg, g.dl, u.Wt);
   hipLaunchKernelGGL(up_count, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts);
   hipLaunchKernelGGL(up_offsets, dim3(1), dim3(256), 0, st, u.counts, g, u.base, u.bin_off, u.bin_cnt,
                      u.tile_off);
   hipLaunchKernelGGL(up_items, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.base, u.items);
   const int64_t max_tiles = ceil_div(static_cast<int64_t>(up_max_items(g)), kBM) + nbins;
-  hipLaunchKernelGGL(up_gemm, dim3(static_cast<unsigned>(max_tiles), static_cast<unsigned>(ceil_div(d_local, kBN))),
-                     dim3(256), 0, st, static_cast<const uint16_t*>(gm), u.Wt,
-                     static_cast<const uint16_t*>(h), g, u.bin_off, u.bin_cnt, u.tile_off, u.items,
-                     static_cast<uint16_t*>(s_out));
+  const int ncol = static_cast<int>(ceil_div(d_local, kBN));
+  const int64_t nblocks = ceil_div(max_tiles, 8) * 8 * ncol;
+  hipLaunchKernelGGL(up_gemm, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(gm), static_cast<const uint16_t*>(W),
+                     static_cast<const uint16_t*>(h), g, u.bin_off,
+                     u.bin_cnt, u.tile_off, u.items, ncol, static_cast<uint16_t*>(s_out));
   return launch_status();
 }

@@ -175,7 +175,8 @@ def _random_idx(rng, nseq, T, K):
 
 
 @pytest.mark.parametrize("nseq,T,K,dg,dl,B", [(2, 300, 40, 64, 32, 16), (3, 1000, 37, 96, 136, 4),
-                                              (1, 64, 64, 32, 8, 16), (2, 500, 1, 64, 64, 16)])
+                                              (1, 64, 64, 32, 8, 16), (2, 500, 1, 64, 64, 16),
+                                              (4, 3000, 300, 200, 320, 16)])
 def test_upsample_vs_oracle(ops, nseq, T, K, dg, dl, B):
     torch = _torch()
     rng = np.random.default_rng(T + K)
