@@ -31,6 +31,10 @@ constexpr int kMaxRun = 16;
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kPA = kBK + 8;   // LDS pitch (bf16) of the A tile [kBM][kBK]
 constexpr int kPB = kBN + 16;  // LDS pitch (bf16) of the B tile [kBK][kBN]: rows 8 banks apart
+#ifndef BLLM_UP_PAIRS
+#define BLLM_UP_PAIRS 2
+#endif
+constexpr int kPairs = BLLM_UP_PAIRS;  // epilogue pairs per thread whose loads are issued together
 
 // row of element r held by `lane` in a 32x32 MFMA accumulator
 __device__ inline int crow_of(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
@@ -39,9 +43,13 @@ struct UpGeom {
   int nseq, T, K, dg, dl, nbins, nblk;
 };
 
-// first position offset of bin b in a chunk of length L: ceil(b L / B)
-__device__ inline int bin_lo(int b, int L, int B) { return (b * L + B - 1) / B; }
-
+// first position offset of bin b in a chunk of length L: ceil(b L / B);
+// BC is B when it is known at compile time (16), else 0
+template <int BC>
+__device__ inline int bin_lo(int b, int L, int B) {
+  if constexpr (BC > 0) return (b * L + BC - 1) / BC;
+  return (b * L + B - 1) / B;
+}
 
 __device__ inline int chunk_len(const int32_t* idx, const UpGeom& g, int64_t cg) {
   const int i = static_cast<int>(cg % g.K);
@@ -50,17 +58,26 @@ __device__ inline int chunk_len(const int32_t* idx, const UpGeom& g, int64_t cg)
 }
 
 // items of bin b of a chunk of length L: its run split into pieces of at most kMaxRun
+template <int BC>
 __device__ inline int bin_pieces(int b, int L, int B) {
-  return (bin_lo(b + 1, L, B) - bin_lo(b, L, B) + kMaxRun - 1) / kMaxRun;
+  return (bin_lo<BC>(b + 1, L, B) - bin_lo<BC>(b, L, B) + kMaxRun - 1) / kMaxRun;
 }
 
+// Wave sum and exclusive wave scan of small counts.  A lane holds at most one
+// item per bin unless its run exceeds kMaxRun positions, so the common case
+// is a ballot and a popcount (mbcnt); otherwise shuffles.
 __device__ inline int wave_sum_i(int v) {
+  if (__ballot(v > 1) == 0) return __popcll(__ballot(v == 1));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
 
 __device__ inline int wave_excl_i(int v, int lane) {
+  if (__ballot(v > 1) == 0) {
+    const uint64_t m = __ballot(v == 1);
+    return __popcll(m & ((uint64_t(1) << lane) - 1));
+  }
   int x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -71,6 +88,7 @@ __device__ inline int wave_excl_i(int v, int lane) {
 }
 
 // per-block, per-bin item counts
+template <int BC>
 __global__ __launch_bounds__(kChunksPerBlock) void up_count(const int32_t* __restrict__ idx, UpGeom g,
                                                             int32_t* __restrict__ counts) {
   __shared__ int wc[4][64];
@@ -79,7 +97,7 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_count(const int32_t* __res
   const bool valid = cg < static_cast<int64_t>(g.nseq) * g.K;
   const int L = valid ? chunk_len(idx, g, cg) : 0;
   for (int b = 0; b < g.nbins; ++b) {
-    const int n = wave_sum_i(valid ? bin_pieces(b, L, g.nbins) : 0);
+    const int n = wave_sum_i(valid ? bin_pieces<BC>(b, L, g.nbins) : 0);
     if (lane == 0) wc[w][b] = n;
   }
   __syncthreads();
@@ -88,67 +106,71 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_count(const int32_t* __res
         wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] + wc[3][threadIdx.x];
 }
 
-// single block: per-bin running offsets of every count block, bin offsets and
-// tile offsets.  Counts are staged through LDS in chunks of 64 blocks.
-__global__ __launch_bounds__(256) void up_offsets(const int32_t* __restrict__ counts, UpGeom g,
-                                                  int32_t* __restrict__ base, int32_t* __restrict__ bin_off,
-                                                  int32_t* __restrict__ bin_cnt, int32_t* __restrict__ tile_off) {
-  constexpr int CB = 64;
-  __shared__ int sc[CB][65];
-  __shared__ int tot[64];
-  const int tid = threadIdx.x;
-  int run = 0;
-  for (int k0 = 0; k0 < g.nblk; k0 += CB) {
-    const int nk = min(CB, g.nblk - k0);
-    __syncthreads();
-    for (int e = tid; e < nk * g.nbins; e += blockDim.x)
-      sc[e / g.nbins][e % g.nbins] = counts[static_cast<int64_t>(k0) * g.nbins + e];
-    __syncthreads();
-    if (tid < g.nbins) {
-      for (int k = 0; k < nk; ++k) {
-        base[static_cast<int64_t>(k0 + k) * g.nbins + tid] = run;
-        run += sc[k][tid];
-      }
-    }
-  }
-  if (tid < g.nbins) tot[tid] = run;
-  __syncthreads();
-  if (tid == 0) {
-    int io = 0, to = 0;
-    for (int q = 0; q < g.nbins; ++q) {
-      bin_off[q] = io;
-      bin_cnt[q] = tot[q];
-      tile_off[q] = to;
-      io += tot[q];
-      to += (tot[q] + kBM - 1) / kBM;
-    }
-    tile_off[g.nbins] = to;
-  }
-  __syncthreads();
-  for (int64_t e = tid; e < static_cast<int64_t>(g.nblk) * g.nbins; e += blockDim.x)
-    base[e] += bin_off[e % g.nbins];
-}
-
-// items grouped by bin, in chunk order inside each bin
+// Items grouped by bin, in chunk order inside each bin.  Each block first
+// derives its own slot base per bin from all blocks' counts (the items of
+// earlier blocks, after all items of earlier bins); block 0 also writes the
+// bins' item offsets, counts and GEMM tile offsets.
+template <int BC>
 __global__ __launch_bounds__(kChunksPerBlock) void up_items(const int32_t* __restrict__ idx, UpGeom g,
-                                                            const int32_t* __restrict__ base,
+                                                            const int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ bin_off,
+                                                            int32_t* __restrict__ bin_cnt,
+                                                            int32_t* __restrict__ tile_off,
                                                             int4* __restrict__ items) {
   __shared__ int wc[4][64];
-  const int64_t cg = static_cast<int64_t>(blockIdx.x) * kChunksPerBlock + threadIdx.x;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ int sBefore[4][64], sTot[4][64], sBase[64];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  {
+    // lane = bin; wave w sums blocks [16 w, 16 w + 16) of every 64, sixteen
+    // independent loads in flight at a time
+    int before = 0, tot = 0;
+    for (int k0 = 16 * w; k0 < g.nblk; k0 += 64) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int k = k0 + j;
+        v[j] = lane < g.nbins && k < g.nblk ? counts[static_cast<int64_t>(k) * g.nbins + lane] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        tot += v[j];
+        if (k0 + j < static_cast<int>(blockIdx.x)) before += v[j];
+      }
+    }
+    sBefore[w][lane] = before;
+    sTot[w][lane] = tot;
+  }
+  const int64_t cg = static_cast<int64_t>(blockIdx.x) * kChunksPerBlock + tid;
   const bool valid = cg < static_cast<int64_t>(g.nseq) * g.K;
   const int L = valid ? chunk_len(idx, g, cg) : 0;
   for (int b = 0; b < g.nbins; ++b) {
-    const int n = wave_sum_i(valid ? bin_pieces(b, L, g.nbins) : 0);
+    const int n = wave_sum_i(valid ? bin_pieces<BC>(b, L, g.nbins) : 0);
     if (lane == 0) wc[w][b] = n;
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int tb = sTot[0][lane] + sTot[1][lane] + sTot[2][lane] + sTot[3][lane];
+    const int off = wave_excl_i(tb, lane);
+    sBase[lane] = off + sBefore[0][lane] + sBefore[1][lane] + sBefore[2][lane] + sBefore[3][lane];
+    if (blockIdx.x == 0) {
+      const int tc = (tb + kBM - 1) / kBM;
+      const int toff = wave_excl_i(tc, lane);
+      if (lane < g.nbins) {
+        bin_off[lane] = off;
+        bin_cnt[lane] = tb;
+        tile_off[lane] = toff;
+      }
+      if (lane == g.nbins - 1) tile_off[g.nbins] = toff + tc;
+    }
   }
   __syncthreads();
   const int64_t row0 = valid ? (cg / g.K) * g.T + idx[cg] : 0;
   for (int b = 0; b < g.nbins; ++b) {
-    const int np = valid ? bin_pieces(b, L, g.nbins) : 0;
-    int slot = base[static_cast<int64_t>(blockIdx.x) * g.nbins + b] + wave_excl_i(np, lane);
+    const int np = valid ? bin_pieces<BC>(b, L, g.nbins) : 0;
+    int slot = sBase[b] + wave_excl_i(np, lane);
     for (int q = 0; q < w; ++q) slot += wc[q][b];
-    const int lo = bin_lo(b, L, g.nbins), hi = bin_lo(b + 1, L, g.nbins);
+    const int lo = bin_lo<BC>(b, L, g.nbins), hi = bin_lo<BC>(b + 1, L, g.nbins);
     for (int e = 0; e < np; ++e) {
       const int a = lo + e * kMaxRun;
       items[slot + e] = make_int4(static_cast<int>(cg), static_cast<int>(row0 + a), min(kMaxRun, hi - a), 0);
@@ -300,37 +322,57 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
             sO[(32 * a + crow_of(r, lane)) * kOLD + 64 * wn + 32 * c + (lane & 31)] = acc[a][c][r];
     }
     __syncthreads();
-    // one (item row, 8-column chunk) pair per thread and round: the pair's
-    // 8 accumulator values are read once and its run (at most kMaxRun
-    // positions) is written four positions at a time, all four h loads
-    // issued before any is used
+    // (item row, 8-column chunk) pairs, kPairs per thread and round: the
+    // first four positions of every pair's run are loaded before any is
+    // written (most runs are that short); longer runs continue four
+    // positions at a time
     const int nchunk = min(kBN, g.dl - n0) / 8;
     const int rows = min(64, max(0, mcount - 64 * p));
-    for (int v = tid; v < rows * nchunk; v += 256) {
-      const int r = v / nchunk, ch = v - r * nchunk;
-      const int4 it = sItem[64 * p + r];
-      float acc8[8];
+    const int npairs = rows * nchunk;
+    for (int v0 = tid; v0 < npairs; v0 += kPairs * 256) {
+      int4 it[kPairs];
+      int so[kPairs];
+      int64_t o0[kPairs];
+      uint4 hv[kPairs][4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc8[e] = sO[r * kOLD + 8 * ch + e];
-      const int64_t o0 = static_cast<int64_t>(it.y) * g.dl + n0 + 8 * ch;
-      for (int q0 = 0; q0 < it.z; q0 += 4) {
-        uint4 hv[4];
+      for (int j = 0; j < kPairs; ++j) {
+        const int v = v0 + j * 256;
+        const int vv = v < npairs ? v : v0;
+        const int r = vv / nchunk, ch = vv - r * nchunk;
+        it[j] = sItem[64 * p + r];
+        if (v >= npairs) it[j].z = 0;
+        so[j] = r * kOLD + 8 * ch;
+        o0[j] = static_cast<int64_t>(it[j].y) * g.dl + n0 + 8 * ch;
+        const int last = max(it[j].z, 1) - 1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int q = min(q0 + e, it.z - 1);  // past the run: reload its last position
-          hv[e] = *reinterpret_cast<const uint4*>(h + o0 + static_cast<int64_t>(q) * g.dl);
-        }
+        for (int e = 0; e < 4; ++e)
+          hv[j][e] = *reinterpret_cast<const uint4*>(h + o0[j] + static_cast<int64_t>(min(e, last)) * g.dl);
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (q0 + e >= it.z) break;
-          const uint32_t wv[4] = {hv[e].x, hv[e].y, hv[e].z, hv[e].w};
-          float sv[8];
+      for (int j = 0; j < kPairs; ++j) {
+        float acc8[8];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            sv[2 * c] = acc8[2 * c] + bf16_to_f32(static_cast<uint16_t>(wv[c] & 0xFFFFu));
-            sv[2 * c + 1] = acc8[2 * c + 1] + bf16_to_f32(static_cast<uint16_t>(wv[c] >> 16));
+        for (int e = 0; e < 8; ++e) acc8[e] = sO[so[j] + e];
+        for (int q0 = 0; q0 < it[j].z; q0 += 4) {
+          if (q0 > 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int q = min(q0 + e, it[j].z - 1);  // past the run: reload its last position
+              hv[j][e] = *reinterpret_cast<const uint4*>(h + o0[j] + static_cast<int64_t>(q) * g.dl);
+            }
           }
-          Vec<BLLM_BF16>::store(out, o0 + static_cast<int64_t>(q0 + e) * g.dl, sv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (q0 + e >= it[j].z) break;
+            const uint32_t wv[4] = {hv[j][e].x, hv[j][e].y, hv[j][e].z, hv[j][e].w};
+            float sv[8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              sv[2 * c] = acc8[2 * c] + bf16_to_f32(static_cast<uint16_t>(wv[c] & 0xFFFFu));
+              sv[2 * c + 1] = acc8[2 * c + 1] + bf16_to_f32(static_cast<uint16_t>(wv[c] >> 16));
+            }
+            Vec<BLLM_BF16>::store(out, o0[j] + static_cast<int64_t>(q0 + e) * g.dl, sv);
+          }
         }
       }
     }
@@ -338,7 +380,7 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
 }
 
 struct UpWs {
-  int32_t *counts, *base, *bin_off, *bin_cnt, *tile_off;
+  int32_t *counts, *bin_off, *bin_cnt, *tile_off;
   int4* items;
 };
 
@@ -353,7 +395,6 @@ UpWs up_carve(void* ws, const UpGeom& g) {
   UpWs u;
   const size_t cb = align_up(static_cast<size_t>(g.nblk) * g.nbins * 4, 256);
   u.counts = reinterpret_cast<int32_t*>(p); p += cb;
-  u.base = reinterpret_cast<int32_t*>(p); p += cb;
   u.bin_off = reinterpret_cast<int32_t*>(p); p += 256;
   u.bin_cnt = reinterpret_cast<int32_t*>(p); p += 256;
   u.tile_off = reinterpret_cast<int32_t*>(p); p += 512;
@@ -363,7 +404,7 @@ UpWs up_carve(void* ws, const UpGeom& g) {
 
 size_t up_ws_bytes(const UpGeom& g) {
   const size_t cb = align_up(static_cast<size_t>(g.nblk) * g.nbins * 4, 256);
-  return 2 * cb + 1024 + align_up(up_max_items(g) * 16, 256) + 256;
+  return cb + 1024 + align_up(up_max_items(g) * 16, 256) + 256;
 }
 
 }  // namespace
@@ -397,10 +438,15 @@ extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* 
   if (!ws || ws_bytes < up_ws_bytes(g) || !aligned16(ws)) return BLLM_E_WS;
   hipStream_t st = static_cast<hipStream_t>(stream);
   UpWs u = up_carve(ws, g);
-  hipLaunchKernelGGL(up_count, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts);
-  hipLaunchKernelGGL(up_offsets, dim3(1), dim3(256), 0, st, u.counts, g, u.base, u.bin_off, u.bin_cnt,
-                     u.tile_off);
-  hipLaunchKernelGGL(up_items, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.base, u.items);
+  if (nbins == 16) {
+    hipLaunchKernelGGL(up_count<16>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts);
+    hipLaunchKernelGGL(up_items<16>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts,
+                       u.bin_off, u.bin_cnt, u.tile_off, u.items);
+  } else {
+    hipLaunchKernelGGL(up_count<0>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts);
+    hipLaunchKernelGGL(up_items<0>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts,
+                       u.bin_off, u.bin_cnt, u.tile_off, u.items);
+  }
   const int64_t max_tiles = ceil_div(static_cast<int64_t>(up_max_items(g)), kBM) + nbins;
   const int ncol = static_cast<int>(ceil_div(d_local, kBN));
   const int64_t nblocks = ceil_div(max_tiles, 8) * 8 * ncol;
