@@ -132,6 +132,18 @@ class Workload:
         self.g4 = (self.z4.float() @ w_g).to(bf).view(self.nseq, self.K, 1536)  # global stand-in
         self._upsample()
         torch.cuda.synchronize()
+        # ---------------- next rows, timed outside the step
+        # cosine-score chunker: stand-in routing projections of ByteFlow's h (untimed)
+        h4f = self.h4.view(-1, 512).float()
+        self.q4 = (h4f @ torch.from_numpy(bfl["wq"]).to(dev, torch.float32)).to(bf)
+        self.k4 = (h4f @ torch.from_numpy(bfl["wk"]).to(dev, torch.float32)).to(bf)
+        del h4f
+        self.p4 = torch.empty(N, device=dev)
+        self.b4 = torch.empty(N, dtype=torch.uint8, device=dev)
+        self.idx5 = torch.empty((self.nseq, self.K), dtype=torch.int32, device=dev)
+        self.mask5 = torch.empty((self.nseq, T), dtype=torch.uint8, device=dev)
+        self._cosine_chunker()
+        torch.cuda.synchronize()
         log(f"setup done: M1={self.M1} ({self.M1 / N:.3f} N), M2={self.M2} ({self.M2 / N:.3f} N)")
 
     # ------------------------------------------------------------ ops of one step
@@ -172,6 +184,20 @@ class Workload:
 
     def _upsample(self):
         self.B.upsample_bins(self.g4, self.W, self.idx4, self.h4, self.nbins, s_out=self.s4, ws=self.ws_up)
+
+    def _cosine_chunker(self):
+        self.B.route(self.q4, self.k4, self.off4, threshold=0.5, p_out=self.p4, b_out=self.b4)
+        self.B.topk_select(self.p4.view(self.nseq, -1), self.K, idx_out=self.idx5, mask_out=self.mask5,
+                           status=self.st)
+
+    def next_ops(self):
+        """Rows past the hot path (the survey's 'next' list), timed on their own."""
+        return [("cosine_chunker", self._cosine_chunker)]
+
+    def next_algorithmic(self):
+        N, nseq, K = self.N, self.nseq, self.K
+        e = 2
+        return {"cosine_chunker": dict(bytes=N * (2 * 512 * e + 4 + 1) + N * 4 + N + nseq * K * 4)}
 
     def ops(self):
         return [("route+compact stage1", self._stage1), ("route+compact stage2", self._stage2),
@@ -223,11 +249,11 @@ def coding_rate_traffic():
     return block["hbm_bytes_per_call"]
 
 
-def time_ops(wl, reps=5):
+def time_ops(wl, reps=5, ops=None):
     """Average duration of each op (HIP events on the stream the kernels run on)."""
     torch = wl.torch
     res = {}
-    for name, f in wl.ops():
+    for name, f in (wl.ops() if ops is None else ops):
         f()
         torch.cuda.synchronize()
         ev0 = torch.cuda.Event(enable_timing=True)
@@ -325,7 +351,7 @@ def main():
         return
     wl = Workload()
     if args.profile_op:
-        f = dict(wl.ops())[args.profile_op]
+        f = dict(wl.ops() + wl.next_ops())[args.profile_op]
         for _ in range(args.steps):
             f()
         torch.cuda.synchronize()
@@ -412,6 +438,17 @@ def main():
                        "hbm_GBps": round(hnet_bytes / (hnet_ms * 1e-3) / 1e9, 1),
                        "hbm_frac": round(hnet_bytes / (hnet_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    nxt = {}
+    nalg = wl.next_algorithmic()
+    for name, t in time_ops(wl, ops=wl.next_ops()).items():
+        a = nalg[name]
+        d = {"ms": round(t, 4)}
+        if "bytes" in a:
+            d["hbm_GBps"] = round(a["bytes"] / (t * 1e-3) / 1e9, 1)
+        if "flops" in a:
+            d["TFLOPs"] = round(a["flops"] / (t * 1e-3) / 1e12, 2)
+        nxt[name] = d
+    out["next_rows"] = nxt
     if not args.no_cpu_baseline:
         log("timing the oracle baseline on the host")
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -10,6 +10,6 @@ any code of the method.
 from .generators import (  # noqa: F401
     bf16_round, bf16_bits, from_bf16_bits, Ragged,
     gen_hnet_tiny, gen_coding_rate_tiny, gen_event_streams, gen_hnet_two_stage, gen_stage2_inputs, gen_stage2_backproj,
-    gen_coding_rate_fp32, gen_byteflow_layer, gen_global_standin, cluster_rows, event_bytes, SEED_HNET_TINY, SEED_EVENT_STREAMS, SEED_HNET_TWO_STAGE,
+    gen_coding_rate_fp32, gen_byteflow_layer, gen_global_standin, gen_cosine_qk, cluster_rows, event_bytes, SEED_HNET_TINY, SEED_EVENT_STREAMS, SEED_HNET_TWO_STAGE,
     SEED_CODING_RATE_FP32, SEED_BYTEFLOW_LAYER,
 )

@@ -214,7 +214,9 @@ def gen_event_streams(seed: int = SEED_EVENT_STREAMS, nseq: int = 16, d: int = 5
     wk = rng.standard_normal((d, d)) / np.sqrt(d)
     q = bf16_round(_matmul_rows(h, wq))
     k = bf16_round(_matmul_rows(h, wk))
-    return dict(bytes=xb, offsets=off, h=bf16_round(h), q=q, k=k, d=d, threshold=0.5, dtype="bf16")
+    # wq, wk rounded to bf16 for a projection computed on the device from the bf16 h
+    return dict(bytes=xb, offsets=off, h=bf16_round(h), q=q, k=k, d=d, threshold=0.5, dtype="bf16",
+                wq=bf16_round(wq), wk=bf16_round(wk))
 
 
 def gen_hnet_two_stage(seed: int = SEED_HNET_TWO_STAGE, nseq: int = 32, d_local: int = 512, d_mid: int = 768,
@@ -265,8 +267,21 @@ def gen_byteflow_layer(seed: int = SEED_BYTEFLOW_LAYER, nseq: int = 32, T: int =
     h = bf16_round(cluster_rows(rng, nseq, T, d_local))
     w_g = rng.standard_normal((d_local, d_global)) / np.sqrt(d_local)
     w_bin = bf16_round(rng.standard_normal((nbins, d_global, d_local)) / np.sqrt(d_global))
-    return dict(h=h, w_g=w_g, w_bin=w_bin, nseq=nseq, T=T, d_local=d_local, d_global=d_global,
-                K=K, nbins=nbins, eps2=eps2, dtype="bf16")
+    # routing projections for the cosine-score variant of the chunker (drawn
+    # after everything above, so those arrays are unchanged)
+    wq = bf16_round(rng.standard_normal((d_local, d_local)) / np.sqrt(d_local))
+    wk = bf16_round(rng.standard_normal((d_local, d_local)) / np.sqrt(d_local))
+    return dict(h=h, w_g=w_g, w_bin=w_bin, wq=wq, wk=wk, nseq=nseq, T=T, d_local=d_local,
+                d_global=d_global, K=K, nbins=nbins, eps2=eps2, dtype="bf16")
+
+
+def gen_cosine_qk(h, cfg, rows=None):
+    """q = h Wq, k = h Wk for the cosine-score chunker (fp64 products of the
+    bf16 inputs, rounded to bf16); ``rows`` limits it to h[:rows]."""
+    hh = np.asarray(h).reshape(-1, h.shape[-1])
+    if rows is not None:
+        hh = hh[:rows]
+    return bf16_round(_matmul_rows(hh, cfg["wq"])), bf16_round(_matmul_rows(hh, cfg["wk"]))
 
 
 def gen_global_standin(z, cfg):

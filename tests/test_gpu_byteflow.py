@@ -3,7 +3,8 @@ import numpy as np
 import pytest
 
 import oracle
-from synthdata import bf16_round, cluster_rows, gen_coding_rate_tiny, gen_coding_rate_fp32, gen_byteflow_layer, gen_global_standin
+from synthdata import (bf16_round, cluster_rows, gen_coding_rate_tiny, gen_coding_rate_fp32, gen_byteflow_layer,
+                       gen_global_standin, gen_cosine_qk)
 from tests.helpers import oracle_dr_parallel, row_rel_err, say, to_dev, to_np, topk_band_compare
 
 pytestmark = pytest.mark.gpu
@@ -214,3 +215,35 @@ def test_byteflow_chain_full_size_bf16_32x8192(ops):
         ref = oracle.upsample_bins(g[q:q + 1], c["w_bin"], idx_np[q:q + 1], c["h"][q:q + 1], c["nbins"])
         assert row_rel_err(s_np[q:q + 1], ref) < 2e-2
     say("ByteFlow chain ok")
+
+
+# ------------------------------------------------------------------ cosine-score chunker
+
+def test_cosine_score_chunker_byteflow_shape(ops):
+    """The cosine-similarity chunker variant: the H-Net routing score p_t of
+    the encoder output, q = h Wq and k = h Wk, takes Delta R's place in the
+    BOS + Top-(K-1) selection.  Four full sequences of the ByteFlow layer
+    input (8192 x 512, K 2048)."""
+    torch = _torch()
+    bf = torch.bfloat16
+    c = gen_byteflow_layer()
+    nseq, T, K = 4, c["T"], c["K"]
+    h = c["h"][:nseq]
+    q, k = gen_cosine_qk(h, c)
+    off = np.arange(nseq + 1, dtype=np.int64) * T
+    p, _, _ = ops.route(to_dev(q, bf), to_dev(k, bf), to_dev(off), threshold=0.5)
+    p_g = to_np(p).reshape(nseq, T)
+    p_o = oracle.route(q, k, off).reshape(nseq, T)
+    assert np.max(np.abs(p_g - p_o)) < 5e-6
+    assert np.all(p_g[:, 0] == 1.0)
+    idx, mask, st = ops.topk_select(p.reshape(nseq, T), K)
+    idx_g = to_np(idx)
+    # bit-exact on the device scores ...
+    assert np.array_equal(idx_g, oracle.topk_select(p_g, K))
+    assert np.array_equal(to_np(mask), oracle.topk_mask(idx_g, T))
+    # ... and the oracle's own selection outside the tie band
+    sel_o = oracle.topk_select(p_o.astype(np.float64), K)
+    for s_ in range(nseq):
+        diff, band = topk_band_compare(idx_g[s_], sel_o[s_], p_o[s_], K)
+        assert len(diff) == 0, (s_, diff[:10], band)
+    say("cosine chunker: selections agree")
