@@ -32,7 +32,7 @@ Every function here is pinned by tests against something other than itself
 (closed forms, brute force on tiny inputs, library routines, invariants);
 none is "parity unpinned".
 """
-from .hnet import route, boundary_mask, stage_quantile, compact, dechunk_ema  # noqa: F401
+from .hnet import route, boundary_mask, stage_quantile, compact, dechunk_ema, dechunk_ema_backward  # noqa: F401
 from .byteflow import (  # noqa: F401
     alpha_of, coding_rate, coding_rate_at, topk_select, topk_mask, gather, chunk_bins, upsample_bins,
 )

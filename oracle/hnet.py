@@ -86,3 +86,46 @@ def dechunk_ema(z, P, idx, chunk_offsets, offsets) -> np.ndarray:
             t_end = int(idx[c + 1]) if c + 1 < c1 else int(offsets[s + 1])
             out[int(idx[c]):t_end] = zbar
     return out
+
+
+def dechunk_ema_backward(z, P, idx, chunk_offsets, offsets, dout):
+    """Gradients of L = sum(dout * dechunk_ema(z, P, ...)) with respect to z
+    and P, float64 ([M x d] and [M]).
+
+    [BG] 2.3 smooths the chunk sequence with the EMA so that the boundary
+    choice stays differentiable end to end; this is the reverse-mode
+    derivative of that recurrence, taken chunk by chunk per sequence:
+        gbar_c = sum of dout over the positions chunk c covers
+        lam_c  = gbar_c + (1 - P_{c+1}) lam_{c+1}   (lam_c = gbar_c for the
+                 sequence's last chunk: the next sequence restarts from 0)
+        dz_c   = P_c lam_c
+        dP_c   = lam_c . (z_c - zbar_{c-1})          (zbar before the first chunk = 0)
+    lam_c is dL/dzbar_c; positions before a sequence's first chunk do not
+    depend on z or P.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    P = np.asarray(P, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    M, d = z.shape[0], z.shape[1]
+    dz = np.zeros((M, d), dtype=np.float64)
+    dP = np.zeros(M, dtype=np.float64)
+    for s in range(len(offsets) - 1):
+        c0, c1 = int(chunk_offsets[s]), int(chunk_offsets[s + 1])
+        if c0 == c1:
+            continue
+        # forward values zbar_{c-1} seen by each chunk
+        zprev = np.zeros((c1 - c0, d))
+        zbar = np.zeros(d)
+        for c in range(c0, c1):
+            zprev[c - c0] = zbar
+            zbar = P[c] * z[c] + (1.0 - P[c]) * zbar
+        lam_next = np.zeros(d)
+        for c in range(c1 - 1, c0 - 1, -1):
+            t_end = int(idx[c + 1]) if c + 1 < c1 else int(offsets[s + 1])
+            gbar = dout[int(idx[c]):t_end].sum(axis=0)
+            lam = gbar + ((1.0 - P[c + 1]) * lam_next if c + 1 < c1 else 0.0)
+            dz[c] = P[c] * lam
+            dP[c] = float(np.dot(lam, z[c] - zprev[c - c0]))
+            lam_next = lam
+    return dz, dP

@@ -165,3 +165,71 @@ def test_ema_chunk_form_equals_per_byte_form():
             zb = Pt * rows[t] + (1 - Pt) * zb if b[t] else zb
             ref[t] = zb
     np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- EMA backward
+
+def _loss(z, P, idx, coff, offsets, dout):
+    return float(np.sum(dout * oracle.dechunk_ema(z, P, idx, coff, offsets)))
+
+
+def test_ema_backward_matches_central_differences():
+    """dz and dP against central differences of the (pinned) forward, on a
+    ragged batch with an empty sequence, a sequence whose first byte is not a
+    boundary and P below 1 at sequence starts; the loss is linear in z, so its
+    z-differences are exact up to rounding, and the quadratic terms in P
+    cancel in central differences."""
+    rng = np.random.default_rng(21)
+    offsets = np.array([0, 9, 9, 23, 29], np.int64)
+    N = int(offsets[-1])
+    b = rng.random(N) < 0.4
+    b[[0, 9, 23]] = True
+    b[23:26] = False  # the last sequence starts without a boundary
+    b[26] = True
+    p = rng.random(N)
+    idx, coff, z, P = oracle.compact(b, p, rng.standard_normal((N, 3)), offsets)
+    dout = rng.standard_normal((N, 3))
+    dz, dP = oracle.dechunk_ema_backward(z, P, idx, coff, offsets, dout)
+    eps = 1e-6
+    for c in range(len(P)):
+        for f in range(3):
+            zp, zm = z.copy(), z.copy()
+            zp[c, f] += eps
+            zm[c, f] -= eps
+            fd = (_loss(zp, P, idx, coff, offsets, dout) - _loss(zm, P, idx, coff, offsets, dout)) / (2 * eps)
+            assert abs(fd - dz[c, f]) <= 1e-7 * max(1.0, abs(fd))
+        Pp, Pm = P.astype(np.float64).copy(), P.astype(np.float64).copy()
+        Pp[c] += eps
+        Pm[c] -= eps
+        fd = (_loss(z, Pp, idx, coff, offsets, dout) - _loss(z, Pm, idx, coff, offsets, dout)) / (2 * eps)
+        assert abs(fd - dP[c]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_ema_backward_P_one_closed_form():
+    """With every P = 1 the output is each chunk's own z: dz_c is the sum of
+    dout over the chunk's positions and dP_c = that sum . (z_c - z_{c-1}),
+    with z_{c-1} = 0 at a sequence's first chunk."""
+    rng = np.random.default_rng(22)
+    offsets, b, p, rows, idx, coff, z, P = _ragged_chunks(rng, [12, 7, 30], 4)
+    P1 = np.ones_like(P)
+    dout = rng.standard_normal((int(offsets[-1]), 4))
+    dz, dP = oracle.dechunk_ema_backward(z, P1, idx, coff, offsets, dout)
+    for s in range(3):
+        for c in range(coff[s], coff[s + 1]):
+            t_end = idx[c + 1] if c + 1 < coff[s + 1] else offsets[s + 1]
+            g = dout[idx[c]:t_end].sum(axis=0)
+            prev = z[c - 1] if c > coff[s] else np.zeros(4)
+            np.testing.assert_allclose(dz[c], g, rtol=1e-13, atol=1e-13)
+            assert abs(dP[c] - g @ (z[c] - prev)) <= 1e-12 * max(1.0, abs(dP[c]))
+
+
+def test_ema_backward_linear_in_dout():
+    rng = np.random.default_rng(23)
+    offsets, b, p, rows, idx, coff, z, P = _ragged_chunks(rng, [20, 11], 5, first_p_one=False)
+    N = int(offsets[-1])
+    g1, g2 = rng.standard_normal((N, 5)), rng.standard_normal((N, 5))
+    a1 = oracle.dechunk_ema_backward(z, P, idx, coff, offsets, g1)
+    a2 = oracle.dechunk_ema_backward(z, P, idx, coff, offsets, g2)
+    a3 = oracle.dechunk_ema_backward(z, P, idx, coff, offsets, 2.0 * g1 - 3.0 * g2)
+    np.testing.assert_allclose(a3[0], 2.0 * a1[0] - 3.0 * a2[0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a3[1], 2.0 * a1[1] - 3.0 * a2[1], rtol=1e-12, atol=1e-12)
