@@ -143,6 +143,14 @@ class Workload:
         self.idx5 = torch.empty((self.nseq, self.K), dtype=torch.int32, device=dev)
         self.mask5 = torch.empty((self.nseq, T), dtype=torch.uint8, device=dev)
         self._cosine_chunker()
+        # EMA dechunk backward of stage 1: a seeded stand-in output gradient (untimed)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(20260005)
+        self.dout1 = torch.randn((N, 512), generator=gen, device=dev).to(bf)
+        self.dz1 = torch.empty((self.M1, 512), dtype=bf, device=dev)
+        self.dP1 = torch.empty(self.M1, device=dev)
+        self.ws_dbwd = torch.empty(B.dechunk_ema_backward_workspace(512, self.M1), dtype=torch.uint8, device=dev)
+        self._dechunk1_backward()
         torch.cuda.synchronize()
         log(f"setup done: M1={self.M1} ({self.M1 / N:.3f} N), M2={self.M2} ({self.M2 / N:.3f} N)")
 
@@ -190,14 +198,20 @@ class Workload:
         self.B.topk_select(self.p4.view(self.nseq, -1), self.K, idx_out=self.idx5, mask_out=self.mask5,
                            status=self.st)
 
+    def _dechunk1_backward(self):
+        self.B.dechunk_ema_backward(self.y1, self.P1, self.dout1, self.idx1, self.coff1, self.off,
+                                    dz_out=self.dz1, dP_out=self.dP1, ws=self.ws_dbwd, max_chunks=self.M1)
+
     def next_ops(self):
         """Rows past the hot path (the survey's 'next' list), timed on their own."""
-        return [("cosine_chunker", self._cosine_chunker)]
+        return [("cosine_chunker", self._cosine_chunker), ("dechunk_backward stage1", self._dechunk1_backward)]
 
     def next_algorithmic(self):
-        N, nseq, K = self.N, self.nseq, self.K
+        N, M1, nseq, K = self.N, self.M1, self.nseq, self.K
         e = 2
-        return {"cosine_chunker": dict(bytes=N * (2 * 512 * e + 4 + 1) + N * 4 + N + nseq * K * 4)}
+        return {"cosine_chunker": dict(bytes=N * (2 * 512 * e + 4 + 1) + N * 4 + N + nseq * K * 4),
+                # dout read once, z and P read, dz and dP written
+                "dechunk_backward stage1": dict(bytes=N * 512 * e + M1 * (2 * 512 * e + 4 + 4 + 4))}
 
     def ops(self):
         return [("route+compact stage1", self._stage1), ("route+compact stage2", self._stage2),

@@ -29,6 +29,9 @@ _SIGS = {
     "bllm_dechunk_workspace": (C.c_size_t, [_i64]),
     "bllm_dechunk_ema": (C.c_int, [_p, _p, C.c_int, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _p,
                                    C.c_size_t, _p]),
+    "bllm_dechunk_ema_backward_workspace": (C.c_size_t, [_i64, _i64]),
+    "bllm_dechunk_ema_backward": (C.c_int, [_p, _p, _p, C.c_int, _i64, _p, _p, _p, _i64, _i64, _i64,
+                                            _p, _p, _p, C.c_size_t, _p]),
     "bllm_coding_rate_workspace": (C.c_size_t, [_i64, _i64, _i64]),
     "bllm_coding_rate": (C.c_int, [_p, C.c_int, _i64, _i64, _i64, C.c_double, _p, _p, _p,
                                    C.c_size_t, _p]),

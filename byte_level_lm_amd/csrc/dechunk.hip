@@ -20,6 +20,8 @@
 // waits on the z rows, which it loads kUnroll chunks at a time.
 // HBM-bound: z is read twice, the [total x d] output is written once
 // (nontemporal); the tile aggregates and carries add 3 * kNT * d * 4 bytes.
+#include <algorithm>
+
 #include "common.h"
 
 namespace bllm {
@@ -28,6 +30,7 @@ namespace {
 constexpr int kNT = 2048;      // tiles of consecutive chunks
 constexpr int kLaneBytes = 8;  // bytes of a row per lane
 constexpr int kUnroll = 4;     // z rows in flight per wave
+constexpr int kRowBatch = 8;   // output-gradient rows in flight per wave (backward)
 constexpr int kCarryCols = 8;                   // float4 columns per carry block
 constexpr int kCarryThreads = 1024;
 constexpr int kCarryGroups = kCarryThreads / kCarryCols;
@@ -87,10 +90,11 @@ __device__ inline Tile tile_range(int64_t M, int64_t i) {
 }
 
 // Metadata of chunk c = cb + lane (cb .. ce-1, ce - cb <= 64), one per lane:
-// the multiplier a_c, P_c, the first and one-past-last row of the chunk.
+// the multiplier a_c, P_c, whether the chunk starts its sequence (1 or 0),
+// the first and one-past-last row of the chunk.
 // The sequences overlapping the range are walked with wave-uniform loads.
 struct ChunkMeta {
-  float a, P;
+  float a, P, start;
   int64_t t0, t1;
 };
 
@@ -116,6 +120,7 @@ __device__ inline ChunkMeta chunk_meta(const float* __restrict__ P, const int32_
     ++s;
   }
   m.a = start ? 0.f : 1.f - m.P;
+  m.start = start ? 1.f : 0.f;
   m.t1 = t1;
   return m;
 }
@@ -367,6 +372,327 @@ void launch_dechunk(const void* z, const float* P, int d, const int32_t* idx,
                      chunk_offsets, offsets, nseq, carry, out);
 }
 
+// ------------------------------------------------------------------ backward
+// Gradients of L = sum(dout * out) for the EMA dechunk (ByteGen report,
+// section 2.3: the EMA keeps the chunking differentiable end to end).  Per
+// chunk c: gbar_c = sum of dout over the chunk's rows; the adjoint
+// lam_c = dL/dzbar_c runs backwards, lam_c = gbar_c + a_{c+1} lam_{c+1}
+// (a_{c+1} = 0 when c + 1 starts a sequence or c is the last chunk);
+// dz_c = P_c lam_c; dP_c = lam_c . (z_c - zbar_{c-1}) with zbar_{c-1} = 0 at a
+// sequence's first chunk.  Same tiles and slices as the forward:
+//   1. per tile: the forward aggregate (A, U_f) over z, the chunk sums gbar_c
+//      (stored, fp32) and the reverse aggregate U_r = a_{c0} sum_c pi_c gbar_c
+//      with pi_c = prod_{c0 < j <= c} a_j, accumulated in ascending order; the
+//      reverse aggregates are stored in reversed tile order
+//   2. the forward carry scan, and the same scan over the reversed tiles,
+//      which gives mu_i = a_{c1} lam_{c1}, what flows into tile i from the right
+//   3. per tile, descending: lam_c from mu_i, written over gbar_c
+//   4. per tile, ascending: zbar from the forward carry; dz_c = P_c lam_c and
+//      one partial dot product per feature slice
+//   5. dP_c = the slice partials summed in slice order
+// HBM: dout read once; z read twice; gbar/lam (fp32, M x d) written twice and
+// read twice; dz written once.
+
+template <int DT>
+__global__ __launch_bounds__(256) void emab_aggregate(const void* __restrict__ z,
+                                                      const float* __restrict__ P,
+                                                      const void* __restrict__ dout, int d,
+                                                      const int32_t* __restrict__ idx,
+                                                      const int64_t* __restrict__ chunk_offsets,
+                                                      const int64_t* __restrict__ offsets, int nseq,
+                                                      float* __restrict__ Aagg, float* __restrict__ Uf,
+                                                      float* __restrict__ Arev, float* __restrict__ Urev,
+                                                      float* __restrict__ gbar) {
+  using V = Lane<DT>;
+  const int lane = threadIdx.x & 63;
+  const int nvec = d / V::N;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int v = blockIdx.y * 64 + lane;
+  const bool active = v < nvec;
+  const int vc = active ? v : nvec - 1;
+  const int64_t col = static_cast<int64_t>(vc) * V::N;
+  const int64_t M = chunk_offsets[nseq];
+  const Tile tr = tile_range(M, i);
+  float xf[V::N], ur[V::N], gs[V::N];
+#pragma unroll
+  for (int e = 0; e < V::N; ++e) xf[e] = ur[e] = gs[e] = 0.f;
+  float A = 1.f, pi = 1.f, a0 = 1.f;
+  for (int64_t cb = tr.c0; cb < tr.c1; cb += 64) {
+    const int64_t ce = cb + 64 < tr.c1 ? cb + 64 : tr.c1;
+    const ChunkMeta m = chunk_meta(P, idx, chunk_offsets, offsets, nseq, M, cb, ce, lane);
+    const int n = static_cast<int>(ce - cb);
+    if (cb > tr.c0) pi *= lane_f(m.a, 0);  // the group's first chunk continues the product
+    // forward aggregate over z, kUnroll chunks in flight
+    for (int j = 0; j < n; j += kUnroll) {
+      float zz[kUnroll][V::N];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) V::load(z, (cb + (j + u < n ? j + u : n - 1)) * d + col, zz[u]);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (j + u < n) {
+          const float a = lane_f(m.a, j + u);
+          const float Pc = lane_f(m.P, j + u);
+#pragma unroll
+          for (int e = 0; e < V::N; ++e) xf[e] = fmaf(a, xf[e], Pc * zz[u][e]);
+          A *= a;
+        }
+      }
+    }
+    // chunk sums of dout over the group's rows, kRowBatch rows in flight; a
+    // chunk is closed when the rows pass its end: gbar stored, reverse
+    // aggregate ur += pi_c gbar_c, then pi picks up the next chunk's a.  Rows
+    // between a sequence's end and the next chunk (a sequence that does not
+    // start with a boundary) belong to no chunk and are skipped.
+    const int64_t r0 = lane_i64(m.t0, 0), r1 = lane_i64(m.t1, n - 1);
+    int j = 0;
+    int64_t tbeg = r0, tend = lane_i64(m.t1, 0);
+    for (int64_t t = r0; t < r1; t += kRowBatch) {
+      float g8[kRowBatch][V::N];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) V::load(dout, (t + u < r1 ? t + u : r1 - 1) * d + col, g8[u]);
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        if (t + u < r1) {
+          if (t + u >= tend) {  // row t + u opens chunk j + 1
+            const int64_t c = cb + j;
+            if (active) {
+              float* gp = gbar + c * d + col;
+#pragma unroll
+              for (int e = 0; e < V::N; ++e) gp[e] = gs[e];
+            }
+            if (c == tr.c0) a0 = lane_f(m.a, j);
+#pragma unroll
+            for (int e = 0; e < V::N; ++e) {
+              ur[e] = fmaf(pi, gs[e], ur[e]);
+              gs[e] = 0.f;
+            }
+            ++j;
+            pi *= lane_f(m.a, j);
+            tbeg = lane_i64(m.t0, j);
+            tend = lane_i64(m.t1, j);
+          }
+          if (t + u >= tbeg) {
+#pragma unroll
+            for (int e = 0; e < V::N; ++e) gs[e] += g8[u][e];
+          }
+        }
+      }
+    }
+    {  // close the group's last chunk
+      const int64_t c = cb + j;
+      if (active) {
+        float* gp = gbar + c * d + col;
+#pragma unroll
+        for (int e = 0; e < V::N; ++e) gp[e] = gs[e];
+      }
+      if (c == tr.c0) a0 = lane_f(m.a, j);
+#pragma unroll
+      for (int e = 0; e < V::N; ++e) {
+        ur[e] = fmaf(pi, gs[e], ur[e]);
+        gs[e] = 0.f;
+      }
+    }
+  }
+  const int64_t ir = kNT - 1 - i;
+  if (active) {
+    float* uf = Uf + i * d + col;
+    float* urp = Urev + ir * d + col;
+#pragma unroll
+    for (int e = 0; e < V::N; ++e) {
+      uf[e] = xf[e];
+      urp[e] = a0 * ur[e];
+    }
+  }
+  if (blockIdx.y == 0 && lane == 0) {
+    Aagg[i] = A;
+    Arev[ir] = A;
+  }
+}
+
+// 3. lam_c over the tile, last chunk first, written over gbar_c
+template <int DT>
+__global__ __launch_bounds__(256) void emab_reverse(const float* __restrict__ P, int d,
+                                                    const int32_t* __restrict__ idx,
+                                                    const int64_t* __restrict__ chunk_offsets,
+                                                    const int64_t* __restrict__ offsets, int nseq,
+                                                    const float* __restrict__ carry_rev,
+                                                    float* __restrict__ lam) {
+  using V = Lane<DT>;
+  const int lane = threadIdx.x & 63;
+  const int nvec = d / V::N;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int v = blockIdx.y * 64 + lane;
+  const bool active = v < nvec;
+  const int vc = active ? v : nvec - 1;
+  const int64_t col = static_cast<int64_t>(vc) * V::N;
+  const int64_t M = chunk_offsets[nseq];
+  const Tile tr = tile_range(M, i);
+  if (tr.c0 >= tr.c1) return;
+  // mu_i: what flows into the tile's last chunk from the right
+  float mu[V::N];
+  {
+    const float* cp = carry_rev + (kNT - 1 - i) * d + col;
+#pragma unroll
+    for (int e = 0; e < V::N; ++e) mu[e] = cp[e];
+  }
+  const int64_t ngrp = (tr.c1 - tr.c0 + 63) / 64;
+  for (int64_t gi = ngrp - 1; gi >= 0; --gi) {
+    const int64_t cb = tr.c0 + gi * 64;
+    const int64_t ce = cb + 64 < tr.c1 ? cb + 64 : tr.c1;
+    const ChunkMeta m = chunk_meta(P, idx, chunk_offsets, offsets, nseq, M, cb, ce, lane);
+    const int n = static_cast<int>(ce - cb);
+    for (int j = n - 1; j >= 0; j -= 4) {
+      float gv[4][V::N];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int jj = j - u >= 0 ? j - u : 0;
+        const float* gp = lam + (cb + jj) * d + col;
+#pragma unroll
+        for (int e = 0; e < V::N; ++e) gv[u][e] = gp[e];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (j - u >= 0) {
+          float* gp = lam + (cb + j - u) * d + col;
+#pragma unroll
+          for (int e = 0; e < V::N; ++e) mu[e] += gv[u][e];  // mu now holds lam_c
+          if (active) {
+#pragma unroll
+            for (int e = 0; e < V::N; ++e) gp[e] = mu[e];
+          }
+          const float a = lane_f(m.a, j - u);  // a_c: carries lam_c to chunk c - 1
+#pragma unroll
+          for (int e = 0; e < V::N; ++e) mu[e] *= a;
+        }
+      }
+    }
+  }
+}
+
+// 4. zbar from the forward carry, dz_c = P_c lam_c, and the slice's partial dP_c
+template <int DT>
+__global__ __launch_bounds__(256) void emab_forward(const void* __restrict__ z,
+                                                    const float* __restrict__ P, int d,
+                                                    const int32_t* __restrict__ idx,
+                                                    const int64_t* __restrict__ chunk_offsets,
+                                                    const int64_t* __restrict__ offsets, int nseq,
+                                                    const float* __restrict__ carry,
+                                                    const float* __restrict__ lam,
+                                                    void* __restrict__ dz, float* __restrict__ dPpart,
+                                                    int64_t mcap) {
+  using V = Lane<DT>;
+  const int lane = threadIdx.x & 63;
+  const int nvec = d / V::N;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int v = blockIdx.y * 64 + lane;
+  const bool active = v < nvec;
+  const int vc = active ? v : nvec - 1;
+  const int64_t col = static_cast<int64_t>(vc) * V::N;
+  const int64_t M = chunk_offsets[nseq];
+  const Tile tr = tile_range(M, i);
+  if (tr.c0 >= tr.c1) return;
+  float x[V::N];
+  {
+    const float* cp = carry + i * d + col;
+#pragma unroll
+    for (int e = 0; e < V::N; ++e) x[e] = cp[e];
+  }
+  float* dpp = dPpart + static_cast<int64_t>(blockIdx.y) * mcap;
+  for (int64_t cb = tr.c0; cb < tr.c1; cb += 64) {
+    const int64_t ce = cb + 64 < tr.c1 ? cb + 64 : tr.c1;
+    const ChunkMeta m = chunk_meta(P, idx, chunk_offsets, offsets, nseq, M, cb, ce, lane);
+    const int n = static_cast<int>(ce - cb);
+    for (int j = 0; j < n; j += kUnroll) {
+      float zz[kUnroll][V::N], lv[kUnroll][V::N];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t c = cb + (j + u < n ? j + u : n - 1);
+        V::load(z, c * d + col, zz[u]);
+        const float* lp = lam + c * d + col;
+#pragma unroll
+        for (int e = 0; e < V::N; ++e) lv[u][e] = lp[e];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (j + u < n) {
+          const int64_t c = cb + j + u;
+          const float a = lane_f(m.a, j + u);
+          const float Pc = lane_f(m.P, j + u);
+          // zbar_{c-1} counts as 0 at a sequence's first chunk
+          const float keep = 1.f - lane_f(m.start, j + u);
+          float part = 0.f, g[V::N];
+#pragma unroll
+          for (int e = 0; e < V::N; ++e) {
+            part = fmaf(lv[u][e], zz[u][e] - keep * x[e], part);
+            g[e] = Pc * lv[u][e];
+            x[e] = fmaf(a, x[e], Pc * zz[u][e]);
+          }
+          if (active) V::store_nt(dz, c * d + col, g);
+          part = group_sum<64>(active ? part : 0.f);
+          if (lane == 0) dpp[c] = part;
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void emab_dp_reduce(const float* __restrict__ dPpart,
+                                                      const int64_t* __restrict__ chunk_offsets, int nseq,
+                                                      int nslices, int64_t mcap, float* __restrict__ dP) {
+  const int64_t M = chunk_offsets[nseq];
+  for (int64_t c = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; c < M;
+       c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float s = 0.f;
+    for (int k = 0; k < nslices; ++k) s += dPpart[k * mcap + c];
+    dP[c] = s;
+  }
+}
+
+struct BwdWs {
+  float *Aagg, *Uf, *Arev, *Urev, *carry, *carry_rev, *lam, *dPpart;
+};
+
+__host__ inline size_t bwd_ws_bytes(int64_t d, int nslices, int64_t mcap) {
+  return (2 * static_cast<size_t>(kNT) + 4 * static_cast<size_t>(kNT) * d +
+          static_cast<size_t>(mcap) * d + static_cast<size_t>(nslices) * mcap) * 4 + 512;
+}
+
+__host__ inline BwdWs bwd_ws(void* ws, int64_t d, int64_t mcap) {
+  float* p = static_cast<float*>(ws);
+  BwdWs b;
+  b.Aagg = p; p += kNT;
+  b.Arev = p; p += kNT;
+  b.Uf = p; p += static_cast<size_t>(kNT) * d;
+  b.Urev = p; p += static_cast<size_t>(kNT) * d;
+  b.carry = p; p += static_cast<size_t>(kNT) * d;
+  b.carry_rev = p; p += static_cast<size_t>(kNT) * d;
+  b.lam = p; p += static_cast<size_t>(mcap) * d;
+  b.dPpart = p;
+  return b;
+}
+
+template <int DT>
+void launch_dechunk_bwd(const void* z, const float* P, const void* dout, int d, const int32_t* idx,
+                        const int64_t* chunk_offsets, const int64_t* offsets, int nseq, int64_t mcap,
+                        void* dz, float* dP, void* ws, hipStream_t st) {
+  constexpr int N = Lane<DT>::N;
+  const int nslices = (d / N + 63) / 64;
+  const BwdWs w = bwd_ws(ws, d, mcap);
+  const dim3 grid(kNT / 4, nslices);
+  const dim3 cgrid((d + kCarryCols * 4 - 1) / (kCarryCols * 4));
+  hipLaunchKernelGGL(emab_aggregate<DT>, grid, dim3(256), 0, st, z, P, dout, d, idx, chunk_offsets, offsets,
+                     nseq, w.Aagg, w.Uf, w.Arev, w.Urev, w.lam);
+  hipLaunchKernelGGL(ema_tile_carry, cgrid, dim3(kCarryThreads), 0, st, w.Aagg, w.Uf, d, w.carry);
+  hipLaunchKernelGGL(ema_tile_carry, cgrid, dim3(kCarryThreads), 0, st, w.Arev, w.Urev, d, w.carry_rev);
+  hipLaunchKernelGGL(emab_reverse<DT>, grid, dim3(256), 0, st, P, d, idx, chunk_offsets, offsets, nseq,
+                     w.carry_rev, w.lam);
+  hipLaunchKernelGGL(emab_forward<DT>, grid, dim3(256), 0, st, z, P, d, idx, chunk_offsets, offsets, nseq,
+                     w.carry, w.lam, dz, w.dPpart, mcap);
+  const unsigned rblocks = static_cast<unsigned>(std::min<int64_t>(ceil_div(mcap, 256), 1024));
+  hipLaunchKernelGGL(emab_dp_reduce, dim3(rblocks > 0 ? rblocks : 1), dim3(256), 0, st, w.dPpart, chunk_offsets,
+                     nseq, nslices, mcap, dP);
+}
+
 }  // namespace
 }  // namespace bllm
 
@@ -396,5 +722,36 @@ extern "C" int bllm_dechunk_ema(const void* z, const float* P, int dtype, int64_
   else
     launch_dechunk<BLLM_BF16>(z, P, static_cast<int>(d), idx, chunk_offsets, offsets,
                               static_cast<int>(nseq), out, static_cast<float*>(ws), st);
+  return launch_status();
+}
+
+extern "C" size_t bllm_dechunk_ema_backward_workspace(int64_t d, int64_t max_chunks) {
+  if (d < 1 || max_chunks < 0) return 0;
+  // the larger of the two dtypes' slice counts (fp32 lanes hold fewer features)
+  const int nslices = static_cast<int>((d * 4 / kLaneBytes + kWave - 1) / kWave);
+  return bwd_ws_bytes(d, nslices, max_chunks);
+}
+
+extern "C" int bllm_dechunk_ema_backward(const void* z, const float* P, const void* dout, int dtype,
+                                         int64_t d, const int32_t* idx, const int64_t* chunk_offsets,
+                                         const int64_t* offsets, int64_t nseq, int64_t total,
+                                         int64_t max_chunks, void* dz_out, float* dP_out, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  if (!z || !P || !dout || !idx || !chunk_offsets || !offsets || !dz_out || !dP_out || d < 1 || nseq < 1 ||
+      total < 0 || max_chunks < 0)
+    return BLLM_E_INVAL;
+  if (!valid_dtype(dtype)) return BLLM_E_NOTSUP;
+  if ((d * elem_size(dtype)) % 16 != 0 || !aligned16(z) || !aligned16(dout) || !aligned16(dz_out))
+    return BLLM_E_NOTSUP;
+  if (total >= (int64_t(1) << 31) || nseq >= (int64_t(1) << 30) || d > (1 << 16)) return BLLM_E_NOTSUP;
+  if (!ws || ws_bytes < bllm_dechunk_ema_backward_workspace(d, max_chunks) || !aligned16(ws)) return BLLM_E_WS;
+  if (total == 0 || max_chunks == 0) return BLLM_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == BLLM_F32)
+    launch_dechunk_bwd<BLLM_F32>(z, P, dout, static_cast<int>(d), idx, chunk_offsets, offsets,
+                                 static_cast<int>(nseq), max_chunks, dz_out, dP_out, ws, st);
+  else
+    launch_dechunk_bwd<BLLM_BF16>(z, P, dout, static_cast<int>(d), idx, chunk_offsets, offsets,
+                                  static_cast<int>(nseq), max_chunks, dz_out, dP_out, ws, st);
   return launch_status();
 }

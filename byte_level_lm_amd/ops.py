@@ -144,6 +144,28 @@ def dechunk_ema(z, P, idx, chunk_offsets, offsets, total: int, *, out=None, ws=N
     return out
 
 
+def dechunk_ema_backward_workspace(d: int, max_chunks: int) -> int:
+    return int(L.lib().bllm_dechunk_ema_backward_workspace(d, max_chunks))
+
+
+def dechunk_ema_backward(z, P, dout, idx, chunk_offsets, offsets, *, dz_out=None, dP_out=None, ws=None,
+                         max_chunks=None):
+    """Gradients (dz, dP) of sum(dout * dechunk_ema(z, P, ...)) with respect to z and P."""
+    _dev(z, P, dout, idx, chunk_offsets, offsets)
+    d = z.shape[1]
+    dev = z.device
+    mc = z.shape[0] if max_chunks is None else int(max_chunks)
+    dz_out = torch.empty((mc, d), dtype=z.dtype, device=dev) if dz_out is None else dz_out
+    dP_out = torch.empty(mc, dtype=torch.float32, device=dev) if dP_out is None else dP_out
+    w = _ws(dechunk_ema_backward_workspace(d, mc), ws, dev)
+    rc = L.lib().bllm_dechunk_ema_backward(z.data_ptr(), P.data_ptr(), dout.data_ptr(), _dt(z), d,
+                                           idx.data_ptr(), chunk_offsets.data_ptr(), offsets.data_ptr(),
+                                           offsets.numel() - 1, dout.shape[0], mc, dz_out.data_ptr(),
+                                           dP_out.data_ptr(), w.data_ptr(), _nbytes(w), _stream())
+    L.check("bllm_dechunk_ema_backward", rc)
+    return dz_out, dP_out
+
+
 def coding_rate(h, eps2: float, *, dR_out=None, status=None, ws=None):
     """Delta R_t for h [nseq, T, d]; returns (dR fp32 [nseq, T], status)."""
     _dev(h)

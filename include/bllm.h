@@ -133,6 +133,32 @@ int bllm_dechunk_ema(const void* z, const float* P, int dtype, int64_t d, const 
                      void* stream);
 
 /*
+ * bllm_dechunk_ema_backward -- gradients of the EMA dechunk ([BG] 2.3: the
+ * EMA over chunks keeps the boundary choice differentiable end to end).
+ *
+ * With L = sum over positions t and features of dout[t] * out[t] for the
+ * out of bllm_dechunk_ema(z, P, idx, chunk_offsets, offsets), per chunk c:
+ *   gbar_c = sum of dout over the positions chunk c covers
+ *   lam_c  = gbar_c + (1 - P_{c+1}) lam_{c+1}   (lam_c = gbar_c for a
+ *            sequence's last chunk)
+ *   dz_out[c] = dL/dz_c = P_c lam_c
+ *   dP_out[c] = dL/dP_c = lam_c . (z_c - zbar_{c-1}), zbar_{c-1} = 0 at a
+ *            sequence's first chunk (zbar: the forward EMA, recomputed here
+ *            in fp32 from z and P)
+ * Arguments as for bllm_dechunk_ema, plus dout : [total x d] dtype (the
+ * gradient of out), dz_out : [M x d] dtype (RNE for bf16), dP_out : fp32 [M].
+ * max_chunks: host upper bound on M; it also sizes the workspace.
+ * ws       : bllm_dechunk_ema_backward_workspace(d, max_chunks) bytes.
+ * Errors   : as bllm_dechunk_ema; dout/dz_out must be 16-byte aligned.
+ */
+size_t bllm_dechunk_ema_backward_workspace(int64_t d, int64_t max_chunks);
+int bllm_dechunk_ema_backward(const void* z, const float* P, const void* dout, int dtype, int64_t d,
+                              const int32_t* idx, const int64_t* chunk_offsets,
+                              const int64_t* offsets, int64_t nseq, int64_t total,
+                              int64_t max_chunks, void* dz_out, float* dP_out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
  * bllm_coding_rate -- marginal lossy coding rate ([BF4] prerequisite "lossy
  * coding rate" and stage 2):
  *   R(H) = 1/2 logdet(I + alpha H H^T) = 1/2 logdet(I_d + alpha H^T H),

@@ -79,6 +79,11 @@ def test_argument_errors_return_before_any_launch(L):
     assert L.bllm_upsample_bins(dummy, dummy, dummy, dummy, 1, 1, 64, 4, 64, 32, 0, dummy, dummy, 1 << 30, None) == -1
     # dechunk: null P
     assert L.bllm_dechunk_ema(dummy, None, 1, 512, dummy, dummy, dummy, 1, 10, 10, dummy, dummy, 1 << 30, None) == -1
+    # dechunk backward: null dout, workspace too small
+    assert L.bllm_dechunk_ema_backward(dummy, dummy, None, 1, 512, dummy, dummy, dummy, 1, 10, 10, dummy, dummy,
+                                       dummy, 1 << 30, None) == -1
+    assert L.bllm_dechunk_ema_backward(dummy, dummy, dummy, 1, 512, dummy, dummy, dummy, 1, 10, 10, dummy, dummy,
+                                       dummy, 16, None) == -3
 
 
 def test_product_path_does_not_touch_the_oracle():

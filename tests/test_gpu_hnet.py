@@ -3,7 +3,8 @@ import numpy as np
 import pytest
 
 import oracle
-from synthdata import gen_hnet_tiny, gen_event_streams, gen_hnet_two_stage, gen_stage2_inputs, gen_stage2_backproj
+from synthdata import (bf16_round, gen_hnet_tiny, gen_event_streams, gen_hnet_two_stage, gen_stage2_inputs,
+                       gen_stage2_backproj)
 from tests.helpers import to_dev, to_np, row_rel_err, say
 
 pytestmark = pytest.mark.gpu
@@ -268,6 +269,102 @@ def test_dechunk_many_short_sequences(ops):
     say("dechunk many short sequences N", N, "M", len(idx))
     for dtype in (torch.float32, torch.bfloat16):
         _dechunk_check(ops, z, PP, idx, coff, off, dtype, 1e-4 if dtype == torch.float32 else 2e-2)
+
+
+# ---------------------------------------------------------------- EMA backward
+
+def _dechunk_bwd_check(ops, z, P, idx, coff, off, dout, dtype, tol):
+    dz, dP = ops.dechunk_ema_backward(to_dev(z, dtype), to_dev(P.astype(np.float32)), to_dev(dout, dtype),
+                                      to_dev(idx.astype(np.int32)), to_dev(coff), to_dev(off))
+    if dtype != _torch().float32:
+        from synthdata import bf16_round
+        z, dout = bf16_round(z), bf16_round(dout)
+    dz_o, dP_o = oracle.dechunk_ema_backward(z, P.astype(np.float32), idx, coff, off, dout)
+    M = len(idx)
+    dz_g, dP_g = to_np(dz)[:M], to_np(dP)[:M]
+    assert row_rel_err(dz_g, dz_o) < tol
+    scale = max(np.max(np.abs(dP_o)), 1e-30)
+    assert np.max(np.abs(dP_g - dP_o)) / scale < tol, np.max(np.abs(dP_g - dP_o)) / scale
+    return dz_g, dP_g
+
+
+@pytest.mark.parametrize("dtname,d", [("f32", 64), ("bf16", 512), ("bf16", 768), ("f32", 8)])
+def test_dechunk_backward_matches_oracle(ops, dtname, d):
+    torch = _torch()
+    dtype = torch.float32 if dtname == "f32" else torch.bfloat16
+    rng = np.random.default_rng(40 + d)
+    off = np.array([0, 3000, 3001, 3001, 8000, 8064], np.int64)
+    N = int(off[-1])
+    b = rng.random(N) < 0.3
+    b[[0, 3000, 3001, 8000]] = True
+    b[8000:8010] = False   # a sequence without a boundary at its start
+    P = rng.uniform(0.02, 1.0, N).astype(np.float32)
+    rows = rng.standard_normal((N, d)).astype(np.float32)
+    idx, coff, z, PP = oracle.compact(b, P, rows, off)
+    dout = rng.standard_normal((N, d)).astype(np.float32)
+    say("dechunk backward", dtname, d, "N", N, "M", len(idx))
+    _dechunk_bwd_check(ops, z.astype(np.float32), PP, idx, coff, off, dout, dtype,
+                       1e-4 if dtname == "f32" else 2e-2)
+
+
+def test_dechunk_backward_P_one_is_dout(ops):
+    """P = 1 at every position and every position a boundary: dz = dout bit for bit."""
+    torch = _torch()
+    rng = np.random.default_rng(41)
+    for dtype in (torch.float32, torch.bfloat16):
+        off = np.array([0, 17, 17, 4000, 9001], np.int64)
+        N = 9001
+        z = to_dev(rng.standard_normal((N, 32)).astype(np.float32), dtype)
+        g = to_dev(rng.standard_normal((N, 32)).astype(np.float32), dtype)
+        idx = to_dev(np.arange(N, dtype=np.int32))
+        dz, dP = ops.dechunk_ema_backward(z, to_dev(np.ones(N, np.float32)), g, idx, to_dev(off), to_dev(off))
+        assert torch.equal(dz, g)
+
+
+def test_dechunk_backward_many_short_sequences(ops):
+    """700 ragged sequences (some empty, some without a start boundary)."""
+    torch = _torch()
+    rng = np.random.default_rng(42)
+    lengths = rng.integers(0, 41, 700)
+    lengths[::7] = 0
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    N = int(off[-1])
+    b = rng.random(N) < 0.3
+    starts = off[:-1][lengths > 0]
+    b[starts[::2]] = True
+    P = rng.uniform(0.0, 1.0, N).astype(np.float32)
+    rows = rng.standard_normal((N, 24)).astype(np.float32)
+    idx, coff, z, PP = oracle.compact(b, P, rows, off)
+    dout = rng.standard_normal((N, 24)).astype(np.float32)
+    _dechunk_bwd_check(ops, z.astype(np.float32), PP, idx, coff, off, dout, torch.float32, 1e-4)
+
+
+def test_dechunk_backward_full_size_stage1_sampled(ops):
+    """Stage-1 backward at the bench.py size (32 x 8192 rows, 65.7k chunks x 512,
+    bf16): two sequences checked against the oracle."""
+    torch = _torch()
+    bf = torch.bfloat16
+    c = gen_hnet_two_stage(fixed_T=8192)
+    off = c["offsets"]
+    p = oracle.route(c["q"], c["k"], off)
+    tau = oracle.stage_quantile(p, 0.75)
+    b = oracle.boundary_mask(p, tau)
+    idx, coff, z, P = oracle.compact(b, p.astype(np.float32), c["h"], off)
+    rng = np.random.default_rng(43)
+    N = int(off[-1])
+    dout = bf16_round(rng.standard_normal((N, 512)).astype(np.float32))
+    dz, dP = ops.dechunk_ema_backward(to_dev(z, bf), to_dev(P.astype(np.float32)), to_dev(dout, bf),
+                                      to_dev(idx.astype(np.int32)), to_dev(coff), to_dev(off))
+    dz, dP = to_np(dz), to_np(dP)
+    for s in (0, 31):
+        c0, c1 = int(coff[s]), int(coff[s + 1])
+        t0, t1 = int(off[s]), int(off[s + 1])
+        o_s = np.array([0, t1 - t0], np.int64)
+        dz_o, dP_o = oracle.dechunk_ema_backward(z[c0:c1], P[c0:c1].astype(np.float32), idx[c0:c1] - t0,
+                                                 np.array([0, c1 - c0], np.int64), o_s, dout[t0:t1])
+        assert row_rel_err(dz[c0:c1], dz_o) < 2e-2
+        assert np.max(np.abs(dP[c0:c1] - dP_o)) / np.max(np.abs(dP_o)) < 2e-2
+    say("dechunk backward full size ok, M", len(idx))
 
 
 def test_c2_two_stage_full_size(ops):
