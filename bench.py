@@ -151,6 +151,14 @@ class Workload:
         self.dP1 = torch.empty(self.M1, device=dev)
         self.ws_dbwd = torch.empty(B.dechunk_ema_backward_workspace(512, self.M1), dtype=torch.uint8, device=dev)
         self._dechunk1_backward()
+        # stage-1 routing straight from h (projections inside the kernel)
+        self.wq1 = torch.from_numpy(hn["wq"]).to(dev, bf)
+        self.wk1 = torch.from_numpy(hn["wk"]).to(dev, bf)
+        self.pf1 = torch.empty(N, device=dev)
+        self.bf1 = torch.empty(N, dtype=torch.uint8, device=dev)
+        self.tauf1 = torch.empty(1, device=dev)
+        self.ws_routef = torch.empty(B.route_workspace(N), dtype=torch.uint8, device=dev)
+        self._route_fused1()
         torch.cuda.synchronize()
         log(f"setup done: M1={self.M1} ({self.M1 / N:.3f} N), M2={self.M2} ({self.M2 / N:.3f} N)")
 
@@ -202,16 +210,24 @@ class Workload:
         self.B.dechunk_ema_backward(self.y1, self.P1, self.dout1, self.idx1, self.coff1, self.off,
                                     dz_out=self.dz1, dP_out=self.dP1, ws=self.ws_dbwd, max_chunks=self.M1)
 
+    def _route_fused1(self):
+        self.B.route_fused(self.h1, self.wq1, self.wk1, self.off, quantile=0.75, p_out=self.pf1, b_out=self.bf1,
+                           tau_out=self.tauf1, ws=self.ws_routef)
+
     def next_ops(self):
         """Rows past the hot path (the survey's 'next' list), timed on their own."""
-        return [("cosine_chunker", self._cosine_chunker), ("dechunk_backward stage1", self._dechunk1_backward)]
+        return [("cosine_chunker", self._cosine_chunker), ("dechunk_backward stage1", self._dechunk1_backward),
+                ("route_fused stage1", self._route_fused1)]
 
     def next_algorithmic(self):
         N, M1, nseq, K = self.N, self.M1, self.nseq, self.K
         e = 2
         return {"cosine_chunker": dict(bytes=N * (2 * 512 * e + 4 + 1) + N * 4 + N + nseq * K * 4),
                 # dout read once, z and P read, dz and dP written
-                "dechunk_backward stage1": dict(bytes=N * 512 * e + M1 * (2 * 512 * e + 4 + 4 + 4))}
+                "dechunk_backward stage1": dict(bytes=N * 512 * e + M1 * (2 * 512 * e + 4 + 4 + 4)),
+                # h read once, Wq and Wk, p and b written; q = h Wq and k = h Wk on bf16 MFMA
+                "route_fused stage1": dict(bytes=N * (512 * e + 5) + 2 * 512 * 512 * e,
+                                           flops=2 * N * 512 * 1024)}
 
     def ops(self):
         return [("route+compact stage1", self._stage1), ("route+compact stage2", self._stage2),

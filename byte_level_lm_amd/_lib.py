@@ -23,6 +23,8 @@ _SIGS = {
     "bllm_route_workspace": (C.c_size_t, [_i64]),
     "bllm_route": (C.c_int, [_p, _p, C.c_int, _i64, _p, _i64, _i64, C.c_float, C.c_double,
                              _p, _p, _p, _p, C.c_size_t, _p]),
+    "bllm_route_fused": (C.c_int, [_p, _p, _p, C.c_int, _i64, _p, _i64, _i64, C.c_float, C.c_double,
+                                   _p, _p, _p, _p, C.c_size_t, _p]),
     "bllm_compact_workspace": (C.c_size_t, [_i64]),
     "bllm_compact": (C.c_int, [_p, _p, _p, C.c_int, _i64, _p, _i64, _i64, _i64, _p, _p, _p, _p,
                                _p, _p, C.c_size_t, _p]),

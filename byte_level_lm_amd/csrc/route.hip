@@ -364,6 +364,206 @@ void launch_route(int gshift, dim3 grid, hipStream_t st, const void* q, const vo
 #undef BLLM_ROUTE_CASE
 }
 
+// ------------------------------------------------------------- fused projection + scoring
+// The routing projections q = h Wq, k = h Wk (row-vector convention) and the
+// score in one kernel, so q and k never reach memory.  A workgroup owns 128
+// rows t0 .. t0+127.  Its h tile is staged with one extra row above
+// (t0 - 1), and the k half of the GEMM reads the staged rows shifted by one:
+// row t of the tile holds q_t and k_{t-1} side by side, so the cosine needs
+// only per-row sums: dot = sum_j q_t[j] k_{t-1}[j], |q_t|^2, |k_{t-1}|^2.
+// Columns are taken in blocks of 128 (of q and of k); four waves in 2 x 2
+// each compute a 64 x 64 quadrant of both (bf16 MFMA 32x32x16, W read down
+// its columns with the transposing LDS read), reduce its per-row sums over
+// its 64 columns with DPP, and add them to an LDS slot of its own, so the
+// sums are formed in a fixed order.  The next K step's operands are in
+// flight in registers while the MFMAs consume the one in LDS.
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kFR = 128;        // rows per tile
+constexpr int kFC = 128;        // q and k columns per block
+constexpr int kFK = 64;         // K step
+constexpr int kFPA = kFK + 8;   // LDS pitch (bf16) of the staged h rows
+constexpr int kFPB = kFC + 16;  // LDS pitch (bf16) of the staged W rows: rows 8 banks apart
+
+// row of element r held by `lane` in a 32x32 MFMA accumulator
+__device__ inline int frow_of(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// two transposing LDS reads (ds_read_b64_tr_b16) give a lane the B operand
+// of a [k][n] tile: with row = 8 (lane / 32) + (lane % 16) / 4 and col =
+// 16 ((lane / 16) % 2) + 4 (lane % 4) added to the origin, lane l receives
+// column l % 32, rows 8 (l / 32) .. +7
+__device__ inline bf16x8 tr_b_frag(const uint16_t* s, int row, int col, int pitch) {
+  typedef __attribute__((address_space(3))) shortx4 lds_s4;
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(s + row * pitch + col));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(s + (row + 4) * pitch + col));
+  bf16x8 v;
+  __builtin_memcpy(&v, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&v) + 8, &hi, 8);
+  return v;
+}
+
+__global__ __launch_bounds__(256, 2) void route_fused_kernel(const uint16_t* __restrict__ h,
+                                                             const uint16_t* __restrict__ Wq,
+                                                             const uint16_t* __restrict__ Wk, int d,
+                                                             const int64_t* __restrict__ offsets, int nseq,
+                                                             int64_t total, float threshold,
+                                                             float* __restrict__ p_out,
+                                                             uint8_t* __restrict__ b_out,
+                                                             float* __restrict__ tau_out, SelectState* sel) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[(kFR + 1) * kFPA];
+  __shared__ __attribute__((aligned(16))) uint16_t sBq[kFK * kFPB];
+  __shared__ __attribute__((aligned(16))) uint16_t sBk[kFK * kFPB];
+  __shared__ float sSum[2][kFR][3];  // [column half][row][dot, |q|^2, |k|^2]
+  __shared__ uint8_t sstart[kFR];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int wm = w >> 1, wn = w & 1;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kFR;
+  const int64_t te = t0 + kFR < total ? t0 + kFR : total;
+  const bool write_mask = sel == nullptr;
+  if (write_mask && tau_out != nullptr && blockIdx.x == 0 && tid == 0) *tau_out = threshold;
+  if (!write_mask && blockIdx.x == 0) select_init(sel);
+  for (int e = tid; e < 2 * kFR * 3; e += 256) (&sSum[0][0][0])[e] = 0.f;
+  if (tid < kFR) sstart[tid] = 0;
+  __syncthreads();
+  {
+    const int slo = lower_seq(offsets, nseq, t0);
+    const int shi = lower_seq(offsets, nseq, te);
+    for (int s = slo + tid; s < shi; s += 256) sstart[offsets[s] - t0] = 1;
+  }
+  // loaders.  h: staged row i is h row t0 - 1 + i (clamped into [0, total));
+  // thread: rows 1 + ra + 32 q (q = 0..3), 16-byte chunk la; threads 0..7 also
+  // row 0.  W: K rows kb + 16 q of the block's 128 columns, chunk nb.
+  const int ra = tid >> 3, la = (tid & 7) * 8;
+  const int kb = tid >> 4, nb = (tid & 15) * 8;
+  auto hrow = [&](int64_t r) { return (r < 0 ? 0 : (r < total ? r : total - 1)) * static_cast<int64_t>(d); };
+  const int64_t ho0 = hrow(t0 + ra) + la, ho1 = hrow(t0 + ra + 32) + la;
+  const int64_t ho2 = hrow(t0 + ra + 64) + la, ho3 = hrow(t0 + ra + 96) + la;
+  const int64_t hoh = hrow(t0 - 1) + (tid & 7) * 8;
+  uint4 pa0, pa1, pa2, pa3, ph, pq0, pq1, pq2, pq3, pk0, pk1, pk2, pk3;
+  auto fetch = [&](int jb, int kt) {
+    const int ko = kt * kFK;
+    pa0 = *reinterpret_cast<const uint4*>(h + ho0 + ko);
+    pa1 = *reinterpret_cast<const uint4*>(h + ho1 + ko);
+    pa2 = *reinterpret_cast<const uint4*>(h + ho2 + ko);
+    pa3 = *reinterpret_cast<const uint4*>(h + ho3 + ko);
+    ph = *reinterpret_cast<const uint4*>(h + hoh + ko);
+    const int64_t wo = static_cast<int64_t>(ko + kb) * d + jb * kFC + nb;
+    const int64_t w16 = static_cast<int64_t>(16) * d;
+    pq0 = *reinterpret_cast<const uint4*>(Wq + wo);
+    pq1 = *reinterpret_cast<const uint4*>(Wq + wo + w16);
+    pq2 = *reinterpret_cast<const uint4*>(Wq + wo + 2 * w16);
+    pq3 = *reinterpret_cast<const uint4*>(Wq + wo + 3 * w16);
+    pk0 = *reinterpret_cast<const uint4*>(Wk + wo);
+    pk1 = *reinterpret_cast<const uint4*>(Wk + wo + w16);
+    pk2 = *reinterpret_cast<const uint4*>(Wk + wo + 2 * w16);
+    pk3 = *reinterpret_cast<const uint4*>(Wk + wo + 3 * w16);
+  };
+  auto stash = [&]() {
+    *reinterpret_cast<uint4*>(sA + (1 + ra) * kFPA + la) = pa0;
+    *reinterpret_cast<uint4*>(sA + (33 + ra) * kFPA + la) = pa1;
+    *reinterpret_cast<uint4*>(sA + (65 + ra) * kFPA + la) = pa2;
+    *reinterpret_cast<uint4*>(sA + (97 + ra) * kFPA + la) = pa3;
+    if (tid < 8) *reinterpret_cast<uint4*>(sA + (tid & 7) * 8) = ph;
+    *reinterpret_cast<uint4*>(sBq + kb * kFPB + nb) = pq0;
+    *reinterpret_cast<uint4*>(sBq + (kb + 16) * kFPB + nb) = pq1;
+    *reinterpret_cast<uint4*>(sBq + (kb + 32) * kFPB + nb) = pq2;
+    *reinterpret_cast<uint4*>(sBq + (kb + 48) * kFPB + nb) = pq3;
+    *reinterpret_cast<uint4*>(sBk + kb * kFPB + nb) = pk0;
+    *reinterpret_cast<uint4*>(sBk + (kb + 16) * kFPB + nb) = pk1;
+    *reinterpret_cast<uint4*>(sBk + (kb + 32) * kFPB + nb) = pk2;
+    *reinterpret_cast<uint4*>(sBk + (kb + 48) * kFPB + nb) = pk3;
+  };
+  const int j16 = lane & 15;
+  const int brow = 8 * (lane >> 5) + (j16 >> 2);
+  const int bcol = 64 * wn + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+  const int nkt = d / kFK, njb = d / kFC;
+  fetch(0, 0);
+  for (int jb = 0; jb < njb; ++jb) {
+    floatx16 aq[2][2], ak[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) aq[a][c][r] = ak[a][c][r] = 0.f;
+    for (int kt = 0; kt < nkt; ++kt) {
+      __syncthreads();
+      stash();
+      __syncthreads();
+      if (kt + 1 < nkt) fetch(jb, kt + 1);
+      else if (jb + 1 < njb) fetch(jb + 1, 0);
+#pragma unroll
+      for (int ks = 0; ks < kFK; ks += 16) {
+        bf16x8 fq[2], fk[2], bq[2], bk[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int r0 = 64 * wm + 32 * a + (lane & 31);
+          fq[a] = *reinterpret_cast<const bf16x8*>(sA + (r0 + 1) * kFPA + ks + 8 * (lane >> 5));
+          fk[a] = *reinterpret_cast<const bf16x8*>(sA + r0 * kFPA + ks + 8 * (lane >> 5));
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          bq[c] = tr_b_frag(sBq, ks + brow, bcol + 32 * c, kFPB);
+          bk[c] = tr_b_frag(sBk, ks + brow, bcol + 32 * c, kFPB);
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            aq[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[a], bq[c], aq[a][c], 0, 0, 0);
+            ak[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[a], bk[c], ak[a][c], 0, 0, 0);
+          }
+      }
+    }
+    // per-row sums over this wave's 64 columns of the block
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float dq = 0.f, nq = 0.f, nk = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          dq = fmaf(aq[a][c][r], ak[a][c][r], dq);
+          nq = fmaf(aq[a][c][r], aq[a][c][r], nq);
+          nk = fmaf(ak[a][c][r], ak[a][c][r], nk);
+        }
+        dq = group_sum<32>(dq);
+        nq = group_sum<32>(nq);
+        nk = group_sum<32>(nk);
+        if ((lane & 31) == 0) {
+          float* sp = sSum[wn][64 * wm + 32 * a + frow_of(r, lane)];
+          sp[0] += dq;
+          sp[1] += nq;
+          sp[2] += nk;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kFR) {
+    const int64_t t = t0 + tid;
+    if (t < total) {
+      float p;
+      if (sstart[tid]) {
+        p = 1.0f;
+      } else {
+        const float dot = sSum[0][tid][0] + sSum[1][tid][0];
+        const float nq = sSum[0][tid][1] + sSum[1][tid][1];
+        const float nk = sSum[0][tid][2] + sSum[1][tid][2];
+        const float den = fmaxf(sqrtf(nq) * sqrtf(nk), 1e-12f);
+        p = 0.5f * (1.0f - dot / den);
+        if (p != p) p = __int_as_float(0x7FC00000);  // canonical NaN
+        else p = fminf(fmaxf(p, 0.0f), 1.0f);
+        if (p == 0.0f) p = 0.0f;  // +0.0
+      }
+      p_out[t] = p;
+      if (write_mask) b_out[t] = static_cast<uint8_t>(p >= threshold);
+    }
+  }
+}
+
 }  // namespace
 }  // namespace bllm
 
@@ -412,6 +612,37 @@ extern "C" int bllm_route(const void* q, const void* k, int dtype, int64_t d,
     launch_route<BLLM_BF16>(gshift, grid, st, q, k, static_cast<int>(d), offsets,
                             static_cast<int>(nseq), total, iters, passes, threshold, p_out, b_out, tau_out,
                             sst);
+  if (!use_q) return launch_status();
+  if (launch_status() != BLLM_OK) return BLLM_E_HIP;
+  const uint32_t rank = static_cast<uint32_t>(std::floor(quantile * static_cast<double>(total - 1)));
+  const unsigned nblk = static_cast<unsigned>(std::min<int64_t>(kSelMaxBlocks, ceil_div(total, kSelTile)));
+  hipLaunchKernelGGL(select_kernel, dim3(nblk), dim3(kSelThreads), 0, st, p_out, total, rank, sst,
+                     tau_out, b_out);
+  return launch_status();
+}
+
+extern "C" int bllm_route_fused(const void* h, const void* Wq, const void* Wk, int dtype, int64_t d,
+                                const int64_t* offsets, int64_t nseq, int64_t total, float threshold,
+                                double quantile, float* p_out, uint8_t* b_out, float* tau_out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!h || !Wq || !Wk || !offsets || !p_out || !b_out || d < 1 || nseq < 1 || total < 0 || quantile > 1.0)
+    return BLLM_E_INVAL;
+  if (dtype != BLLM_BF16) return BLLM_E_NOTSUP;
+  if (d % kFC != 0 || d > 4096 || !aligned16(h) || !aligned16(Wq) || !aligned16(Wk)) return BLLM_E_NOTSUP;
+  if (total >= (int64_t(1) << 31) || nseq >= (int64_t(1) << 30)) return BLLM_E_NOTSUP;
+  const bool use_q = quantile >= 0.0;
+  if (use_q && (!ws || ws_bytes < sizeof(SelectState))) return BLLM_E_WS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (total == 0) {
+    if (tau_out) hipLaunchKernelGGL(fill_f32, dim3(1), dim3(64), 0, st, tau_out, 1,
+                                    use_q ? __builtin_nanf("") : threshold);
+    return launch_status();
+  }
+  SelectState* sst = use_q ? static_cast<SelectState*>(ws) : nullptr;
+  hipLaunchKernelGGL(route_fused_kernel, dim3(static_cast<unsigned>(ceil_div(total, kFR))), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(Wq),
+                     static_cast<const uint16_t*>(Wk), static_cast<int>(d), offsets, static_cast<int>(nseq),
+                     total, threshold, p_out, b_out, tau_out, sst);
   if (!use_q) return launch_status();
   if (launch_status() != BLLM_OK) return BLLM_E_HIP;
   const uint32_t rank = static_cast<uint32_t>(std::floor(quantile * static_cast<double>(total - 1)));

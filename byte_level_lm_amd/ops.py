@@ -95,6 +95,25 @@ def route(q, k, offsets, *, threshold: float = 0.5, quantile=None, p_out=None, b
     return p_out, b_out, tau_out
 
 
+def route_fused(h, Wq, Wk, offsets, *, threshold: float = 0.5, quantile=None, p_out=None, b_out=None,
+                tau_out=None, ws=None):
+    """bllm_route with q = h Wq and k = h Wk formed inside the kernel (bf16 h, Wq, Wk)."""
+    _dev(h, Wq, Wk, offsets)
+    total, d = h.shape
+    dev = h.device
+    p_out = torch.empty(total, dtype=torch.float32, device=dev) if p_out is None else p_out
+    b_out = torch.empty(total, dtype=torch.uint8, device=dev) if b_out is None else b_out
+    tau_out = torch.empty(1, dtype=torch.float32, device=dev) if tau_out is None else tau_out
+    w = _ws(route_workspace(total), ws, dev) if quantile is not None else ws
+    rc = L.lib().bllm_route_fused(h.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), _dt(h), d, offsets.data_ptr(),
+                                  offsets.numel() - 1, total, float(threshold),
+                                  -1.0 if quantile is None else float(quantile), p_out.data_ptr(),
+                                  b_out.data_ptr(), tau_out.data_ptr(), _ptr(w),
+                                  0 if w is None else _nbytes(w), _stream())
+    L.check("bllm_route_fused", rc)
+    return p_out, b_out, tau_out
+
+
 def compact(mask, offsets, *, rows=None, p=None, capacity=None, idx_out=None,
             chunk_offsets_out=None, rows_out=None, P_out=None, status=None, ws=None):
     """Keep set mask positions: returns (idx, chunk_offsets, rows_out, P_out, status).

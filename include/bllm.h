@@ -91,6 +91,22 @@ int bllm_route(const void* q, const void* k, int dtype, int64_t d, const int64_t
                uint8_t* b_out, float* tau_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * bllm_route_fused -- bllm_route computed straight from the encoder output:
+ * q = h Wq and k = h Wk (row-vector convention, fp32 accumulation of the bf16
+ * products) are formed on the fly and never stored; p, b and tau follow
+ * exactly as in bllm_route.
+ *
+ * h        : [total x d] bf16 rows; Wq, Wk : [d x d] bf16, row-major.
+ * d        : a multiple of 128, at most 4096 (else BLLM_E_NOTSUP); bf16 only.
+ * Other arguments, outputs, workspace (bllm_route_workspace) and errors as
+ * for bllm_route.
+ */
+int bllm_route_fused(const void* h, const void* Wq, const void* Wk, int dtype, int64_t d,
+                     const int64_t* offsets, int64_t nseq, int64_t total, float threshold,
+                     double quantile, float* p_out, uint8_t* b_out, float* tau_out, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
  * bllm_compact -- keep the boundary positions of a ragged batch ([BG] 2.3
  * chunking into a shorter sequence; also the gather z = [h_{s_1} .. h_{s_K}]
  * of [BF4] stage 2 when `mask` is the Top-K mask).

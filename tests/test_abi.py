@@ -79,6 +79,9 @@ def test_argument_errors_return_before_any_launch(L):
     assert L.bllm_upsample_bins(dummy, dummy, dummy, dummy, 1, 1, 64, 4, 64, 32, 0, dummy, dummy, 1 << 30, None) == -1
     # dechunk: null P
     assert L.bllm_dechunk_ema(dummy, None, 1, 512, dummy, dummy, dummy, 1, 10, 10, dummy, dummy, 1 << 30, None) == -1
+    # fused route: fp32 unsupported, d not a multiple of 128
+    assert L.bllm_route_fused(dummy, dummy, dummy, 0, 512, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, 0, None) == -2
+    assert L.bllm_route_fused(dummy, dummy, dummy, 1, 192, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, 0, None) == -2
     # dechunk backward: null dout, workspace too small
     assert L.bllm_dechunk_ema_backward(dummy, dummy, None, 1, 512, dummy, dummy, dummy, 1, 10, 10, dummy, dummy,
                                        dummy, 1 << 30, None) == -1

@@ -147,6 +147,50 @@ def test_route_quantile_crowded_scores(ops):
     assert np.isnan(tau_g) and not to_np(b).any()
 
 
+# ---------------------------------------------------------------- fused projection + route
+
+def _fused_oracle(h, wq, wk, off):
+    """The plain definition: q = h Wq, k = h Wk in fp64 from the bf16 inputs, then the route."""
+    h64 = np.asarray(h, np.float64)
+    return oracle.route(h64 @ np.asarray(wq, np.float64), h64 @ np.asarray(wk, np.float64), off)
+
+
+@pytest.mark.parametrize("d", [128, 512, 768])
+def test_route_fused_matches_oracle(ops, d):
+    torch = _torch()
+    bf = torch.bfloat16
+    rng = np.random.default_rng(50 + d)
+    off = np.concatenate([[0], np.cumsum([1, 0, 127, 128, 129, 900, 2])]).astype(np.int64)
+    N = int(off[-1])
+    h = bf16_round(rng.standard_normal((N, d)))
+    wq = bf16_round(rng.standard_normal((d, d)) / np.sqrt(d))
+    wk = bf16_round(rng.standard_normal((d, d)) / np.sqrt(d))
+    p, b, tau = ops.route_fused(to_dev(h, bf), to_dev(wq, bf), to_dev(wk, bf), to_dev(off), threshold=0.5)
+    p_g, b_g = to_np(p), to_np(b).astype(bool)
+    p_o = _fused_oracle(h, wq, wk, off)
+    say("route fused d", d, "N", N, "max |dp|", float(np.max(np.abs(p_g - p_o))))
+    assert np.max(np.abs(p_g - p_o)) < 1e-5
+    assert np.all(p_g[off[:-1][np.diff(off) > 0]] == 1.0)
+    keep = np.abs(p_o - 0.5) > 1e-5
+    assert np.array_equal(b_g[keep], (p_o >= 0.5)[keep])
+    assert float(to_np(tau)[0]) == 0.5
+
+
+def test_route_fused_quantile_event_streams(ops):
+    """Stage-1 routing from h on ByteGen-style streams (projections formed in
+    the kernel), with the stage's 0.75 score quantile."""
+    torch = _torch()
+    bf = torch.bfloat16
+    c = gen_event_streams(nseq=6, d=512, min_events=3, max_events=40)
+    off = c["offsets"]
+    p, b, tau = ops.route_fused(to_dev(c["h"], bf), to_dev(c["wq"], bf), to_dev(c["wk"], bf), to_dev(off),
+                                quantile=0.75)
+    p_g, tau_g = _check_quantile(p, b, tau, 0.75)
+    p_o = _fused_oracle(c["h"], c["wq"], c["wk"], off)
+    assert np.max(np.abs(p_g - p_o)) < 1e-5
+    assert abs(tau_g - oracle.stage_quantile(p_o, 0.75)) < 1e-5
+
+
 def _compact_check(ops, b, p, rows, off, dtype, capacity=None):
     idx, coff, z, P, st = ops.compact(to_dev(b.astype(np.uint8)), to_dev(off), rows=to_dev(rows, dtype),
                                       p=to_dev(p.astype(np.float32)), capacity=capacity)
