@@ -20,7 +20,8 @@ Sources (page titles; sections named as on the page):
         coding rate" (R_eps formula), "method step details" stages 2 and 4
         (Delta R, S = {1} + Top-(K-1) in time order, chunk map c(t), bins,
         residual), "independent analysis of weaknesses" (incremental
-        Sherman-Morrison-Woodbury evaluation suggested).
+        Sherman-Morrison-Woodbury evaluation suggested; streaming inference
+        by a sliding window with a local Top-K suggested).
 
 Where the pages are silent the reading taken is stated in the docstring of
 the function concerned.  [BG] describes H-Net routing and the EMA only in
@@ -34,5 +35,5 @@ none is "parity unpinned".
 """
 from .hnet import route, boundary_mask, stage_quantile, compact, dechunk_ema, dechunk_ema_backward  # noqa: F401
 from .byteflow import (  # noqa: F401
-    alpha_of, coding_rate, coding_rate_at, topk_select, topk_mask, gather, chunk_bins, upsample_bins,
+    alpha_of, coding_rate, coding_rate_at, coding_rate_stream, topk_select, topk_select_window, topk_mask, gather, chunk_bins, upsample_bins,
 )

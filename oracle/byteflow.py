@@ -89,6 +89,65 @@ def topk_select(score, K: int) -> np.ndarray:
     return out[0] if squeeze else out
 
 
+def coding_rate_stream(h, eps2: float, A_in=None):
+    """Delta R_t of one window of a byte stream, given the carried prefix matrix.
+
+    The streaming chunker that the [BF4] weakness analysis suggests for
+    autoregressive inference (sliding window with a local Top-K): the bytes
+    arrive in windows, and the chunker carries A = I_d + alpha sum h h^T over
+    every byte already seen.  Delta R is causal, so with that carry each
+    window's values are the whole-sequence values (same definition as
+    ``coding_rate``): A <- A + alpha h_t h_t^T, Delta R_t = R(A) - R(A before).
+    h: [nseq, W, d] or [W, d]; A_in: [nseq, d, d] (or [d, d]), None for the
+    stream's start (A = I).  Returns (dR [nseq, W], A_out [nseq, d, d])."""
+    h = np.asarray(h, dtype=np.float64)
+    squeeze = h.ndim == 2
+    if squeeze:
+        h = h[None]
+    nseq, W, d = h.shape
+    a = alpha_of(d, eps2)
+    if A_in is None:
+        A_in = np.broadcast_to(np.eye(d), (nseq, d, d))
+    A_in = np.asarray(A_in, dtype=np.float64).reshape(nseq, d, d)
+    out = np.empty((nseq, W))
+    A_out = np.empty((nseq, d, d))
+    for s in range(nseq):
+        A = A_in[s].copy()
+        r_prev = _rate(A)
+        for t in range(W):
+            A = A + a * np.outer(h[s, t], h[s, t])
+            r = _rate(A)
+            out[s, t] = r - r_prev
+            r_prev = r
+        A_out[s] = A
+    if squeeze:
+        return out[0], A_out[0]
+    return out, A_out
+
+
+def topk_select_window(score, K: int, first: bool) -> np.ndarray:
+    """Local Top-K of one window of a stream.  The stream's first window is
+    selected as a whole sequence (``topk_select``: BOS plus K-1); every later
+    window keeps its K largest scores, with no forced position (the stream's
+    BOS lies in the first window).  Ties go to the earlier position, NaN ranks
+    below every number; the set is returned in time order (positions inside
+    the window).  score: [nseq, W]."""
+    if first:
+        return topk_select(score, K)
+    score = np.asarray(score)
+    squeeze = score.ndim == 1
+    if squeeze:
+        score = score[None]
+    nseq, W = score.shape
+    if not (1 <= K <= W):
+        raise ValueError("need 1 <= K <= W")
+    out = np.empty((nseq, K), dtype=np.int64)
+    for s in range(nseq):
+        key = lambda t: (0 if np.isnan(score[s, t]) else 1, 0.0 if np.isnan(score[s, t]) else float(score[s, t]), -t)
+        out[s] = sorted(sorted(range(W), key=key, reverse=True)[:K])
+    return out[0] if squeeze else out
+
+
 def topk_mask(idx, T: int) -> np.ndarray:
     idx = np.atleast_2d(idx)
     m = np.zeros((idx.shape[0], T), dtype=np.uint8)

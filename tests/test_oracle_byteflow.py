@@ -137,6 +137,73 @@ def test_topk_invariants_and_nan():
     assert np.array_equal(oracle.topk_select(sc, 64)[0], np.arange(64))
 
 
+# ---------------------------------------------------------------- streaming chunker
+
+def test_coding_rate_stream_windows_equal_whole_sequence():
+    """Windows of ragged widths with the carried matrix give the pinned
+    whole-sequence values, and the final carry is I + alpha H^T H."""
+    rng = np.random.default_rng(31)
+    h = cluster_rows(rng, 2, 40, 8)
+    eps2 = 0.7
+    whole = oracle.coding_rate(h, eps2)
+    A = None
+    t = 0
+    for w in (7, 1, 20, 12):
+        dr, A = oracle.coding_rate_stream(h[:, t:t + w], eps2, A)
+        np.testing.assert_allclose(dr, whole[:, t:t + w], rtol=1e-10, atol=1e-12)
+        t += w
+    a = 8 / eps2
+    for s in range(2):
+        np.testing.assert_allclose(A[s], np.eye(8) + a * h[s].T @ h[s], rtol=1e-13, atol=1e-12)
+
+
+def test_coding_rate_stream_closed_forms_with_a_carry():
+    """After one past row u: a row orthogonal to u adds 1/2 log(1 + alpha|v|^2);
+    the row c u adds 1/2 log((1 + alpha (1 + c^2)|u|^2) / (1 + alpha|u|^2))."""
+    d, eps2 = 5, 0.5
+    a = d / eps2
+    u = np.array([0.3, -0.2, 0.5, 0.0, 0.1])
+    A_in = np.eye(d) + a * np.outer(u, u)
+    v = np.array([0.2, 0.3, 0.0, 0.7, 0.0])
+    assert abs(u @ v) < 1e-15
+    c = 1.7
+    dr, A_out = oracle.coding_rate_stream(np.stack([v]), eps2, A_in)
+    assert abs(dr[0] - 0.5 * np.log1p(a * v @ v)) < 1e-13
+    dr, _ = oracle.coding_rate_stream(np.stack([c * u]), eps2, A_in)
+    uu = u @ u
+    assert abs(dr[0] - 0.5 * np.log((1 + a * (1 + c * c) * uu) / (1 + a * uu))) < 1e-13
+    # no carry: the stream's start is the whole-sequence definition
+    dr0, _ = oracle.coding_rate_stream(np.stack([c * u]), eps2)
+    assert abs(dr0[0] - 0.5 * np.log1p(a * c * c * uu)) < 1e-13
+
+
+def test_topk_window_first_is_whole_sequence_rule():
+    rng = np.random.default_rng(32)
+    sc = rng.random((2, 50))
+    for K in (1, 5, 50):
+        assert np.array_equal(oracle.topk_select_window(sc, K, True), oracle.topk_select(sc, K))
+
+
+def test_topk_window_later_brute_force_enumeration():
+    """A later window keeps the unique K-subset whose every member beats every
+    non-member (larger score, or equal and earlier); position 0 is not forced."""
+    rng = np.random.default_rng(33)
+    for W in (1, 4, 8):
+        sc = rng.integers(0, 3, size=W).astype(np.float64)
+        if W > 1:
+            sc[0] = -1.0  # the lowest score, so a forced position 0 would show
+        for K in range(1, W + 1):
+            got = set(oracle.topk_select_window(sc, K, False).tolist())
+            ok = []
+            for sub in itertools.combinations(range(W), K):
+                S = set(sub)
+                if all((sc[i] > sc[j]) or (sc[i] == sc[j] and i < j) for i in S for j in range(W) if j not in S):
+                    ok.append(S)
+            assert len(ok) == 1 and ok[0] == got
+    sc = np.array([0.5, np.nan, 0.1, 0.9])
+    assert list(oracle.topk_select_window(sc, 3, False)) == [0, 2, 3]
+
+
 # ---------------------------------------------------------------- gather / bins / upsample
 
 def test_chunk_bins_golden_hand_derived():
