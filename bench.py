@@ -158,6 +158,17 @@ class Workload:
         self.bf1 = torch.empty(N, dtype=torch.uint8, device=dev)
         self.tauf1 = torch.empty(1, device=dev)
         self.ws_routef = torch.empty(B.route_workspace(N), dtype=torch.uint8, device=dev)
+        # streaming chunker: the same byte streams arriving in windows of 1024
+        # bytes, each its own dense buffer; the carried matrix is updated in place
+        self.win = 1024
+        self.Kw = self.K * self.win // T
+        self.h4w = [self.h4[:, i * self.win:(i + 1) * self.win].contiguous() for i in range(T // self.win)]
+        self.state4 = torch.empty((self.nseq, 512, 512), device=dev)
+        self.dRw = torch.empty((self.nseq, self.win), device=dev)
+        self.idxw = torch.empty((T // self.win, self.nseq, self.Kw), dtype=torch.int32, device=dev)
+        self.maskw = torch.empty((T // self.win, self.nseq, self.win), dtype=torch.uint8, device=dev)
+        self.ws_crw = torch.empty(B.coding_rate_workspace(self.nseq, self.win, 512), dtype=torch.uint8, device=dev)
+        self._streaming_chunker()
         self._route_fused1()
         torch.cuda.synchronize()
         log(f"setup done: M1={self.M1} ({self.M1 / N:.3f} N), M2={self.M2} ({self.M2 / N:.3f} N)")
@@ -206,6 +217,13 @@ class Workload:
         self.B.topk_select(self.p4.view(self.nseq, -1), self.K, idx_out=self.idx5, mask_out=self.mask5,
                            status=self.st)
 
+    def _streaming_chunker(self):
+        for i, hw in enumerate(self.h4w):
+            self.B.coding_rate_stream(hw, 0.5, None if i == 0 else self.state4, state_out=self.state4,
+                                      dR_out=self.dRw, status=self.st, ws=self.ws_crw)
+            self.B.topk_select_window(self.dRw, self.Kw, i == 0, idx_out=self.idxw[i], mask_out=self.maskw[i],
+                                      status=self.st)
+
     def _dechunk1_backward(self):
         self.B.dechunk_ema_backward(self.y1, self.P1, self.dout1, self.idx1, self.coff1, self.off,
                                     dz_out=self.dz1, dP_out=self.dP1, ws=self.ws_dbwd, max_chunks=self.M1)
@@ -217,7 +235,7 @@ class Workload:
     def next_ops(self):
         """Rows past the hot path (the survey's 'next' list), timed on their own."""
         return [("cosine_chunker", self._cosine_chunker), ("dechunk_backward stage1", self._dechunk1_backward),
-                ("route_fused stage1", self._route_fused1)]
+                ("route_fused stage1", self._route_fused1), ("streaming_chunker", self._streaming_chunker)]
 
     def next_algorithmic(self):
         N, M1, nseq, K = self.N, self.M1, self.nseq, self.K
@@ -227,7 +245,12 @@ class Workload:
                 "dechunk_backward stage1": dict(bytes=N * 512 * e + M1 * (2 * 512 * e + 4 + 4 + 4)),
                 # h read once, Wq and Wk, p and b written; q = h Wq and k = h Wk on bf16 MFMA
                 "route_fused stage1": dict(bytes=N * (512 * e + 5) + 2 * 512 * 512 * e,
-                                           flops=2 * N * 512 * 1024)}
+                                           flops=2 * N * 512 * 1024),
+                # every window: h read, Delta R written, the carried matrix read and written, the
+                # local selection; the same 3 T d^2 MFMA count as the whole-sequence coding rate
+                "streaming_chunker": dict(flops=3 * N * 512 * 512,
+                                          bytes=N * (512 * e + 4 + 4 + 1) + nseq * K * 4
+                                          + len(self.h4w) * nseq * 512 * 512 * 4 * 2)}
 
     def ops(self):
         return [("route+compact stage1", self._stage1), ("route+compact stage2", self._stage2),

@@ -6,7 +6,8 @@ stream) into it.  See ``byte_level_lm_amd.ops``.
 """
 from ._lib import lib, LIB_PATH, EXPORTS, BllmError  # noqa: F401
 from .ops import (  # noqa: F401
-    route, route_fused, compact, dechunk_ema, dechunk_ema_backward, coding_rate, topk_select, upsample_bins,
+    route, route_fused, compact, dechunk_ema, dechunk_ema_backward, coding_rate, coding_rate_stream, topk_select,
+    topk_select_window, upsample_bins,
     route_workspace, compact_workspace, dechunk_workspace, dechunk_ema_backward_workspace,
     coding_rate_workspace, upsample_workspace,
 )

@@ -37,7 +37,10 @@ _SIGS = {
     "bllm_coding_rate_workspace": (C.c_size_t, [_i64, _i64, _i64]),
     "bllm_coding_rate": (C.c_int, [_p, C.c_int, _i64, _i64, _i64, C.c_double, _p, _p, _p,
                                    C.c_size_t, _p]),
+    "bllm_coding_rate_stream": (C.c_int, [_p, C.c_int, _i64, _i64, _i64, C.c_double, _p, _p, _p, _p, _p,
+                                          C.c_size_t, _p]),
     "bllm_topk_select": (C.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
+    "bllm_topk_select_window": (C.c_int, [_p, _i64, _i64, _i64, C.c_int, _p, _p, _p, _p]),
     "bllm_upsample_workspace": (C.c_size_t, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "bllm_upsample_bins": (C.c_int, [_p, _p, _p, _p, C.c_int, _i64, _i64, _i64, _i64, _i64, _i64,
                                      _p, _p, C.c_size_t, _p]),

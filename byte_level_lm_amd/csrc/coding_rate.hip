@@ -26,6 +26,7 @@
 //                   X = acc L_kk^-T) and the next diagonal tile
 // Workspace: nmat = nseq * nblk matrices of ldm^2 fp32 (ldm = d' + c), plus a
 // 64x64 inverse slot per matrix.
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -135,11 +136,44 @@ __device__ inline floatx16 gram_chunk(const typename GramLds<DT>::T* sI, const t
   return acc;
 }
 
+// The carried prefix matrix of a stream (fp32 [d x d] per sequence, row
+// major), or the identity where there is none or past d: the entries
+// (r0 + crow(r), c0 + lane % 32) of one wave's 32x32 quadrant.
+__device__ inline void carried_tile(const float* sin, const CRGeom& g, int s, int r0, int c0, int lane,
+                                    float* s0) {
+  const int col = c0 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = r0 + crow(r, lane);
+    float v = row == col ? 1.f : 0.f;
+    if (sin && row < g.d && col < g.d)
+      v = sin[(static_cast<int64_t>(s) * g.d + row) * g.d + col];
+    s0[r] = v;
+  }
+}
+
+// The next window's carry: s0 + alpha * (Gram of every row of the window),
+// written to the quadrant and to its mirror image above the diagonal.
+__device__ inline void write_carry(float* sout, const CRGeom& g, int s, int r0, int c0, int lane,
+                                   const float* s0, const floatx16& acc, float alpha) {
+  if (!sout) return;
+  const int col = c0 + (lane & 31);
+  float* o = sout + static_cast<int64_t>(s) * g.d * g.d;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = r0 + crow(r, lane);
+    if (row >= g.d || col >= g.d) continue;
+    const float v = s0[r] + alpha * acc[r];
+    o[static_cast<int64_t>(row) * g.d + col] = v;
+    if (row / 64 != col / 64) o[static_cast<int64_t>(col) * g.d + row] = v;
+  }
+}
+
 // One 64x64 tile (I >= J) of A_j for all blocks j of one sequence; wave
 // (wm, wn) owns the 32x32 quadrant and keeps its running sum in registers.
 template <int DT>
 __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h, float* __restrict__ ws,
-                                                      CRGeom g, float alpha) {
+                                                      CRGeom g, float alpha, const float* sin, float* sout) {
   typedef typename GramLds<DT>::T E;
   constexpr int LD = GramLds<DT>::LD;
   __shared__ __attribute__((aligned(16))) E sI[64 * LD];
@@ -153,15 +187,21 @@ __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h
   const int wm = w >> 1, wn = w & 1;
   const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
   const int64_t hrow0 = static_cast<int64_t>(s) * g.T;
+  float s0[16];
+  carried_tile(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, s0);
   floatx16 acc = zero16();
-  for (int j = 0; j < g.nblk; ++j) {
+  for (int j = 0; j <= g.nblk; ++j) {
+    if (j == g.nblk) {
+      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, s0, acc, alpha);
+      break;
+    }
     float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
-      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
+      Mj[static_cast<int64_t>(row) * g.ldm + col] = s0[r] + alpha * acc[r];
     }
-    if (j == g.nblk - 1) break;
+    if (j == g.nblk - 1 && !sout) break;
     const int rbeg = j * g.c, rend = min(rbeg + g.c, g.T);
     for (int r0 = rbeg; r0 < rend; r0 += 32) {
       __syncthreads();
@@ -195,7 +235,8 @@ __device__ inline bf16x8 tr_frag(const uint16_t* s, int row, int col, int pitch)
 }
 
 __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __restrict__ h,
-                                                           float* __restrict__ ws, CRGeom g, float alpha) {
+                                                           float* __restrict__ ws, CRGeom g, float alpha,
+                                                           const float* sin, float* sout) {
   constexpr int GP = 72;  // LDS pitch (bf16) of a staged row: 64 features + 8 pad
   __shared__ __attribute__((aligned(16))) uint16_t sI[128 * GP];
   __shared__ __attribute__((aligned(16))) uint16_t sJ[128 * GP];
@@ -210,7 +251,7 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
   const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
   const int R = g.c % 128 == 0 ? 128 : 64;
   const int spb = g.c / R;                // sub-chunks per block
-  const int nq = (g.nblk - 1) * spb;      // sub-chunks that feed some prefix
+  const int nq = (g.nblk - (sout ? 0 : 1)) * spb;  // sub-chunks that feed some prefix or the carry
   const int lr = tid >> 3, lc = (tid & 7) * 8;  // rows lr + 32 q, features lc .. lc + 7
   const bool fiok = 64 * I + lc < g.d, fjok = 64 * J + lc < g.d;
   const uint16_t* hI = h + static_cast<int64_t>(s) * g.T * g.d + 64 * I + lc;
@@ -256,16 +297,22 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
     }
   };
+  float s0[16];
+  carried_tile(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, s0);
   if (nq > 0) fetch_a(0);
   int q = 0;
-  for (int j = 0; j < g.nblk; ++j) {
+  for (int j = 0; j <= g.nblk; ++j) {
+    if (j == g.nblk) {
+      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, s0, acc, alpha);
+      break;
+    }
     float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
-      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
+      Mj[static_cast<int64_t>(row) * g.ldm + col] = s0[r] + alpha * acc[r];
     }
-    if (j == g.nblk - 1) break;
+    if (j == g.nblk - 1 && !sout) break;
     for (int sq = 0; sq < spb; ++sq, ++q) {
       lds_barrier();
       stash(ai0, ai1, ai2, ai3, aj0, aj1, aj2, aj3);
@@ -454,8 +501,9 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
 //   cr_diag(k)   one wave per matrix factors the diagonal tile D_k (the Gram
 //                prefix for k = 0, else written by cr_panel(k-1)), stores
 //                Linv_k and, in the S part, the logs of the pivots
-//   cr_panel(k)  one workgroup per matrix builds every tile below the diagonal
-//                of panel k, in passes of kPassTiles tiles:
+//   cr_panel(k)  workgroups of each matrix build every tile below the diagonal
+//                of panel k, in passes of kPassTiles tiles (pp consecutive
+//                passes per workgroup; the passes are independent):
 //                  ACC_i = orig(i, k) -/+ sum_{cols < 64k} L[i, :] L[k, :]^T
 //                  L[i, k] = ACC_i Linv_k^T                            (TRSM)
 //                from row strips of L staged through LDS kChunk columns at a
@@ -530,14 +578,18 @@ __global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __r
 template <int DT>
 __global__ __launch_bounds__(256, 4) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
                                                    const float* __restrict__ linv, CRGeom g,
-                                                   float salpha, int k) {
+                                                   float salpha, int k, int pp) {
   __shared__ __attribute__((aligned(16))) float lds[kPanelFloats];
   float* sLi = lds + kStripFloats;      // Linv_k
   float* sX = lds;                      // X_{k+1} (over the strip buffers)
-  const int m = blockIdx.x;
+  const int m = blockIdx.x % g.nmat, grp = blockIdx.x / g.nmat;
   const int s = m / g.nblk, j = m % g.nblk;
   const int npan = block_n(g, j) / NB;
   if (k + 1 >= npan) return;
+  const int nt = npan - k - 1;
+  const int tbeg = grp * pp * kPassTiles, tend = min(nt, tbeg + pp * kPassTiles);
+  if (tbeg >= nt) return;
+  const bool look = grp == 0;  // this workgroup also builds the next diagonal tile
   const int cj = block_rows(g, j);
   const int64_t hrow0 = static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c;
   float* Mx = ws + static_cast<int64_t>(m) * g.ldm * g.ldm;
@@ -546,7 +598,6 @@ __global__ __launch_bounds__(256, 4) void cr_panel(const void* __restrict__ h, f
   const int dm = w >> 1, dn = w & 1;  // block of the lookahead tile
   const bool panelS = NB * k >= g.dp;
   const bool rowS1 = NB * (k + 1) >= g.dp;
-  const int nt = npan - k - 1;
   const int nch = NB * k / kChunk;
   {
     const float* Li = linv + static_cast<int64_t>(m) * NB * NB;
@@ -556,9 +607,10 @@ __global__ __launch_bounds__(256, 4) void cr_panel(const void* __restrict__ h, f
     }
   }
   // lookahead tile, symmetric: read orig transposed for row-contiguous loads
-  floatx16 accD = orig_tile_t<DT>(h, Mx, g, hrow0, cj, salpha, NB * (k + 1) + 32 * dn + l32,
-                                  NB * (k + 1) + 32 * dm, hh);
-  for (int t0 = 0; t0 < nt; t0 += kPassTiles) {
+  floatx16 accD = zero16();
+  if (look)
+    accD = orig_tile_t<DT>(h, Mx, g, hrow0, cj, salpha, NB * (k + 1) + 32 * dn + l32, NB * (k + 1) + 32 * dm, hh);
+  for (int t0 = tbeg; t0 < tend; t0 += kPassTiles) {
     const int npt = min(kPassTiles, nt - t0);
     const bool first = t0 == 0;
     floatx16 acc[kSlots][2];  // [slot][panel-column half]
@@ -723,6 +775,7 @@ __global__ __launch_bounds__(256, 4) void cr_panel(const void* __restrict__ h, f
     }
     __syncthreads();  // sX and the strip buffers are reused next
   }
+  if (!look) return;
   // D_{k+1} over the diagonal tile (k+1, k+1), whose original is consumed
   float* Dt = Mx + static_cast<int64_t>(NB * (k + 1) + 32 * dm) * g.ldm + NB * (k + 1) + 32 * dn;
 #pragma unroll
@@ -749,23 +802,41 @@ size_t cr_ws_bytes(const CRGeom& g) {
   return static_cast<size_t>(g.nmat) * (static_cast<size_t>(g.ldm) * g.ldm + NB * NB) * 4 + 256;
 }
 
+// Passes of one panel launch per workgroup: all of them (one workgroup per
+// matrix) when the matrices alone fill the chip, else split so that the
+// launch has about kPanelGroups workgroups.
+#ifndef BLLM_CR_PANEL_GROUPS
+#define BLLM_CR_PANEL_GROUPS 1024
+#endif
+constexpr int kPanelGroups = BLLM_CR_PANEL_GROUPS;
+int passes_per_group(int nmat, int npass) {
+  if (nmat >= kPanelGroups) return npass;
+  const int ngrp = std::min(npass, (kPanelGroups + nmat - 1) / nmat);
+  return (npass + ngrp - 1) / ngrp;
+}
+
 template <int DT>
 void cr_launch(const void* h, const CRGeom& g, int nseq, double alpha, float* dR, int32_t* status,
-               float* ws, hipStream_t st) {
+               float* ws, hipStream_t st, const float* sin, float* sout) {
   const int nt = g.dp / NB;
   const unsigned ggrid = static_cast<unsigned>((nseq + 7) / 8 * 8 * (nt * (nt + 1) / 2));
   if (DT == BLLM_BF16)
     hipLaunchKernelGGL(cr_gram_prefix_bf16, dim3(ggrid), dim3(256), 0, st, static_cast<const uint16_t*>(h), ws, g,
-                       static_cast<float>(alpha));
+                       static_cast<float>(alpha), sin, sout);
   else
-    hipLaunchKernelGGL(cr_gram_prefix<DT>, dim3(ggrid), dim3(256), 0, st, h, ws, g, static_cast<float>(alpha));
+    hipLaunchKernelGGL(cr_gram_prefix<DT>, dim3(ggrid), dim3(256), 0, st, h, ws, g, static_cast<float>(alpha), sin,
+                       sout);
   float* linv = ws + static_cast<int64_t>(g.nmat) * g.ldm * g.ldm;
   const int npan = g.ldm / NB;
   const float salpha = static_cast<float>(std::sqrt(alpha));
   for (int k = 0; k < npan; ++k) {
     hipLaunchKernelGGL(cr_diag, dim3(g.nmat), dim3(64), 0, st, ws, linv, dR, status, g, k);
-    if (k + 1 < npan)
-      hipLaunchKernelGGL(cr_panel<DT>, dim3(g.nmat), dim3(256), 0, st, h, ws, linv, g, salpha, k);
+    if (k + 1 < npan) {
+      const int npass = (npan - k - 1 + kPassTiles - 1) / kPassTiles;
+      const int pp = passes_per_group(g.nmat, npass);
+      const int ngrp = (npass + pp - 1) / pp;
+      hipLaunchKernelGGL(cr_panel<DT>, dim3(g.nmat * ngrp), dim3(256), 0, st, h, ws, linv, g, salpha, k, pp);
+    }
   }
 }
 
@@ -779,9 +850,9 @@ extern "C" size_t bllm_coding_rate_workspace(int64_t nseq, int64_t T, int64_t d)
   return cr_ws_bytes(cr_geometry(nseq, T, d));
 }
 
-extern "C" int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d,
-                                double eps2, float* dR_out, int32_t* status, void* ws,
-                                size_t ws_bytes, void* stream) {
+static int coding_rate_entry(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d, double eps2,
+                             const float* state_in, float* state_out, float* dR_out, int32_t* status,
+                             void* ws, size_t ws_bytes, void* stream) {
   if (!h || !dR_out || nseq < 1 || T < 1 || d < 1 || !(eps2 > 0.0)) return BLLM_E_INVAL;
   if (!valid_dtype(dtype)) return BLLM_E_NOTSUP;
   if (d > 640 || nseq > 65535 || T > (int64_t(1) << 24)) return BLLM_E_NOTSUP;
@@ -792,8 +863,22 @@ extern "C" int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t 
   const double alpha = static_cast<double>(d) / eps2;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == BLLM_F32)
-    cr_launch<BLLM_F32>(h, g, static_cast<int>(nseq), alpha, dR_out, status, static_cast<float*>(ws), st);
+    cr_launch<BLLM_F32>(h, g, static_cast<int>(nseq), alpha, dR_out, status, static_cast<float*>(ws), st, state_in,
+                        state_out);
   else
-    cr_launch<BLLM_BF16>(h, g, static_cast<int>(nseq), alpha, dR_out, status, static_cast<float*>(ws), st);
+    cr_launch<BLLM_BF16>(h, g, static_cast<int>(nseq), alpha, dR_out, status, static_cast<float*>(ws), st,
+                         state_in, state_out);
   return launch_status();
+}
+
+extern "C" int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d,
+                                double eps2, float* dR_out, int32_t* status, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return coding_rate_entry(h, dtype, nseq, T, d, eps2, nullptr, nullptr, dR_out, status, ws, ws_bytes, stream);
+}
+
+extern "C" int bllm_coding_rate_stream(const void* h, int dtype, int64_t nseq, int64_t W, int64_t d,
+                                       double eps2, const float* state_in, float* state_out, float* dR_out,
+                                       int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  return coding_rate_entry(h, dtype, nseq, W, d, eps2, state_in, state_out, dR_out, status, ws, ws_bytes, stream);
 }

@@ -5,6 +5,10 @@
 // the largest marginal coding rate among the rest are added; the set is
 // returned in time order.  A fixed K keeps every output the same size.
 //
+// A later window of a stream (the local Top-K of a streaming chunker, which
+// the paper page's weakness analysis suggests for autoregressive inference)
+// forces no position: its K largest scores are kept.
+//
 // One workgroup (1024 threads) per sequence.  Scores become order-preserving
 // uint32 keys in LDS (NaN -> 0, the lowest; -0 -> +0), an 8-bit radix select
 // finds the key of the (K-1)-th largest, ties at that key are resolved by time
@@ -54,7 +58,7 @@ __device__ inline int block_excl_scan1024(int v, int* sh, int* tot) {
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ score, int T,
-                                                            int K, int32_t* __restrict__ idx_out,
+                                                            int K, int bos, int32_t* __restrict__ idx_out,
                                                             uint8_t* __restrict__ mask_out,
                                                             int32_t* __restrict__ status) {
   extern __shared__ uint32_t keys[];  // [T]
@@ -64,21 +68,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const int s = blockIdx.x;
   const float* sc = score + static_cast<int64_t>(s) * T;
   bool nan = false;
-  for (int t = threadIdx.x; t < T; t += blockDim.x) keys[t] = t == 0 ? 0u : order_key(sc[t], &nan);
+  for (int t = threadIdx.x; t < T; t += blockDim.x) keys[t] = t == 0 && bos ? 0u : order_key(sc[t], &nan);
   if (nan && status) atomicOr(status, BLLM_S_NONFINITE);
   const int per = (T + kTopkThreads - 1) / kTopkThreads;
   const int t0 = threadIdx.x * per;
   const int t1 = min(t0 + per, T);
-  if (threadIdx.x == 0) { sel_prefix = 0; sel_want = static_cast<uint32_t>(K - 1); }
+  const int want0 = K - bos;  // positions chosen by score; 0 is forced when bos
+  if (threadIdx.x == 0) { sel_prefix = 0; sel_want = static_cast<uint32_t>(want0); }
   __syncthreads();
   uint32_t kth = 0xFFFFFFFFu, take_eq = 0;
-  if (K > 1) {
+  if (want0 > 0) {
     uint32_t mask = 0;
     for (int shift = 24; shift >= 0; shift -= 8) {
       for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
       __syncthreads();
       const uint32_t prefix = sel_prefix;
-      for (int t = max(t0, 1); t < t1; ++t) {
+      for (int t = max(t0, bos); t < t1; ++t) {
         const uint32_t k = keys[t];
         if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 0xFFu], 1u);
       }
@@ -117,15 +122,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
   // rank of each equal key in time order
   int neq = 0;
-  for (int t = max(t0, 1); t < t1; ++t) neq += keys[t] == kth;
+  for (int t = max(t0, bos); t < t1; ++t) neq += keys[t] == kth;
   int tot;
   int eq_rank = block_excl_scan1024(neq, scan_sh, &tot);
   int nsel = 0;
   uint32_t selbits = 0;  // per <= 32
   for (int t = t0; t < t1; ++t) {
     bool sel;
-    if (t == 0) sel = true;
-    else if (K <= 1) sel = false;
+    if (t == 0 && bos) sel = true;
+    else if (want0 <= 0) sel = false;
     else if (keys[t] > kth) sel = true;
     else if (keys[t] == kth) sel = static_cast<uint32_t>(eq_rank++) < take_eq;
     else sel = false;
@@ -145,14 +150,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 
 using namespace bllm;
 
-extern "C" int bllm_topk_select(const float* score, int64_t nseq, int64_t T, int64_t K,
-                                int32_t* idx_out, uint8_t* mask_out, int32_t* status,
-                                void* stream) {
+static int topk_entry(const float* score, int64_t nseq, int64_t T, int64_t K, int bos, int32_t* idx_out,
+                      uint8_t* mask_out, int32_t* status, void* stream) {
   if (!score || !idx_out || nseq < 1 || T < 1 || K < 1 || K > T) return BLLM_E_INVAL;
   if (T > 16384 || nseq > 0x7FFFFFFF) return BLLM_E_NOTSUP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t shmem = static_cast<size_t>(T) * 4;
   hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(nseq)), dim3(kTopkThreads), shmem, st,
-                     score, static_cast<int>(T), static_cast<int>(K), idx_out, mask_out, status);
+                     score, static_cast<int>(T), static_cast<int>(K), bos, idx_out, mask_out, status);
   return launch_status();
+}
+
+extern "C" int bllm_topk_select(const float* score, int64_t nseq, int64_t T, int64_t K,
+                                int32_t* idx_out, uint8_t* mask_out, int32_t* status,
+                                void* stream) {
+  return topk_entry(score, nseq, T, K, 1, idx_out, mask_out, status, stream);
+}
+
+extern "C" int bllm_topk_select_window(const float* score, int64_t nseq, int64_t W, int64_t K, int first,
+                                       int32_t* idx_out, uint8_t* mask_out, int32_t* status, void* stream) {
+  return topk_entry(score, nseq, W, K, first ? 1 : 0, idx_out, mask_out, status, stream);
 }

@@ -200,6 +200,31 @@ def coding_rate(h, eps2: float, *, dR_out=None, status=None, ws=None):
     return dR_out, status
 
 
+def coding_rate_stream(h, eps2: float, state_in=None, *, state_out=None, want_state=True, dR_out=None,
+                       status=None, ws=None):
+    """Delta R_t of one window h [nseq, W, d] of a stream, given the carried
+    prefix matrix state_in (fp32 [nseq, d, d]; None at the stream's start).
+    Returns (dR fp32 [nseq, W], state_out fp32 [nseq, d, d] or None, status);
+    state_out may be state_in itself (updated in place); want_state=False
+    skips the next carry."""
+    _dev(h)
+    nseq, W, d = h.shape
+    dev = h.device
+    dR_out = torch.empty((nseq, W), dtype=torch.float32, device=dev) if dR_out is None else dR_out
+    if not want_state:
+        state_out = None
+    elif state_out is None:
+        state_out = torch.empty((nseq, d, d), dtype=torch.float32, device=dev)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    w = _ws(coding_rate_workspace(nseq, W, d), ws, dev)
+    rc = L.lib().bllm_coding_rate_stream(h.data_ptr(), _dt(h), nseq, W, d, float(eps2), _ptr(state_in),
+                                         _ptr(state_out), dR_out.data_ptr(), status.data_ptr(),
+                                         w.data_ptr(), _nbytes(w), _stream())
+    L.check("bllm_coding_rate_stream", rc)
+    return dR_out, state_out, status
+
+
 def topk_select(score, K: int, *, idx_out=None, mask_out=None, status=None, want_mask=True):
     """BOS + Top-(K-1) positions per sequence in time order: (idx int32, mask uint8, status)."""
     _dev(score)
@@ -213,6 +238,23 @@ def topk_select(score, K: int, *, idx_out=None, mask_out=None, status=None, want
     rc = L.lib().bllm_topk_select(score.data_ptr(), nseq, T, int(K), idx_out.data_ptr(),
                                   _ptr(mask_out), status.data_ptr(), _stream())
     L.check("bllm_topk_select", rc)
+    return idx_out, mask_out, status
+
+
+def topk_select_window(score, K: int, first: bool, *, idx_out=None, mask_out=None, status=None, want_mask=True):
+    """Local Top-K of one window [nseq, W] of a stream: the first window as
+    ``topk_select`` (BOS + K-1), later windows their K largest scores."""
+    _dev(score)
+    nseq, W = score.shape
+    dev = score.device
+    idx_out = torch.empty((nseq, K), dtype=torch.int32, device=dev) if idx_out is None else idx_out
+    if want_mask and mask_out is None:
+        mask_out = torch.empty((nseq, W), dtype=torch.uint8, device=dev)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    rc = L.lib().bllm_topk_select_window(score.data_ptr(), nseq, W, int(K), 1 if first else 0, idx_out.data_ptr(),
+                                         _ptr(mask_out), status.data_ptr(), _stream())
+    L.check("bllm_topk_select_window", rc)
     return idx_out, mask_out, status
 
 

@@ -196,6 +196,28 @@ int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t T, int64_t 
                      float* dR_out, int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * bllm_coding_rate_stream -- the coding rate of one window of a byte stream
+ * (the streaming chunker that the [BF4] weakness analysis suggests for
+ * autoregressive inference: a sliding window with a local Top-K).  The
+ * chunker carries the prefix matrix A = I_d + alpha sum h h^T over every byte
+ * already seen; Delta R is causal, so each window's values equal the
+ * whole-sequence values of bllm_coding_rate (up to fp32 rounding).
+ *
+ * h         : [nseq x W x d] dtype, dense (the window's rows).
+ * state_in  : fp32 [nseq x d x d] row major, symmetric (entries on both
+ *             sides of the diagonal are read), or NULL at the stream's start
+ *             (A = I).  Device memory, caller-owned.
+ * state_out : fp32 [nseq x d x d] or NULL; receives state_in + alpha H^T H
+ *             over the window (full symmetric matrix).  May equal state_in
+ *             (updated in place); any other overlap is an error of the caller.
+ * dR_out, status, eps2, limits, errors : as bllm_coding_rate, with T = W.
+ * ws        : bllm_coding_rate_workspace(nseq, W, d) bytes.
+ */
+int bllm_coding_rate_stream(const void* h, int dtype, int64_t nseq, int64_t W, int64_t d, double eps2,
+                            const float* state_in, float* state_out, float* dR_out, int32_t* status,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
  * bllm_topk_select -- ByteFlow boundary set ([BF4] stage 2, [BF2] key design 2):
  *   S = {0} U {the K-1 largest score_t, t = 1..T-1}, in increasing time order.
  *   Ties go to the earlier position; NaN ranks below every number (and sets
@@ -206,6 +228,17 @@ int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t T, int64_t 
  */
 int bllm_topk_select(const float* score, int64_t nseq, int64_t T, int64_t K, int32_t* idx_out,
                      uint8_t* mask_out, int32_t* status, void* stream);
+
+/*
+ * bllm_topk_select_window -- the local Top-K of one window of a stream (the
+ * [BF4] weakness analysis: sliding window plus local Top-K at inference).
+ * first != 0 (the stream's first window): exactly bllm_topk_select.
+ * first == 0: the K largest scores of the window, no forced position.
+ * Ties, NaN, layouts, limits and errors as bllm_topk_select with T = W;
+ * idx_out holds positions inside the window.
+ */
+int bllm_topk_select_window(const float* score, int64_t nseq, int64_t W, int64_t K, int first,
+                            int32_t* idx_out, uint8_t* mask_out, int32_t* status, void* stream);
 
 /*
  * bllm_upsample_bins -- multi-linear reconstruction with the large residual

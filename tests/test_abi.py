@@ -74,6 +74,13 @@ def test_argument_errors_return_before_any_launch(L):
     assert L.bllm_topk_select(dummy, 1, 10, 11, dummy, None, None, None) == -1
     assert L.bllm_topk_select(dummy, 1, 10, 0, dummy, None, None, None) == -1
     assert L.bllm_topk_select(dummy, 1, 20000, 5, dummy, None, None, None) == -2
+    assert L.bllm_coding_rate_stream(dummy, 0, 1, 8, 8, 0.0, None, None, dummy, None, dummy, 1 << 30, None) == -1
+    assert L.bllm_coding_rate_stream(None, 0, 1, 8, 8, 0.5, dummy, dummy, dummy, None, dummy, 1 << 30, None) == -1
+    assert L.bllm_coding_rate_stream(dummy, 0, 1, 8, 1024, 0.5, None, dummy, dummy, None, dummy, 1 << 30, None) == -2
+    assert L.bllm_coding_rate_stream(dummy, 0, 1, 64, 8, 0.5, dummy, dummy, dummy, None, dummy, 16, None) == -3
+    assert L.bllm_topk_select_window(dummy, 1, 10, 11, 0, dummy, None, None, None) == -1
+    assert L.bllm_topk_select_window(dummy, 1, 10, 0, 1, dummy, None, None, None) == -1
+    assert L.bllm_topk_select_window(dummy, 1, 20000, 5, 0, dummy, None, None, None) == -2
     # upsample: fp32 unsupported, nbins < 1
     assert L.bllm_upsample_bins(dummy, dummy, dummy, dummy, 0, 1, 64, 4, 64, 32, 16, dummy, dummy, 1 << 30, None) == -2
     assert L.bllm_upsample_bins(dummy, dummy, dummy, dummy, 1, 1, 64, 4, 64, 32, 0, dummy, dummy, 1 << 30, None) == -1

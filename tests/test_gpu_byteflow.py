@@ -153,6 +153,123 @@ def test_coding_rate_full_size_bf16_32x8192x512_sampled(ops):
     assert len(bad) == 0, bad
 
 
+# ------------------------------------------------------------------ streaming chunker
+
+def _stream(ops, h, eps2, dtype, widths, inplace=False):
+    """h [nseq, T, d] through windows of the given widths on the GPU, the
+    carried matrix passed from window to window (updated in place if asked).
+    Returns (dR [nseq, T], final carried matrix)."""
+    nseq, T, d = h.shape
+    assert sum(widths) == T
+    out = np.empty((nseq, T), np.float32)
+    state = None
+    t = 0
+    for w in widths:
+        say("stream window", t, "+", w, "d", d, "inplace", inplace)
+        win = to_dev(np.ascontiguousarray(h[:, t:t + w]), dtype)
+        so = state if (inplace and state is not None) else None
+        dR, state, st = ops.coding_rate_stream(win, eps2, state, state_out=so)
+        assert int(to_np(st)[0]) == 0
+        out[:, t:t + w] = to_np(dR)
+        t += w
+    return out, to_np(state)
+
+
+def _oracle_stream(h, eps2, widths):
+    outs, A, t = [], None, 0
+    for w in widths:
+        dr, A = oracle.coding_rate_stream(h[:, t:t + w].astype(np.float64), eps2, A)
+        outs.append(dr)
+        t += w
+    return np.concatenate(outs, axis=1), A
+
+
+@pytest.mark.parametrize("dt,d,widths,inplace", [
+    ("f32", 40, (129, 1, 64, 70), False),
+    ("f32", 64, (300, 256, 145), True),
+    ("bf16", 128, (257, 3, 300), True),
+    ("bf16", 72, (1, 130), False),
+])
+def test_coding_rate_stream_vs_oracle(ops, dt, d, widths, inplace):
+    """Windows of ragged widths (a one-row window, widths off the block size,
+    d off the 64-wide tiles) against the oracle's streaming chunker: every
+    Delta R and the carried matrix after the last window."""
+    torch = _torch()
+    rng = np.random.default_rng(40 + d)
+    h = cluster_rows(rng, 2, sum(widths), d)
+    h = bf16_round(h) if dt == "bf16" else h.astype(np.float32)
+    g, A = _stream(ops, h, 0.5, torch.bfloat16 if dt == "bf16" else torch.float32, widths, inplace)
+    o, oA = _oracle_stream(h, 0.5, widths)
+    assert np.max(np.abs(g - o) / np.abs(o)) < 1e-3
+    assert np.max(np.abs(A - oA)) <= 1e-5 * np.max(np.abs(oA))
+    assert np.array_equal(A, np.transpose(A, (0, 2, 1)))
+
+
+def test_coding_rate_stream_state_out_optional(ops):
+    """state_out NULL: Delta R of a later window is still exact, and the
+    carried matrix passed in is left as it was."""
+    torch = _torch()
+    rng = np.random.default_rng(44)
+    h = cluster_rows(rng, 1, 200, 64).astype(np.float32)
+    _, A1 = oracle.coding_rate_stream(h[:, :120].astype(np.float64), 0.5)
+    st_in = to_dev(A1.astype(np.float32))
+    dR, none, st = ops.coding_rate_stream(to_dev(h[:, 120:], torch.float32), 0.5, st_in, want_state=False)
+    assert none is None
+    o, _ = oracle.coding_rate_stream(h[:, 120:].astype(np.float64), 0.5, A1.astype(np.float32))
+    assert int(to_np(st)[0]) == 0
+    assert np.max(np.abs(to_np(dR) - o) / np.abs(o)) < 1e-3
+    assert np.array_equal(to_np(st_in), A1.astype(np.float32))
+
+
+def test_topk_window_first_and_later_bitexact(ops):
+    rng = np.random.default_rng(45)
+    for W in (1, 2, 5, 1023, 1025, 3000):
+        sc = rng.integers(0, 5, size=(2, W)).astype(np.float32)
+        sc[0, ::9] = -0.0
+        sc[1, ::5] = -np.inf
+        for K in sorted({1, min(W, 2), max(1, W // 4), W}):
+            for first in (True, False):
+                idx, mask, _ = ops.topk_select_window(to_dev(sc), K, first)
+                want = oracle.topk_select_window(sc, K, first)
+                assert np.array_equal(to_np(idx), want), (W, K, first)
+                assert np.array_equal(to_np(mask), oracle.topk_mask(want, W))
+    sc = rng.standard_normal((1, 64)).astype(np.float32)
+    sc[0, 0] = np.nan
+    idx, _, st = ops.topk_select_window(to_dev(sc), 10, False)
+    assert np.array_equal(to_np(idx), oracle.topk_select_window(sc, 10, False))
+    assert 0 not in set(to_np(idx)[0].tolist()) and int(to_np(st)[0]) & 2
+
+
+def test_streaming_chunker_full_size_bf16_32x8192x512_windows_1024(ops):
+    """The 32 x 8192 x 512 bf16 workload streamed in windows of 1024 bytes
+    with the carried matrix updated in place: sampled Delta R against the
+    oracle's whole-sequence values (equal to the streamed ones by the
+    oracle's own pin), window edges included; the streamed values against
+    the whole-sequence kernel; the local Top-256 of every window equal to
+    the oracle's selection on the device scores; the final carried matrix
+    of one sequence against I + alpha H^T H in fp64."""
+    torch = _torch()
+    c = gen_byteflow_layer()
+    W, Kw = 1024, 256
+    g, A = _stream(ops, c["h"], c["eps2"], torch.bfloat16, (W,) * (c["T"] // W), inplace=True)
+    rng = np.random.default_rng(46)
+    for s in (0, 13, 31):
+        pos = np.sort(np.concatenate([[1023, 1024, 4096, 8191], rng.choice(c["T"], 4, replace=False)]))
+        o = oracle.coding_rate_at(c["h"][s], c["eps2"], pos)
+        assert np.max(np.abs(g[s, pos] - o) / np.abs(o)) < 1e-3, s
+    whole, st = _dr(ops, c["h"], c["eps2"], torch.bfloat16)
+    assert st == 0
+    assert np.max(np.abs(g - whole) / np.abs(whole)) < 1e-3
+    for wi in range(c["T"] // W):
+        sc = np.ascontiguousarray(g[:, wi * W:(wi + 1) * W])
+        idx, _, _ = ops.topk_select_window(to_dev(sc), Kw, wi == 0)
+        assert np.array_equal(to_np(idx), oracle.topk_select_window(sc, Kw, wi == 0)), wi
+    h0 = c["h"][5].astype(np.float64)
+    d = h0.shape[1]
+    want = np.eye(d) + oracle.alpha_of(d, c["eps2"]) * h0.T @ h0
+    assert np.max(np.abs(A[5] - want)) <= 1e-5 * np.max(np.abs(want))
+
+
 # ------------------------------------------------------------------ gather + upsample
 
 def test_gather_via_compact_on_topk_mask(ops):
