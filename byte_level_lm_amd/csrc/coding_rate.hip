@@ -21,9 +21,11 @@
 //   for each panel k:
 //     cr_diag       one wave per matrix factors the 64x64 diagonal tile (k, k),
 //                   writes the S-part pivots' logs and the inverse of the factor
-//     cr_panel      one workgroup per matrix: every tile below the diagonal of
-//                   panel k (left-looking update over the earlier panels, then
-//                   X = acc L_kk^-T) and the next diagonal tile
+//     cr_panel      every tile below the diagonal of panel k, two tiles per
+//                   workgroup (left-looking update over the earlier panels on
+//                   bf16 MFMA with three-part splits, then X = acc L_kk^-T on
+//                   fp32 MFMA); the first workgroup also builds the next
+//                   diagonal tile
 // Workspace: nmat = nseq * nblk matrices of ldm^2 fp32 (ldm = d' + c), plus a
 // 64x64 inverse slot per matrix.
 #include <algorithm>
@@ -516,16 +518,72 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
 // tile is exactly the B element that lane supplies.
 constexpr int kChunk = 16;                      // columns per staged strip chunk
 constexpr int kWaitVmcnt0 = 0x0F70;             // s_waitcnt vmcnt(0), other counters unconstrained
-constexpr int kSP = 20;                         // LDS row pitch of a strip chunk (floats)
+constexpr int kSRow = 56;                       // LDS row of a strip chunk: 3 x 16 bf16 parts + 8 pad
 constexpr int kPassTiles = 2;                   // tiles below the diagonal per pass
 constexpr int kSlots = kPassTiles / 2;          // pass tiles per wave
 constexpr int kStripRows = 64 * (kPassTiles + 1);
 constexpr int kXP = 68;                         // LDS row pitch of 64x64 tiles
 // one strip stage, also large enough for the staged X_{k+1} tile
-constexpr int kStripFloats = kStripRows * kSP > 64 * kXP ? kStripRows * kSP : 64 * kXP;
+constexpr int kStripFloats = kStripRows * kSRow / 2 > 64 * kXP ? kStripRows * kSRow / 2 : 64 * kXP;
 constexpr int kPanelFloats = kStripFloats + 64 * kXP;
 static_assert(64 * kXP <= kStripFloats, "X staging must fit in the strip buffers");
 static_assert(kPassTiles == 2, "the strip loader below issues kPassTiles + 1 = 3 loads per set");
+
+// Strip products on bf16 MFMA: an fp32 value x is the exact sum of three
+// bf16 parts, x = hi + mid + lo (hi = x with its low 16 bits cleared, mid the
+// same of x - hi, lo = x - hi - mid, which has at most 8 significant bits).
+// A product takes the six part products down to 2^-24 of |x y| (hi hi, hi mid,
+// mid hi, hi lo, lo hi, mid mid), each exact in the fp32 accumulator, so the
+// sums keep fp32 accuracy at 6 x 32 instead of 8 x 64 MFMA cycles per 16 columns.
+// LDS strip row (kSRow bf16): [hi 0..15][mid 0..15][lo 0..15][pad 8].
+__device__ inline void stash_split(uint16_t* dst, const float4& v) {
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h = __float_as_uint(x[e]) & 0xFFFF0000u;
+    const float r = x[e] - __uint_as_float(h);
+    const uint32_t m = __float_as_uint(r) & 0xFFFF0000u;
+    hw[e] = h;
+    mw[e] = m;
+    lw[e] = __float_as_uint(r - __uint_as_float(m));
+  }
+  // perm(s0, s1, sel): result low half = high half of s1, result high half = high half of s0
+  const uint32_t sel = 0x07060302u;
+  *reinterpret_cast<uint2*>(dst) =
+      make_uint2(__builtin_amdgcn_perm(hw[1], hw[0], sel), __builtin_amdgcn_perm(hw[3], hw[2], sel));
+  *reinterpret_cast<uint2*>(dst + 16) =
+      make_uint2(__builtin_amdgcn_perm(mw[1], mw[0], sel), __builtin_amdgcn_perm(mw[3], mw[2], sel));
+  *reinterpret_cast<uint2*>(dst + 32) =
+      make_uint2(__builtin_amdgcn_perm(lw[1], lw[0], sel), __builtin_amdgcn_perm(lw[3], lw[2], sel));
+}
+
+// part p of the 8 columns 8 hh .. 8 hh + 7 of staged row r (16-byte LDS read)
+__device__ inline uint4 frag(const uint16_t* sb, int r, int p, int hh) {
+  return *reinterpret_cast<const uint4*>(sb + r * kSRow + 16 * p + 8 * hh);
+}
+
+__device__ inline uint4 xor4(uint4 v, uint32_t m) {
+  v.x ^= m; v.y ^= m; v.z ^= m; v.w ^= m;
+  return v;
+}
+
+__device__ inline floatx16 mfma_bf(const uint4& a, const uint4& b, const floatx16& c) {
+  bf16x8 x, y;
+  __builtin_memcpy(&x, &a, 16);
+  __builtin_memcpy(&y, &b, 16);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+}
+
+// sum over 16 columns of a[m][k] b[n][k] from the parts of both operands
+__device__ inline floatx16 mfma_split(const uint4* a, const uint4* b, floatx16 c) {
+  c = mfma_bf(a[1], b[1], c);
+  c = mfma_bf(a[0], b[2], c);
+  c = mfma_bf(a[2], b[0], c);
+  c = mfma_bf(a[0], b[1], c);
+  c = mfma_bf(a[1], b[0], c);
+  return mfma_bf(a[0], b[0], c);
+}
 
 // elements (row, col .. col+3), col % 4 == 0; a group lies wholly in one part
 template <int DT>
@@ -576,13 +634,18 @@ __global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __r
 }
 
 template <int DT>
-__global__ __launch_bounds__(256, 4) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
+__global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
                                                    const float* __restrict__ linv, CRGeom g,
                                                    float salpha, int k, int pp) {
   __shared__ __attribute__((aligned(16))) float lds[kPanelFloats];
   float* sLi = lds + kStripFloats;      // Linv_k
   float* sX = lds;                      // X_{k+1} (over the strip buffers)
-  const int m = blockIdx.x % g.nmat, grp = blockIdx.x / g.nmat;
+  uint16_t* sst = reinterpret_cast<uint16_t*>(lds);  // staged strip chunk, split into bf16 parts
+  // the workgroups of one matrix are consecutive on one XCD (block b runs on XCD b % 8)
+  const int ngrp = (g.ldm / NB - k - 1 + kPassTiles * pp - 1) / (kPassTiles * pp);
+  const int bq = blockIdx.x >> 3, grp = bq % ngrp;
+  const int m = (bq / ngrp) * 8 + (blockIdx.x & 7);
+  if (m >= g.nmat) return;
   const int s = m / g.nblk, j = m % g.nblk;
   const int npan = block_n(g, j) / NB;
   if (k + 1 >= npan) return;
@@ -648,45 +711,40 @@ __global__ __launch_bounds__(256, 4) void cr_panel(const void* __restrict__ h, f
       const int co = ch * kChunk;
       qb0 = ldq(0, co); qb1 = ldq(1, co); qb2 = ldq(2, co);
     };
-    auto stash = [&](float* sb, const float4& v0, const float4& v1, const float4& v2) {
-      *reinterpret_cast<float4*>(sb + lr * kSP + lc) = v0;
-      *reinterpret_cast<float4*>(sb + (lr + 64) * kSP + lc) = v1;
-      *reinterpret_cast<float4*>(sb + (lr + 128) * kSP + lc) = v2;
+    auto stash = [&](uint16_t* sb, const float4& v0, const float4& v1, const float4& v2) {
+      stash_split(sb + lr * kSRow + lc, v0);
+      stash_split(sb + (lr + 64) * kSRow + lc, v1);
+      stash_split(sb + (lr + 128) * kSRow + lc, v2);
     };
-    auto compute = [&](const float* sb, int ch) {
+    auto compute = [&](const uint16_t* sb, int ch) {
       const bool chA = ch * kChunk < g.dp;
-      const float sg = (panelS && chA) ? 1.f : -1.f;
-      float a0[8], a1[8];
-      ld4(sb + l32 * kSP + 8 * hh, a0);
-      ld4(sb + l32 * kSP + 8 * hh + 4, a0 + 4);
-      ld4(sb + (32 + l32) * kSP + 8 * hh, a1);
-      ld4(sb + (32 + l32) * kSP + 8 * hh + 4, a1 + 4);
+      const uint32_t sg = (panelS && chA) ? 0u : 0x80008000u;  // sign flip of the panel rows
+      uint4 a0[3], a1[3];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { a0[e] *= sg; a1[e] *= sg; }
+      for (int p = 0; p < 3; ++p) {
+        a0[p] = xor4(frag(sb, l32, p, hh), sg);
+        a1[p] = xor4(frag(sb, 32 + l32, p, hh), sg);
+      }
 #pragma unroll
       for (int sl = 0; sl < kSlots; ++sl) {
         const int u = wp + 2 * sl;
         if (u < npt) {
-          float b[8];
-          const float* pb = sb + (NB + NB * u + 32 * wn + l32) * kSP + 8 * hh;
-          ld4(pb, b);
-          ld4(pb + 4, b + 4);
+          uint4 b[3];
 #pragma unroll
-          for (int st = 0; st < 8; ++st) {
-            acc[sl][0] = mfma32(a0[st], b[st], acc[sl][0]);
-            acc[sl][1] = mfma32(a1[st], b[st], acc[sl][1]);
-          }
+          for (int p = 0; p < 3; ++p) b[p] = frag(sb, NB + NB * u + 32 * wn + l32, p, hh);
+          acc[sl][0] = mfma_split(a0, b, acc[sl][0]);
+          acc[sl][1] = mfma_split(a1, b, acc[sl][1]);
         }
       }
       if (first) {
-        const float sd = (rowS1 && chA) ? 1.f : -1.f;
-        float da[8], db[8];
-        ld4(sb + (NB + 32 * dm + l32) * kSP + 8 * hh, da);
-        ld4(sb + (NB + 32 * dm + l32) * kSP + 8 * hh + 4, da + 4);
-        ld4(sb + (NB + 32 * dn + l32) * kSP + 8 * hh, db);
-        ld4(sb + (NB + 32 * dn + l32) * kSP + 8 * hh + 4, db + 4);
+        const uint32_t sd = (rowS1 && chA) ? 0u : 0x80008000u;
+        uint4 da[3], db[3];
 #pragma unroll
-        for (int st = 0; st < 8; ++st) accD = mfma32(sd * da[st], db[st], accD);
+        for (int p = 0; p < 3; ++p) {
+          da[p] = xor4(frag(sb, NB + 32 * dm + l32, p, hh), sd);
+          db[p] = frag(sb, NB + 32 * dn + l32, p, hh);
+        }
+        accD = mfma_split(da, db, accD);
       }
     };
     // the accumulators were loaded from memory: wait here once, so that the
@@ -700,16 +758,16 @@ __global__ __launch_bounds__(256, 4) void cr_panel(const void* __restrict__ h, f
     // flight across them)
     for (int ch = 0; ch < nch; ch += 2) {
       lds_barrier();
-      stash(lds, qa0, qa1, qa2);
+      stash(sst, qa0, qa1, qa2);
       lds_barrier();
       fetch_a(ch + 2);
-      compute(lds, ch);
+      compute(sst, ch);
       if (ch + 1 < nch) {
         lds_barrier();
-        stash(lds, qb0, qb1, qb2);
+        stash(sst, qb0, qb1, qb2);
         lds_barrier();
         fetch_b(ch + 3);
-        compute(lds, ch + 1);
+        compute(sst, ch + 1);
       }
     }
     __syncthreads();  // strip buffers free (sX lives there); sLi staged
@@ -802,16 +860,15 @@ size_t cr_ws_bytes(const CRGeom& g) {
   return static_cast<size_t>(g.nmat) * (static_cast<size_t>(g.ldm) * g.ldm + NB * NB) * 4 + 256;
 }
 
-// Passes of one panel launch per workgroup: all of them (one workgroup per
-// matrix) when the matrices alone fill the chip, else split so that the
-// launch has about kPanelGroups workgroups.
+// Passes of one panel launch per workgroup: one (a workgroup per pass, the
+// passes of a matrix consecutive on one XCD so that they share the panel
+// rows in its L2) unless the launch would exceed kPanelGroups workgroups.
 #ifndef BLLM_CR_PANEL_GROUPS
-#define BLLM_CR_PANEL_GROUPS 1024
+#define BLLM_CR_PANEL_GROUPS (1 << 20)
 #endif
 constexpr int kPanelGroups = BLLM_CR_PANEL_GROUPS;
 int passes_per_group(int nmat, int npass) {
-  if (nmat >= kPanelGroups) return npass;
-  const int ngrp = std::min(npass, (kPanelGroups + nmat - 1) / nmat);
+  const int ngrp = std::max(1, std::min(npass, kPanelGroups / std::max(nmat, 1)));
   return (npass + ngrp - 1) / ngrp;
 }
 
@@ -835,7 +892,8 @@ void cr_launch(const void* h, const CRGeom& g, int nseq, double alpha, float* dR
       const int npass = (npan - k - 1 + kPassTiles - 1) / kPassTiles;
       const int pp = passes_per_group(g.nmat, npass);
       const int ngrp = (npass + pp - 1) / pp;
-      hipLaunchKernelGGL(cr_panel<DT>, dim3(g.nmat * ngrp), dim3(256), 0, st, h, ws, linv, g, salpha, k, pp);
+      hipLaunchKernelGGL(cr_panel<DT>, dim3((g.nmat + 7) / 8 * 8 * ngrp), dim3(256), 0, st, h, ws, linv, g, salpha, k,
+                         pp);
     }
   }
 }
