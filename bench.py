@@ -450,7 +450,8 @@ def main():
         breakdown[name] = d
     cr = alg["coding_rate"]
     roof = {
-        "kernel": "one bllm_coding_rate call: cr_gram_prefix_bf16 + 12 cr_diag + 11 cr_panel, fp32 MFMA",
+        "kernel": ("one bllm_coding_rate call: cr_gram_prefix_bf16 + 12 cr_diag + 11 cr_panel; fp32 arithmetic "
+                   "(strip products as exact three-part bf16 MFMA, diagonal and TRSM on fp32 MFMA)"),
         "bound": "mfma",
         "achieved": round(cr["flops"] / (dom_ms * 1e-3) / 1e12, 3),
         "peak": FP32_MFMA_PEAK_TFLOPS,

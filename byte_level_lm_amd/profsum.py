@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--copy-fetch")
     ap.add_argument("--copy-write")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--last", type=int, default=0,
+                    help="summarise the last N calls (the profiled steps); default: all but the first")
     ap.add_argument("--cmd", required=True, help="the full commands that produced the runs")
     ap.add_argument("--workload", required=True)
     ap.add_argument("--out", required=True)
@@ -136,7 +138,10 @@ def main():
         return
 
     calls = trace_calls(a.op, a.trace)
-    timed = calls[1:] if len(calls) > 1 else calls  # the first call is bench.py's set-up pass
+    if a.last > 0:
+        timed = calls[-a.last:]  # bench.py's set-up may call the op's kernels more than once
+    else:
+        timed = calls[1:] if len(calls) > 1 else calls  # the first call is bench.py's set-up pass
     per_kernel = {}
     for c in timed:
         for r in c:
@@ -147,7 +152,7 @@ def main():
 
     lines = [f"# rocprofv3 summary: {a.op}, {a.workload}", "", "Commands (run from the repository root on the GPU host):", "",
              "```", a.cmd, "```", "",
-             f"Calls profiled: {len(timed)} (after the set-up call).  Kernel time per call "
+             f"Calls profiled: {len(timed)} (the last ones of the run).  Kernel time per call "
              f"(sum of its kernels): {statistics.mean(call_ns) / 1e3:.1f} us; first-to-last span "
              f"{statistics.mean(span_ns) / 1e3:.1f} us.", "",
              "| kernel | launches per call | avg us | total us per call |", "|---|---|---|---|"]
