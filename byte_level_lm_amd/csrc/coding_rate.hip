@@ -335,8 +335,9 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
 //   2. D22 - L21 L21^T, eliminate columns 32..63  -> L22 (lanes 32..63)
 //   3. columns of L11^-1 (lanes 0..31) and L22^-1 (lanes 32..63) by forward
 //      substitution that pushes each solved entry into the later ones
-//   4. Y = -L22^-1 (L21 L11^-1) as two plain products:
+//   4. Y = -L22^-1 (L21 L11^-1) as two products on fp32 MFMA:
 //      Linv = [[L11^-1, 0], [Y, L22^-1]]
+// (step 2's product L21 L21^T also runs on fp32 MFMA)
 // Each elimination step broadcasts the pivot with one readlane and the scaled
 // column through LDS; lanes above the diagonal also run the updates, on
 // entries of the upper triangle that are never read.  Reciprocal square roots
@@ -396,17 +397,26 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
   float b[32];
 #pragma unroll
   for (int q = 0; q < 32; q += 4) ld4(D + i * ldd + 32 + q, b + q);
-  if (hi) {
+  {
+    // L21 L21^T on fp32 MFMA (32x32x2: in step st lane l supplies column
+    // 2 st + l / 32 of row l % 32 as both operands), rows back through sT22
+    floatx16 c = zero16();
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      float rw[32];
-#pragma unroll
-      for (int p = 0; p < 32; p += 4) ld4(sL + (32 + q) * kF + p, rw + p);
-      float acc = b[q];
-#pragma unroll
-      for (int p = 0; p < 32; ++p) acc = fmaf(-a[p], rw[p], acc);
-      b[q] = acc;
+    for (int st = 0; st < 16; ++st) {
+      const float v = sL[(32 + ih) * kF + 2 * st + (i >> 5)];
+      c = mfma32(v, v, c);
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT22[crow(r, i) * kF + ih] = c[r];
+    wave_lds_sync();
+    if (hi) {
+      float cr[32];
+#pragma unroll
+      for (int q = 0; q < 32; q += 4) ld4(sT22 + ih * kF + q, cr + q);
+#pragma unroll
+      for (int q = 0; q < 32; ++q) b[q] -= cr[q];
+    }
+    wave_lds_sync();
   }
 #pragma unroll
   for (int jj = 0; jj < 32; ++jj) {
@@ -466,30 +476,22 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
     }
   }
   wave_lds_sync();
-  if (hi) {
-    // 4. lane 32+c: column c of Z = L21 L11^-1, then of Y = -L22^-1 Z
+  {
+    // 4. Z = L21 L11^-1 and Y = -L22^-1 Z on fp32 MFMA; Z goes row-major over
+    // the rows of L11 in sL (no longer read), Y to the lower left block of Li
+    floatx16 z = zero16();
 #pragma unroll
-    for (int p = 0; p < 32; ++p) cv[p] = sT11[p * kF + ih];
+    for (int st = 0; st < 16; ++st)
+      z = mfma32(sL[(32 + ih) * kF + 2 * st + (i >> 5)], sT11[(2 * st + (i >> 5)) * kF + ih], z);
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      float rw[32];
+    for (int r = 0; r < 16; ++r) sL[crow(r, i) * kF + ih] = z[r];
+    wave_lds_sync();
+    floatx16 y = zero16();
 #pragma unroll
-      for (int p = 0; p < 32; p += 4) ld4(sL + (32 + q) * kF + p, rw + p);
-      float acc = 0.f;
+    for (int st = 0; st < 16; ++st)
+      y = mfma32(sT22[ih * kF + 2 * st + (i >> 5)], sL[(2 * st + (i >> 5)) * kF + ih], y);
 #pragma unroll
-      for (int p = 0; p < 32; ++p) acc = fmaf(rw[p], cv[p], acc);
-      x[q] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      float rw[32];
-#pragma unroll
-      for (int q = 0; q < 32; q += 4) ld4(sT22 + r * kF + q, rw + q);
-      float acc = 0.f;
-#pragma unroll
-      for (int q = 0; q < 32; ++q) acc = fmaf(rw[q], x[q], acc);
-      Li[(32 + r) * lip + ih] = -acc;
-    }
+    for (int r = 0; r < 16; ++r) Li[(32 + crow(r, i)) * lip + ih] = -y[r];
   }
   if (dR_blk != nullptr) {
     const int rr = rr0 + i;  // row of the block (S part)
