@@ -138,26 +138,30 @@ __device__ inline floatx16 gram_chunk(const typename GramLds<DT>::T* sI, const t
   return acc;
 }
 
-// The carried prefix matrix of a stream (fp32 [d x d] per sequence, row
-// major), or the identity where there is none or past d: the entries
-// (r0 + crow(r), c0 + lane % 32) of one wave's 32x32 quadrant.
-__device__ inline void carried_tile(const float* sin, const CRGeom& g, int s, int r0, int c0, int lane,
-                                    float* s0) {
+// The carried prefix matrix S of a stream (fp32 [d x d] per sequence, row
+// major) enters as the accumulator's start, (S - I) / alpha, so that
+// I + alpha acc is S before the window's first row (zero where there is no
+// carry and past d): the entries (r0 + crow(r), c0 + lane % 32) of one
+// wave's 32x32 quadrant.
+__device__ inline floatx16 carried_acc(const float* sin, const CRGeom& g, int s, int r0, int c0, int lane,
+                                       float alpha) {
+  floatx16 a = zero16();
+  if (!sin) return a;
   const int col = c0 + (lane & 31);
+  const float inv = 1.f / alpha;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = r0 + crow(r, lane);
-    float v = row == col ? 1.f : 0.f;
-    if (sin && row < g.d && col < g.d)
-      v = sin[(static_cast<int64_t>(s) * g.d + row) * g.d + col];
-    s0[r] = v;
+    if (row < g.d && col < g.d)
+      a[r] = (sin[(static_cast<int64_t>(s) * g.d + row) * g.d + col] - (row == col ? 1.f : 0.f)) * inv;
   }
+  return a;
 }
 
-// The next window's carry: s0 + alpha * (Gram of every row of the window),
+// The next window's carry, I + alpha acc after the window's last row,
 // written to the quadrant and to its mirror image above the diagonal.
 __device__ inline void write_carry(float* sout, const CRGeom& g, int s, int r0, int c0, int lane,
-                                   const float* s0, const floatx16& acc, float alpha) {
+                                   const floatx16& acc, float alpha) {
   if (!sout) return;
   const int col = c0 + (lane & 31);
   float* o = sout + static_cast<int64_t>(s) * g.d * g.d;
@@ -165,7 +169,7 @@ __device__ inline void write_carry(float* sout, const CRGeom& g, int s, int r0, 
   for (int r = 0; r < 16; ++r) {
     const int row = r0 + crow(r, lane);
     if (row >= g.d || col >= g.d) continue;
-    const float v = s0[r] + alpha * acc[r];
+    const float v = (row == col ? 1.f : 0.f) + alpha * acc[r];
     o[static_cast<int64_t>(row) * g.d + col] = v;
     if (row / 64 != col / 64) o[static_cast<int64_t>(col) * g.d + row] = v;
   }
@@ -189,19 +193,17 @@ __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h
   const int wm = w >> 1, wn = w & 1;
   const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
   const int64_t hrow0 = static_cast<int64_t>(s) * g.T;
-  float s0[16];
-  carried_tile(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, s0);
-  floatx16 acc = zero16();
+  floatx16 acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
   for (int j = 0; j <= g.nblk; ++j) {
     if (j == g.nblk) {
-      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, s0, acc, alpha);
+      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
       break;
     }
     float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
-      Mj[static_cast<int64_t>(row) * g.ldm + col] = s0[r] + alpha * acc[r];
+      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
     }
     if (j == g.nblk - 1 && !sout) break;
     const int rbeg = j * g.c, rend = min(rbeg + g.c, g.T);
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       *reinterpret_cast<uint4*>(sJ + (lr + 96) * GP + lc) = y3;
     }
   };
-  floatx16 acc = zero16();
+  floatx16 acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
   const uint16_t* sJr = same ? sI : sJ;
   const int j16 = lane & 15;
   const int frow = 8 * (lane >> 5) + (j16 >> 2);                  // + k0
@@ -299,20 +301,18 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
     }
   };
-  float s0[16];
-  carried_tile(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, s0);
   if (nq > 0) fetch_a(0);
   int q = 0;
   for (int j = 0; j <= g.nblk; ++j) {
     if (j == g.nblk) {
-      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, s0, acc, alpha);
+      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
       break;
     }
     float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
-      Mj[static_cast<int64_t>(row) * g.ldm + col] = s0[r] + alpha * acc[r];
+      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
     }
     if (j == g.nblk - 1 && !sout) break;
     for (int sq = 0; sq < spb; ++sq, ++q) {
