@@ -248,7 +248,7 @@ class Workload:
                                            flops=2 * N * 512 * 1024),
                 # every window: h read, Delta R written, the carried matrix read and written, the
                 # local selection; the same 3 T d^2 MFMA count as the whole-sequence coding rate
-                "streaming_chunker": dict(flops=3 * N * 512 * 512,
+                "streaming_chunker": dict(flops=3 * N * 512 * 512, peak_tflops=FP32_MFMA_PEAK_TFLOPS,
                                           bytes=N * (512 * e + 4 + 4 + 1) + nseq * K * 4
                                           + len(self.h4w) * nseq * 512 * 512 * 4 * 2)}
 
@@ -279,7 +279,8 @@ class Workload:
             "route+compact stage2": dict(bytes=M1 * (2 * 768 * e + 4 + 1) + M1 + M2 * (4 + 4 + 4 + 2 * 768 * e)),
             "dechunk stage2": dict(bytes=M2 * (768 * e + 8) + M1 * 768 * e),
             "dechunk stage1": dict(bytes=M1 * (512 * e + 8) + N * 512 * e),
-            "coding_rate": dict(flops=3 * T * 512 * 512 * nseq, bytes=N * 512 * e + N * 4),
+            "coding_rate": dict(flops=3 * T * 512 * 512 * nseq, bytes=N * 512 * e + N * 4,
+                                peak_tflops=FP32_MFMA_PEAK_TFLOPS),
             "topk_select": dict(bytes=N * 4 + N + nseq * K * 4),
             "gather": dict(bytes=N + nseq * K * (4 + 2 * 512 * e)),
             "upsample_bins": dict(flops=2 * 1536 * 512 * items, bytes=2 * N * 512 * e + nseq * K * 1536 * e),
@@ -300,6 +301,23 @@ def coding_rate_traffic():
     if block.get("sources_sha256") != sources_sha256("coding_rate") or "hbm_bytes_per_call" not in block:
         return None
     return block["hbm_bytes_per_call"]
+
+
+def op_rates(a, t):
+    """Time of one op with its algorithmic HBM rate and MFMA rate, each also as
+    a fraction of MI355X's peak (8 TB/s; dense MFMA of the op's arithmetic type)."""
+    d = {"ms": round(t, 4)}
+    if "bytes" in a:
+        gbps = a["bytes"] / (t * 1e-3) / 1e9
+        d["hbm_GBps"] = round(gbps, 1)
+        d["hbm_frac"] = round(gbps / HBM_PEAK_GBS, 4)
+    if "flops" in a:
+        tf = a["flops"] / (t * 1e-3) / 1e12
+        peak = a.get("peak_tflops", BF16_MFMA_PEAK_TFLOPS)
+        d["TFLOPs"] = round(tf, 2)
+        d["mfma_frac"] = round(tf / peak, 4)
+        d["mfma_peak"] = peak
+    return d
 
 
 def time_ops(wl, reps=5, ops=None):
@@ -439,15 +457,7 @@ def main():
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f}s)")
     per_op = time_ops(wl)
     alg = wl.algorithmic()
-    breakdown = {}
-    for name, t in per_op.items():
-        a = alg[name]
-        d = {"ms": round(t, 4)}
-        if "bytes" in a:
-            d["hbm_GBps"] = round(a["bytes"] / (t * 1e-3) / 1e9, 1)
-        if "flops" in a:
-            d["TFLOPs"] = round(a["flops"] / (t * 1e-3) / 1e12, 2)
-        breakdown[name] = d
+    breakdown = {name: op_rates(alg[name], t) for name, t in per_op.items()}
     cr = alg["coding_rate"]
     roof = {
         "kernel": ("one bllm_coding_rate call: cr_gram_prefix_bf16 + 12 cr_diag + 11 cr_panel; fp32 arithmetic "
@@ -495,13 +505,7 @@ def main():
     nxt = {}
     nalg = wl.next_algorithmic()
     for name, t in time_ops(wl, ops=wl.next_ops()).items():
-        a = nalg[name]
-        d = {"ms": round(t, 4)}
-        if "bytes" in a:
-            d["hbm_GBps"] = round(a["bytes"] / (t * 1e-3) / 1e9, 1)
-        if "flops" in a:
-            d["TFLOPs"] = round(a["flops"] / (t * 1e-3) / 1e12, 2)
-        nxt[name] = d
+        nxt[name] = op_rates(nalg[name], t)
     out["next_rows"] = nxt
     if not args.no_cpu_baseline:
         log("timing the oracle baseline on the host")
