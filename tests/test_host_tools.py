@@ -1,0 +1,84 @@
+"""Host-side logic of bench.py and of the rocprofv3 summary tool (no GPU)."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from byte_level_lm_amd import profsum  # noqa: E402
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_op_rates_fractions():
+    d = bench.op_rates({"bytes": 8e9, "flops": 157.3e12 * 1e-3, "peak_tflops": bench.FP32_MFMA_PEAK_TFLOPS}, 2.0)
+    assert d["ms"] == 2.0
+    assert d["hbm_GBps"] == pytest.approx(4000.0) and d["hbm_frac"] == pytest.approx(0.5)
+    assert d["TFLOPs"] == pytest.approx(78.65) and d["mfma_frac"] == pytest.approx(0.5)
+    # contractions without a stated type are priced at the bf16 peak
+    d = bench.op_rates({"flops": 2.5e9}, 1.0)
+    assert d["mfma_peak"] == bench.BF16_MFMA_PEAK_TFLOPS and d["mfma_frac"] == pytest.approx(1e-3)
+
+
+def test_coding_rate_traffic_tracks_the_sources():
+    """The committed counter summary is used only while it matches the kernel sources."""
+    path = os.path.join(ROOT, "profiles", "coding_rate_bf16_32x8192x512.md")
+    text = open(path).read()
+    block = json.loads(text.split("```json\n")[-1].split("\n```")[0])
+    t = bench.coding_rate_traffic()
+    if block["sources_sha256"] == profsum.sources_sha256("coding_rate"):
+        assert t == block["hbm_bytes_per_call"] and t > 0
+    else:
+        assert t is None
+
+
+def _write_trace(path, kernels):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for name, s, e in kernels:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": s, "End_Timestamp": e})
+
+
+def test_profsum_groups_calls_and_keeps_the_last(tmp_path):
+    gram = "bllm::(anonymous namespace)::cr_gram_prefix_bf16(unsigned short const*)"
+    diag = "bllm::(anonymous namespace)::cr_diag(float*)"
+    panel = "void bllm::(anonymous namespace)::cr_panel<1>(void const*)"
+    other = "at::native::elementwise_kernel"
+    ks = []
+    t = 0
+    # a set-up call of 1000 ns per kernel, then two profiled calls of 100 and 300 ns per kernel
+    for per in (1000, 100, 300):
+        for name in (gram, diag, panel, other, panel):
+            ks.append((name, t, t + per))
+            t += per + 10
+    d = tmp_path / "trace"
+    d.mkdir()
+    _write_trace(d / "x_kernel_trace.csv", ks)
+    calls = profsum.trace_calls("coding_rate", str(d))
+    assert [len(c) for c in calls] == [4, 4, 4]  # the unrelated kernel is not part of a call
+    out = tmp_path / "sum.md"
+    sys_argv = sys.argv
+    try:
+        sys.argv = ["profsum", "--op", "coding_rate", "--last", "2", "--trace", str(d), "--cmd", "c",
+                    "--workload", "w", "--out", str(out)]
+        profsum.main()
+    finally:
+        sys.argv = sys_argv
+    text = out.read_text()
+    assert "Calls profiled: 2" in text
+    block = json.loads(text.split("```json\n")[-1].split("\n```")[0])
+    assert block["kernel_us_per_call"] == pytest.approx(4 * 200 / 1e3)
+    assert block["sources_sha256"] == profsum.sources_sha256("coding_rate")
