@@ -320,6 +320,26 @@ def op_rates(a, t):
     return d
 
 
+def op_ideal_ms(name, a):
+    """Ideal time of one op at MI355X's peaks: max(algorithmic HBM bytes / 8 TB/s,
+    algorithmic flops / the peak of the narrowest type that keeps the op's
+    accuracy).  The coding rate's Gram (2 of its 3 T d^2 flops per sequence)
+    is exact in bf16, its solves need fp32; the upsample is a bf16 GEMM."""
+    t_hbm = a.get("bytes", 0) / (HBM_PEAK_GBS * 1e9)
+    f = a.get("flops", 0)
+    if name == "coding_rate":
+        t_mfma = 2 * f / 3 / (BF16_MFMA_PEAK_TFLOPS * 1e12) + f / 3 / (FP32_MFMA_PEAK_TFLOPS * 1e12)
+    else:
+        t_mfma = f / (a.get("peak_tflops", BF16_MFMA_PEAK_TFLOPS) * 1e12)
+    return max(t_hbm, t_mfma) * 1e3
+
+
+def step_roofline(alg, ms):
+    """% roofline of a whole step: the sum of the ops' ideal times over the measured step time."""
+    ideal = sum(op_ideal_ms(n, a) for n, a in alg.items())
+    return {"ideal_ms": round(ideal, 4), "measured_ms": round(ms, 4), "frac": round(ideal / ms, 4)}
+
+
 def time_ops(wl, reps=5, ops=None):
     """Average duration of each op (HIP events on the stream the kernels run on)."""
     torch = wl.torch
@@ -496,6 +516,7 @@ def main():
                                 "upsample_items": wl.up_items},
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "step_roofline": step_roofline(alg, ms),
         "dominant_op": dom_name,
         "breakdown": breakdown,
         "hnet_layer": {"ms": round(hnet_ms, 4), "bytes_per_s": wl.N / (hnet_ms * 1e-3),

@@ -32,6 +32,15 @@ def test_op_rates_fractions():
     assert d["mfma_peak"] == bench.BF16_MFMA_PEAK_TFLOPS and d["mfma_frac"] == pytest.approx(1e-3)
 
 
+def test_step_roofline_sums_op_ideals():
+    alg = {"hbm op": {"bytes": 8e9},  # 1 ms at 8 TB/s
+           "coding_rate": {"flops": 3e12, "bytes": 1.0},  # 2e12 at bf16 peak + 1e12 at fp32 peak
+           "upsample_bins": {"flops": 2.5e12, "bytes": 4e9}}  # 1 ms of MFMA beats 0.5 ms of HBM
+    want = 1.0 + (2e12 / 2.5e15 + 1e12 / 157.3e12) * 1e3 + 1.0
+    r = bench.step_roofline(alg, 20.0)
+    assert r["ideal_ms"] == pytest.approx(want, rel=1e-3) and r["frac"] == pytest.approx(want / 20.0, rel=1e-3)
+
+
 def test_coding_rate_traffic_tracks_the_sources():
     """The committed counter summary is used only while it matches the kernel sources."""
     path = os.path.join(ROOT, "profiles", "coding_rate_bf16_32x8192x512.md")
