@@ -223,8 +223,9 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
   float* sO = reinterpret_cast<float*>(smem);  // [64][kOLD] fp32, reused after the K loop
   static_assert(64 * kOLD * 4 <= (kBM * kPA + kBK * kPB) * 2, "epilogue staging must fit");
   const int grp = blockIdx.x / (8 * ncol), rem = blockIdx.x % (8 * ncol);
-  const int tau = 8 * grp + (rem & 7);
-  if (tau >= tile_off[g.nbins]) return;
+  const int tau_f = 8 * grp + (rem & 7);
+  if (tau_f >= tile_off[g.nbins]) return;
+  const int tau = tile_off[g.nbins] - 1 - tau_f;  // last bins first: they hold the longest runs
   int b = 0;
   while (tile_off[b + 1] <= tau) ++b;
   const int first = (tau - tile_off[b]) * kBM;
