@@ -101,6 +101,26 @@ def test_coding_rate_bf16_d512_vs_oracle(ops):
     assert np.max(np.abs(g[0] - o) / np.abs(o)) < 1e-3
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_coding_rate_largest_d(ops, dt):
+    """The largest supported width, d = 640 (ten 64-wide tiles, block
+    matrices of 640 + 256), whole sequence and two streamed windows."""
+    torch = _torch()
+    rng = np.random.default_rng(640)
+    h = cluster_rows(rng, 1, 400, 640)
+    h = bf16_round(h) if dt == "bf16" else h.astype(np.float32)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    say("coding_rate d 640", dt)
+    g, st = _dr(ops, h, 0.5, tdt)
+    assert st == 0
+    o = oracle.coding_rate(h[0].astype(np.float64), 0.5)
+    assert np.max(np.abs(g[0] - o) / np.abs(o)) < 1e-3
+    gs, A = _stream(ops, h, 0.5, tdt, (150, 250), inplace=True)
+    assert np.max(np.abs(gs[0] - o) / np.abs(o)) < 1e-3
+    want = np.eye(640) + oracle.alpha_of(640, 0.5) * h[0].astype(np.float64).T @ h[0].astype(np.float64)
+    assert np.max(np.abs(A[0] - want)) <= 1e-5 * np.max(np.abs(want))
+
+
 def test_coding_rate_nonfinite_sets_status(ops):
     torch = _torch()
     h = cluster_rows(np.random.default_rng(6), 1, 100, 16).astype(np.float32)
@@ -294,7 +314,7 @@ def _random_idx(rng, nseq, T, K):
 
 @pytest.mark.parametrize("nseq,T,K,dg,dl,B", [(2, 300, 40, 64, 32, 16), (3, 1000, 37, 96, 136, 4),
                                               (1, 64, 64, 32, 8, 16), (2, 500, 1, 64, 64, 16),
-                                              (4, 3000, 300, 200, 320, 16)])
+                                              (4, 3000, 300, 200, 320, 16), (2, 2000, 20, 64, 64, 64)])
 def test_upsample_vs_oracle(ops, nseq, T, K, dg, dl, B):
     torch = _torch()
     rng = np.random.default_rng(T + K)

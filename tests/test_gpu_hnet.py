@@ -176,6 +176,25 @@ def test_route_fused_matches_oracle(ops, d):
     assert float(to_np(tau)[0]) == 0.5
 
 
+def test_route_fused_largest_d(ops):
+    """The largest supported width, d = 4096 (32 column blocks of q and k)."""
+    torch = _torch()
+    bf = torch.bfloat16
+    d = 4096
+    rng = np.random.default_rng(4096)
+    off = np.array([0, 129, 130, 300], np.int64)
+    N = int(off[-1])
+    h = bf16_round(rng.standard_normal((N, d)))
+    wq = bf16_round(rng.standard_normal((d, d)) / np.sqrt(d))
+    wk = bf16_round(rng.standard_normal((d, d)) / np.sqrt(d))
+    say("route fused d 4096")
+    p, b, tau = ops.route_fused(to_dev(h, bf), to_dev(wq, bf), to_dev(wk, bf), to_dev(off), threshold=0.5)
+    p_o = _fused_oracle(h, wq, wk, off)
+    assert np.max(np.abs(to_np(p) - p_o)) < 1e-5
+    keep = np.abs(p_o - 0.5) > 1e-5
+    assert np.array_equal(to_np(b).astype(bool)[keep], (p_o >= 0.5)[keep])
+
+
 def test_route_fused_quantile_event_streams(ops):
     """Stage-1 routing from h on ByteGen-style streams (projections formed in
     the kernel), with the stage's 0.75 score quantile."""
