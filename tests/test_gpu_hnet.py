@@ -54,7 +54,7 @@ def test_route_c0_fp32(ops):
     _check_route(ops, c["q"], c["k"], c["offsets"], torch.float32)
 
 
-@pytest.mark.parametrize("d", [8, 64, 512, 768])
+@pytest.mark.parametrize("d", [8, 64, 512, 768, 4096])
 def test_route_ragged_bf16(ops, d):
     torch = _torch()
     rng = np.random.default_rng(100 + d)
@@ -267,7 +267,7 @@ def _dechunk_check(ops, z, P, idx, coff, off, dtype, tol):
     return out
 
 
-@pytest.mark.parametrize("dtname,d", [("f32", 64), ("bf16", 512), ("bf16", 768), ("f32", 8)])
+@pytest.mark.parametrize("dtname,d", [("f32", 64), ("bf16", 512), ("bf16", 768), ("f32", 8), ("bf16", 4096)])
 def test_dechunk_matches_oracle(ops, dtname, d):
     torch = _torch()
     dtype = torch.float32 if dtname == "f32" else torch.bfloat16
@@ -351,7 +351,7 @@ def _dechunk_bwd_check(ops, z, P, idx, coff, off, dout, dtype, tol):
     return dz_g, dP_g
 
 
-@pytest.mark.parametrize("dtname,d", [("f32", 64), ("bf16", 512), ("bf16", 768), ("f32", 8)])
+@pytest.mark.parametrize("dtname,d", [("f32", 64), ("bf16", 512), ("bf16", 768), ("f32", 8), ("bf16", 2048)])
 def test_dechunk_backward_matches_oracle(ops, dtname, d):
     torch = _torch()
     dtype = torch.float32 if dtname == "f32" else torch.bfloat16
