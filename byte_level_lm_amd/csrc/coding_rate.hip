@@ -312,7 +312,10 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
-      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
+      // streaming stores: the 600 MB of prefix tiles would otherwise push the
+      // rows of h that the other tiles of the sequence still read out of L2
+      __builtin_nontemporal_store((row == col ? 1.f : 0.f) + alpha * acc[r],
+                                  Mj + static_cast<int64_t>(row) * g.ldm + col);
     }
     if (j == g.nblk - 1 && !sout) break;
     for (int sq = 0; sq < spb; ++sq, ++q) {
