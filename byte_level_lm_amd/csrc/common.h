@@ -156,10 +156,10 @@ inline bool valid_dtype(int dtype) { return dtype == BLLM_F32 || dtype == BLLM_B
 
 namespace bllm {
 // tiny fills used instead of hipMemsetAsync (safe under stream capture)
-static __global__ void fill_f32(float* p, int64_t n, float v) {
+[[maybe_unused]] static __global__ void fill_f32(float* p, int64_t n, float v) {
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x) p[i] = v;
 }
-static __global__ void fill_i64(int64_t* p, int64_t n, int64_t v) {
+[[maybe_unused]] static __global__ void fill_i64(int64_t* p, int64_t n, int64_t v) {
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x) p[i] = v;
 }
 }  // namespace bllm

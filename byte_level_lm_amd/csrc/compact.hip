@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void compact_scatter(
   shb[threadIdx.x] = part;
   __syncthreads();
   for (int off = 128; off >= 1; off >>= 1) {
-    if (threadIdx.x < off) shb[threadIdx.x] += shb[threadIdx.x + off];
+    if (static_cast<int>(threadIdx.x) < off) shb[threadIdx.x] += shb[threadIdx.x + off];
     __syncthreads();
   }
   const int64_t base = shb[0];

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_count(const int32_t* __res
     if (lane == 0) wc[w][b] = n;
   }
   __syncthreads();
-  if (threadIdx.x < g.nbins)
+  if (static_cast<int>(threadIdx.x) < g.nbins)
     counts[static_cast<int64_t>(blockIdx.x) * g.nbins + threadIdx.x] =
         wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] + wc[3][threadIdx.x];
 }
