@@ -64,6 +64,16 @@ template <int DT> struct Lane {
       }
     }
   }
+  __device__ static inline void store(void* base, int64_t elem, const float* x) {
+    uint32_t* p = reinterpret_cast<uint32_t*>(static_cast<char*>(base) + elem * E);
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      if constexpr (DT == BLLM_F32)
+        p[i] = __float_as_uint(x[i]);
+      else
+        p[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+    }
+  }
   __device__ static inline void store_nt(void* base, int64_t elem, const float* x) {
     uint32_t* p = reinterpret_cast<uint32_t*>(static_cast<char*>(base) + elem * E);
 #pragma unroll
@@ -381,7 +391,7 @@ void launch_dechunk(const void* z, const float* P, int d, const int32_t* idx,
 // dz_c = P_c lam_c; dP_c = lam_c . (z_c - zbar_{c-1}) with zbar_{c-1} = 0 at a
 // sequence's first chunk.  Same tiles and slices as the forward:
 //   1. per tile: the forward aggregate (A, U_f) over z, the chunk sums gbar_c
-//      (stored, fp32) and the reverse aggregate U_r = a_{c0} sum_c pi_c gbar_c
+//      (stored in the activations' type) and the reverse aggregate U_r = a_{c0} sum_c pi_c gbar_c
 //      with pi_c = prod_{c0 < j <= c} a_j, accumulated in ascending order; the
 //      reverse aggregates are stored in reversed tile order
 //   2. the forward carry scan, and the same scan over the reversed tiles,
@@ -390,8 +400,9 @@ void launch_dechunk(const void* z, const float* P, int d, const int32_t* idx,
 //   4. per tile, ascending: zbar from the forward carry; dz_c = P_c lam_c and
 //      one partial dot product per feature slice
 //   5. dP_c = the slice partials summed in slice order
-// HBM: dout read once; z read twice; gbar/lam (fp32, M x d) written twice and
-// read twice; dz written once.
+// HBM: dout read once; z read twice; gbar/lam (M x d, the activations' type;
+// every sum and scan runs in fp32) written twice and read twice; dz written
+// once.
 
 template <int DT>
 __global__ __launch_bounds__(256) void emab_aggregate(const void* __restrict__ z,
@@ -402,7 +413,7 @@ __global__ __launch_bounds__(256) void emab_aggregate(const void* __restrict__ z
                                                       const int64_t* __restrict__ offsets, int nseq,
                                                       float* __restrict__ Aagg, float* __restrict__ Uf,
                                                       float* __restrict__ Arev, float* __restrict__ Urev,
-                                                      float* __restrict__ gbar) {
+                                                      void* __restrict__ gbar) {
   using V = Lane<DT>;
   const int lane = threadIdx.x & 63;
   const int nvec = d / V::N;
@@ -455,11 +466,7 @@ __global__ __launch_bounds__(256) void emab_aggregate(const void* __restrict__ z
         if (t + u < r1) {
           if (t + u >= tend) {  // row t + u opens chunk j + 1
             const int64_t c = cb + j;
-            if (active) {
-              float* gp = gbar + c * d + col;
-#pragma unroll
-              for (int e = 0; e < V::N; ++e) gp[e] = gs[e];
-            }
+            if (active) V::store(gbar, c * d + col, gs);
             if (c == tr.c0) a0 = lane_f(m.a, j);
 #pragma unroll
             for (int e = 0; e < V::N; ++e) {
@@ -480,11 +487,7 @@ __global__ __launch_bounds__(256) void emab_aggregate(const void* __restrict__ z
     }
     {  // close the group's last chunk
       const int64_t c = cb + j;
-      if (active) {
-        float* gp = gbar + c * d + col;
-#pragma unroll
-        for (int e = 0; e < V::N; ++e) gp[e] = gs[e];
-      }
+      if (active) V::store(gbar, c * d + col, gs);
       if (c == tr.c0) a0 = lane_f(m.a, j);
 #pragma unroll
       for (int e = 0; e < V::N; ++e) {
@@ -516,7 +519,7 @@ __global__ __launch_bounds__(256) void emab_reverse(const float* __restrict__ P,
                                                     const int64_t* __restrict__ chunk_offsets,
                                                     const int64_t* __restrict__ offsets, int nseq,
                                                     const float* __restrict__ carry_rev,
-                                                    float* __restrict__ lam) {
+                                                    void* __restrict__ lam) {
   using V = Lane<DT>;
   const int lane = threadIdx.x & 63;
   const int nvec = d / V::N;
@@ -546,20 +549,14 @@ __global__ __launch_bounds__(256) void emab_reverse(const float* __restrict__ P,
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int jj = j - u >= 0 ? j - u : 0;
-        const float* gp = lam + (cb + jj) * d + col;
-#pragma unroll
-        for (int e = 0; e < V::N; ++e) gv[u][e] = gp[e];
+        V::load(lam, (cb + jj) * d + col, gv[u]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (j - u >= 0) {
-          float* gp = lam + (cb + j - u) * d + col;
 #pragma unroll
           for (int e = 0; e < V::N; ++e) mu[e] += gv[u][e];  // mu now holds lam_c
-          if (active) {
-#pragma unroll
-            for (int e = 0; e < V::N; ++e) gp[e] = mu[e];
-          }
+          if (active) V::store(lam, (cb + j - u) * d + col, mu);
           const float a = lane_f(m.a, j - u);  // a_c: carries lam_c to chunk c - 1
 #pragma unroll
           for (int e = 0; e < V::N; ++e) mu[e] *= a;
@@ -577,7 +574,7 @@ __global__ __launch_bounds__(256) void emab_forward(const void* __restrict__ z,
                                                     const int64_t* __restrict__ chunk_offsets,
                                                     const int64_t* __restrict__ offsets, int nseq,
                                                     const float* __restrict__ carry,
-                                                    const float* __restrict__ lam,
+                                                    const void* __restrict__ lam,
                                                     void* __restrict__ dz, float* __restrict__ dPpart,
                                                     int64_t mcap) {
   using V = Lane<DT>;
@@ -608,9 +605,7 @@ __global__ __launch_bounds__(256) void emab_forward(const void* __restrict__ z,
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t c = cb + (j + u < n ? j + u : n - 1);
         V::load(z, c * d + col, zz[u]);
-        const float* lp = lam + c * d + col;
-#pragma unroll
-        for (int e = 0; e < V::N; ++e) lv[u][e] = lp[e];
+        V::load(lam, c * d + col, lv[u]);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
