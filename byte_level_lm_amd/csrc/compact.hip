@@ -156,8 +156,8 @@ extern "C" int bllm_compact(const uint8_t* mask, const float* p, const void* row
                             int64_t capacity, int32_t* idx_out, int64_t* chunk_offsets_out,
                             void* rows_out, float* P_out, int32_t* status, void* ws,
                             size_t ws_bytes, void* stream) {
-  if (!mask || !offsets || !idx_out || !chunk_offsets_out || nseq < 1 || total < 0 || capacity < 0)
-    return BLLM_E_INVAL;
+  if (!offsets || !chunk_offsets_out || nseq < 1 || total < 0 || capacity < 0) return BLLM_E_INVAL;
+  if (total > 0 && (!mask || (capacity > 0 && !idx_out))) return BLLM_E_INVAL;  // NULL allowed when empty
   if ((rows && !rows_out) || (p && !P_out)) return BLLM_E_INVAL;
   if (rows) {
     if (d < 1) return BLLM_E_INVAL;

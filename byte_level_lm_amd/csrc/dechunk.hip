@@ -702,9 +702,8 @@ extern "C" int bllm_dechunk_ema(const void* z, const float* P, int dtype, int64_
                                 const int64_t* offsets, int64_t nseq, int64_t total,
                                 int64_t max_chunks, void* out, void* ws, size_t ws_bytes,
                                 void* stream) {
-  if (!z || !P || !idx || !chunk_offsets || !offsets || !out || d < 1 || nseq < 1 || total < 0 ||
-      max_chunks < 0)
-    return BLLM_E_INVAL;
+  if (!chunk_offsets || !offsets || d < 1 || nseq < 1 || total < 0 || max_chunks < 0) return BLLM_E_INVAL;
+  if (total > 0 && (!z || !P || !idx || !out)) return BLLM_E_INVAL;  // may be NULL for an empty batch
   if (!valid_dtype(dtype)) return BLLM_E_NOTSUP;
   if ((d * elem_size(dtype)) % 16 != 0 || !aligned16(z) || !aligned16(out)) return BLLM_E_NOTSUP;
   if (total >= (int64_t(1) << 31) || nseq >= (int64_t(1) << 30) || d > (1 << 16)) return BLLM_E_NOTSUP;
@@ -732,9 +731,8 @@ extern "C" int bllm_dechunk_ema_backward(const void* z, const float* P, const vo
                                          const int64_t* offsets, int64_t nseq, int64_t total,
                                          int64_t max_chunks, void* dz_out, float* dP_out, void* ws,
                                          size_t ws_bytes, void* stream) {
-  if (!z || !P || !dout || !idx || !chunk_offsets || !offsets || !dz_out || !dP_out || d < 1 || nseq < 1 ||
-      total < 0 || max_chunks < 0)
-    return BLLM_E_INVAL;
+  if (!chunk_offsets || !offsets || d < 1 || nseq < 1 || total < 0 || max_chunks < 0) return BLLM_E_INVAL;
+  if (total > 0 && (!z || !P || !dout || !idx || !dz_out || !dP_out)) return BLLM_E_INVAL;  // NULL when empty
   if (!valid_dtype(dtype)) return BLLM_E_NOTSUP;
   if ((d * elem_size(dtype)) % 16 != 0 || !aligned16(z) || !aligned16(dout) || !aligned16(dz_out))
     return BLLM_E_NOTSUP;

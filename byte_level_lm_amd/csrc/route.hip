@@ -578,8 +578,8 @@ extern "C" int bllm_route(const void* q, const void* k, int dtype, int64_t d,
                           const int64_t* offsets, int64_t nseq, int64_t total, float threshold,
                           double quantile, float* p_out, uint8_t* b_out, float* tau_out, void* ws,
                           size_t ws_bytes, void* stream) {
-  if (!q || !k || !offsets || !p_out || !b_out || d < 1 || nseq < 1 || total < 0 || quantile > 1.0)
-    return BLLM_E_INVAL;
+  if (!offsets || d < 1 || nseq < 1 || total < 0 || quantile > 1.0) return BLLM_E_INVAL;
+  if (total > 0 && (!q || !k || !p_out || !b_out)) return BLLM_E_INVAL;  // may be NULL for an empty batch
   if (!valid_dtype(dtype)) return BLLM_E_NOTSUP;
   if ((d * elem_size(dtype)) % 16 != 0 || !aligned16(q) || !aligned16(k)) return BLLM_E_NOTSUP;
   if (total >= (int64_t(1) << 31) || nseq >= (int64_t(1) << 30)) return BLLM_E_NOTSUP;
@@ -625,8 +625,8 @@ extern "C" int bllm_route_fused(const void* h, const void* Wq, const void* Wk, i
                                 const int64_t* offsets, int64_t nseq, int64_t total, float threshold,
                                 double quantile, float* p_out, uint8_t* b_out, float* tau_out, void* ws,
                                 size_t ws_bytes, void* stream) {
-  if (!h || !Wq || !Wk || !offsets || !p_out || !b_out || d < 1 || nseq < 1 || total < 0 || quantile > 1.0)
-    return BLLM_E_INVAL;
+  if (!Wq || !Wk || !offsets || d < 1 || nseq < 1 || total < 0 || quantile > 1.0) return BLLM_E_INVAL;
+  if (total > 0 && (!h || !p_out || !b_out)) return BLLM_E_INVAL;  // may be NULL for an empty batch
   if (dtype != BLLM_BF16) return BLLM_E_NOTSUP;
   if (d % kFC != 0 || d > 4096 || !aligned16(h) || !aligned16(Wq) || !aligned16(Wk)) return BLLM_E_NOTSUP;
   if (total >= (int64_t(1) << 31) || nseq >= (int64_t(1) << 30)) return BLLM_E_NOTSUP;

@@ -31,6 +31,8 @@
  *   - dtype is BLLM_F32 or BLLM_BF16 (bf16 bit patterns, fp32 accumulation,
  *     round-to-nearest-even on output).  Row pointers must be 16-byte aligned
  *     and d * element size a multiple of 16 bytes.
+ *   - An empty batch (total = 0) is valid: data pointers of the empty arrays
+ *     may then be NULL (offsets and chunk offsets are still required).
  *   - Return value: BLLM_OK or a negative BLLM_E_* code.  Argument errors are
  *     detected on the host before anything is enqueued.  Data-dependent
  *     conditions (capacity overflow, non-finite values) are reported through

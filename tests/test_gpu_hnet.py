@@ -257,6 +257,30 @@ def test_compact_edges_no_start_boundary_and_empty(ops):
     _compact_check(ops, np.zeros(25, bool), p, h, off, torch.float32)
 
 
+def test_empty_batch_through_the_chain(ops):
+    """A batch whose sequences are all empty: route (threshold and quantile),
+    compact, dechunk and its backward accept empty tensors (NULL data
+    pointers) and produce empty outputs, chunk offsets of zeros and tau as
+    set (the threshold, or NaN for a quantile of no scores)."""
+    torch = _torch()
+    off = to_dev(np.array([0, 0, 0], np.int64))
+    e = to_dev(np.zeros((0, 64), np.float32))
+    p, b, tau = ops.route(e, e, off, threshold=0.5)
+    assert p.numel() == 0 and b.numel() == 0 and float(to_np(tau)[0]) == 0.5
+    p, b, tau = ops.route(e, e, off, quantile=0.75)
+    assert np.isnan(float(to_np(tau)[0]))
+    eb = to_dev(np.zeros((0, 128), np.float32), torch.bfloat16)
+    w = to_dev(np.zeros((128, 128), np.float32), torch.bfloat16)
+    p, b, tau = ops.route_fused(eb, w, w, off, threshold=0.25)
+    assert p.numel() == 0 and float(to_np(tau)[0]) == 0.25
+    idx, coff, z, P, st = ops.compact(b, off, rows=e, p=p)
+    assert np.array_equal(to_np(coff), [0, 0, 0]) and int(to_np(st)[0]) == 0
+    out = ops.dechunk_ema(z, P, idx, coff, off, 0)
+    assert out.shape == (0, 64)
+    dz, dP = ops.dechunk_ema_backward(z[:0], P[:0], e, idx[:0], coff, off)
+    assert dz.numel() == 0 and dP.numel() == 0
+
+
 def _dechunk_check(ops, z, P, idx, coff, off, dtype, tol):
     N = int(off[-1])
     out = ops.dechunk_ema(to_dev(z, dtype), to_dev(P.astype(np.float32)), to_dev(idx.astype(np.int32)),
