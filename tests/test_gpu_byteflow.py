@@ -121,6 +121,23 @@ def test_coding_rate_largest_d(ops, dt):
     assert np.max(np.abs(A[0] - want)) <= 1e-5 * np.max(np.abs(want))
 
 
+@pytest.mark.parametrize("T", [1, 2, 65])
+def test_coding_rate_shortest_sequences(ops, T):
+    """One- and two-row sequences (a single partial block), and one row past a
+    64-row tile; the first value is R(h_1) = 1/2 log(1 + alpha |h_1|^2)."""
+    torch = _torch()
+    rng = np.random.default_rng(60 + T)
+    h = cluster_rows(rng, 3, T, 64).astype(np.float32)
+    g, st = _dr(ops, h, 0.5, torch.float32)
+    assert st == 0
+    a = oracle.alpha_of(64, 0.5)
+    first = 0.5 * np.log1p(a * (h[:, 0].astype(np.float64) ** 2).sum(1))
+    assert np.max(np.abs(g[:, 0] - first) / first) < 1e-5
+    for s in range(3):
+        o = oracle.coding_rate(h[s], 0.5)
+        assert np.max(np.abs(g[s] - o) / np.abs(o)) < 1e-3
+
+
 def test_coding_rate_nonfinite_sets_status(ops):
     torch = _torch()
     h = cluster_rows(np.random.default_rng(6), 1, 100, 16).astype(np.float32)
