@@ -233,7 +233,8 @@ class Workload:
                            tau_out=self.tauf1, ws=self.ws_routef)
 
     def next_ops(self):
-        """Rows past the hot path (the survey's 'next' list), timed on their own."""
+        """Rows past the hot path (fused projection, cosine chunker, EMA backward, streaming
+        chunker), timed on their own."""
         return [("cosine_chunker", self._cosine_chunker), ("dechunk_backward stage1", self._dechunk1_backward),
                 ("route_fused stage1", self._route_fused1), ("streaming_chunker", self._streaming_chunker)]
 
@@ -424,7 +425,7 @@ def cpu_baseline(wl):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
