@@ -454,7 +454,8 @@ def main():
     torch.cuda.synchronize()
     log("warmup done")
     # the dominant op is bracketed by events of its own inside the timed steps
-    # (all ops run on torch's current stream)
+    # (all ops are queued on torch's current stream; the coding rate's second
+    # stream is joined back to it before the closing event)
     dom_name = "coding_rate"
     dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
@@ -481,7 +482,8 @@ def main():
     breakdown = {name: op_rates(alg[name], t) for name, t in per_op.items()}
     cr = alg["coding_rate"]
     roof = {
-        "kernel": ("one bllm_coding_rate call: cr_gram_prefix_bf16 + 12 cr_diag + 11 cr_panel; fp32 arithmetic "
+        "kernel": ("one bllm_coding_rate call: two halves of 16 sequences on two streams, each "
+                   "cr_gram_prefix_bf16 + 12 cr_diag + 11 cr_panel; fp32 arithmetic "
                    "(strip products as exact three-part bf16 MFMA, diagonal and TRSM on fp32 MFMA)"),
         "bound": "mfma",
         "achieved": round(cr["flops"] / (dom_ms * 1e-3) / 1e12, 3),

@@ -59,23 +59,29 @@ def _of_op(op: str, name: str) -> bool:
     return any(_short(name).startswith(p) for p in OPS[op][0])
 
 
-def trace_calls(op: str, d: str):
-    """Kernel dispatches of the op grouped into calls (a call starts at its first kernel)."""
+def trace_calls(op: str, d: str, parts: int = 1):
+    """Kernel dispatches of the op grouped into calls.  A call starts at its
+    first kernel; a call that runs as `parts` halves on several streams has
+    `parts` first kernels, which are grouped in runs of `parts` counted from the
+    end of the run (the profiled calls are the last ones)."""
     rows = list(csv.DictReader(open(_one(d, "*kernel_trace.csv"))))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    rows = [r for r in rows if _of_op(op, r["Kernel_Name"])]
     first = OPS[op][0][0]
+    heads = [i for i, r in enumerate(rows) if _short(r["Kernel_Name"]).startswith(first)]
+    keep = set(heads[len(heads) % parts::parts]) if parts > 1 else set(heads)
     calls = []
-    for r in rows:
-        if not _of_op(op, r["Kernel_Name"]):
-            continue
-        if _short(r["Kernel_Name"]).startswith(first) or not calls:
+    for i, r in enumerate(rows):
+        if i in keep or not calls:
             calls.append([])
         calls[-1].append(r)
     return calls
 
 
-def counter_last_call(op: str, d: str, counter: str) -> float:
-    """Sum of a counter (KiB) over the kernels of the op's last call in a --pmc run."""
+def counter_last_call(op: str, d: str, counter: str, parts: int = 1) -> float:
+    """Sum of a counter (KiB) over the kernels of the op's last call in a --pmc
+    run (dispatch ids follow the order of enqueue, so a call made of `parts`
+    halves starts at the `parts`-th first kernel from the end)."""
     rows = list(csv.DictReader(open(_one(d, "*counter_collection.csv"))))
     per = {}
     for r in rows:
@@ -87,9 +93,9 @@ def counter_last_call(op: str, d: str, counter: str) -> float:
     disp = sorted(per.items())
     first = OPS[op][0][0]
     starts = [i for i, (_, (n, _)) in enumerate(disp) if _short(n).startswith(first)]
-    if not starts:
-        raise ValueError(f"no {first} dispatch in {d}")
-    return sum(v for _, (n, v) in disp[starts[-1]:] if _of_op(op, n))
+    if len(starts) < parts:
+        raise ValueError(f"fewer than {parts} {first} dispatches in {d}")
+    return sum(v for _, (n, v) in disp[starts[-parts]:] if _of_op(op, n))
 
 
 def counter_copy(d: str, counter: str) -> float:
@@ -129,6 +135,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--last", type=int, default=0,
                     help="summarise the last N calls (the profiled steps); default: all but the first")
+    ap.add_argument("--parts", type=int, default=1,
+                    help="streams one call of the op runs on (first kernels per call)")
     ap.add_argument("--cmd", required=True, help="the full commands that produced the runs")
     ap.add_argument("--workload", required=True)
     ap.add_argument("--out", required=True)
@@ -137,7 +145,7 @@ def main():
         step_summary(a.trace, a.cmd, a.workload, a.out)
         return
 
-    calls = trace_calls(a.op, a.trace)
+    calls = trace_calls(a.op, a.trace, a.parts)
     if a.last > 0:
         timed = calls[-a.last:]  # bench.py's set-up may call the op's kernels more than once
     else:
@@ -148,22 +156,24 @@ def main():
             per_kernel.setdefault(_short(r["Kernel_Name"]), []).append(
                 int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     call_ns = [sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in c) for c in timed]
-    span_ns = [int(c[-1]["End_Timestamp"]) - int(c[0]["Start_Timestamp"]) for c in timed]
+    span_ns = [max(int(r["End_Timestamp"]) for r in c) - min(int(r["Start_Timestamp"]) for r in c) for c in timed]
 
     lines = [f"# rocprofv3 summary: {a.op}, {a.workload}", "", "Commands (run from the repository root on the GPU host):", "",
              "```", a.cmd, "```", "",
-             f"Calls profiled: {len(timed)} (the last ones of the run).  Kernel time per call "
-             f"(sum of its kernels): {statistics.mean(call_ns) / 1e3:.1f} us; first-to-last span "
-             f"{statistics.mean(span_ns) / 1e3:.1f} us.", "",
+             f"Calls profiled: {len(timed)} (the last ones of the run), each on {a.parts} stream(s).  "
+             f"Time per call from its first kernel's start to its last kernel's end: "
+             f"{statistics.mean(span_ns) / 1e3:.1f} us; sum of its kernels' durations "
+             f"{statistics.mean(call_ns) / 1e3:.1f} us (more than the span where streams overlap).", "",
              "| kernel | launches per call | avg us | total us per call |", "|---|---|---|---|"]
     for k, v in sorted(per_kernel.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| {k} | {len(v) / len(timed):g} | {statistics.mean(v) / 1e3:.1f} | "
                      f"{sum(v) / len(timed) / 1e3:.1f} |")
-    block = {"op": a.op, "workload": a.workload, "kernel_us_per_call": round(statistics.mean(call_ns) / 1e3, 2),
+    block = {"op": a.op, "workload": a.workload, "us_per_call": round(statistics.mean(span_ns) / 1e3, 2),
+             "kernel_us_per_call": round(statistics.mean(call_ns) / 1e3, 2), "parts": a.parts,
              "sources_sha256": sources_sha256(a.op)}
     if a.fetch and a.write and a.copy_fetch and a.copy_write:
-        f_kib = counter_last_call(a.op, a.fetch, "FETCH_SIZE")
-        w_kib = counter_last_call(a.op, a.write, "WRITE_SIZE")
+        f_kib = counter_last_call(a.op, a.fetch, "FETCH_SIZE", a.parts)
+        w_kib = counter_last_call(a.op, a.write, "WRITE_SIZE", a.parts)
         cf_kib = counter_copy(a.copy_fetch, "FETCH_SIZE")
         cw_kib = counter_copy(a.copy_write, "WRITE_SIZE")
         f_scale = a.copy_bytes / (cf_kib * 1024)

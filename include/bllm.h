@@ -192,6 +192,17 @@ int bllm_dechunk_ema_backward(const void* z, const float* P, const void* dout, i
  *          positive definiteness).
  * Limits : 1 <= d <= 640 (BLLM_E_NOTSUP beyond), T >= 1, eps2 > 0.
  * ws     : bllm_coding_rate_workspace(nseq, T, d) bytes.
+ * Streams: a batch of two or more sequences with 512 or more row blocks in
+ *          all (nseq * ceil(T / c), c = min(256, d'/2 rounded up to a multiple
+ *          of 64), d' = d rounded up to a multiple of 64) runs half of its sequences
+ *          on a second stream the library creates on the device of `stream`
+ *          at the first such call (kept until the process ends), forked from
+ *          and joined back to `stream` with events, so work queued on
+ *          `stream` after the call still sees every result.  Under graph
+ *          capture, make one such call before capturing (stream creation is
+ *          not allowed while capturing); if the stream cannot be created the
+ *          batch runs on `stream` alone.  Calls from several host threads are
+ *          serialised while they queue their launches.
  */
 size_t bllm_coding_rate_workspace(int64_t nseq, int64_t T, int64_t d);
 int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d, double eps2,

@@ -190,6 +190,64 @@ def test_coding_rate_full_size_bf16_32x8192x512_sampled(ops):
     assert len(bad) == 0, bad
 
 
+
+@pytest.mark.parametrize("dt,nseq,T,d", [("f32", 3, 11000, 64), ("bf16", 2, 65536, 512)])
+def test_coding_rate_split_batch_matches_single_sequences(ops, dt, nseq, T, d):
+    """A batch of 512 or more row blocks runs as two halves on two streams
+    (3 sequences: 2 + 1, with a ragged last block; 2 sequences of 256 blocks:
+    1 + 1).  Each sequence's Delta R must equal, bit for bit, a call on that
+    sequence alone (under 512 blocks: one stream), and sampled positions of
+    the last sequence (the second stream's) match the oracle."""
+    torch = _torch()
+    rng = np.random.default_rng(50 + d)
+    h = cluster_rows(rng, nseq, T, d)
+    h = bf16_round(h) if dt == "bf16" else h.astype(np.float32)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    say("split batch", nseq, "x", T, "x", d, dt)
+    g, st = _dr(ops, h, 0.5, tdt)
+    assert st == 0
+    for s in range(nseq):
+        one, st1 = _dr(ops, h[s:s + 1], 0.5, tdt)
+        assert st1 == 0
+        assert np.array_equal(g[s], one[0]), s
+    if d <= 64:
+        pos = np.sort(np.concatenate([[0, T - 1], rng.choice(T, 6, replace=False)]))
+        o = oracle.coding_rate_at(h[-1], 0.5, pos)
+        assert np.max(np.abs(g[-1, pos] - o) / np.abs(o)) < 1e-3
+
+
+
+def test_coding_rate_split_batch_in_a_captured_graph(ops):
+    """The two-stream form (fork and join by events) inside a HIP graph: after
+    an eager call, one call is captured; replays with new inputs copied in,
+    eager work and synchronisations between them, each equal the eager result
+    bit for bit."""
+    torch = _torch()
+    rng = np.random.default_rng(60)
+    hs = [cluster_rows(rng, 2, 16384, 64).astype(np.float32) for _ in range(2)]  # 2 x 256 blocks
+    want = [_dr(ops, h, 0.5, torch.float32)[0] for h in hs]
+    hd = to_dev(hs[0], torch.float32)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ops.coding_rate(hd, 0.5)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out, st = ops.coding_rate(hd, 0.5)
+    for r in range(4):
+        i = r % 2
+        hd.copy_(torch.from_numpy(hs[i]).to(hd.device))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say("graph replay", r)
+        assert np.array_equal(to_np(out), want[i]), r
+        assert int(to_np(st)[0]) == 0
+        _dr(ops, hs[1 - i][:1, :4096], 0.5, torch.float32)  # eager work between replays
+
+
 # ------------------------------------------------------------------ streaming chunker
 
 def _stream(ops, h, eps2, dtype, widths, inplace=False):

@@ -91,3 +91,47 @@ def test_profsum_groups_calls_and_keeps_the_last(tmp_path):
     block = json.loads(text.split("```json\n")[-1].split("\n```")[0])
     assert block["kernel_us_per_call"] == pytest.approx(4 * 200 / 1e3)
     assert block["sources_sha256"] == profsum.sources_sha256("coding_rate")
+
+
+def test_profsum_calls_split_over_two_streams(tmp_path):
+    """A call made of two halves on two streams: its kernels interleave in
+    time, both halves' first kernels open the same call, the span runs from
+    the first start to the last end, and the counters of the last call start
+    at its first half's first dispatch."""
+    gram = "bllm::(anonymous namespace)::cr_gram_prefix_bf16(unsigned short const*)"
+    diag = "bllm::(anonymous namespace)::cr_diag(float*)"
+    panel = "void bllm::(anonymous namespace)::cr_panel<1>(void const*)"
+    ks, t = [], 0
+    ks.append((gram, 0, 50))  # a set-up call on one stream
+    ks.append((diag, 60, 70))
+    t = 1000
+    for _ in range(2):  # two calls, each: half A and half B overlapping
+        ks += [(gram, t, t + 100), (gram, t + 5, t + 110), (diag, t + 100, t + 120), (diag, t + 110, t + 125),
+               (panel, t + 120, t + 300), (panel, t + 125, t + 320)]
+        t += 1000
+    d = tmp_path / "trace"
+    d.mkdir()
+    _write_trace(d / "x_kernel_trace.csv", ks)
+    calls = profsum.trace_calls("coding_rate", str(d), parts=2)
+    assert [len(c) for c in calls] == [2, 6, 6]
+    out = tmp_path / "sum.md"
+    # counters: dispatch ids in order of enqueue (half A's kernels, then half B's)
+    cdir = tmp_path / "pmc"
+    cdir.mkdir()
+    names = [gram, diag] + [gram, diag, panel, gram, diag, panel] * 2
+    with open(cdir / "x_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, n in enumerate(names):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": n, "Counter_Name": "FETCH_SIZE", "Counter_Value": 1 + i})
+    assert profsum.counter_last_call("coding_rate", str(cdir), "FETCH_SIZE", parts=2) == sum(range(9, 15))
+    sys_argv = sys.argv
+    try:
+        sys.argv = ["profsum", "--op", "coding_rate", "--parts", "2", "--last", "2", "--trace", str(d), "--cmd", "c",
+                    "--workload", "w", "--out", str(out)]
+        profsum.main()
+    finally:
+        sys.argv = sys_argv
+    block = json.loads(out.read_text().split("```json\n")[-1].split("\n```")[0])
+    assert block["us_per_call"] == pytest.approx(0.32) and block["parts"] == 2
+    assert block["kernel_us_per_call"] == pytest.approx((100 + 105 + 20 + 15 + 180 + 195) / 1e3, abs=0.01)
