@@ -248,6 +248,46 @@ def test_coding_rate_split_batch_in_a_captured_graph(ops):
         _dr(ops, hs[1 - i][:1, :4096], 0.5, torch.float32)  # eager work between replays
 
 
+
+def test_coding_rate_split_batch_from_two_host_threads(ops):
+    """Two host threads, each on a stream of its own, queue split batches at
+    the same time (they share the library's second stream): every result
+    equals the same call made alone."""
+    import threading
+    torch = _torch()
+    rng = np.random.default_rng(61)
+    hs = [cluster_rows(rng, 2, 16384, 64).astype(np.float32) for _ in range(2)]  # 2 x 256 blocks each
+    want = [_dr(ops, h, 0.5, torch.float32)[0] for h in hs]
+    hd = [to_dev(h, torch.float32) for h in hs]
+    torch.cuda.synchronize()
+    got = [[None] * 3 for _ in range(2)]
+    errs = []
+
+    def run(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for r in range(3):
+                    dR, status = ops.coding_rate(hd[i], 0.5)
+                    got[i][r] = (dR, status)
+            st.synchronize()
+        except Exception as e:  # reported below, in the main thread
+            errs.append(e)
+
+    th = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errs, errs
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r in range(3):
+            dR, status = got[i][r]
+            assert np.array_equal(to_np(dR), want[i]), (i, r)
+            assert int(to_np(status)[0]) == 0
+
+
 # ------------------------------------------------------------------ streaming chunker
 
 def _stream(ops, h, eps2, dtype, widths, inplace=False):
