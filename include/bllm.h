@@ -18,9 +18,11 @@
  *
  * Conventions shared by every entry point
  *   - Tensor arguments are DEVICE pointers to caller-owned memory.  The
- *     library never allocates, frees or synchronises; every call only
- *     enqueues kernels on `stream` (a hipStream_t passed as void*; NULL is the
- *     default stream) and returns.
+ *     library never allocates device memory, frees or synchronises; every
+ *     call only enqueues kernels on `stream` (a hipStream_t passed as void*;
+ *     NULL is the default stream) and returns.  The one exception is
+ *     bllm_coding_rate on large batches, which also forks work onto a stream
+ *     of its own and joins it back to `stream` (see there).
  *   - Scratch memory comes in through (ws, ws_bytes); its size is given by the
  *     matching bllm_*_workspace() function.  Contents need not be initialised
  *     and are clobbered.  Workspaces must not be shared by calls that may
