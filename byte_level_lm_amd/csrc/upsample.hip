@@ -27,7 +27,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kChunksPerBlock = 256;
-constexpr int kMaxRun = 16;
+constexpr int kMaxRun = 32;  // positions per item at most (of 8..64, 32 is fastest on 32 x 8192, K 2048)
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kPA = kBK + 8;   // LDS pitch (bf16) of the A tile [kBM][kBK]
 constexpr int kPB = kBN + 16;  // LDS pitch (bf16) of the B tile [kBK][kBN]: rows 8 banks apart

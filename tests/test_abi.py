@@ -49,8 +49,9 @@ def test_workspace_sizes(L):
     # (512 + 256)^2 fp32 plus a 64 x 64 inverse slot each
     assert L.bllm_coding_rate_workspace(32, 8192, 512) == 32 * 32 * (768 * 768 + 64 * 64) * 4 + 256
     assert L.bllm_coding_rate_workspace(0, 8192, 512) == 0
-    # at most T + T/16 + 1 work items per sequence, 16 bytes each
-    assert L.bllm_upsample_workspace(32, 8192, 2048, 1536, 512, 16) >= 32 * (8192 + 512 + 1) * 16
+    # at most T + T/32 + 1 work items per sequence (one per present bin, one
+    # more per 32 positions of a run), 16 bytes each
+    assert L.bllm_upsample_workspace(32, 8192, 2048, 1536, 512, 16) >= 32 * (8192 + 256 + 1) * 16
 
 
 def test_argument_errors_return_before_any_launch(L):
