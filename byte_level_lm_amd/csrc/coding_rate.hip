@@ -956,8 +956,10 @@ SideStream* side_stream(hipStream_t st) {
     ok = ok && hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess;
     ok = ok && hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
     if (hipSetDevice(cur) != hipSuccess) ok = false;
-    if (!ok) x.st = nullptr;
-    (void)hipGetLastError();
+    if (!ok) {
+      x.st = nullptr;
+      (void)hipGetLastError();  // clear the failure just met (the call then runs on st alone)
+    }
   }
   return x.st ? &x : nullptr;
 }
