@@ -83,9 +83,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
       __syncthreads();
       const uint32_t prefix = sel_prefix;
-      for (int t = max(t0, bos); t < t1; ++t) {
-        const uint32_t k = keys[t];
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 0xFFu], 1u);
+      // each wave takes 64 consecutive keys at a time (no LDS bank
+      // conflicts); the scores crowd into few digits, so the lanes that
+      // share the first active lane's digit add with one atomic
+      const int lane = threadIdx.x & 63;
+      for (int base = bos + static_cast<int>(threadIdx.x) - lane; base < T; base += kTopkThreads) {
+        const int t = base + lane;
+        const bool act = t < T && (keys[t] & mask) == prefix;
+        const uint32_t dg = act ? (keys[t] >> shift) & 0xFFu : 0u;
+        const uint64_t am = __ballot(act);
+        if (am == 0) continue;
+        const int fl = __ffsll(static_cast<unsigned long long>(am)) - 1;
+        const uint32_t d0 = __shfl(dg, fl, 64);
+        const uint64_t m0 = __ballot(act && dg == d0);
+        if (lane == fl) atomicAdd(&hist[d0], static_cast<uint32_t>(__popcll(m0)));
+        if (act && dg != d0) atomicAdd(&hist[dg], 1u);
       }
       __syncthreads();
       if (threadIdx.x < 64) {
