@@ -359,7 +359,7 @@ void launch_route(int gshift, dim3 grid, hipStream_t st, const void* q, const vo
                        total, iters, passes, threshold, p_out, b_out, tau_out, sel);             \
     break;
   switch (gshift) {
-    BLLM_ROUTE_CASE(0) BLLM_ROUTE_CASE(1) BLLM_ROUTE_CASE(2) BLLM_ROUTE_CASE(3)
+    BLLM_ROUTE_CASE(0) BLLM_ROUTE_CASE(1) BLLM_ROUTE_CASE(2) BLLM_ROUTE_CASE(3) BLLM_ROUTE_CASE(4)
   }
 #undef BLLM_ROUTE_CASE
 }
@@ -594,9 +594,11 @@ extern "C" int bllm_route(const void* q, const void* k, int dtype, int64_t d,
   const int vn = dtype == BLLM_F32 ? 4 : 8;
   const int nvec = static_cast<int>(d / vn);
   // 8 lanes per row (fewer for rows of under 8 vectors): 128-byte segments
-  // per load instruction and three DPP steps per reduction
+  // per load instruction and three DPP steps per reduction; 16 lanes for rows
+  // of 96 vectors or more (1.5 KB: stage-2 rows of 768 bf16), 4 DPP steps
   int gshift = 0;
-  while ((1 << gshift) < nvec && gshift < 3) ++gshift;
+  const int gmax = nvec >= 96 ? 4 : 3;
+  while ((1 << gshift) < nvec && gshift < gmax) ++gshift;
   const int iters = static_cast<int>(ceil_div(nvec, 1 << gshift));
   const int64_t rows_per_pass = (256 >> gshift) * kRows;
   const int passes = static_cast<int>(
