@@ -4,7 +4,8 @@
 //   route    p_t = (1 - cos(q_t, k_{t-1})) / 2, p = 1 at the sequence start
 //   compact  the positions with p >= 1/2 and their rows
 //   dechunk  P = 1 gives each byte its chunk's row
-//   coding   orthogonal rows: Delta R_t = 1/2 log(1 + alpha |h_t|^2)
+//   coding   orthogonal rows: Delta R_t = 1/2 log(1 + alpha |h_t|^2); a batch
+//            split over two streams equals its sequences computed alone
 //   top-k    BOS plus the K - 1 largest scores, in time order
 //   upsample g = 0 leaves the residual h unchanged
 // Prints "abi smoke ok" and exits 0 on success.
@@ -149,6 +150,36 @@ int main() {
     EXPECT(std::fabs(dr[t] - want) <= 1e-5 * want, "coding rate closed form");
   }
   EXPECT(to_host(dstat, 1)[0] == 0, "coding rate status");
+
+  // ---- coding rate, a batch large enough to run as two halves on two streams
+  // (2 sequences x 16384 rows, d 64: 2 x 256 row blocks): after synchronising
+  // only `st`, the batch's Delta R equals that of each sequence alone
+  {
+    const int64_t Tb = 16384, db2 = 64, nb = 2;
+    std::vector<float> hb(nb * Tb * db2);
+    uint32_t x = 12345u;
+    for (auto& v : hb) {  // small integers / 64: exact in fp32
+      x = x * 1664525u + 1013904223u;
+      v = static_cast<float>(static_cast<int>(x >> 27) - 16) / 64.f;
+    }
+    float* dhb = to_dev(hb);
+    float* dall = static_cast<float*>(dev_bytes(nb * Tb * 4));
+    float* done = static_cast<float*>(dev_bytes(Tb * 4));
+    const size_t wsb = bllm_coding_rate_workspace(nb, Tb, db2);
+    void* wsbuf = dev_bytes(wsb);
+    EXPECT(dhb && dall && done && wsbuf, "alloc");
+    CK(hipMemset(dstat, 0, 4));
+    OK(bllm_coding_rate(dhb, BLLM_F32, nb, Tb, db2, 0.5, dall, dstat, wsbuf, wsb, st));
+    CK(hipStreamSynchronize(st));
+    const std::vector<float> all = to_host(dall, nb * Tb);
+    for (int64_t q = 0; q < nb; ++q) {
+      OK(bllm_coding_rate(dhb + q * Tb * db2, BLLM_F32, 1, Tb, db2, 0.5, done, dstat, wsbuf, wsb, st));
+      CK(hipStreamSynchronize(st));
+      const std::vector<float> one = to_host(done, Tb);
+      EXPECT(std::memcmp(one.data(), all.data() + q * Tb, Tb * 4) == 0, "split batch = single sequences");
+    }
+    EXPECT(to_host(dstat, 1)[0] == 0, "split batch status");
+  }
 
   // ---- top-k: scores of one sequence, K = 2 -> {0, argmax of the rest}
   std::vector<float> sc = {5.f, 1.f, 7.f, 3.f};
