@@ -288,6 +288,23 @@ def test_coding_rate_split_batch_from_two_host_threads(ops):
             assert int(to_np(status)[0]) == 0
 
 
+
+def test_coding_rate_stream_split_batch_carries_state_per_sequence(ops):
+    """Streaming windows large enough to run as two halves on two streams
+    (4 sequences x 16384-row windows, d 64: 4 x 256 row blocks): the Delta R
+    of both windows and the carried matrices equal, bit for bit, the same
+    windows run for each sequence alone (one stream)."""
+    torch = _torch()
+    rng = np.random.default_rng(62)
+    h = cluster_rows(rng, 4, 32768, 64).astype(np.float32)
+    widths = (16384, 16384)
+    g, A = _stream(ops, h, 0.5, torch.float32, widths)
+    for s_ in range(4):
+        g1, A1 = _stream(ops, h[s_:s_ + 1], 0.5, torch.float32, widths)
+        assert np.array_equal(g[s_], g1[0]), s_
+        assert np.array_equal(A[s_], A1[0]), s_
+
+
 # ------------------------------------------------------------------ streaming chunker
 
 def _stream(ops, h, eps2, dtype, widths, inplace=False):
