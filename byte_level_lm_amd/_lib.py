@@ -12,7 +12,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("BLLM_LIB", os.path.join(_HERE, "libbllm.so"))
 
 OK, E_INVAL, E_NOTSUP, E_WS, E_HIP = 0, -1, -2, -3, -4
-S_CAPACITY, S_NONFINITE = 1, 2
+S_CAPACITY, S_NONFINITE, S_INCOMPLETE = 1, 2, 4
 F32, BF16 = 0, 1
 
 _p = C.c_void_p
@@ -22,9 +22,9 @@ _SIGS = {
     "bllm_status_string": (C.c_char_p, [C.c_int]),
     "bllm_route_workspace": (C.c_size_t, [_i64]),
     "bllm_route": (C.c_int, [_p, _p, C.c_int, _i64, _p, _i64, _i64, C.c_float, C.c_double,
-                             _p, _p, _p, _p, C.c_size_t, _p]),
+                             _p, _p, _p, _p, _p, C.c_size_t, _p]),
     "bllm_route_fused": (C.c_int, [_p, _p, _p, C.c_int, _i64, _p, _i64, _i64, C.c_float, C.c_double,
-                                   _p, _p, _p, _p, C.c_size_t, _p]),
+                                   _p, _p, _p, _p, _p, C.c_size_t, _p]),
     "bllm_compact_workspace": (C.c_size_t, [_i64]),
     "bllm_compact": (C.c_int, [_p, _p, _p, C.c_int, _i64, _p, _i64, _i64, _i64, _p, _p, _p, _p,
                                _p, _p, C.c_size_t, _p]),

@@ -50,6 +50,33 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+def build_variant(out: str, sources, defines, verbose: bool = False) -> str:
+    """A separate library from some of the sources built with extra -D
+    definitions (the tests use one whose bounded device-side waits give up at
+    once, to check how the library reports it).  Objects go to _build/ under a
+    name of their own."""
+    os.makedirs(BUILD, exist_ok=True)
+    tag = os.path.splitext(os.path.basename(out))[0]
+    objs = []
+    for name in sources:
+        src = os.path.join(CSRC, name)
+        obj = os.path.join(BUILD, f"{tag}.{name}.o")
+        cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        objs.append(obj)
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, out)
+    if verbose:
+        print("built", out)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

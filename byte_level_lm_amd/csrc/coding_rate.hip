@@ -28,16 +28,8 @@
 //                   diagonal tile
 // Workspace: nmat = nseq * nblk matrices of ldm^2 fp32 (ldm = d' + c), plus a
 // 64x64 inverse slot per matrix.
-//
-// A batch of at least kSplitMatrices block matrices runs as two halves (whole
-// sequences each): one on the caller's stream, one on a stream the library
-// owns, forked and joined with events.  The halves' launch sequences then
-// overlap, so one half's latency-bound diagonal launches and the partly
-// filled last rounds of its panel launches share the chip with the other
-// half's work (-5% at 32 x 8192 x 512 against one sequence of launches).
 #include <algorithm>
 #include <cmath>
-#include <mutex>
 
 #include "common.h"
 
@@ -62,6 +54,30 @@ __device__ inline floatx16 zero16() {
 #pragma unroll
   for (int r = 0; r < 16; ++r) z[r] = 0.f;
   return z;
+}
+
+// The running prefix sum over the row blocks is kept compensated: each
+// block's Gram is accumulated on its own (from zero) and then added to the
+// running sum hi with its rounding error carried in lo (TwoSum, Knuth), so
+// the prefix matrices carry no accumulated rounding beyond one block's Gram
+// and the final fp32 rounding of hi + lo.
+__device__ inline void two_sum_acc(floatx16& hi, floatx16& lo, const floatx16& blk) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float a = hi[r], b = blk[r];
+    const float s = a + b;
+    const float bb = s - a;
+    const float err = (a - (s - bb)) + (b - bb);
+    hi[r] = s;
+    lo[r] += err;
+  }
+}
+
+__device__ inline floatx16 add16(const floatx16& a, const floatx16& b) {
+  floatx16 c;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c[r] = a[r] + b[r];
+  return c;
 }
 
 struct CRGeom {
@@ -201,27 +217,30 @@ __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h
   const int wm = w >> 1, wn = w & 1;
   const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
   const int64_t hrow0 = static_cast<int64_t>(s) * g.T;
-  floatx16 acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
+  floatx16 hi = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
+  floatx16 lo = zero16();
   for (int j = 0; j <= g.nblk; ++j) {
     if (j == g.nblk) {
-      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
+      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, add16(hi, lo), alpha);
       break;
     }
     float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
-      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
+      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * (hi[r] + lo[r]);
     }
     if (j == g.nblk - 1 && !sout) break;
     const int rbeg = j * g.c, rend = min(rbeg + g.c, g.T);
+    floatx16 blk = zero16();
     for (int r0 = rbeg; r0 < rend; r0 += 32) {
       __syncthreads();
       stage_strip<DT>(h, hrow0, g.d, r0, rend, 64 * I, sI);
       if (I != J) stage_strip<DT>(h, hrow0, g.d, r0, rend, 64 * J, sJ);
       __syncthreads();
-      acc = gram_chunk<DT>(sI, I != J ? sJ : sI, wm, wn, lane, acc);
+      blk = gram_chunk<DT>(sI, I != J ? sJ : sI, wm, wn, lane, blk);
     }
+    two_sum_acc(hi, lo, blk);
   }
 }
 
@@ -296,7 +315,8 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       *reinterpret_cast<uint4*>(sJ + (lr + 96) * GP + lc) = y3;
     }
   };
-  floatx16 acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
+  floatx16 hi = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
+  floatx16 lo = zero16(), acc;
   const uint16_t* sJr = same ? sI : sJ;
   const int j16 = lane & 15;
   const int frow = 8 * (lane >> 5) + (j16 >> 2);                  // + k0
@@ -313,7 +333,7 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
   int q = 0;
   for (int j = 0; j <= g.nblk; ++j) {
     if (j == g.nblk) {
-      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
+      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, add16(hi, lo), alpha);
       break;
     }
     float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
@@ -322,10 +342,11 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
       // streaming stores: the 600 MB of prefix tiles would otherwise push the
       // rows of h that the other tiles of the sequence still read out of L2
-      __builtin_nontemporal_store((row == col ? 1.f : 0.f) + alpha * acc[r],
+      __builtin_nontemporal_store((row == col ? 1.f : 0.f) + alpha * (hi[r] + lo[r]),
                                   Mj + static_cast<int64_t>(row) * g.ldm + col);
     }
     if (j == g.nblk - 1 && !sout) break;
+    acc = zero16();
     for (int sq = 0; sq < spb; ++sq, ++q) {
       lds_barrier();
       stash(ai0, ai1, ai2, ai3, aj0, aj1, aj2, aj3);
@@ -333,6 +354,7 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       fetch_a(q + 1);
       compute();
     }
+    two_sum_acc(hi, lo, acc);
   }
 }
 
@@ -925,45 +947,6 @@ void cr_step(const CRCall& c, int i) {
   }
 }
 
-// The second stream of a split batch: one per device, created on first use
-// and kept until the process ends, with the two events of the fork and join.
-constexpr int kSplitMatrices = 512;
-constexpr int kMaxDevices = 64;
-
-struct SideStream {
-  hipStream_t st = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool tried = false;
-};
-
-std::mutex g_side_mu;  // guards g_side and orders the fork / launches / join of one call
-SideStream g_side[kMaxDevices];
-
-// the side stream of the device that runs st (caller holds g_side_mu); nullptr
-// if it could not be made, and then the batch runs on st alone
-SideStream* side_stream(hipStream_t st) {
-  hipDevice_t dev = 0;
-  if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  SideStream& x = g_side[dev];
-  if (!x.tried) {
-    x.tried = true;
-    int cur = 0;
-    bool ok = hipGetDevice(&cur) == hipSuccess && hipSetDevice(dev) == hipSuccess;
-    ok = ok && hipStreamCreateWithFlags(&x.st, hipStreamNonBlocking) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
-    if (hipSetDevice(cur) != hipSuccess) ok = false;
-    if (!ok) {
-      x.st = nullptr;
-      (void)hipGetLastError();  // clear the failure just met (the call then runs on st alone)
-    }
-  }
-  return x.st ? &x : nullptr;
-}
-
 }  // namespace
 }  // namespace bllm
 
@@ -988,52 +971,23 @@ static int coding_rate_entry(const void* h, int dtype, int64_t nseq, int64_t T, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* wsf = static_cast<float*>(ws);
   float* linv = wsf + static_cast<int64_t>(g.nmat) * g.ldm * g.ldm;
-  const int64_t es = elem_size(dtype);
-  // sequences [s0, s0 + ns) on stream sx: their matrices, inverse slots, rows
-  // of h, dR and carried state are contiguous slices of the batch's
-  auto part = [&](int64_t s0, int64_t ns, hipStream_t sx) {
-    CRCall c;
-    c.g = cr_geometry(ns, T, d);
-    c.h = static_cast<const char*>(h) + s0 * T * d * es;
-    c.alpha = alpha;
-    c.dR = dR_out + s0 * T;
-    c.ws = wsf + s0 * g.nblk * static_cast<int64_t>(g.ldm) * g.ldm;
-    c.linv = linv + s0 * g.nblk * static_cast<int64_t>(NB) * NB;
-    c.sin = state_in ? state_in + s0 * d * d : nullptr;
-    c.sout = state_out ? state_out + s0 * d * d : nullptr;
-    c.status = status;
-    c.st = sx;
-    return c;
-  };
-  auto step = [&](const CRCall& c, int i) {
+  CRCall c;
+  c.g = g;
+  c.h = h;
+  c.alpha = alpha;
+  c.dR = dR_out;
+  c.ws = wsf;
+  c.linv = linv;
+  c.sin = state_in;
+  c.sout = state_out;
+  c.status = status;
+  c.st = st;
+  for (int i = 0; i < cr_steps(g); ++i) {
     if (dtype == BLLM_F32)
       cr_step<BLLM_F32>(c, i);
     else
       cr_step<BLLM_BF16>(c, i);
-  };
-  if (g.nmat < kSplitMatrices || nseq < 2) {
-    const CRCall c = part(0, nseq, st);
-    for (int i = 0; i < cr_steps(g); ++i) step(c, i);
-    return launch_status();
   }
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream* side = side_stream(st);
-  if (!side) {
-    const CRCall c = part(0, nseq, st);
-    for (int i = 0; i < cr_steps(g); ++i) step(c, i);
-    return launch_status();
-  }
-  const int64_t half = (nseq + 1) / 2;
-  if (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(side->st, side->fork, 0) != hipSuccess)
-    return BLLM_E_HIP;
-  // the halves' launches are queued alternately, so both start at once
-  const CRCall a = part(0, half, st), b = part(half, nseq - half, side->st);
-  for (int i = 0; i < cr_steps(g); ++i) {
-    step(a, i);
-    step(b, i);
-  }
-  if (hipEventRecord(side->join, side->st) != hipSuccess || hipStreamWaitEvent(st, side->join, 0) != hipSuccess)
-    return BLLM_E_HIP;
   return launch_status();
 }
 

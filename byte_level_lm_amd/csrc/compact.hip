@@ -7,6 +7,13 @@
 //
 // Three launches: per-tile counts, per-tile wave-ballot prefix + scatter of
 // idx/P/chunk offsets, then a row gather with one lane group per kept row.
+// The scatter finds the number of kept positions before its tile by a
+// look-back over the tile words: the count kernel stores every tile's count,
+// and a scatter block replaces its tile's word by the inclusive prefix (flag
+// bit set) as soon as it knows it; a block sums the counts of the tiles
+// before it, 64 words per step, back to the nearest inclusive prefix.  Every
+// count is in memory before the scatter starts, so no block ever waits on
+// another, and the look-back is short because tiles finish roughly in order.
 // HBM-bound: 1 byte read per position, then (M/N)(8 + 2*d*e) bytes per position.
 #include <algorithm>
 
@@ -66,38 +73,60 @@ __device__ inline int block_excl_scan256(int v, int* sh, int* tot) {
   return wbase + x - v;
 }
 
+constexpr uint64_t kInclusive = uint64_t(1) << 63;  // tile word holds the inclusive prefix
+
 __global__ __launch_bounds__(256) void compact_count(const uint8_t* __restrict__ mask,
-                                                     int64_t total, uint32_t* __restrict__ counts) {
+                                                     int64_t total, uint64_t* __restrict__ words) {
   __shared__ int sh[4];
   const int64_t pos0 = static_cast<int64_t>(blockIdx.x) * kTile + threadIdx.x * 16;
   const int c = __popc(load_flags16(mask, pos0, total));
   int tot;
   block_excl_scan256(c, sh, &tot);
-  if (threadIdx.x == 0) counts[blockIdx.x] = static_cast<uint32_t>(tot);
+  if (threadIdx.x == 0) words[blockIdx.x] = static_cast<uint64_t>(tot);
+}
+
+// number of kept positions in tiles [0, tile): the first wave walks the tile
+// words backwards 64 at a time (lane j reads tile t - j) and stops at the
+// nearest word that holds an inclusive prefix (tiles below 0 count as an
+// inclusive 0); every tile's count is already in memory, so nothing waits
+__device__ inline int64_t tiles_before(const uint64_t* words, int64_t tile) {
+  const int lane = threadIdx.x & 63;
+  int64_t base = 0;
+  for (int64_t t = tile - 1;; t -= 64) {
+    const int64_t i = t - lane;
+    const uint64_t w = i >= 0 ? __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : kInclusive;
+    const uint64_t incl = __ballot((w & kInclusive) != 0);
+    const int stop = incl ? __builtin_ctzll(incl) : 64;
+    int64_t v = lane <= stop ? static_cast<int64_t>(w & ~kInclusive) : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    base += v;
+    if (incl) return base;
+  }
 }
 
 __global__ __launch_bounds__(256) void compact_scatter(
     const uint8_t* __restrict__ mask, const float* __restrict__ p, const int64_t* __restrict__ offsets,
-    int nseq, int64_t total, int64_t capacity, const uint32_t* __restrict__ counts,
+    int nseq, int64_t total, int64_t capacity, uint64_t* __restrict__ words,
     int32_t* __restrict__ idx_out, int64_t* __restrict__ chunk_offsets, float* __restrict__ P_out,
     int64_t* __restrict__ m_out, int32_t* __restrict__ status) {
   __shared__ int sh[4];
-  __shared__ int64_t shb[256];
+  __shared__ int64_t sbase;
   const int tile = blockIdx.x;
-  // base = number of kept positions in all earlier tiles
-  int64_t part = 0;
-  for (int t = threadIdx.x; t < tile; t += blockDim.x) part += counts[t];
-  shb[threadIdx.x] = part;
-  __syncthreads();
-  for (int off = 128; off >= 1; off >>= 1) {
-    if (static_cast<int>(threadIdx.x) < off) shb[threadIdx.x] += shb[threadIdx.x + off];
-    __syncthreads();
-  }
-  const int64_t base = shb[0];
   const int64_t pos0 = static_cast<int64_t>(tile) * kTile + threadIdx.x * 16;
   const uint32_t f = load_flags16(mask, pos0, total);
+  if (threadIdx.x < 64) {
+    const int64_t b = tiles_before(words, tile);
+    if (threadIdx.x == 0) sbase = b;
+  }
   int tile_tot;
-  const int64_t mine = base + block_excl_scan256(__popc(f), sh, &tile_tot);
+  const int64_t local = block_excl_scan256(__popc(f), sh, &tile_tot);  // its barriers also publish sbase
+  const int64_t base = sbase;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(words + tile, kInclusive | static_cast<uint64_t>(base + tile_tot), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  const int64_t mine = base + local;
   uint32_t rest = f;
   int64_t r = mine;
   while (rest) {
@@ -148,7 +177,7 @@ __global__ __launch_bounds__(256) void compact_gather(const uint8_t* __restrict_
 using namespace bllm;
 
 extern "C" size_t bllm_compact_workspace(int64_t total) {
-  return align_up(static_cast<size_t>(ceil_div(total, kTile) + 1) * 4, 256) + 256;
+  return align_up(static_cast<size_t>(ceil_div(total, kTile) + 1) * 8, 256) + 256;
 }
 
 extern "C" int bllm_compact(const uint8_t* mask, const float* p, const void* rows, int dtype,
@@ -167,21 +196,21 @@ extern "C" int bllm_compact(const uint8_t* mask, const float* p, const void* row
   }
   if (!aligned16(mask)) return BLLM_E_NOTSUP;
   if (total >= (int64_t(1) << 31) || nseq >= (int64_t(1) << 30)) return BLLM_E_NOTSUP;
-  if (!ws || ws_bytes < bllm_compact_workspace(total)) return BLLM_E_WS;
+  if (!ws || ws_bytes < bllm_compact_workspace(total) || !aligned16(ws)) return BLLM_E_WS;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t ntiles = ceil_div(total, kTile);
-  uint32_t* counts = static_cast<uint32_t*>(ws);
+  uint64_t* words = static_cast<uint64_t*>(ws);
   int64_t* m_dev = reinterpret_cast<int64_t*>(static_cast<char*>(ws) +
-                                              align_up(static_cast<size_t>(ntiles + 1) * 4, 256));
+                                              align_up(static_cast<size_t>(ntiles + 1) * 8, 256));
   if (total == 0) {
     hipLaunchKernelGGL(fill_i64, dim3(1), dim3(256), 0, st, chunk_offsets_out, nseq + 1, int64_t(0));
     hipLaunchKernelGGL(fill_i64, dim3(1), dim3(64), 0, st, m_dev, int64_t(1), int64_t(0));
     return launch_status();
   }
   hipLaunchKernelGGL(compact_count, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, st, mask,
-                     total, counts);
+                     total, words);
   hipLaunchKernelGGL(compact_scatter, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, st, mask, p,
-                     offsets, static_cast<int>(nseq), total, capacity, counts, idx_out,
+                     offsets, static_cast<int>(nseq), total, capacity, words, idx_out,
                      chunk_offsets_out, P_out, m_dev, status);
   if (rows && capacity > 0) {
     const int row_bytes = static_cast<int>(d * elem_size(dtype));

@@ -93,6 +93,31 @@ struct Tile {
   int64_t c0, c1;
 };
 
+// Chunk offsets as the kernels see them: every entry clamped to the number of
+// chunk rows the caller provides (max_chunks).  When a compaction overflowed
+// its capacity, chunk_offsets hold the true counts while only `capacity` rows
+// of z, P and idx exist; the chunks past the bound are then treated as absent
+// (a sequence cut short keeps its last available chunk to its end, a sequence
+// left without chunks gets zero rows), so no kernel reads or writes past them.
+struct ChunkOffs {
+  const int64_t* p;
+  int64_t cap;
+  __device__ int64_t operator[](int64_t s) const {
+    const int64_t v = p[s];
+    return v < cap ? v : cap;
+  }
+};
+
+// last s in [0, n) with co[s] <= x (co non-decreasing, co[0] <= x)
+__device__ inline int upper_seq(const ChunkOffs& co, int n, int64_t x) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (co[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 __device__ inline Tile tile_range(int64_t M, int64_t i) {
   const int64_t L = (M + kNT - 1) / kNT;
   const int64_t c0 = i * L < M ? i * L : M;
@@ -109,7 +134,7 @@ struct ChunkMeta {
 };
 
 __device__ inline ChunkMeta chunk_meta(const float* __restrict__ P, const int32_t* __restrict__ idx,
-                                       const int64_t* __restrict__ chunk_offsets,
+                                       ChunkOffs chunk_offsets,
                                        const int64_t* __restrict__ offsets, int nseq, int64_t M,
                                        int64_t cb, int64_t ce, int lane) {
   const int64_t c = cb + lane < ce ? cb + lane : ce - 1;
@@ -151,7 +176,7 @@ template <int DT>
 __global__ __launch_bounds__(256) void ema_tile_aggregate(const void* __restrict__ z,
                                                           const float* __restrict__ P, int d,
                                                           const int32_t* __restrict__ idx,
-                                                          const int64_t* __restrict__ chunk_offsets,
+                                                          ChunkOffs chunk_offsets,
                                                           const int64_t* __restrict__ offsets,
                                                           int nseq, float* __restrict__ Aagg,
                                                           float* __restrict__ Uagg,
@@ -316,7 +341,7 @@ template <int DT>
 __global__ __launch_bounds__(256) void ema_tile_expand(const void* __restrict__ z,
                                                        const float* __restrict__ P, int d,
                                                        const int32_t* __restrict__ idx,
-                                                       const int64_t* __restrict__ chunk_offsets,
+                                                       ChunkOffs chunk_offsets,
                                                        const int64_t* __restrict__ offsets, int nseq,
                                                        const float* __restrict__ carry,
                                                        void* __restrict__ out) {
@@ -366,9 +391,10 @@ __global__ __launch_bounds__(256) void ema_tile_expand(const void* __restrict__ 
 
 template <int DT>
 void launch_dechunk(const void* z, const float* P, int d, const int32_t* idx,
-                    const int64_t* chunk_offsets, const int64_t* offsets, int nseq, void* out,
-                    float* ws, hipStream_t st) {
+                    const int64_t* chunk_offsets_in, int64_t max_chunks, const int64_t* offsets, int nseq,
+                    void* out, float* ws, hipStream_t st) {
   constexpr int N = Lane<DT>::N;
+  const ChunkOffs chunk_offsets{chunk_offsets_in, max_chunks};
   float* Aagg = ws;
   float* Uagg = ws + kNT;
   float* carry = Uagg + static_cast<int64_t>(kNT) * d;
@@ -409,7 +435,7 @@ __global__ __launch_bounds__(256) void emab_aggregate(const void* __restrict__ z
                                                       const float* __restrict__ P,
                                                       const void* __restrict__ dout, int d,
                                                       const int32_t* __restrict__ idx,
-                                                      const int64_t* __restrict__ chunk_offsets,
+                                                      ChunkOffs chunk_offsets,
                                                       const int64_t* __restrict__ offsets, int nseq,
                                                       float* __restrict__ Aagg, float* __restrict__ Uf,
                                                       float* __restrict__ Arev, float* __restrict__ Urev,
@@ -516,7 +542,7 @@ __global__ __launch_bounds__(256) void emab_aggregate(const void* __restrict__ z
 template <int DT>
 __global__ __launch_bounds__(256) void emab_reverse(const float* __restrict__ P, int d,
                                                     const int32_t* __restrict__ idx,
-                                                    const int64_t* __restrict__ chunk_offsets,
+                                                    ChunkOffs chunk_offsets,
                                                     const int64_t* __restrict__ offsets, int nseq,
                                                     const float* __restrict__ carry_rev,
                                                     void* __restrict__ lam) {
@@ -571,7 +597,7 @@ template <int DT>
 __global__ __launch_bounds__(256) void emab_forward(const void* __restrict__ z,
                                                     const float* __restrict__ P, int d,
                                                     const int32_t* __restrict__ idx,
-                                                    const int64_t* __restrict__ chunk_offsets,
+                                                    ChunkOffs chunk_offsets,
                                                     const int64_t* __restrict__ offsets, int nseq,
                                                     const float* __restrict__ carry,
                                                     const void* __restrict__ lam,
@@ -632,7 +658,7 @@ __global__ __launch_bounds__(256) void emab_forward(const void* __restrict__ z,
 }
 
 __global__ __launch_bounds__(256) void emab_dp_reduce(const float* __restrict__ dPpart,
-                                                      const int64_t* __restrict__ chunk_offsets, int nseq,
+                                                      ChunkOffs chunk_offsets, int nseq,
                                                       int nslices, int64_t mcap, float* __restrict__ dP) {
   const int64_t M = chunk_offsets[nseq];
   for (int64_t c = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; c < M;
@@ -668,9 +694,10 @@ __host__ inline BwdWs bwd_ws(void* ws, int64_t d, int64_t mcap) {
 
 template <int DT>
 void launch_dechunk_bwd(const void* z, const float* P, const void* dout, int d, const int32_t* idx,
-                        const int64_t* chunk_offsets, const int64_t* offsets, int nseq, int64_t mcap,
+                        const int64_t* chunk_offsets_in, const int64_t* offsets, int nseq, int64_t mcap,
                         void* dz, float* dP, void* ws, hipStream_t st) {
   constexpr int N = Lane<DT>::N;
+  const ChunkOffs chunk_offsets{chunk_offsets_in, mcap};
   const int nslices = (d / N + 63) / 64;
   const BwdWs w = bwd_ws(ws, d, mcap);
   const dim3 grid(kNT / 4, nslices);
@@ -703,7 +730,8 @@ extern "C" int bllm_dechunk_ema(const void* z, const float* P, int dtype, int64_
                                 int64_t max_chunks, void* out, void* ws, size_t ws_bytes,
                                 void* stream) {
   if (!chunk_offsets || !offsets || d < 1 || nseq < 1 || total < 0 || max_chunks < 0) return BLLM_E_INVAL;
-  if (total > 0 && (!z || !P || !idx || !out)) return BLLM_E_INVAL;  // may be NULL for an empty batch
+  if (total > 0 && !out) return BLLM_E_INVAL;  // may be NULL for an empty batch
+  if (total > 0 && max_chunks > 0 && (!z || !P || !idx)) return BLLM_E_INVAL;  // never read without chunks
   if (!valid_dtype(dtype)) return BLLM_E_NOTSUP;
   if ((d * elem_size(dtype)) % 16 != 0 || !aligned16(z) || !aligned16(out)) return BLLM_E_NOTSUP;
   if (total >= (int64_t(1) << 31) || nseq >= (int64_t(1) << 30) || d > (1 << 16)) return BLLM_E_NOTSUP;
@@ -711,10 +739,10 @@ extern "C" int bllm_dechunk_ema(const void* z, const float* P, int dtype, int64_
   if (total == 0) return BLLM_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == BLLM_F32)
-    launch_dechunk<BLLM_F32>(z, P, static_cast<int>(d), idx, chunk_offsets, offsets,
+    launch_dechunk<BLLM_F32>(z, P, static_cast<int>(d), idx, chunk_offsets, max_chunks, offsets,
                              static_cast<int>(nseq), out, static_cast<float*>(ws), st);
   else
-    launch_dechunk<BLLM_BF16>(z, P, static_cast<int>(d), idx, chunk_offsets, offsets,
+    launch_dechunk<BLLM_BF16>(z, P, static_cast<int>(d), idx, chunk_offsets, max_chunks, offsets,
                               static_cast<int>(nseq), out, static_cast<float*>(ws), st);
   return launch_status();
 }

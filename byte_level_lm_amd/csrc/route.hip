@@ -44,8 +44,12 @@ constexpr int kSelDigits = 3;
 // takes 256 threads, 64 VGPRs and 8 KB of LDS, so eight CUs already hold 64
 // of them, and the launch follows the scoring kernel on the same stream.
 // The spin bound (each round sleeps ~100 clocks, ~1 s in all) is never
-// reached in that case; if it were, tau comes out NaN and the kernel ends.
-constexpr uint32_t kSelSpinLimit = 1u << 22;
+// reached in that case; if it were, tau comes out NaN, b is 0 everywhere,
+// BLLM_S_INCOMPLETE is ORed into the caller's status word and the kernel ends.
+#ifndef BLLM_SELECT_SPIN_LIMIT
+#define BLLM_SELECT_SPIN_LIMIT (1u << 22)
+#endif
+constexpr uint32_t kSelSpinLimit = BLLM_SELECT_SPIN_LIMIT;
 constexpr uint32_t kNoKey = 0xFFFFFFFFu;  // past the end: bit 31 set, never selected
 
 struct SelectState {
@@ -135,7 +139,8 @@ __device__ inline void sel_mark(const uint32_t (&key)[kSelPerThread], int64_t n,
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ p, int64_t n,
                                                              uint32_t rank, SelectState* st,
                                                              float* __restrict__ tau_out,
-                                                             uint8_t* __restrict__ b) {
+                                                             uint8_t* __restrict__ b,
+                                                             int32_t* __restrict__ status) {
   __shared__ uint32_t lh[kSelBins];
   __shared__ uint32_t wtot[kSelThreads / kWave];
   __shared__ uint32_t found[2];
@@ -207,6 +212,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   }
   const float tau = ok ? __uint_as_float(prefix) : __builtin_nanf("");
   if (blockIdx.x == 0 && tid == 0 && tau_out != nullptr) *tau_out = tau;
+  if (!ok && tid == 0 && status != nullptr) atomicOr(status, BLLM_S_INCOMPLETE);
   if (resident) {
     sel_mark(key, n, blockIdx.x, tau, b);
   } else {
@@ -576,8 +582,8 @@ extern "C" size_t bllm_route_workspace(int64_t total) {
 
 extern "C" int bllm_route(const void* q, const void* k, int dtype, int64_t d,
                           const int64_t* offsets, int64_t nseq, int64_t total, float threshold,
-                          double quantile, float* p_out, uint8_t* b_out, float* tau_out, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          double quantile, float* p_out, uint8_t* b_out, float* tau_out,
+                          int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   if (!offsets || d < 1 || nseq < 1 || total < 0 || quantile > 1.0) return BLLM_E_INVAL;
   if (total > 0 && (!q || !k || !p_out || !b_out)) return BLLM_E_INVAL;  // may be NULL for an empty batch
   if (!valid_dtype(dtype)) return BLLM_E_NOTSUP;
@@ -619,14 +625,14 @@ extern "C" int bllm_route(const void* q, const void* k, int dtype, int64_t d,
   const uint32_t rank = static_cast<uint32_t>(std::floor(quantile * static_cast<double>(total - 1)));
   const unsigned nblk = static_cast<unsigned>(std::min<int64_t>(kSelMaxBlocks, ceil_div(total, kSelTile)));
   hipLaunchKernelGGL(select_kernel, dim3(nblk), dim3(kSelThreads), 0, st, p_out, total, rank, sst,
-                     tau_out, b_out);
+                     tau_out, b_out, status);
   return launch_status();
 }
 
 extern "C" int bllm_route_fused(const void* h, const void* Wq, const void* Wk, int dtype, int64_t d,
                                 const int64_t* offsets, int64_t nseq, int64_t total, float threshold,
-                                double quantile, float* p_out, uint8_t* b_out, float* tau_out, void* ws,
-                                size_t ws_bytes, void* stream) {
+                                double quantile, float* p_out, uint8_t* b_out, float* tau_out,
+                                int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   if (!Wq || !Wk || !offsets || d < 1 || nseq < 1 || total < 0 || quantile > 1.0) return BLLM_E_INVAL;
   if (total > 0 && (!h || !p_out || !b_out)) return BLLM_E_INVAL;  // may be NULL for an empty batch
   if (dtype != BLLM_BF16) return BLLM_E_NOTSUP;
@@ -650,6 +656,6 @@ extern "C" int bllm_route_fused(const void* h, const void* Wq, const void* Wk, i
   const uint32_t rank = static_cast<uint32_t>(std::floor(quantile * static_cast<double>(total - 1)));
   const unsigned nblk = static_cast<unsigned>(std::min<int64_t>(kSelMaxBlocks, ceil_div(total, kSelTile)));
   hipLaunchKernelGGL(select_kernel, dim3(nblk), dim3(kSelThreads), 0, st, p_out, total, rank, sst,
-                     tau_out, b_out);
+                     tau_out, b_out, status);
   return launch_status();
 }

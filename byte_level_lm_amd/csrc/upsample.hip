@@ -106,63 +106,82 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_count(const int32_t* __res
         wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] + wc[3][threadIdx.x];
 }
 
-// Items grouped by bin, in chunk order inside each bin.  Each block first
-// derives its own slot base per bin from all blocks' counts (the items of
-// earlier blocks, after all items of earlier bins); block 0 also writes the
-// bins' item offsets, counts and GEMM tile offsets.
+// Slot bases of the items: one workgroup turns the per-block counts into,
+// for every (block, bin), the first item slot of that block's items of that
+// bin (all items of earlier bins, then those of earlier blocks), in place,
+// and writes the bins' item offsets, counts and GEMM tile offsets.  Wave w
+// scans bins w, w + 16, ... over the blocks, 64 blocks per step: a first pass
+// for the bin totals, a second for the bases.
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void up_scan(UpGeom g, int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ bin_off,
+                                                        int32_t* __restrict__ bin_cnt,
+                                                        int32_t* __restrict__ tile_off) {
+  __shared__ int sTot[64], sOff[64];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  constexpr int nw = kScanThreads / 64;
+  for (int b = w; b < g.nbins; b += nw) {
+    int tot = 0;
+    for (int k0 = 0; k0 < g.nblk; k0 += 64) {
+      const int k = k0 + lane;
+      int v = k < g.nblk ? counts[static_cast<int64_t>(k) * g.nbins + b] : 0;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+      tot += v;
+    }
+    if (lane == 0) sTot[b] = tot;
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int tb = lane < g.nbins ? sTot[lane] : 0;
+    const int off = wave_excl_i(tb, lane);
+    const int tc = (tb + kBM - 1) / kBM;
+    const int toff = wave_excl_i(tc, lane);
+    if (lane < g.nbins) {
+      sOff[lane] = off;
+      bin_off[lane] = off;
+      bin_cnt[lane] = tb;
+      tile_off[lane] = toff;
+    }
+    if (lane == g.nbins - 1) tile_off[g.nbins] = toff + tc;
+  }
+  __syncthreads();
+  for (int b = w; b < g.nbins; b += nw) {
+    int run = sOff[b];
+    for (int k0 = 0; k0 < g.nblk; k0 += 64) {
+      const int k = k0 + lane;
+      int32_t* cp = counts + static_cast<int64_t>(k < g.nblk ? k : 0) * g.nbins + b;
+      const int v = k < g.nblk ? *cp : 0;
+      int x = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+      }
+      if (k < g.nblk) *cp = run + x - v;
+      run += __shfl(x, 63, kWave);
+    }
+  }
+}
+
+// Items grouped by bin, in chunk order inside each bin: each block takes its
+// slot base per bin from the scanned counts.
 template <int BC>
 __global__ __launch_bounds__(kChunksPerBlock) void up_items(const int32_t* __restrict__ idx, UpGeom g,
-                                                            const int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ bin_off,
-                                                            int32_t* __restrict__ bin_cnt,
-                                                            int32_t* __restrict__ tile_off,
+                                                            const int32_t* __restrict__ base,
                                                             int4* __restrict__ items) {
   __shared__ int wc[4][64];
-  __shared__ int sBefore[4][64], sTot[4][64], sBase[64];
+  __shared__ int sBase[64];
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
-  {
-    // lane = bin; wave w sums blocks [16 w, 16 w + 16) of every 64, sixteen
-    // independent loads in flight at a time
-    int before = 0, tot = 0;
-    for (int k0 = 16 * w; k0 < g.nblk; k0 += 64) {
-      int v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int k = k0 + j;
-        v[j] = lane < g.nbins && k < g.nblk ? counts[static_cast<int64_t>(k) * g.nbins + lane] : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        tot += v[j];
-        if (k0 + j < static_cast<int>(blockIdx.x)) before += v[j];
-      }
-    }
-    sBefore[w][lane] = before;
-    sTot[w][lane] = tot;
-  }
+  if (tid < g.nbins) sBase[tid] = base[static_cast<int64_t>(blockIdx.x) * g.nbins + tid];
   const int64_t cg = static_cast<int64_t>(blockIdx.x) * kChunksPerBlock + tid;
   const bool valid = cg < static_cast<int64_t>(g.nseq) * g.K;
   const int L = valid ? chunk_len(idx, g, cg) : 0;
   for (int b = 0; b < g.nbins; ++b) {
     const int n = wave_sum_i(valid ? bin_pieces<BC>(b, L, g.nbins) : 0);
     if (lane == 0) wc[w][b] = n;
-  }
-  __syncthreads();
-  if (w == 0) {
-    const int tb = sTot[0][lane] + sTot[1][lane] + sTot[2][lane] + sTot[3][lane];
-    const int off = wave_excl_i(tb, lane);
-    sBase[lane] = off + sBefore[0][lane] + sBefore[1][lane] + sBefore[2][lane] + sBefore[3][lane];
-    if (blockIdx.x == 0) {
-      const int tc = (tb + kBM - 1) / kBM;
-      const int toff = wave_excl_i(tc, lane);
-      if (lane < g.nbins) {
-        bin_off[lane] = off;
-        bin_cnt[lane] = tb;
-        tile_off[lane] = toff;
-      }
-      if (lane == g.nbins - 1) tile_off[g.nbins] = toff + tc;
-    }
   }
   __syncthreads();
   const int64_t row0 = valid ? (cg / g.K) * g.T + idx[cg] : 0;
@@ -441,12 +460,12 @@ extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* 
   UpWs u = up_carve(ws, g);
   if (nbins == 16) {
     hipLaunchKernelGGL(up_count<16>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts);
-    hipLaunchKernelGGL(up_items<16>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts,
-                       u.bin_off, u.bin_cnt, u.tile_off, u.items);
+    hipLaunchKernelGGL(up_scan, dim3(1), dim3(kScanThreads), 0, st, g, u.counts, u.bin_off, u.bin_cnt, u.tile_off);
+    hipLaunchKernelGGL(up_items<16>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts, u.items);
   } else {
     hipLaunchKernelGGL(up_count<0>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts);
-    hipLaunchKernelGGL(up_items<0>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts,
-                       u.bin_off, u.bin_cnt, u.tile_off, u.items);
+    hipLaunchKernelGGL(up_scan, dim3(1), dim3(kScanThreads), 0, st, g, u.counts, u.bin_off, u.bin_cnt, u.tile_off);
+    hipLaunchKernelGGL(up_items<0>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts, u.items);
   }
   const int64_t max_tiles = ceil_div(static_cast<int64_t>(up_max_items(g)), kBM) + nbins;
   const int ncol = static_cast<int>(ceil_div(d_local, kBN));

@@ -75,8 +75,10 @@ def upsample_workspace(nseq: int, T: int, K: int, d_global: int, d_local: int, n
 # ------------------------------------------------------------------ ops
 
 def route(q, k, offsets, *, threshold: float = 0.5, quantile=None, p_out=None, b_out=None,
-          tau_out=None, ws=None):
-    """H-Net boundary scores p, mask b and threshold tau (device tensors)."""
+          tau_out=None, status=None, ws=None):
+    """H-Net boundary scores p, mask b and threshold tau (device tensors).
+    `status` (int32 [1], device, optional) receives BLLM_S_INCOMPLETE if the
+    quantile's bounded device-side wait gave up."""
     _dev(q, k, offsets)
     total, d = q.shape
     if k.shape != q.shape or k.dtype != q.dtype or offsets.dtype != torch.int64:
@@ -89,14 +91,14 @@ def route(q, k, offsets, *, threshold: float = 0.5, quantile=None, p_out=None, b
     w = _ws(route_workspace(total), ws, dev) if quantile is not None else ws
     rc = L.lib().bllm_route(q.data_ptr(), k.data_ptr(), _dt(q), d, offsets.data_ptr(),
                             offsets.numel() - 1, total, float(threshold), quant, p_out.data_ptr(),
-                            b_out.data_ptr(), tau_out.data_ptr(), _ptr(w),
+                            b_out.data_ptr(), tau_out.data_ptr(), _ptr(status), _ptr(w),
                             0 if w is None else _nbytes(w), _stream())
     L.check("bllm_route", rc)
     return p_out, b_out, tau_out
 
 
 def route_fused(h, Wq, Wk, offsets, *, threshold: float = 0.5, quantile=None, p_out=None, b_out=None,
-                tau_out=None, ws=None):
+                tau_out=None, status=None, ws=None):
     """bllm_route with q = h Wq and k = h Wk formed inside the kernel (bf16 h, Wq, Wk)."""
     _dev(h, Wq, Wk, offsets)
     total, d = h.shape
@@ -108,7 +110,7 @@ def route_fused(h, Wq, Wk, offsets, *, threshold: float = 0.5, quantile=None, p_
     rc = L.lib().bllm_route_fused(h.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), _dt(h), d, offsets.data_ptr(),
                                   offsets.numel() - 1, total, float(threshold),
                                   -1.0 if quantile is None else float(quantile), p_out.data_ptr(),
-                                  b_out.data_ptr(), tau_out.data_ptr(), _ptr(w),
+                                  b_out.data_ptr(), tau_out.data_ptr(), _ptr(status), _ptr(w),
                                   0 if w is None else _nbytes(w), _stream())
     L.check("bllm_route_fused", rc)
     return p_out, b_out, tau_out

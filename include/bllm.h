@@ -20,9 +20,9 @@
  *   - Tensor arguments are DEVICE pointers to caller-owned memory.  The
  *     library never allocates device memory, frees or synchronises; every
  *     call only enqueues kernels on `stream` (a hipStream_t passed as void*;
- *     NULL is the default stream) and returns.  The one exception is
- *     bllm_coding_rate on large batches, which also forks work onto a stream
- *     of its own and joins it back to `stream` (see there).
+ *     NULL is the default stream) and returns.  The library keeps no state
+ *     between calls (no streams, events or memory of its own), so calls from
+ *     several host threads on different streams are independent.
  *   - Scratch memory comes in through (ws, ws_bytes); its size is given by the
  *     matching bllm_*_workspace() function.  Contents need not be initialised
  *     and are clobbered.  Workspaces must not be shared by calls that may
@@ -62,6 +62,9 @@ extern "C" {
 /* device status flags (ORed into *status) */
 #define BLLM_S_CAPACITY 1  /* compaction produced more rows than `capacity`   */
 #define BLLM_S_NONFINITE 2 /* a NaN/Inf input or a non-positive pivot was met */
+#define BLLM_S_INCOMPLETE 4 /* a bounded device-side wait gave up: the stage
+                               quantile's workgroups were not all resident
+                               within about a second; tau and b are invalid   */
 
 /* dtypes */
 #define BLLM_F32 0
@@ -85,6 +88,10 @@ const char* bllm_status_string(int code);
  * offsets  : int64 [nseq+1] device.
  * p_out    : fp32 [total]; b_out : uint8 [total] (0/1); tau_out : fp32 [1]
  *            device, may be NULL.
+ * status   : optional device word (may be NULL).  With a quantile, the
+ *            threshold is found by one launch whose workgroups meet at
+ *            grid-wide barriers with a bounded wait; if a wait gives up,
+ *            BLLM_S_INCOMPLETE is ORed in and tau (NaN) and b must not be used.
  * ws       : bllm_route_workspace(total) bytes (needed when quantile >= 0).
  * Errors   : BLLM_E_INVAL for null q/k/offsets/p_out/b_out, d < 1, nseq < 1,
  *            total < 0, quantile > 1; BLLM_E_NOTSUP for bad dtype/alignment.
@@ -92,7 +99,8 @@ const char* bllm_status_string(int code);
 size_t bllm_route_workspace(int64_t total);
 int bllm_route(const void* q, const void* k, int dtype, int64_t d, const int64_t* offsets,
                int64_t nseq, int64_t total, float threshold, double quantile, float* p_out,
-               uint8_t* b_out, float* tau_out, void* ws, size_t ws_bytes, void* stream);
+               uint8_t* b_out, float* tau_out, int32_t* status, void* ws, size_t ws_bytes,
+               void* stream);
 
 /*
  * bllm_route_fused -- bllm_route computed straight from the encoder output:
@@ -107,8 +115,8 @@ int bllm_route(const void* q, const void* k, int dtype, int64_t d, const int64_t
  */
 int bllm_route_fused(const void* h, const void* Wq, const void* Wk, int dtype, int64_t d,
                      const int64_t* offsets, int64_t nseq, int64_t total, float threshold,
-                     double quantile, float* p_out, uint8_t* b_out, float* tau_out, void* ws,
-                     size_t ws_bytes, void* stream);
+                     double quantile, float* p_out, uint8_t* b_out, float* tau_out,
+                     int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * bllm_compact -- keep the boundary positions of a ragged batch ([BG] 2.3
@@ -139,11 +147,20 @@ int bllm_compact(const uint8_t* mask, const float* p, const void* rows, int dtyp
  *   out_t = zbar_{c(t)} for every position t of the sequence, c(t) the last chunk
  *   with idx[c] <= t; positions before a sequence's first chunk get 0.
  *
- * z        : [>= M x d] dtype, P : fp32 [M], idx : int32 [M] (global positions,
- *            ascending, inside their sequence), chunk_offsets : int64 [nseq+1]
- *            device (M = chunk_offsets[nseq], read on the device).
- * max_chunks: host upper bound on M (grid sizing; typically the compaction
- *            capacity).  out : [total x d] dtype.
+ * z        : [max_chunks x d] dtype, P : fp32 [max_chunks], idx : int32
+ *            [max_chunks] (global positions, ascending, inside their
+ *            sequence), chunk_offsets : int64 [nseq+1] device (read on the
+ *            device).
+ * max_chunks: the number of chunk rows the caller provides (typically the
+ *            compaction capacity).  Every chunk offset is clamped to it on the
+ *            device, so M = min(chunk_offsets[nseq], max_chunks) chunks are
+ *            used and nothing past row max_chunks - 1 of z, P or idx is read:
+ *            after a compaction that overflowed its capacity (BLLM_S_CAPACITY;
+ *            chunk_offsets then hold the true counts), the chunks it could not
+ *            store are absent -- a sequence cut short keeps its last stored
+ *            chunk to its end, a sequence left without chunks gets zero rows.
+ *            z, P and idx may be NULL when max_chunks = 0.
+ * out      : [total x d] dtype.
  * ws       : bllm_dechunk_workspace(d) bytes.
  */
 size_t bllm_dechunk_workspace(int64_t d);
@@ -167,7 +184,9 @@ int bllm_dechunk_ema(const void* z, const float* P, int dtype, int64_t d, const 
  *            in fp32 from z and P)
  * Arguments as for bllm_dechunk_ema, plus dout : [total x d] dtype (the
  * gradient of out), dz_out : [M x d] dtype (RNE for bf16), dP_out : fp32 [M].
- * max_chunks: host upper bound on M; it also sizes the workspace.
+ * max_chunks: the number of chunk rows provided, clamping the chunk offsets
+ *            exactly as in bllm_dechunk_ema (dz_out and dP_out are written for
+ *            the M used); it also sizes the workspace.
  * ws       : bllm_dechunk_ema_backward_workspace(d, max_chunks) bytes.
  * Errors   : as bllm_dechunk_ema; dout/dz_out must be 16-byte aligned.
  */
@@ -194,17 +213,6 @@ int bllm_dechunk_ema_backward(const void* z, const float* P, const void* dout, i
  *          positive definiteness).
  * Limits : 1 <= d <= 640 (BLLM_E_NOTSUP beyond), T >= 1, eps2 > 0.
  * ws     : bllm_coding_rate_workspace(nseq, T, d) bytes.
- * Streams: a batch of two or more sequences with 512 or more row blocks in
- *          all (nseq * ceil(T / c), c = min(256, d'/2 rounded up to a multiple
- *          of 64), d' = d rounded up to a multiple of 64) runs half of its sequences
- *          on a second stream the library creates on the device of `stream`
- *          at the first such call (kept until the process ends), forked from
- *          and joined back to `stream` with events, so work queued on
- *          `stream` after the call still sees every result.  Under graph
- *          capture, make one such call before capturing (stream creation is
- *          not allowed while capturing); if the stream cannot be created the
- *          batch runs on `stream` alone.  Calls from several host threads are
- *          serialised while they queue their launches.
  */
 size_t bllm_coding_rate_workspace(int64_t nseq, int64_t T, int64_t d);
 int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d, double eps2,
@@ -264,7 +272,7 @@ int bllm_topk_select_window(const float* score, int64_t nseq, int64_t W, int64_t
  * g : [nseq x K x d_global], W : [nbins x d_global x d_local],
  * idx : int32 [nseq x K] (ascending, idx[s*K] = 0), h, s_out : [nseq x T x d_local].
  * dtype must be BLLM_BF16 (bf16 MFMA, fp32 accumulate).
- * Limits: nbins <= 64, d_global % 32 == 0, d_local % 8 == 0, nseq * T < 2^31.
+ * Limits: nbins <= 64, d_global % 8 == 0, d_local % 8 == 0, nseq * T < 2^31.
  * ws : bllm_upsample_workspace(nseq, T, K, d_global, d_local, nbins) bytes
  *      (bin-bucketed work items and a transposed copy of W).
  */

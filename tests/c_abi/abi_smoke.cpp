@@ -87,7 +87,7 @@ int main() {
   uint8_t* db = static_cast<uint8_t*>(dev_bytes(T));
   float* dtau = static_cast<float*>(dev_bytes(4));
   EXPECT(dq && dk && doff && dp && db && dtau, "alloc");
-  OK(bllm_route(dq, dk, BLLM_F32, d, doff, 1, T, 0.5f, -1.0, dp, db, dtau, nullptr, 0, st));
+  OK(bllm_route(dq, dk, BLLM_F32, d, doff, 1, T, 0.5f, -1.0, dp, db, dtau, nullptr, nullptr, 0, st));
   CK(hipStreamSynchronize(st));
   const std::vector<float> p = to_host(dp, T);
   const std::vector<uint8_t> b = to_host(db, T);
@@ -151,9 +151,8 @@ int main() {
   }
   EXPECT(to_host(dstat, 1)[0] == 0, "coding rate status");
 
-  // ---- coding rate, a batch large enough to run as two halves on two streams
-  // (2 sequences x 16384 rows, d 64: 2 x 256 row blocks): after synchronising
-  // only `st`, the batch's Delta R equals that of each sequence alone
+  // ---- coding rate of a batch (2 sequences x 16384 rows, d 64: 2 x 256 row
+  // blocks): the batch's Delta R equals that of each sequence alone, bit for bit
   {
     const int64_t Tb = 16384, db2 = 64, nb = 2;
     std::vector<float> hb(nb * Tb * db2);
@@ -176,9 +175,9 @@ int main() {
       OK(bllm_coding_rate(dhb + q * Tb * db2, BLLM_F32, 1, Tb, db2, 0.5, done, dstat, wsbuf, wsb, st));
       CK(hipStreamSynchronize(st));
       const std::vector<float> one = to_host(done, Tb);
-      EXPECT(std::memcmp(one.data(), all.data() + q * Tb, Tb * 4) == 0, "split batch = single sequences");
+      EXPECT(std::memcmp(one.data(), all.data() + q * Tb, Tb * 4) == 0, "batch = single sequences");
     }
-    EXPECT(to_host(dstat, 1)[0] == 0, "split batch status");
+    EXPECT(to_host(dstat, 1)[0] == 0, "batch status");
   }
 
   // ---- top-k: scores of one sequence, K = 2 -> {0, argmax of the rest}

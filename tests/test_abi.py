@@ -57,13 +57,13 @@ def test_workspace_sizes(L):
 def test_argument_errors_return_before_any_launch(L):
     dummy = C.c_void_p(16)
     # null q
-    assert L.bllm_route(None, dummy, 0, 64, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, 0, None) == -1
+    assert L.bllm_route(None, dummy, 0, 64, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, None, 0, None) == -1
     # bad dtype
-    assert L.bllm_route(dummy, dummy, 7, 64, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, 0, None) == -2
+    assert L.bllm_route(dummy, dummy, 7, 64, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, None, 0, None) == -2
     # d*e not a multiple of 16 bytes
-    assert L.bllm_route(dummy, dummy, 0, 3, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, 0, None) == -2
+    assert L.bllm_route(dummy, dummy, 0, 3, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, None, 0, None) == -2
     # quantile mode without workspace
-    assert L.bllm_route(dummy, dummy, 0, 64, dummy, 1, 10, 0.5, 0.75, dummy, dummy, None, None, 0, None) == -3
+    assert L.bllm_route(dummy, dummy, 0, 64, dummy, 1, 10, 0.5, 0.75, dummy, dummy, None, None, None, 0, None) == -3
     # compact: negative capacity, missing rows_out
     assert L.bllm_compact(dummy, None, None, 0, 0, dummy, 1, 10, -1, dummy, dummy, None, None, None, dummy, 1 << 20, None) == -1
     assert L.bllm_compact(dummy, None, dummy, 0, 64, dummy, 1, 10, 5, dummy, dummy, None, None, None, dummy, 1 << 20, None) == -1
@@ -88,8 +88,8 @@ def test_argument_errors_return_before_any_launch(L):
     # dechunk: null P
     assert L.bllm_dechunk_ema(dummy, None, 1, 512, dummy, dummy, dummy, 1, 10, 10, dummy, dummy, 1 << 30, None) == -1
     # fused route: fp32 unsupported, d not a multiple of 128
-    assert L.bllm_route_fused(dummy, dummy, dummy, 0, 512, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, 0, None) == -2
-    assert L.bllm_route_fused(dummy, dummy, dummy, 1, 192, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, 0, None) == -2
+    assert L.bllm_route_fused(dummy, dummy, dummy, 0, 512, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, None, 0, None) == -2
+    assert L.bllm_route_fused(dummy, dummy, dummy, 1, 192, dummy, 1, 10, 0.5, -1.0, dummy, dummy, None, None, None, 0, None) == -2
     # dechunk backward: null dout, workspace too small
     assert L.bllm_dechunk_ema_backward(dummy, dummy, None, 1, 512, dummy, dummy, dummy, 1, 10, 10, dummy, dummy,
                                        dummy, 1 << 30, None) == -1

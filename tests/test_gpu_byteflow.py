@@ -146,64 +146,71 @@ def test_coding_rate_nonfinite_sets_status(ops):
     assert st & 2
 
 
+def _near_cut_error(g, o, K, width=1e-4):
+    """max |Delta R_gpu - Delta R_oracle| over positions within `width` of the
+    oracle's K-th value (the values that decide the Top-K set)."""
+    vK = np.sort(o[1:])[::-1][K - 2]
+    near = np.abs(o - vK) <= width
+    return float(np.max(np.abs(g[near] - o[near]))) if near.any() else 0.0, int(near.sum())
+
+
+def _topk_sets_vs_oracle(ops, g, H, eps2, K, seqs, tag):
+    """Every listed sequence: all Delta R within 1e-3 relative of the oracle,
+    the Top-K set equal to the oracle's outside the 1e-5 band around the K-th
+    value, and the error near the cut small enough (< 5e-6, half the band)
+    that no position outside the band can change sides."""
+    import torch
+    idx, _, _ = ops.topk_select(to_dev(g), K)
+    idx = to_np(idx)
+    worst = 0.0
+    for s_ in seqs:
+        o = oracle_dr_parallel(H[s_].astype(np.float64), eps2)
+        assert np.max(np.abs(g[s_] - o) / o) < 1e-3, s_
+        bad, nband = topk_band_compare(idx[s_], oracle.topk_select(o, K), o, K)
+        near, nnear = _near_cut_error(g[s_], o, K)
+        worst = max(worst, near)
+        say(tag, "seq", s_, "max abs err", float(np.max(np.abs(g[s_] - o))), "near-cut err", near,
+            "positions within 1e-4", nnear, "band", nband, "flips", len(bad))
+        assert len(bad) == 0, (s_, bad)
+        assert near < 5e-6, (s_, near)
+    say(tag, "worst near-cut error", worst, "over", len(seqs), "sequences")
+
+
 def test_coding_rate_topk_full_size_fp32_8x8192x256(ops):
-    """Full size: 8 x 8192 x 256 fp32.  Sampled Delta R against the oracle
-    in every sequence, then the Top-K set of one full sequence against the
-    oracle's, outside the 1e-5 band around the K-th value."""
+    """Full size: 8 x 8192 x 256 fp32.  Every sequence's Delta R against the
+    oracle and its Top-K set (K = 2048) outside the 1e-5 band."""
     torch = _torch()
     c = gen_coding_rate_fp32()
     say("fp32 8 x 8192 x 256 generated")
     g, st = _dr(ops, c["h"], c["eps2"], torch.float32)
     assert st == 0
-    rng = np.random.default_rng(9)
-    for s in range(c["nseq"]):
-        pos = np.sort(rng.choice(c["T"], 24, replace=False))
-        o = oracle.coding_rate_at(c["h"][s], c["eps2"], pos)
-        assert np.max(np.abs(g[s, pos] - o) / np.abs(o)) < 1e-3
-    o0 = oracle_dr_parallel(c["h"][0].astype(np.float64), c["eps2"])
-    assert np.max(np.abs(g[0] - o0) / o0) < 1e-3
-    idx, mask, _ = ops.topk_select(to_dev(g), c["K"])
-    bad, nband = topk_band_compare(to_np(idx)[0], oracle.topk_select(o0, c["K"]), o0, c["K"])
-    say("fp32 max abs err", np.max(np.abs(g[0] - o0)), "band size", nband)
-    assert len(bad) == 0, bad
+    _topk_sets_vs_oracle(ops, g, c["h"], c["eps2"], c["K"], range(c["nseq"]), "fp32")
 
 
-def test_coding_rate_full_size_bf16_32x8192x512_sampled(ops):
+def test_coding_rate_full_size_bf16_32x8192x512(ops):
+    """Full size: 32 x 8192 x 512 bf16 (the launch configuration of bench.py).
+    Eight of the 32 sequences (every fourth) against the oracle in full:
+    Delta R within 1e-3 relative and the Top-K set outside the 1e-5 band."""
     torch = _torch()
     c = gen_byteflow_layer()
     say("bf16 32 x 8192 x 512 generated")
     g, st = _dr(ops, c["h"], c["eps2"], torch.bfloat16)
     assert st == 0
-    rng = np.random.default_rng(10)
-    for s in (0, 13, 31):
-        pos = np.sort(rng.choice(c["T"], 8, replace=False))
-        o = oracle.coding_rate_at(c["h"][s], c["eps2"], pos)
-        assert np.max(np.abs(g[s, pos] - o) / np.abs(o)) < 1e-3
-    # one whole sequence: every Delta R, then the Top-K set outside the 1e-5 band
-    s = 7
-    say("oracle on one full sequence (parallel workers)")
-    o = oracle_dr_parallel(c["h"][s].astype(np.float64), c["eps2"])
-    assert np.max(np.abs(g[s] - o) / o) < 1e-3
-    idx, _, _ = ops.topk_select(to_dev(g[s:s + 1]), c["K"])
-    bad, nband = topk_band_compare(to_np(idx)[0], oracle.topk_select(o, c["K"]), o, c["K"])
-    say("bf16 seq", s, "max abs err", np.max(np.abs(g[s] - o)), "band size", nband)
-    assert len(bad) == 0, bad
-
+    _topk_sets_vs_oracle(ops, g, c["h"], c["eps2"], c["K"], range(0, 32, 4), "bf16")
 
 
 @pytest.mark.parametrize("dt,nseq,T,d", [("f32", 3, 11000, 64), ("bf16", 2, 65536, 512)])
-def test_coding_rate_split_batch_matches_single_sequences(ops, dt, nseq, T, d):
-    """A batch of 512 or more row blocks runs as two halves on two streams
-    (3 sequences: 2 + 1, with a ragged last block; 2 sequences of 256 blocks:
-    1 + 1).  Each sequence's Delta R must equal, bit for bit, a call on that
-    sequence alone (under 512 blocks: one stream), and sampled positions of
-    the last sequence (the second stream's) match the oracle."""
+def test_coding_rate_batch_matches_single_sequences(ops, dt, nseq, T, d):
+    """Batches of 512 or more row blocks (3 sequences with a ragged last
+    block; 2 sequences of 256 blocks): each sequence's Delta R equals, bit for
+    bit, a call on that sequence alone, and sampled positions of the last
+    sequence match the oracle."""
     torch = _torch()
     rng = np.random.default_rng(50 + d)
     h = cluster_rows(rng, nseq, T, d)
     h = bf16_round(h) if dt == "bf16" else h.astype(np.float32)
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
-    say("split batch", nseq, "x", T, "x", d, dt)
+    say("batch", nseq, "x", T, "x", d, dt)
     g, st = _dr(ops, h, 0.5, tdt)
     assert st == 0
     for s in range(nseq):
@@ -217,21 +224,15 @@ def test_coding_rate_split_batch_matches_single_sequences(ops, dt, nseq, T, d):
 
 
 
-def test_coding_rate_split_batch_in_a_captured_graph(ops):
-    """The two-stream form (fork and join by events) inside a HIP graph: after
-    an eager call, one call is captured; replays with new inputs copied in,
-    eager work and synchronisations between them, each equal the eager result
-    bit for bit."""
+def test_coding_rate_in_a_captured_graph(ops):
+    """A coding-rate call captured in a HIP graph (no warm-up call needed: the
+    library keeps no state); replays with new inputs copied in, eager work and
+    synchronisations between them, each equal the eager result bit for bit."""
     torch = _torch()
     rng = np.random.default_rng(60)
     hs = [cluster_rows(rng, 2, 16384, 64).astype(np.float32) for _ in range(2)]  # 2 x 256 blocks
     want = [_dr(ops, h, 0.5, torch.float32)[0] for h in hs]
     hd = to_dev(hs[0], torch.float32)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        ops.coding_rate(hd, 0.5)
-    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -249,10 +250,9 @@ def test_coding_rate_split_batch_in_a_captured_graph(ops):
 
 
 
-def test_coding_rate_split_batch_from_two_host_threads(ops):
-    """Two host threads, each on a stream of its own, queue split batches at
-    the same time (they share the library's second stream): every result
-    equals the same call made alone."""
+def test_coding_rate_from_two_host_threads(ops):
+    """Two host threads, each on a stream of its own, queue large batches at
+    the same time: every result equals the same call made alone."""
     import threading
     torch = _torch()
     rng = np.random.default_rng(61)
@@ -289,11 +289,10 @@ def test_coding_rate_split_batch_from_two_host_threads(ops):
 
 
 
-def test_coding_rate_stream_split_batch_carries_state_per_sequence(ops):
-    """Streaming windows large enough to run as two halves on two streams
-    (4 sequences x 16384-row windows, d 64: 4 x 256 row blocks): the Delta R
-    of both windows and the carried matrices equal, bit for bit, the same
-    windows run for each sequence alone (one stream)."""
+def test_coding_rate_stream_batch_carries_state_per_sequence(ops):
+    """Streaming windows of a batch (4 sequences x 16384-row windows, d 64:
+    4 x 256 row blocks): the Delta R of both windows and the carried matrices
+    equal, bit for bit, the same windows run for each sequence alone."""
     torch = _torch()
     rng = np.random.default_rng(62)
     h = cluster_rows(rng, 4, 32768, 64).astype(np.float32)
@@ -462,8 +461,8 @@ def test_upsample_vs_oracle(ops, nseq, T, K, dg, dl, B):
 
 def test_byteflow_chain_full_size_bf16_32x8192(ops):
     """32 x 8192 x 512 bf16 at full size (the launch configuration of bench.py): Delta R, Top-K,
-    gather, global stand-in, 16-bin upsample + residual; upsample rows of two
-    sequences checked against the oracle."""
+    gather, global stand-in, 16-bin upsample + residual; every upsample row of
+    four sequences checked against the oracle."""
     torch = _torch()
     bf = torch.bfloat16
     c = gen_byteflow_layer()
@@ -480,9 +479,11 @@ def test_byteflow_chain_full_size_bf16_32x8192(ops):
     g = gen_global_standin(z_np, c)
     s = ops.upsample_bins(to_dev(g, bf), to_dev(c["w_bin"], bf), idx, h_t, c["nbins"])
     s_np = to_np(s)
-    for q in (0, 31):
+    for q in (0, 10, 21, 31):
         ref = oracle.upsample_bins(g[q:q + 1], c["w_bin"], idx_np[q:q + 1], c["h"][q:q + 1], c["nbins"])
-        assert row_rel_err(s_np[q:q + 1], ref) < 2e-2
+        err = row_rel_err(s_np[q:q + 1], ref)
+        say("upsample seq", q, "max row rel err", err)
+        assert err < 2e-2
     say("ByteFlow chain ok")
 
 

@@ -454,15 +454,17 @@ def test_dechunk_backward_full_size_stage1_sampled(ops):
     say("dechunk backward full size ok, M", len(idx))
 
 
-def test_c2_two_stage_full_size(ops):
-    """The headline H-Net workload: 32 streams of 8192 bytes, two stages at the
-    0.75 score quantile each, both EMA scans back to full length (launch
-    configuration of bench.py)."""
+@pytest.mark.parametrize("fixed_T", [8192, None], ids=["T8192", "ragged"])
+def test_c2_two_stage_full_size(ops, fixed_T):
+    """The two-stage H-Net workload at full size: 32 streams (every one 8192
+    bytes, the launch configuration of bench.py, or ragged lengths of 32 x
+    U{32..256} events up to 8192 bytes), two stages at the 0.75 score quantile
+    each, both EMA scans back to full length."""
     torch = _torch()
     bf = torch.bfloat16
-    c = gen_hnet_two_stage(fixed_T=8192)
+    c = gen_hnet_two_stage(fixed_T=fixed_T)
     off = c["offsets"]; N = int(off[-1])
-    say("two-stage 32 x 8192 generated N", N)
+    say("two-stage 32 streams generated, fixed_T", fixed_T, "N", N)
     p1, b1, tau1 = ops.route(to_dev(c["q"], bf), to_dev(c["k"], bf), to_dev(off), quantile=0.75)
     p1g, b1g = to_np(p1), to_np(b1).astype(bool)
     p1o = oracle.route(c["q"], c["k"], off)
@@ -495,3 +497,112 @@ def test_c2_two_stage_full_size(ops):
     outo = oracle.dechunk_ema(y1, P1o, i1o, c1o, off)
     assert row_rel_err(to_np(out), outo) < 2e-2
     say("two-stage chain ok")
+
+
+def test_c1_event_streams_chain_full_size(ops):
+    """The ByteGen-style workload at full size: 16 ragged streams of 32 x
+    U{32..256} events, d 512 bf16, threshold 0.5: route, compact and EMA
+    dechunk of the compacted rows back to byte length, every position and row
+    against the oracle."""
+    torch = _torch()
+    bf = torch.bfloat16
+    c = gen_event_streams()
+    off = c["offsets"]; N = int(off[-1])
+    say("event streams generated N", N, "lengths", np.diff(off).min(), np.diff(off).max())
+    p, b, tau = ops.route(to_dev(c["q"], bf), to_dev(c["k"], bf), to_dev(off), threshold=0.5)
+    p_g, b_g = to_np(p), to_np(b).astype(bool)
+    p_o = oracle.route(c["q"], c["k"], off)
+    assert np.max(np.abs(p_g - p_o)) < 5e-6
+    keep = np.abs(p_o - 0.5) > 1e-5
+    assert np.array_equal(b_g[keep], oracle.boundary_mask(p_o, 0.5)[keep])
+    idx, coff, z, P, st = ops.compact(b, to_dev(off), rows=to_dev(c["h"], bf), p=p)
+    i_o, c_o, z_o, P_o = oracle.compact(b_g, p_g, c["h"], off)
+    M = len(i_o)
+    say("M", M, "ratio", M / N)
+    assert int(to_np(st)[0]) == 0
+    assert np.array_equal(to_np(coff), c_o) and np.array_equal(to_np(idx)[:M], i_o)
+    assert np.array_equal(to_np(z)[:M], z_o) and np.array_equal(to_np(P)[:M], P_o)
+    out = ops.dechunk_ema(z, P, idx, coff, to_dev(off), N)
+    ref = oracle.dechunk_ema(z_o, P_o, i_o, c_o, off)
+    assert row_rel_err(to_np(out), ref) < 2e-2
+    say("event-stream chain ok")
+
+
+def test_dechunk_after_capacity_overflow_stays_in_bounds(ops):
+    """A compaction whose capacity is below the boundary count flags
+    BLLM_S_CAPACITY and keeps the true counts in its chunk offsets; the EMA
+    dechunk and its backward given max_chunks = capacity use only the stored
+    chunks (offsets clamped to the capacity: the sequence cut short keeps its
+    last stored chunk to its end, later sequences get zero rows) and never
+    touch rows past the capacity, which hold sentinel values here."""
+    torch = _torch()
+    rng = np.random.default_rng(77)
+    lengths = np.array([40, 0, 55, 33, 61], np.int64)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    N, d = int(off[-1]), 16
+    b = rng.random(N) < 0.5
+    b[off[:-1][lengths > 0]] = True
+    p = rng.uniform(0.05, 1.0, N).astype(np.float32)
+    h = rng.standard_normal((N, d)).astype(np.float32)
+    M = int(b.sum())
+    i_o, c_o, z_o, P_o = oracle.compact(b, p, h, off)
+    cap = int(c_o[3]) - 2  # drops the last two chunks of sequence 2 and all chunks after it
+    assert c_o[2] < cap
+    # outputs larger than the capacity, the rows past it filled with sentinels
+    # (idx 0 is a valid position: a read past the capacity shows as a wrong result)
+    idx_buf = torch.zeros((M,), dtype=torch.int32, device="cuda")
+    rows_buf = torch.full((M, d), float("nan"), dtype=torch.float32, device="cuda")
+    P_buf = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    idx, coff, z, P, st = ops.compact(to_dev(b.astype(np.uint8)), to_dev(off), rows=to_dev(h), p=to_dev(p),
+                                      capacity=cap, idx_out=idx_buf, rows_out=rows_buf, P_out=P_buf)
+    assert int(to_np(st)[0]) & 1
+    assert np.array_equal(to_np(coff), c_o)  # true counts
+    assert np.array_equal(to_np(idx)[:cap], i_o[:cap]) and np.all(to_np(idx)[cap:] == 0)
+    cc = np.minimum(c_o, cap)
+    out = ops.dechunk_ema(z, P, idx, coff, to_dev(off), N, max_chunks=cap)
+    ref = oracle.dechunk_ema(z_o[:cap], P_o[:cap], i_o[:cap], cc, off)
+    o = to_np(out)
+    assert np.all(np.isfinite(o))
+    assert row_rel_err(o, ref) < 1e-4
+    dout = rng.standard_normal((N, d)).astype(np.float32)
+    dz, dP = ops.dechunk_ema_backward(z, P, to_dev(dout), idx, coff, to_dev(off), max_chunks=cap)
+    dz_o, dP_o = oracle.dechunk_ema_backward(z_o[:cap], P_o[:cap], i_o[:cap], cc, off, dout)
+    dz, dP = to_np(dz), to_np(dP)
+    assert dz.shape[0] == cap and np.all(np.isfinite(dz)) and np.all(np.isfinite(dP))
+    assert row_rel_err(dz, dz_o) < 1e-4
+    assert np.max(np.abs(dP - dP_o)) <= 1e-4 * max(1.0, np.max(np.abs(dP_o)))
+    # no stored chunk at all: every output row is zero
+    out0 = ops.dechunk_ema(z, P, idx, coff, to_dev(off), N, max_chunks=0)
+    assert np.all(to_np(out0) == 0)
+
+
+def test_route_quantile_reports_a_wait_that_gave_up(ops):
+    """The stage quantile's bounded grid-wide waits: the library built with a
+    spin limit of 0 (every wait gives up at once; every kernel still exits
+    normally) ORs BLLM_S_INCOMPLETE into the status word and returns tau = NaN;
+    the real library leaves the word clear on the same input."""
+    import ctypes as C
+    import os
+    torch = _torch()
+    from byte_level_lm_amd import _lib as L
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "libbllm_spin0.so")
+    assert os.path.exists(path), f"{path} not built: run __graft_entry__.build()"
+    spin0 = C.CDLL(path)
+    spin0.bllm_route.restype = C.c_int
+    spin0.bllm_route.argtypes = L._SIGS["bllm_route"][1]
+    rng = np.random.default_rng(78)
+    off, q, k, _ = _ragged(rng, [5000, 7000, 9000], 64, torch.float32)
+    N = int(off[-1])
+    qd, kd, od = to_dev(q), to_dev(k), to_dev(off)
+    for lib, want in ((spin0, L.S_INCOMPLETE), (L.lib(), 0)):
+        p = torch.empty(N, device="cuda"); b = torch.empty(N, dtype=torch.uint8, device="cuda")
+        tau = torch.empty(1, device="cuda"); st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ws = torch.empty(ops.route_workspace(N), dtype=torch.uint8, device="cuda")
+        rc = lib.bllm_route(qd.data_ptr(), kd.data_ptr(), L.F32, 64, od.data_ptr(), 3, N, 0.5, 0.75,
+                            p.data_ptr(), b.data_ptr(), tau.data_ptr(), st.data_ptr(), ws.data_ptr(),
+                            ws.numel(), torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        assert int(to_np(st)[0]) == want
+        t = float(to_np(tau)[0])
+        assert np.isnan(t) if want else t == np.sort(to_np(p))[int(np.floor(0.75 * (N - 1)))]

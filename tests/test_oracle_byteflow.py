@@ -266,3 +266,14 @@ def test_gather_picks_rows_in_time_order():
     idx = np.array([[0, 4, 9], [0, 1, 2]])
     z = oracle.gather(h, idx)
     assert np.array_equal(z[0], h[0, [0, 4, 9]]) and np.array_equal(z[1], h[1, :3])
+
+
+def test_topk_mask_hand_written():
+    """The mask of a boundary set, written out by hand: 1 exactly at the
+    selected positions, one row per sequence, uint8."""
+    m = oracle.topk_mask([[0, 2, 5], [0, 1, 3]], 6)
+    assert m.dtype == np.uint8
+    assert np.array_equal(m, np.array([[1, 0, 1, 0, 0, 1], [1, 1, 0, 1, 0, 0]], np.uint8))
+    one = oracle.topk_mask(np.array([0, 4]), 5)  # a single sequence given as one row
+    assert np.array_equal(one, np.array([[1, 0, 0, 0, 1]], np.uint8))
+    assert np.array_equal(oracle.topk_mask([[0, 1, 2]], 3), np.ones((1, 3), np.uint8))  # K = T
