@@ -177,7 +177,7 @@ class Workload:
     def _stage1(self):
         B = self.B
         B.route(self.q1, self.k1, self.off, quantile=0.75, p_out=self.p1, b_out=self.b1, tau_out=self.tau1,
-                ws=self.ws_route)
+                status=self.st, ws=self.ws_route)
         B.compact(self.b1, self.off, rows=self.h1, p=self.p1, capacity=self.N, idx_out=self.idx1,
                   chunk_offsets_out=self.coff1, rows_out=self.z1, P_out=self.P1, status=self.st,
                   ws=self.ws_compact)
@@ -185,7 +185,7 @@ class Workload:
     def _stage2(self):
         B = self.B
         B.route(self.q2, self.k2, self.coff1, quantile=0.75, p_out=self.p2, b_out=self.b2,
-                tau_out=self.tau2, ws=self.ws_route)
+                tau_out=self.tau2, status=self.st, ws=self.ws_route)
         B.compact(self.b2, self.coff1, rows=self.x2, p=self.p2, capacity=self.M1, idx_out=self.idx2,
                   chunk_offsets_out=self.coff2, rows_out=self.z2, P_out=self.P2, status=self.st,
                   ws=self.ws_compact)
@@ -288,6 +288,101 @@ class Workload:
         }
 
 
+def time_fn(torch, f, reps=7):
+    """Median of `reps` timed calls of f (HIP events on torch's current stream)."""
+    f()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        f()
+        ev1.record()
+        torch.cuda.synchronize()
+        ts.append(ev0.elapsed_time(ev1))
+    return float(np.median(ts))
+
+
+def other_workloads(B, torch):
+    """The other two full-size workloads, each timed on its own (median of 7
+    calls of the whole chain, inputs resident): the ByteGen-style event
+    streams through one H-Net stage (16 ragged streams of 32 x U{32..256}
+    events, d 512 bf16, threshold 0.5: route, compact, EMA dechunk) and the
+    fp32 coding-rate chunker (8 x 8192 x 256, K 2048: Delta R, Top-K,
+    gather)."""
+    from synthdata import gen_event_streams, gen_coding_rate_fp32
+    bf = torch.bfloat16
+    out = {}
+    # ---- event streams, one H-Net stage
+    c = gen_event_streams()
+    off = torch.from_numpy(c["offsets"]).cuda()
+    N = int(c["offsets"][-1])
+    nseq = len(c["offsets"]) - 1
+    q = torch.from_numpy(c["q"]).to("cuda", bf)
+    k = torch.from_numpy(c["k"]).to("cuda", bf)
+    h = torch.from_numpy(c["h"]).to("cuda", bf)
+    p = torch.empty(N, device="cuda")
+    b = torch.empty(N, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(N, dtype=torch.int32, device="cuda")
+    coff = torch.empty(nseq + 1, dtype=torch.int64, device="cuda")
+    z = torch.empty((N, 512), dtype=bf, device="cuda")
+    P = torch.empty(N, device="cuda")
+    o = torch.empty((N, 512), dtype=bf, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wsc = torch.empty(B.compact_workspace(N), dtype=torch.uint8, device="cuda")
+    wsd = torch.empty(B.dechunk_workspace(512), dtype=torch.uint8, device="cuda")
+
+    def c1():
+        B.route(q, k, off, threshold=0.5, p_out=p, b_out=b, status=st)
+        B.compact(b, off, rows=h, p=p, capacity=N, idx_out=idx, chunk_offsets_out=coff, rows_out=z, P_out=P,
+                  status=st, ws=wsc)
+        B.dechunk_ema(z, P, idx, coff, off, N, out=o, ws=wsd, max_chunks=N)
+
+    ms = time_fn(torch, c1)
+    M = int(coff[-1].item())
+    e = 2
+    alg = N * (2 * 512 * e + 5) + N + M * (4 + 4 + 4 + 2 * 512 * e) + M * (512 * e + 8) + N * 512 * e
+    out["event_streams_hnet_stage_B16_ragged"] = {
+        "ms": round(ms, 4), "bytes_per_s": N / (ms * 1e-3), "positions": N, "boundaries": M,
+        "hbm_GBps": round(alg / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "status_word": int(st.item())}
+    del q, k, h, z, o
+    # ---- fp32 coding-rate chunker
+    c = gen_coding_rate_fp32()
+    ns, T, d, K = c["nseq"], c["T"], c["d"], c["K"]
+    hf = torch.from_numpy(c["h"]).cuda()
+    dR = torch.empty((ns, T), device="cuda")
+    ws = torch.empty(B.coding_rate_workspace(ns, T, d), dtype=torch.uint8, device="cuda")
+    sel = torch.empty((ns, K), dtype=torch.int32, device="cuda")
+    mask = torch.empty((ns, T), dtype=torch.uint8, device="cuda")
+    off3 = torch.arange(ns + 1, dtype=torch.int64, device="cuda") * T
+    gidx = torch.empty(ns * K, dtype=torch.int32, device="cuda")
+    co3 = torch.empty(ns + 1, dtype=torch.int64, device="cuda")
+    z3 = torch.empty((ns * K, d), device="cuda")
+    wsc3 = torch.empty(B.compact_workspace(ns * T), dtype=torch.uint8, device="cuda")
+    st.zero_()
+
+    def c3_dr():
+        B.coding_rate(hf, c["eps2"], dR_out=dR, status=st, ws=ws)
+
+    def c3():
+        c3_dr()
+        B.topk_select(dR, K, idx_out=sel, mask_out=mask, status=st)
+        B.compact(mask.view(-1), off3, rows=hf.view(-1, d), capacity=ns * K, idx_out=gidx, chunk_offsets_out=co3,
+                  rows_out=z3, status=st, ws=wsc3)
+
+    ms = time_fn(torch, c3)
+    ms_dr = time_fn(torch, c3_dr)
+    flops = 3 * T * d * d * ns
+    out["coding_rate_fp32_B8_T8192_d256_K2048"] = {
+        "ms": round(ms, 4), "bytes_per_s": ns * T / (ms * 1e-3), "coding_rate_ms": round(ms_dr, 4),
+        "coding_rate_TFLOPs": round(flops / (ms_dr * 1e-3) / 1e12, 2),
+        "coding_rate_fp32_mfma_frac": round(flops / (ms_dr * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+        "status_word": int(st.item())}
+    return out
+
+
 def coding_rate_traffic():
     """HBM bytes per bllm_coding_rate call from the committed rocprofv3 counter
     summary, or None when it is missing or its sources have changed since."""
@@ -341,37 +436,61 @@ def step_roofline(alg, ms):
     return {"ideal_ms": round(ideal, 4), "measured_ms": round(ms, 4), "frac": round(ideal / ms, 4)}
 
 
-def time_ops(wl, reps=5, ops=None):
-    """Average duration of each op (HIP events on the stream the kernels run on)."""
+MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
+
+
+def time_ops(wl, reps=7, ops=None):
+    """Median duration of each op (HIP events on the stream the kernels run
+    on), each call preceded by a write of 512 MB so that no op finds its
+    inputs in the 256 MB Infinity Cache from its previous call."""
     torch = wl.torch
+    flush = torch.empty(MALL_FLUSH_BYTES // 4, device="cuda")
     res = {}
     for name, f in (wl.ops() if ops is None else ops):
         f()
         torch.cuda.synchronize()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record()
+        ts = []
         for _ in range(reps):
+            flush.fill_(1.0)
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record()
             f()
-        ev1.record()
-        torch.cuda.synchronize()
-        res[name] = ev0.elapsed_time(ev1) / reps
+            ev1.record()
+            torch.cuda.synchronize()
+            ts.append(ev0.elapsed_time(ev1))
+        res[name] = float(np.median(ts))
+    del flush
     return res
 
 
-def cpu_baseline(wl):
-    """The oracle, as it stands, on a bounded sample of the same workload, one thread."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_sample(args):
+    """The oracle on one stream of each workload (stream index i), one BLAS
+    thread: per-byte seconds of the H-Net layer, Delta R, Top-K + gather and
+    the upsample, and the seconds spent."""
+    i, dR_i = args
     from threadpoolctl import threadpool_limits
     import oracle
     from synthdata import gen_stage2_inputs, gen_stage2_backproj, gen_global_standin
 
-    hn, bfl = wl.hn, wl.bfl
+    hn, bfl = _POOL_DATA["hn"], _POOL_DATA["bfl"]
     T = 8192
     with threadpool_limits(limits=1):
-        # H-Net two-stage layer on the first stream (8192 bytes)
+        # H-Net two-stage layer on stream i (8192 bytes)
         t0 = time.perf_counter()
         off = np.array([0, T], np.int64)
-        q, k, h = hn["q"][:T], hn["k"][:T], hn["h"][:T]
+        q, k, h = hn["q"][i * T:(i + 1) * T], hn["k"][i * T:(i + 1) * T], hn["h"][i * T:(i + 1) * T]
         p1 = oracle.route(q, k, off)
         tau1 = oracle.stage_quantile(p1, 0.75)
         b1 = oracle.boundary_mask(p1, tau1)
@@ -387,38 +506,66 @@ def cpu_baseline(wl):
         y1 = gen_stage2_backproj(y2, hn)
         oracle.dechunk_ema(y1, P1, i1, co1, off)
         t_hnet = time.perf_counter() - t0
-        # ByteFlow: Delta R on the first 768 positions of stream 0
+        # ByteFlow: Delta R on the first npos positions of stream i
         npos = 3072  # the per-position cost (one d x d Cholesky) does not depend on t
         t0 = time.perf_counter()
-        oracle.coding_rate_at(bfl["h"][0].astype(np.float64), 0.5, np.arange(npos))
+        oracle.coding_rate_at(bfl["h"][i].astype(np.float64), 0.5, np.arange(npos))
         t_dr = time.perf_counter() - t0
-        dr = wl.dR[0:1].cpu().numpy()
         t0 = time.perf_counter()
-        sel = oracle.topk_select(dr, wl.K)
-        z = oracle.gather(bfl["h"][0:1], sel)
+        sel = oracle.topk_select(dR_i[None], _POOL_DATA["K"])
+        z = oracle.gather(bfl["h"][i:i + 1], sel)
         t_topk = time.perf_counter() - t0
         g = gen_global_standin(z, bfl)
         nup = 2048
         t0 = time.perf_counter()
         # upsample of the first nup positions of the stream (same per-position work)
         cmap, bins = oracle.chunk_bins(sel[0], T, bfl["nbins"])
-        hh = bfl["h"][0].astype(np.float64)
+        hh = bfl["h"][i].astype(np.float64)
         W = bfl["w_bin"].astype(np.float64)
         gg = g[0].astype(np.float64)
         for t in range(nup):
             _ = hh[t] + gg[cmap[t]] @ W[bins[t]]
         t_up = time.perf_counter() - t0
-    sec_per_byte = t_hnet / T + t_dr / npos + t_topk / T + t_up / nup
-    total = t_hnet + t_dr + t_topk + t_up
+    return dict(sec_per_byte=t_hnet / T + t_dr / npos + t_topk / T + t_up / nup,
+                secs=(t_hnet, t_dr, t_topk, t_up), npos=npos, nup=nup)
+
+
+_POOL_DATA = {}
+
+
+def cpu_baseline(wl):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    the same per-stream sample (H-Net layer, Delta R at 3072 positions, Top-K
+    + gather, 2048 upsampled positions) once on one core, then on one stream
+    per worker process over all the host cores this process may use (at most
+    16, the GPU's share of the box), each worker on its own stream."""
+    import multiprocessing as mp
+    T = 8192
+    _POOL_DATA.update(hn=wl.hn, bfl=wl.bfl, K=wl.K)
+    dR = wl.dR.cpu().numpy()
+    one = _oracle_sample((0, dR[0]))
+    ncores = max(1, min(16, len(os.sched_getaffinity(0)), wl.nseq))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(ncores) as pool:
+        res = pool.map(_oracle_sample, [(i, dR[i]) for i in range(ncores)])
+    wall = time.perf_counter() - t0
+    # every worker covered one stream's worth of bytes at its own per-byte cost
+    bytes_per_s = sum(1.0 / r["sec_per_byte"] for r in res)
+    t_hnet, t_dr, t_topk, t_up = one["secs"]
     return {
-        "value": 1.0 / sec_per_byte,
+        "value": bytes_per_s,
         "unit": "bytes/s",
-        "cores": 1,
+        "cores": ncores,
         "kind": "oracle",
-        "sample": (f"oracle fp64, 1 thread: H-Net two-stage layer on 1 of the 32 streams ({T} B, "
-                   f"{t_hnet:.1f}s incl. stand-ins), Delta R at the first {npos} positions of one stream "
-                   f"({t_dr:.1f}s), Top-K + gather of one stream ({t_topk:.2f}s), upsample of {nup} "
-                   f"positions ({t_up:.1f}s); per-byte costs summed, {total:.1f}s of CPU work"),
+        "cpu_model": _cpu_model(),
+        "one_core_value": 1.0 / one["sec_per_byte"],
+        "sample": (f"oracle fp64, one BLAS thread per process, {ncores} processes (one stream of the "
+                   f"32 each; {wall:.1f}s wall) after one process alone: per stream the H-Net two-stage "
+                   f"layer ({T} B, {t_hnet:.1f}s alone incl. stand-ins), Delta R at the first "
+                   f"{one['npos']} positions ({t_dr:.1f}s), Top-K + gather ({t_topk:.2f}s), upsample of "
+                   f"{one['nup']} positions ({t_up:.1f}s); per-byte costs summed per stream, the "
+                   f"streams' rates added"),
     }
 
 
@@ -481,22 +628,27 @@ def main():
     alg = wl.algorithmic()
     breakdown = {name: op_rates(alg[name], t) for name, t in per_op.items()}
     cr = alg["coding_rate"]
+    # The 3 T d^2 algorithmic flops of Delta R: the Gram's 2 T d^2 are exact in
+    # bf16 (priced at the bf16 MFMA peak), the solves' T d^2 need fp32 (fp32
+    # MFMA peak).  The op's peak is the blend of the two, flops / ideal time,
+    # so that achieved / peak = ideal time / measured time.
+    ideal_ms = op_ideal_ms("coding_rate", cr)
+    blended_peak = cr["flops"] / (ideal_ms * 1e-3) / 1e12
     roof = {
-        "kernel": ("one bllm_coding_rate call: two halves of 16 sequences on two streams, each "
-                   "cr_gram_prefix_bf16 + 12 cr_diag + 11 cr_panel; fp32 arithmetic "
-                   "(strip products as exact three-part bf16 MFMA, diagonal and TRSM on fp32 MFMA)"),
+        "kernel": ("one bllm_coding_rate call (32 x 8192 x 512 bf16): cr_gram_prefix_bf16 + 12 cr_diag + "
+                   "11 cr_panel; Gram on bf16 MFMA, factorization in fp32 arithmetic (strip products as "
+                   "exact three-part bf16 MFMA, diagonal and TRSM on fp32 MFMA)"),
         "bound": "mfma",
         "achieved": round(cr["flops"] / (dom_ms * 1e-3) / 1e12, 3),
-        "peak": FP32_MFMA_PEAK_TFLOPS,
+        "peak": round(blended_peak, 2),
+        "peak_basis": "2/3 of the flops at 2500 TFLOP/s (bf16 Gram), 1/3 at 157.3 TFLOP/s (fp32 solves)",
         "unit": "TFLOP/s",
         "traffic": coding_rate_traffic(),
     }
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    # the Gram's 2d^2 of the 3d^2 flops per row are exact in bf16: mixed ideal time
-    ideal_ms = (2 * cr["flops"] / 3 / (BF16_MFMA_PEAK_TFLOPS * 1e12) + cr["flops"] / 3 / (FP32_MFMA_PEAK_TFLOPS * 1e12)) * 1e3
     roof["op_ms"] = round(dom_ms, 4)
-    roof["mixed_precision_ideal_ms"] = round(ideal_ms, 4)
-    roof["mixed_precision_frac"] = round(ideal_ms / dom_ms, 4)
+    roof["ideal_ms"] = round(ideal_ms, 4)
+    roof["fp32_only_frac"] = round(roof["achieved"] / FP32_MFMA_PEAK_TFLOPS, 4)
     hnet_ms = sum(per_op[n] for n in ("route+compact stage1", "route+compact stage2", "dechunk stage2", "dechunk stage1"))
     hnet_bytes = sum(alg[n]["bytes"] for n in ("route+compact stage1", "route+compact stage2", "dechunk stage2", "dechunk stage1"))
     out = {
@@ -531,6 +683,9 @@ def main():
     for name, t in time_ops(wl, ops=wl.next_ops()).items():
         nxt[name] = op_rates(nalg[name], t)
     out["next_rows"] = nxt
+    out["status_word"] = int(wl.st.item())  # 0: no capacity overflow, non-finite value or abandoned wait
+    log("timing the other workloads")
+    out["other_workloads"] = other_workloads(wl.B, torch)
     if not args.no_cpu_baseline:
         log("timing the oracle baseline on the host")
         out["cpu_baseline"] = cpu_baseline(wl)
