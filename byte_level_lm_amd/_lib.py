@@ -28,6 +28,8 @@ _SIGS = {
     "bllm_compact_workspace": (C.c_size_t, [_i64]),
     "bllm_compact": (C.c_int, [_p, _p, _p, C.c_int, _i64, _p, _i64, _i64, _i64, _p, _p, _p, _p,
                                _p, _p, C.c_size_t, _p]),
+    "bllm_compact_noalloc": (C.c_int, [_p, _p, _p, C.c_int, _i64, _p, _i64, _i64, _i64, _p, _p, _p, _p,
+                                       _p, _p]),
     "bllm_dechunk_workspace": (C.c_size_t, [_i64]),
     "bllm_dechunk_ema": (C.c_int, [_p, _p, C.c_int, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _p,
                                    C.c_size_t, _p]),

@@ -16,6 +16,8 @@
 // another, and the look-back is short because tiles finish roughly in order.
 // HBM-bound: 1 byte read per position, then (M/N)(8 + 2*d*e) bytes per position.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "common.h"
 
@@ -171,20 +173,69 @@ __global__ __launch_bounds__(256) void compact_gather(const uint8_t* __restrict_
   }
 }
 
+// workspace: the tile words, then the total count M
+constexpr size_t compact_ws_bytes(int64_t total) {
+  return (static_cast<size_t>((total + kTile - 1) / kTile + 1) * 8 + 255) / 256 * 256 + 256;
+}
+
+// ------------------------------------------------------------- no-allocation variant
+// bllm_compact_noalloc runs the same kernels on a scratch array of this file
+// (device memory of the library, one copy per GPU, held until the process
+// ends) instead of a workspace argument, for callers that cannot allocate.
+// The kernels write every word of the scratch they later read (the count
+// kernel stores each tile's word, the scatter stores M), so nothing needs
+// clearing between calls.  Calls that overlap on one GPU share the array and
+// race.
+constexpr int64_t kNoAllocMaxTotal = int64_t(1) << 27;  // 134M positions
+constexpr size_t kNoAllocScratchBytes = compact_ws_bytes(kNoAllocMaxTotal);  // 262,656 bytes
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the GPU that runs `st`, looked up once
+// per device with that device current; nullptr if it cannot be found.
+void* scratch_for(hipStream_t st) {
+  int dev = 0;
+  if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch[dev].load(std::memory_order_relaxed);
+  if (ptr) return ptr;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  bool ok = cur == dev || hipSetDevice(dev) == hipSuccess;
+  ok = ok && hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr != nullptr;
+  if (cur != dev && hipSetDevice(cur) != hipSuccess) ok = false;
+  if (!ok) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
 }  // namespace
 }  // namespace bllm
 
 using namespace bllm;
 
-extern "C" size_t bllm_compact_workspace(int64_t total) {
-  return align_up(static_cast<size_t>(ceil_div(total, kTile) + 1) * 8, 256) + 256;
-}
+extern "C" size_t bllm_compact_workspace(int64_t total) { return compact_ws_bytes(total); }
 
-extern "C" int bllm_compact(const uint8_t* mask, const float* p, const void* rows, int dtype,
-                            int64_t d, const int64_t* offsets, int64_t nseq, int64_t total,
-                            int64_t capacity, int32_t* idx_out, int64_t* chunk_offsets_out,
-                            void* rows_out, float* P_out, int32_t* status, void* ws,
-                            size_t ws_bytes, void* stream) {
+// argument checks shared by both entry points (host only, before any HIP call)
+static int compact_args(const uint8_t* mask, const float* p, const void* rows, int dtype, int64_t d,
+                        const int64_t* offsets, int64_t nseq, int64_t total, int64_t capacity,
+                        const int32_t* idx_out, const int64_t* chunk_offsets_out, const void* rows_out,
+                        const float* P_out) {
   if (!offsets || !chunk_offsets_out || nseq < 1 || total < 0 || capacity < 0) return BLLM_E_INVAL;
   if (total > 0 && (!mask || (capacity > 0 && !idx_out))) return BLLM_E_INVAL;  // NULL allowed when empty
   if ((rows && !rows_out) || (p && !P_out)) return BLLM_E_INVAL;
@@ -196,6 +247,17 @@ extern "C" int bllm_compact(const uint8_t* mask, const float* p, const void* row
   }
   if (!aligned16(mask)) return BLLM_E_NOTSUP;
   if (total >= (int64_t(1) << 31) || nseq >= (int64_t(1) << 30)) return BLLM_E_NOTSUP;
+  return BLLM_OK;
+}
+
+extern "C" int bllm_compact(const uint8_t* mask, const float* p, const void* rows, int dtype,
+                            int64_t d, const int64_t* offsets, int64_t nseq, int64_t total,
+                            int64_t capacity, int32_t* idx_out, int64_t* chunk_offsets_out,
+                            void* rows_out, float* P_out, int32_t* status, void* ws,
+                            size_t ws_bytes, void* stream) {
+  const int rc = compact_args(mask, p, rows, dtype, d, offsets, nseq, total, capacity, idx_out,
+                              chunk_offsets_out, rows_out, P_out);
+  if (rc != BLLM_OK) return rc;
   if (!ws || ws_bytes < bllm_compact_workspace(total) || !aligned16(ws)) return BLLM_E_WS;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t ntiles = ceil_div(total, kTile);
@@ -224,4 +286,18 @@ extern "C" int bllm_compact(const uint8_t* mask, const float* p, const void* row
                        static_cast<uint8_t*>(rows_out));
   }
   return launch_status();
+}
+
+extern "C" int bllm_compact_noalloc(const uint8_t* mask, const float* p, const void* rows, int dtype,
+                                    int64_t d, const int64_t* offsets, int64_t nseq, int64_t total,
+                                    int64_t capacity, int32_t* idx_out, int64_t* chunk_offsets_out,
+                                    void* rows_out, float* P_out, int32_t* status, void* stream) {
+  const int rc = compact_args(mask, p, rows, dtype, d, offsets, nseq, total, capacity, idx_out,
+                              chunk_offsets_out, rows_out, P_out);
+  if (rc != BLLM_OK) return rc;
+  if (total > kNoAllocMaxTotal) return BLLM_E_WS;  // the scratch holds the tile words of 2^27 positions
+  void* ws = scratch_for(static_cast<hipStream_t>(stream));
+  if (!ws) return BLLM_E_HIP;
+  return bllm_compact(mask, p, rows, dtype, d, offsets, nseq, total, capacity, idx_out, chunk_offsets_out,
+                      rows_out, P_out, status, ws, kNoAllocScratchBytes, stream);
 }

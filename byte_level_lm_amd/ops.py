@@ -148,6 +148,37 @@ def compact(mask, offsets, *, rows=None, p=None, capacity=None, idx_out=None,
     return idx_out, chunk_offsets_out, rows_out, P_out, status
 
 
+def compact_noalloc(mask, offsets, *, rows=None, p=None, capacity=None, idx_out=None,
+                    chunk_offsets_out=None, rows_out=None, P_out=None, status=None):
+    """bllm_compact on the library's own scratch array (no workspace; at most
+    2^27 positions).  Outputs must be passed in by a caller that cannot
+    allocate; any left as None are allocated here for convenience."""
+    _dev(mask, offsets, rows, p)
+    total = mask.numel()
+    nseq = offsets.numel() - 1
+    dev = mask.device
+    cap = total if capacity is None else int(capacity)
+    idx_out = torch.empty(max(cap, 1), dtype=torch.int32, device=dev) if idx_out is None else idx_out
+    chunk_offsets_out = (torch.empty(nseq + 1, dtype=torch.int64, device=dev)
+                         if chunk_offsets_out is None else chunk_offsets_out)
+    d = 0
+    dt = L.F32
+    if rows is not None:
+        d = rows.shape[1]
+        dt = _dt(rows)
+        if rows_out is None:
+            rows_out = torch.empty((max(cap, 1), d), dtype=rows.dtype, device=dev)
+    if p is not None and P_out is None:
+        P_out = torch.empty(max(cap, 1), dtype=torch.float32, device=dev)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    rc = L.lib().bllm_compact_noalloc(mask.data_ptr(), _ptr(p), _ptr(rows), dt, d, offsets.data_ptr(), nseq,
+                                      total, cap, idx_out.data_ptr(), chunk_offsets_out.data_ptr(),
+                                      _ptr(rows_out), _ptr(P_out), status.data_ptr(), _stream())
+    L.check("bllm_compact_noalloc", rc)
+    return idx_out, chunk_offsets_out, rows_out, P_out, status
+
+
 def dechunk_ema(z, P, idx, chunk_offsets, offsets, total: int, *, out=None, ws=None,
                 max_chunks=None):
     """EMA over chunks expanded back to `total` byte rows."""

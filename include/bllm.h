@@ -140,6 +140,27 @@ int bllm_compact(const uint8_t* mask, const float* p, const void* rows, int dtyp
                  int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * bllm_compact_noalloc -- bllm_compact for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts that
+ * forbid hipMalloc): the same operation, arguments, outputs and status, with
+ * no workspace argument.  The scratch the kernels need lives in a static
+ * device array of the library (262,656 bytes, one copy per GPU, held until the
+ * process ends); its address is looked up once per device at the first call.
+ * The call allocates nothing and calls no allocating routine.
+ * Limit  : total <= 2^27 (134,217,728 positions), else BLLM_E_WS and nothing
+ *          is enqueued.
+ * Sharing: every call on one GPU uses that GPU's one array, so calls that
+ *          may overlap on the same GPU (other streams, other threads) race;
+ *          calls queued in order on one stream are safe.  The kernels write
+ *          every scratch word before reading it, so no clearing is needed.
+ * Errors : as bllm_compact; BLLM_E_HIP if the array's address cannot be found.
+ */
+int bllm_compact_noalloc(const uint8_t* mask, const float* p, const void* rows, int dtype, int64_t d,
+                         const int64_t* offsets, int64_t nseq, int64_t total, int64_t capacity,
+                         int32_t* idx_out, int64_t* chunk_offsets_out, void* rows_out, float* P_out,
+                         int32_t* status, void* stream);
+
+/*
  * bllm_dechunk_ema -- EMA smoothing back to byte length ([BG] 2.3).
  *
  *   per sequence s, over its chunks c = chunk_offsets[s] .. chunk_offsets[s+1]-1:

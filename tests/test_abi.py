@@ -85,6 +85,11 @@ def test_argument_errors_return_before_any_launch(L):
     # upsample: fp32 unsupported, nbins < 1
     assert L.bllm_upsample_bins(dummy, dummy, dummy, dummy, 0, 1, 64, 4, 64, 32, 16, dummy, dummy, 1 << 30, None) == -2
     assert L.bllm_upsample_bins(dummy, dummy, dummy, dummy, 1, 1, 64, 4, 64, 32, 0, dummy, dummy, 1 << 30, None) == -1
+    # compact without a workspace: more positions than its scratch holds (checked before any HIP call)
+    assert L.bllm_compact_noalloc(dummy, None, None, 0, 0, dummy, 1, (1 << 27) + 1, 5, dummy, dummy, None, None,
+                                  None, None) == -3
+    assert L.bllm_compact_noalloc(dummy, None, None, 0, 0, dummy, 1, 10, -1, dummy, dummy, None, None,
+                                  None, None) == -1
     # dechunk: null P
     assert L.bllm_dechunk_ema(dummy, None, 1, 512, dummy, dummy, dummy, 1, 10, 10, dummy, dummy, 1 << 30, None) == -1
     # fused route: fp32 unsupported, d not a multiple of 128
