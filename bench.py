@@ -38,7 +38,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-op", default=None, help="time only this op in a loop (for rocprofv3)")
+    ap.add_argument("--profile-op", default=None,
+                    help="run only this op (or 'step': the whole step; 'copy': a 1 GiB device copy) "
+                         "--steps times after set-up, untimed (for rocprofv3)")
     return ap.parse_args()
 
 
@@ -590,7 +592,7 @@ def main():
         return
     wl = Workload()
     if args.profile_op:
-        f = dict(wl.ops() + wl.next_ops())[args.profile_op]
+        f = wl.step if args.profile_op == "step" else dict(wl.ops() + wl.next_ops())[args.profile_op]
         for _ in range(args.steps):
             f()
         torch.cuda.synchronize()

@@ -56,30 +56,6 @@ __device__ inline floatx16 zero16() {
   return z;
 }
 
-// The running prefix sum over the row blocks is kept compensated: each
-// block's Gram is accumulated on its own (from zero) and then added to the
-// running sum hi with its rounding error carried in lo (TwoSum, Knuth), so
-// the prefix matrices carry no accumulated rounding beyond one block's Gram
-// and the final fp32 rounding of hi + lo.
-__device__ inline void two_sum_acc(floatx16& hi, floatx16& lo, const floatx16& blk) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float a = hi[r], b = blk[r];
-    const float s = a + b;
-    const float bb = s - a;
-    const float err = (a - (s - bb)) + (b - bb);
-    hi[r] = s;
-    lo[r] += err;
-  }
-}
-
-__device__ inline floatx16 add16(const floatx16& a, const floatx16& b) {
-  floatx16 c;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) c[r] = a[r] + b[r];
-  return c;
-}
-
 struct CRGeom {
   int T, d, dp, c, nblk, ldm, nmat, nseq;
 };
@@ -217,30 +193,27 @@ __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h
   const int wm = w >> 1, wn = w & 1;
   const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
   const int64_t hrow0 = static_cast<int64_t>(s) * g.T;
-  floatx16 hi = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
-  floatx16 lo = zero16();
+  floatx16 acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
   for (int j = 0; j <= g.nblk; ++j) {
     if (j == g.nblk) {
-      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, add16(hi, lo), alpha);
+      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
       break;
     }
     float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
-      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * (hi[r] + lo[r]);
+      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
     }
     if (j == g.nblk - 1 && !sout) break;
     const int rbeg = j * g.c, rend = min(rbeg + g.c, g.T);
-    floatx16 blk = zero16();
     for (int r0 = rbeg; r0 < rend; r0 += 32) {
       __syncthreads();
       stage_strip<DT>(h, hrow0, g.d, r0, rend, 64 * I, sI);
       if (I != J) stage_strip<DT>(h, hrow0, g.d, r0, rend, 64 * J, sJ);
       __syncthreads();
-      blk = gram_chunk<DT>(sI, I != J ? sJ : sI, wm, wn, lane, blk);
+      acc = gram_chunk<DT>(sI, I != J ? sJ : sI, wm, wn, lane, acc);
     }
-    two_sum_acc(hi, lo, blk);
   }
 }
 
@@ -315,8 +288,7 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       *reinterpret_cast<uint4*>(sJ + (lr + 96) * GP + lc) = y3;
     }
   };
-  floatx16 hi = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
-  floatx16 lo = zero16(), acc;
+  floatx16 acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
   const uint16_t* sJr = same ? sI : sJ;
   const int j16 = lane & 15;
   const int frow = 8 * (lane >> 5) + (j16 >> 2);                  // + k0
@@ -333,7 +305,7 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
   int q = 0;
   for (int j = 0; j <= g.nblk; ++j) {
     if (j == g.nblk) {
-      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, add16(hi, lo), alpha);
+      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
       break;
     }
     float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
@@ -342,11 +314,10 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
       // streaming stores: the 600 MB of prefix tiles would otherwise push the
       // rows of h that the other tiles of the sequence still read out of L2
-      __builtin_nontemporal_store((row == col ? 1.f : 0.f) + alpha * (hi[r] + lo[r]),
+      __builtin_nontemporal_store((row == col ? 1.f : 0.f) + alpha * acc[r],
                                   Mj + static_cast<int64_t>(row) * g.ldm + col);
     }
     if (j == g.nblk - 1 && !sout) break;
-    acc = zero16();
     for (int sq = 0; sq < spb; ++sq, ++q) {
       lds_barrier();
       stash(ai0, ai1, ai2, ai3, aj0, aj1, aj2, aj3);
@@ -354,7 +325,6 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       fetch_a(q + 1);
       compute();
     }
-    two_sum_acc(hi, lo, acc);
   }
 }
 

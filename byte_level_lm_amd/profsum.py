@@ -124,9 +124,127 @@ def step_summary(d: str, cmd: str, workload: str, out: str, top: int = 25):
     print("\n".join(lines))
 
 
+# the kernels that open each op of a bench.py step, in step order (the H-Net
+# stage and dechunk ops appear twice: stage 1 then stage 2, stage 2 then 1)
+STEP_OPS = (("route_kernel", ("route+compact stage1", "route+compact stage2")),
+            ("ema_tile_aggregate", ("dechunk stage2", "dechunk stage1")),
+            ("cr_gram_prefix", ("coding_rate",)),
+            ("topk_kernel", ("topk_select",)),
+            ("compact_count", ("gather",)),
+            ("up_count", ("upsample_bins",)))
+STEP_KERNELS = 48  # dispatches of one step (coding rate at d 512: gram + 12 diag + 11 panel)
+MOPS_FLOPS = 512   # SQ_INSTS_VALU_MFMA_MOPS_* count MFMA work in units of 512 flops
+
+
+def _dispatches(path: str):
+    """(dispatch id, short kernel name, row) sorted by dispatch id (the order of enqueue)."""
+    rows = list(csv.DictReader(open(path)))
+    return sorted(((int(r["Dispatch_Id"]), _short(r["Kernel_Name"]), r) for r in rows), key=lambda t: t[0])
+
+
+def _label_step(names):
+    """Op label of every kernel of one step, from the kernels that open each op."""
+    labels, seen, cur = [], {}, None
+    for n in names:
+        for head, ops in STEP_OPS:
+            # compact_count opens the gather only after the Top-K kernel
+            if n.startswith(head) and (head != "compact_count" or cur == "topk_select"):
+                i = seen.get(head, 0)
+                cur = ops[min(i, len(ops) - 1)]
+                seen[head] = i + 1
+                break
+        labels.append(cur)
+    return labels
+
+
+def _last_steps(path: str, nsteps: int):
+    """The dispatches of the last `nsteps` steps, grouped per step: [(kernel, op, row), ...]."""
+    ds = _dispatches(path)
+    ids = sorted({d for d, _, _ in ds})
+    keep = set(ids[-STEP_KERNELS * nsteps:])
+    rows = [(d, n, r) for d, n, r in ds if d in keep]
+    # a counter file has one row per (dispatch, counter): merge them per dispatch
+    per, order = {}, []
+    for d, n, r in rows:
+        if d not in per:
+            per[d] = (n, {}, r)
+            order.append(d)
+        if "Counter_Name" in r:
+            per[d][1][r["Counter_Name"]] = per[d][1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    steps = []
+    for i in range(nsteps):
+        ds_i = order[i * STEP_KERNELS:(i + 1) * STEP_KERNELS]
+        names = [per[d][0] for d in ds_i]
+        labels = _label_step(names)
+        steps.append([(per[d][0], lab, per[d][1], per[d][2]) for d, lab in zip(ds_i, labels)])
+    return steps
+
+
+def step_kernels(a):
+    """Per (op, kernel) table of one bench.py step: time from the kernel trace
+    (mean over the traced steps), HBM bytes from FETCH_SIZE / WRITE_SIZE
+    (calibrated by the copy), MFMA flops from SQ_INSTS_VALU_MFMA_MOPS_*."""
+    tsteps = _last_steps(_one(a.trace, "*kernel_trace.csv"), a.trace_steps)
+    dur = {}
+    for st in tsteps:
+        for n, lab, _, r in st:
+            key = (lab, n)
+            dur.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    per_step = a.trace_steps
+
+    def counters(d, name):
+        if not d:
+            return {}
+        out = {}
+        for n, lab, c, _ in _last_steps(_one(d, "*counter_collection.csv"), 1)[0]:
+            if name in c:
+                out[(lab, n)] = out.get((lab, n), 0.0) + c[name]
+        return out
+
+    fs = a.copy_bytes / (counter_copy(a.copy_fetch, "FETCH_SIZE") * 1024) if a.copy_fetch else None
+    wsc = a.copy_bytes / (counter_copy(a.copy_write, "WRITE_SIZE") * 1024) if a.copy_write else None
+    fetch = counters(a.fetch, "FETCH_SIZE")
+    write = counters(a.write, "WRITE_SIZE")
+    mb = counters(a.mfma, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    mf = counters(a.mfma, "SQ_INSTS_VALU_MFMA_MOPS_F32")
+    lines = [f"# rocprofv3 summary: {a.workload}", "", "Commands (run from the repository root on the GPU host):",
+             "", "```", a.cmd, "```", "",
+             f"One step = the last {STEP_KERNELS} dispatches of each run.  Time: mean over the last "
+             f"{a.trace_steps} traced steps of each kernel's summed durations per step.  Bytes: "
+             f"FETCH_SIZE x {fs:.3f} and WRITE_SIZE x {wsc:.3f} (KiB per dispatch, scaled by a "
+             f"{a.copy_bytes}-byte device copy), summed per step.  MFMA: SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32 "
+             f"x {MOPS_FLOPS} flops; fraction of the 2500 (bf16) and 157.3 (fp32) TFLOP/s dense peaks.",
+             "", "| op | kernel | launches | us per step | read GB | written GB | GB/s | HBM frac | "
+             "bf16 TFLOP/s | fp32 TFLOP/s | MFMA frac |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    block = []
+    for key in sorted(dur, key=lambda k: [lab for _, lab in STEP_OPS for lab in lab].index(k[0])
+                      if k[0] in [x for _, l in STEP_OPS for x in l] else 99):
+        lab, n = key
+        us = sum(dur[key]) / per_step
+        launches = len(dur[key]) / per_step
+        rd = fetch.get(key, float("nan")) * 1024 * fs / 1e9 if fs else float("nan")
+        wr = write.get(key, float("nan")) * 1024 * wsc / 1e9 if wsc else float("nan")
+        gbs = (rd + wr) / (us * 1e-6)
+        bft = mb.get(key, 0.0) * MOPS_FLOPS / (us * 1e-6) / 1e12
+        f3t = mf.get(key, 0.0) * MOPS_FLOPS / (us * 1e-6) / 1e12
+        mfrac = bft / 2500.0 + f3t / 157.3
+        lines.append(f"| {lab} | {n} | {launches:g} | {us:.1f} | {rd:.3f} | {wr:.3f} | {gbs:.0f} | "
+                     f"{gbs / 8000:.3f} | {bft:.1f} | {f3t:.1f} | {mfrac:.3f} |")
+        block.append({"op": lab, "kernel": n, "launches": launches, "us": round(us, 2), "read_GB": round(rd, 4),
+                      "write_GB": round(wr, 4), "GBps": round(gbs), "bf16_TFLOPs": round(bft, 1),
+                      "fp32_TFLOPs": round(f3t, 1), "mfma_frac": round(mfrac, 4)})
+    lines += ["", "```json", json.dumps({"step_kernels": block}), "```", ""]
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--op", required=True, choices=sorted(OPS) + ["step"])
+    ap.add_argument("--op", required=True, choices=sorted(OPS) + ["step", "step-kernels"])
+    ap.add_argument("--mfma", help="--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 ... run")
+    ap.add_argument("--trace-steps", type=int, default=3, help="steps in the kernel-trace run (step-kernels)")
     ap.add_argument("--trace", required=True)
     ap.add_argument("--fetch")
     ap.add_argument("--write")
@@ -141,6 +259,9 @@ def main():
     ap.add_argument("--workload", required=True)
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.op == "step-kernels":
+        step_kernels(a)
+        return
     if a.op == "step":
         step_summary(a.trace, a.cmd, a.workload, a.out)
         return
