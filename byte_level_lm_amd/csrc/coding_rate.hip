@@ -927,10 +927,19 @@ extern "C" size_t bllm_coding_rate_workspace(int64_t nseq, int64_t T, int64_t d)
   return cr_ws_bytes(cr_geometry(nseq, T, d));
 }
 
+// The caller's second stream and two events (all caller-owned; NULL for the
+// one-stream form) split the batch into two halves of whole sequences: the
+// first half on `stream`, the second on `stream2`, forked from `stream` by
+// recording `fork` and joined back by recording `join` on `stream2` and
+// making `stream` wait for it, so work queued on `stream` after the call sees
+// every result.  The halves' launches are queued alternately, so one half's
+// latency-bound diagonal launches run beside the other half's panel work.
 static int coding_rate_entry(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d, double eps2,
                              const float* state_in, float* state_out, float* dR_out, int32_t* status,
-                             void* ws, size_t ws_bytes, void* stream) {
+                             void* ws, size_t ws_bytes, void* stream, void* stream2 = nullptr,
+                             void* fork = nullptr, void* join = nullptr) {
   if (!h || !dR_out || nseq < 1 || T < 1 || d < 1 || !(eps2 > 0.0)) return BLLM_E_INVAL;
+  if (stream2 && (!fork || !join || stream2 == stream)) return BLLM_E_INVAL;
   if (!valid_dtype(dtype)) return BLLM_E_NOTSUP;
   if (d > 640 || nseq > 65535 || T > (int64_t(1) << 24)) return BLLM_E_NOTSUP;
   if ((d * elem_size(dtype)) % 16 != 0 || !aligned16(h)) return BLLM_E_NOTSUP;
@@ -938,26 +947,47 @@ static int coding_rate_entry(const void* h, int dtype, int64_t nseq, int64_t T, 
   if (static_cast<int64_t>(g.nmat) * g.nblk > (int64_t(1) << 31)) return BLLM_E_NOTSUP;
   if (!ws || ws_bytes < cr_ws_bytes(g) || !aligned16(ws)) return BLLM_E_WS;
   const double alpha = static_cast<double>(d) / eps2;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   float* wsf = static_cast<float*>(ws);
   float* linv = wsf + static_cast<int64_t>(g.nmat) * g.ldm * g.ldm;
-  CRCall c;
-  c.g = g;
-  c.h = h;
-  c.alpha = alpha;
-  c.dR = dR_out;
-  c.ws = wsf;
-  c.linv = linv;
-  c.sin = state_in;
-  c.sout = state_out;
-  c.status = status;
-  c.st = st;
-  for (int i = 0; i < cr_steps(g); ++i) {
+  const int64_t es = elem_size(dtype);
+  // sequences [s0, s0 + ns) on stream sx: their matrices, inverse slots, rows
+  // of h, dR and carried state are contiguous slices of the batch's
+  auto part = [&](int64_t s0, int64_t ns, hipStream_t sx) {
+    CRCall c;
+    c.g = cr_geometry(ns, T, d);
+    c.h = static_cast<const char*>(h) + s0 * T * d * es;
+    c.alpha = alpha;
+    c.dR = dR_out + s0 * T;
+    c.ws = wsf + s0 * g.nblk * static_cast<int64_t>(g.ldm) * g.ldm;
+    c.linv = linv + s0 * g.nblk * static_cast<int64_t>(NB) * NB;
+    c.sin = state_in ? state_in + s0 * d * d : nullptr;
+    c.sout = state_out ? state_out + s0 * d * d : nullptr;
+    c.status = status;
+    c.st = sx;
+    return c;
+  };
+  auto step = [&](const CRCall& c, int i) {
     if (dtype == BLLM_F32)
       cr_step<BLLM_F32>(c, i);
     else
       cr_step<BLLM_BF16>(c, i);
+  };
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!stream2 || nseq < 2) {
+    const CRCall c = part(0, nseq, st);
+    for (int i = 0; i < cr_steps(g); ++i) step(c, i);
+    return launch_status();
   }
+  hipStream_t st2 = static_cast<hipStream_t>(stream2);
+  hipEvent_t evf = static_cast<hipEvent_t>(fork), evj = static_cast<hipEvent_t>(join);
+  if (hipEventRecord(evf, st) != hipSuccess || hipStreamWaitEvent(st2, evf, 0) != hipSuccess) return BLLM_E_HIP;
+  const int64_t half = (nseq + 1) / 2;
+  const CRCall a = part(0, half, st), b = part(half, nseq - half, st2);
+  for (int i = 0; i < cr_steps(g); ++i) {
+    step(a, i);
+    step(b, i);
+  }
+  if (hipEventRecord(evj, st2) != hipSuccess || hipStreamWaitEvent(st, evj, 0) != hipSuccess) return BLLM_E_HIP;
   return launch_status();
 }
 
@@ -971,4 +1001,12 @@ extern "C" int bllm_coding_rate_stream(const void* h, int dtype, int64_t nseq, i
                                        double eps2, const float* state_in, float* state_out, float* dR_out,
                                        int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   return coding_rate_entry(h, dtype, nseq, W, d, eps2, state_in, state_out, dR_out, status, ws, ws_bytes, stream);
+}
+
+extern "C" int bllm_coding_rate_split(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d, double eps2,
+                                      float* dR_out, int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                                      void* stream2, void* fork_event, void* join_event) {
+  if (!stream2) return BLLM_E_INVAL;
+  return coding_rate_entry(h, dtype, nseq, T, d, eps2, nullptr, nullptr, dR_out, status, ws, ws_bytes, stream,
+                           stream2, fork_event, join_event);
 }

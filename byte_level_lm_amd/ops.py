@@ -233,6 +233,26 @@ def coding_rate(h, eps2: float, *, dR_out=None, status=None, ws=None):
     return dR_out, status
 
 
+def coding_rate_split(h, eps2: float, stream2, fork_event, join_event, *, dR_out=None, status=None, ws=None):
+    """coding_rate with the batch's second half on `stream2` (a torch.cuda.Stream),
+    forked and joined with the caller's two torch.cuda.Event objects."""
+    _dev(h)
+    nseq, T, d = h.shape
+    dev = h.device
+    dR_out = torch.empty((nseq, T), dtype=torch.float32, device=dev) if dR_out is None else dR_out
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+    w = _ws(coding_rate_workspace(nseq, T, d), ws, dev)
+    for ev in (fork_event, join_event):
+        if not ev.cuda_event:  # torch creates the event at its first record
+            ev.record()
+    rc = L.lib().bllm_coding_rate_split(h.data_ptr(), _dt(h), nseq, T, d, float(eps2), dR_out.data_ptr(),
+                                        status.data_ptr(), w.data_ptr(), _nbytes(w), _stream(),
+                                        stream2.cuda_stream, fork_event.cuda_event, join_event.cuda_event)
+    L.check("bllm_coding_rate_split", rc)
+    return dR_out, status
+
+
 def coding_rate_stream(h, eps2: float, state_in=None, *, state_out=None, want_state=True, dR_out=None,
                        status=None, ws=None):
     """Delta R_t of one window h [nseq, W, d] of a stream, given the carried

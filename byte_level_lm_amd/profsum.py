@@ -132,7 +132,7 @@ STEP_OPS = (("route_kernel", ("route+compact stage1", "route+compact stage2")),
             ("topk_kernel", ("topk_select",)),
             ("compact_count", ("gather",)),
             ("up_count", ("upsample_bins",)))
-STEP_KERNELS = 48  # dispatches of one step (coding rate at d 512: gram + 12 diag + 11 panel)
+STEP_KERNELS = 72  # dispatches of one step (coding rate at d 512 in two halves: 2 x (gram + 12 diag + 11 panel))
 MOPS_FLOPS = 512   # SQ_INSTS_VALU_MFMA_MOPS_* count MFMA work in units of 512 flops
 
 
@@ -157,11 +157,11 @@ def _label_step(names):
     return labels
 
 
-def _last_steps(path: str, nsteps: int):
+def _last_steps(path: str, nsteps: int, per_step: int = STEP_KERNELS):
     """The dispatches of the last `nsteps` steps, grouped per step: [(kernel, op, row), ...]."""
     ds = _dispatches(path)
     ids = sorted({d for d, _, _ in ds})
-    keep = set(ids[-STEP_KERNELS * nsteps:])
+    keep = set(ids[-per_step * nsteps:])
     rows = [(d, n, r) for d, n, r in ds if d in keep]
     # a counter file has one row per (dispatch, counter): merge them per dispatch
     per, order = {}, []
@@ -173,7 +173,7 @@ def _last_steps(path: str, nsteps: int):
             per[d][1][r["Counter_Name"]] = per[d][1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     steps = []
     for i in range(nsteps):
-        ds_i = order[i * STEP_KERNELS:(i + 1) * STEP_KERNELS]
+        ds_i = order[i * per_step:(i + 1) * per_step]
         names = [per[d][0] for d in ds_i]
         labels = _label_step(names)
         steps.append([(per[d][0], lab, per[d][1], per[d][2]) for d, lab in zip(ds_i, labels)])
@@ -184,7 +184,7 @@ def step_kernels(a):
     """Per (op, kernel) table of one bench.py step: time from the kernel trace
     (mean over the traced steps), HBM bytes from FETCH_SIZE / WRITE_SIZE
     (calibrated by the copy), MFMA flops from SQ_INSTS_VALU_MFMA_MOPS_*."""
-    tsteps = _last_steps(_one(a.trace, "*kernel_trace.csv"), a.trace_steps)
+    tsteps = _last_steps(_one(a.trace, "*kernel_trace.csv"), a.trace_steps, a.step_kernels)
     dur = {}
     for st in tsteps:
         for n, lab, _, r in st:
@@ -196,7 +196,7 @@ def step_kernels(a):
         if not d:
             return {}
         out = {}
-        for n, lab, c, _ in _last_steps(_one(d, "*counter_collection.csv"), 1)[0]:
+        for n, lab, c, _ in _last_steps(_one(d, "*counter_collection.csv"), 1, a.step_kernels)[0]:
             if name in c:
                 out[(lab, n)] = out.get((lab, n), 0.0) + c[name]
         return out
@@ -209,7 +209,7 @@ def step_kernels(a):
     mf = counters(a.mfma, "SQ_INSTS_VALU_MFMA_MOPS_F32")
     lines = [f"# rocprofv3 summary: {a.workload}", "", "Commands (run from the repository root on the GPU host):",
              "", "```", a.cmd, "```", "",
-             f"One step = the last {STEP_KERNELS} dispatches of each run.  Time: mean over the last "
+             f"One step = the last {a.step_kernels} dispatches of each run.  Time: mean over the last "
              f"{a.trace_steps} traced steps of each kernel's summed durations per step.  Bytes: "
              f"FETCH_SIZE x {fs:.3f} and WRITE_SIZE x {wsc:.3f} (KiB per dispatch, scaled by a "
              f"{a.copy_bytes}-byte device copy), summed per step.  MFMA: SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32 "
@@ -245,6 +245,7 @@ def main():
     ap.add_argument("--op", required=True, choices=sorted(OPS) + ["step", "step-kernels"])
     ap.add_argument("--mfma", help="--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 ... run")
     ap.add_argument("--trace-steps", type=int, default=3, help="steps in the kernel-trace run (step-kernels)")
+    ap.add_argument("--step-kernels", type=int, default=STEP_KERNELS, help="dispatches per step (step-kernels)")
     ap.add_argument("--trace", required=True)
     ap.add_argument("--fetch")
     ap.add_argument("--write")

@@ -240,6 +240,25 @@ int bllm_coding_rate(const void* h, int dtype, int64_t nseq, int64_t T, int64_t 
                      float* dR_out, int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * bllm_coding_rate_split -- bllm_coding_rate with the batch split over two
+ * streams of the caller: the first half of the sequences on `stream`, the
+ * second on `stream2`, forked from `stream` by recording `fork_event` there
+ * and joined back by recording `join_event` on `stream2` and making `stream`
+ * wait for it.  Work queued on `stream` after the call sees every result; the
+ * halves' launch sequences overlap, so one half's latency-bound launches run
+ * beside the other half's work.  Each sequence's values are bit-identical to
+ * the one-stream call's.  The streams (on the same device) and the events are
+ * caller-owned (created beforehand, e.g. outside a graph capture; the call
+ * records and waits on them and creates nothing).  A call on a one-sequence
+ * batch runs on `stream` alone.
+ * Errors : as bllm_coding_rate; BLLM_E_INVAL for a NULL stream2, fork or join
+ *          event, or stream2 == stream; BLLM_E_HIP if recording or waiting fails.
+ */
+int bllm_coding_rate_split(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d, double eps2,
+                           float* dR_out, int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                           void* stream2, void* fork_event, void* join_event);
+
+/*
  * bllm_coding_rate_stream -- the coding rate of one window of a byte stream
  * (the streaming chunker that the [BF4] weakness analysis suggests for
  * autoregressive inference: a sliding window with a local Top-K).  The

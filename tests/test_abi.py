@@ -71,6 +71,13 @@ def test_argument_errors_return_before_any_launch(L):
     assert L.bllm_coding_rate(dummy, 0, 1, 8, 8, 0.0, dummy, None, dummy, 1 << 30, None) == -1
     assert L.bllm_coding_rate(dummy, 0, 1, 8, 1024, 0.5, dummy, None, dummy, 1 << 30, None) == -2
     assert L.bllm_coding_rate(dummy, 0, 1, 64, 8, 0.5, dummy, None, dummy, 16, None) == -3
+    # split coding rate: no second stream or events, second stream equal to the first
+    assert L.bllm_coding_rate_split(dummy, 0, 2, 64, 8, 0.5, dummy, None, dummy, 1 << 30, None, None, dummy,
+                                    dummy) == -1
+    assert L.bllm_coding_rate_split(dummy, 0, 2, 64, 8, 0.5, dummy, None, dummy, 1 << 30, dummy, dummy, dummy,
+                                    dummy) == -1
+    assert L.bllm_coding_rate_split(dummy, 0, 2, 64, 8, 0.5, dummy, None, dummy, 1 << 30, None, dummy, None,
+                                    dummy) == -1
     # top-k: K > T, K < 1, T too large
     assert L.bllm_topk_select(dummy, 1, 10, 11, dummy, None, None, None) == -1
     assert L.bllm_topk_select(dummy, 1, 10, 0, dummy, None, None, None) == -1

@@ -224,6 +224,55 @@ def test_coding_rate_batch_matches_single_sequences(ops, dt, nseq, T, d):
 
 
 
+@pytest.mark.parametrize("dt,nseq,T,d", [("f32", 3, 11000, 64), ("bf16", 32, 8192, 512)])
+def test_coding_rate_split_equals_one_stream(ops, dt, nseq, T, d):
+    """The batch split over the caller's two streams (3 sequences: 2 + 1 with a
+    ragged last block; the full 32 x 8192 x 512 bf16 workload, 16 + 16):
+    bit-identical to the one-stream call, read after synchronising only the
+    caller's stream."""
+    torch = _torch()
+    rng = np.random.default_rng(63 + d)
+    h = cluster_rows(rng, nseq, T, d)
+    h = bf16_round(h) if dt == "bf16" else h.astype(np.float32)
+    hd = to_dev(h, torch.bfloat16 if dt == "bf16" else torch.float32)
+    say("split vs one stream", nseq, "x", T, "x", d, dt)
+    one, st1 = ops.coding_rate(hd, 0.5)
+    torch.cuda.synchronize()
+    s2, fe, je = torch.cuda.Stream(), torch.cuda.Event(), torch.cuda.Event()
+    for rep in range(2):
+        two, st2 = ops.coding_rate_split(hd, 0.5, s2, fe, je)
+        torch.cuda.current_stream().synchronize()
+        assert np.array_equal(to_np(two), to_np(one)), rep
+        assert int(to_np(st2)[0]) == 0 and int(to_np(st1)[0]) == 0
+
+
+def test_coding_rate_split_in_a_captured_graph(ops):
+    """The two-stream form captured in a HIP graph (the fork and join events
+    recorded inside the capture): replays with new inputs equal the eager
+    one-stream result bit for bit."""
+    torch = _torch()
+    rng = np.random.default_rng(64)
+    hs = [cluster_rows(rng, 2, 16384, 64).astype(np.float32) for _ in range(2)]
+    want = [_dr(ops, h, 0.5, torch.float32)[0] for h in hs]
+    hd = to_dev(hs[0], torch.float32)
+    s2, fe, je = torch.cuda.Stream(), torch.cuda.Event(), torch.cuda.Event()
+    ops.coding_rate_split(hd, 0.5, s2, fe, je)  # creates the events before the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out, st = ops.coding_rate_split(hd, 0.5, s2, fe, je)
+    for r in range(4):
+        i = r % 2
+        hd.copy_(torch.from_numpy(hs[i]).to(hd.device))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say("split graph replay", r)
+        assert np.array_equal(to_np(out), want[i]), r
+        assert int(to_np(st)[0]) == 0
+        _dr(ops, hs[1 - i][:1, :4096], 0.5, torch.float32)  # eager work between replays
+
+
 def test_coding_rate_in_a_captured_graph(ops):
     """A coding-rate call captured in a HIP graph (no warm-up call needed: the
     library keeps no state); replays with new inputs copied in, eager work and
