@@ -38,6 +38,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", default="after_dr", choices=["after_dr", "with_dr", "serial"],
+                    help="where the H-Net layer runs in a step: on a stream of its own beside Top-K, gather "
+                         "and upsample (after_dr, the default) or beside Delta R (with_dr), or every op on "
+                         "one stream in turn (serial); the other two are timed as well")
     ap.add_argument("--profile-op", default=None,
                     help="run only this op (or 'step': the whole step; 'copy': a 1 GiB device copy) "
                          "--steps times after set-up, untimed (for rocprofv3)")
@@ -121,6 +125,11 @@ class Workload:
         # (forked from and joined back to the current stream by two events)
         self.cr_stream2 = torch.cuda.Stream()
         self.cr_fork, self.cr_join = torch.cuda.Event(), torch.cuda.Event()
+        # the H-Net layer shares no buffer with the ByteFlow chain: in a step it
+        # runs on a stream of its own, forked from and joined back to the
+        # current stream
+        self.h_stream = torch.cuda.Stream()
+        self.h_fork, self.h_join = torch.cuda.Event(), torch.cuda.Event()
         self.ws_cr = torch.empty(B.coding_rate_workspace(self.nseq, T, 512), dtype=torch.uint8, device=dev)
         self.idx4 = torch.empty((self.nseq, self.K), dtype=torch.int32, device=dev)
         self.mask4 = torch.empty((self.nseq, T), dtype=torch.uint8, device=dev)
@@ -266,9 +275,46 @@ class Workload:
                 ("coding_rate", self._coding_rate), ("topk_select", self._topk),
                 ("gather", self._gather), ("upsample_bins", self._upsample)]
 
-    def step(self):
-        for _, f in self.ops():
-            f()
+    def hnet_ops(self):
+        return self.ops()[:4]
+
+    def byteflow_ops(self):
+        return self.ops()[4:]
+
+    def step(self, dom=None, schedule="after_dr"):
+        """One pass of the whole path.  The H-Net layer (stage 1 and 2 routing
+        and compaction, both dechunks) and the ByteFlow chain (Delta R, Top-K,
+        gather, upsample) take different inputs and share no buffer.
+        schedule "serial" queues every op on the current stream in turn; the
+        others run the H-Net layer on a stream of its own, forked from the
+        current stream at the start of the step ("with_dr") or once Delta R is
+        queued, beside Top-K, gather and upsample ("after_dr"), and joined back
+        before the step ends.  dom: a pair of events recorded around the coding
+        rate on the current stream."""
+        torch = self.torch
+        cur = torch.cuda.current_stream()
+
+        def fork_hnet():
+            self.h_fork.record(cur)
+            self.h_stream.wait_event(self.h_fork)
+            with torch.cuda.stream(self.h_stream):
+                for _, f in self.hnet_ops():
+                    f()
+                self.h_join.record(self.h_stream)
+
+        if schedule == "with_dr":
+            fork_hnet()
+        for name, f in (self.ops() if schedule == "serial" else self.byteflow_ops()):
+            if dom is not None and name == "coding_rate":
+                dom[0].record(cur)
+                f()
+                dom[1].record(cur)
+            else:
+                f()
+            if name == "coding_rate" and schedule == "after_dr":
+                fork_hnet()
+        if schedule != "serial":
+            cur.wait_event(self.h_join)
 
     # ------------------------------------------------------------ algorithmic work
     def algorithmic(self):
@@ -435,6 +481,11 @@ def op_ideal_ms(name, a):
     else:
         t_mfma = f / (a.get("peak_tflops", BF16_MFMA_PEAK_TFLOPS) * 1e12)
     return max(t_hbm, t_mfma) * 1e3
+
+
+SCHEDULES = {"after_dr": "H-Net layer on a stream of its own beside Top-K, gather and upsample",
+             "with_dr": "H-Net layer on a stream of its own beside Delta R",
+             "serial": "every op on one stream in turn"}
 
 
 def step_roofline(alg, ms):
@@ -604,33 +655,34 @@ def main():
         log("profiled", args.profile_op, args.steps, "launches")
         return
     for _ in range(args.warmup):
-        wl.step()
+        for sch in SCHEDULES:
+            wl.step(schedule=sch)
     torch.cuda.synchronize()
     log("warmup done")
-    # the dominant op is bracketed by events of its own inside the timed steps
-    # (all ops are queued on torch's current stream; the coding rate's second
-    # stream is joined back to it before the closing event)
+    # the dominant op is bracketed by events of its own on the current stream
+    # inside the timed steps (the coding rate's second stream is joined back
+    # to it before the closing event)
     dom_name = "coding_rate"
-    dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(args.steps):
-        for name, f in wl.ops():
-            if name == dom_name:
-                dom_ev[i][0].record()
-                f()
-                dom_ev[i][1].record()
-            else:
-                f()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    dom_ms = sum(a.elapsed_time(b) for a, b in dom_ev) / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f}s)")
+
+    def timed_steps(schedule):
+        dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(args.steps):
+            wl.step(dom=dom_ev[i], schedule=schedule)
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = ev0.elapsed_time(ev1) / args.steps
+        dom_ms = sum(a.elapsed_time(b) for a, b in dom_ev) / args.steps
+        log(f"timed {args.steps} steps ({schedule}): {ms:.3f} ms/step (wall {wall:.2f}s)")
+        return ms, dom_ms
+
+    ms, dom_ms = timed_steps(args.schedule)
+    others = {sch: timed_steps(sch) for sch in SCHEDULES if sch != args.schedule}
     per_op = time_ops(wl)
     alg = wl.algorithmic()
     breakdown = {name: op_rates(alg[name], t) for name, t in per_op.items()}
@@ -677,9 +729,13 @@ def main():
                                              "M1": wl.M1, "M2": wl.M2},
                    "byteflow": {"d_local": 512, "d_global": 1536, "K": 2048, "bins": 16, "eps2": 0.5,
                                 "upsample_items": wl.up_items},
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "schedule": SCHEDULES[args.schedule]},
         "roofline": roof,
         "step_roofline": step_roofline(alg, ms),
+        "other_schedules": {sch: {"schedule": SCHEDULES[sch], "ms_per_step": round(t[0], 4),
+                                  "value": wl.N / (t[0] * 1e-3), "coding_rate_ms": round(t[1], 4)}
+                            for sch, t in others.items()},
         "dominant_op": dom_name,
         "breakdown": breakdown,
         "hnet_layer": {"ms": round(hnet_ms, 4), "bytes_per_s": wl.N / (hnet_ms * 1e-3),

@@ -331,9 +331,11 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
 // ------------------------------------------------------------------ diagonal tile
 
 
-// Factor the 64x64 tile D (lower triangle; LDS, row stride ldd) with one wave
-// of a larger workgroup: the logs of its pivots that fall in the S part go to
-// dR, the inverse of the factor to Li (LDS, row stride lip).  2x2 blocks of 32, lane i owns row i:
+// Factor the 64x64 tile D (lower triangle, row stride ldd) with one wave of a
+// larger workgroup: the logs of its pivots that fall in the S part go to dR,
+// the inverse of the factor to Li (row stride lip) unless want_inv is false
+// (the last diagonal tile of a matrix: steps 3 and 4 are then skipped).
+// 2x2 blocks of 32, lane i owns row i:
 //   1. eliminate columns 0..31 over all 64 rows  -> L11 (lanes 0..31), L21 (lanes 32..63)
 //   2. D22 - L21 L21^T, eliminate columns 32..63  -> L22 (lanes 32..63)
 //   3. columns of L11^-1 (lanes 0..31) and L22^-1 (lanes 32..63) by forward
@@ -360,7 +362,7 @@ __device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMI
 
 __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, float* __restrict__ sW,
                                          float* __restrict__ Li, int lip, float* __restrict__ dR_blk,
-                                         int rr0, int cj, int32_t* __restrict__ status) {
+                                         int rr0, int cj, int32_t* __restrict__ status, bool want_inv = true) {
   float* col = sW;                 // [64]    column broadcast
   float* rinv = sW + 64;           // [64]    reciprocals of the diagonal of L
   float* sL = sW + 128;            // [64][kF] rows of L11 (0..31) and L21 (32..63)
@@ -441,6 +443,11 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
     for (int q = 0; q < 32; ++q) sT22[q * kF + ih] = q <= ih ? b[q] : 0.f;
   }
   rinv[i] = rd;
+  if (dR_blk != nullptr) {
+    const int rr = rr0 + i;  // row of the block (S part)
+    if (rr >= 0 && rr < cj) dR_blk[rr] = __logf(piv);  // hardware log2 scaled by ln 2
+  }
+  if (!want_inv) return;
   wave_lds_sync();
   // 3. lane m < 32: column m of L11^-1; lane 32+m: column m of L22^-1.
   // sT holds L^T, so column p of L is the contiguous row p of sT.
@@ -495,10 +502,6 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
       y = mfma32(sT22[ih * kF + 2 * st + (i >> 5)], sL[(2 * st + (i >> 5)) * kF + ih], y);
 #pragma unroll
     for (int r = 0; r < 16; ++r) Li[(32 + crow(r, i)) * lip + ih] = -y[r];
-  }
-  if (dR_blk != nullptr) {
-    const int rr = rr0 + i;  // row of the block (S part)
-    if (rr >= 0 && rr < cj) dR_blk[rr] = __logf(piv);  // hardware log2 scaled by ln 2
   }
 }
 
@@ -634,8 +637,9 @@ __global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __r
   if (NB * k >= block_n(g, j)) return;
   const float* D = ws + static_cast<int64_t>(m) * g.ldm * g.ldm + static_cast<int64_t>(NB * k) * g.ldm + NB * k;
   float* dRb = NB * k >= g.dp ? dR + static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c : nullptr;
+  // the last diagonal tile of a matrix has no rows below it: no inverse
   factor64(D, g.ldm, sW, linv + static_cast<int64_t>(m) * NB * NB, NB, dRb, NB * k - g.dp,
-           block_rows(g, j), status);
+           block_rows(g, j), status, NB * (k + 1) < block_n(g, j));
 }
 
 template <int DT>
