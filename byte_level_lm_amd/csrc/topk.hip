@@ -10,16 +10,20 @@
 // forces no position: its K largest scores are kept.
 //
 // One workgroup (1024 threads) per sequence.  Scores become order-preserving
-// uint32 keys in LDS (NaN -> 0, the lowest; -0 -> +0), an 8-bit radix select
-// finds the key of the (K-1)-th largest, ties at that key are resolved by time
-// order with a block scan, and a second block scan compacts the chosen
-// positions in time order.
+// uint32 keys (NaN -> 0, the lowest; -0 -> +0), an 8-bit radix select finds
+// the key of the (K-1)-th largest, ties at that key are resolved by time order
+// with a block scan, and a second block scan compacts the chosen positions in
+// time order.  Up to kLdsKeys positions the keys are kept in LDS; longer
+// sequences (up to 64 positions per thread) recompute them from the scores,
+// which stay in L2, in every pass.
 #include "common.h"
 
 namespace bllm {
 namespace {
 
 constexpr int kTopkThreads = 1024;
+constexpr int kLdsKeys = 16384;                 // keys kept in LDS (64 KB) up to this length
+constexpr int kMaxT = 64 * kTopkThreads;        // one 64-bit selection word per thread
 
 __device__ inline uint32_t order_key(float x, bool* nan) {
   uint32_t u = __float_as_uint(x);
@@ -57,19 +61,28 @@ __device__ inline int block_excl_scan1024(int v, int* sh, int* tot) {
   return r;
 }
 
+template <bool kInLds>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ score, int T,
                                                             int K, int bos, int32_t* __restrict__ idx_out,
                                                             uint8_t* __restrict__ mask_out,
                                                             int32_t* __restrict__ status) {
-  extern __shared__ uint32_t keys[];  // [T]
+  extern __shared__ uint32_t lkeys[];  // [T] when kInLds
   __shared__ uint32_t hist[256];
   __shared__ int scan_sh[40];
   __shared__ uint32_t sel_prefix, sel_want;
   const int s = blockIdx.x;
   const float* sc = score + static_cast<int64_t>(s) * T;
   bool nan = false;
-  for (int t = threadIdx.x; t < T; t += blockDim.x) keys[t] = t == 0 && bos ? 0u : order_key(sc[t], &nan);
+  for (int t = threadIdx.x; t < T; t += blockDim.x) {
+    const uint32_t k = t == 0 && bos ? 0u : order_key(sc[t], &nan);
+    if (kInLds) lkeys[t] = k;
+  }
   if (nan && status) atomicOr(status, BLLM_S_NONFINITE);
+  auto key = [&](int t) {
+    if (kInLds) return lkeys[t];
+    bool ignored = false;
+    return t == 0 && bos ? 0u : order_key(sc[t], &ignored);
+  };
   const int per = (T + kTopkThreads - 1) / kTopkThreads;
   const int t0 = threadIdx.x * per;
   const int t1 = min(t0 + per, T);
@@ -89,8 +102,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       const int lane = threadIdx.x & 63;
       for (int base = bos + static_cast<int>(threadIdx.x) - lane; base < T; base += kTopkThreads) {
         const int t = base + lane;
-        const bool act = t < T && (keys[t] & mask) == prefix;
-        const uint32_t dg = act ? (keys[t] >> shift) & 0xFFu : 0u;
+        const uint32_t kt = t < T ? key(t) : 0u;
+        const bool act = t < T && (kt & mask) == prefix;
+        const uint32_t dg = act ? (kt >> shift) & 0xFFu : 0u;
         const uint64_t am = __ballot(act);
         if (am == 0) continue;
         const int fl = __ffsll(static_cast<unsigned long long>(am)) - 1;
@@ -134,19 +148,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
   // rank of each equal key in time order
   int neq = 0;
-  for (int t = max(t0, bos); t < t1; ++t) neq += keys[t] == kth;
+  for (int t = max(t0, bos); t < t1; ++t) neq += key(t) == kth;
   int tot;
   int eq_rank = block_excl_scan1024(neq, scan_sh, &tot);
   int nsel = 0;
-  uint32_t selbits = 0;  // per <= 32
+  uint64_t selbits = 0;  // per <= 64
   for (int t = t0; t < t1; ++t) {
     bool sel;
+    const uint32_t kt = key(t);
     if (t == 0 && bos) sel = true;
     else if (want0 <= 0) sel = false;
-    else if (keys[t] > kth) sel = true;
-    else if (keys[t] == kth) sel = static_cast<uint32_t>(eq_rank++) < take_eq;
+    else if (kt > kth) sel = true;
+    else if (kt == kth) sel = static_cast<uint32_t>(eq_rank++) < take_eq;
     else sel = false;
-    if (sel) { selbits |= 1u << (t - t0); ++nsel; }
+    if (sel) { selbits |= uint64_t(1) << (t - t0); ++nsel; }
   }
   int pos = block_excl_scan1024(nsel, scan_sh, &tot);
   int32_t* out = idx_out + static_cast<int64_t>(s) * K;
@@ -165,11 +180,15 @@ using namespace bllm;
 static int topk_entry(const float* score, int64_t nseq, int64_t T, int64_t K, int bos, int32_t* idx_out,
                       uint8_t* mask_out, int32_t* status, void* stream) {
   if (!score || !idx_out || nseq < 1 || T < 1 || K < 1 || K > T) return BLLM_E_INVAL;
-  if (T > 16384 || nseq > 0x7FFFFFFF) return BLLM_E_NOTSUP;
+  if (T > kMaxT || nseq > 0x7FFFFFFF) return BLLM_E_NOTSUP;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const size_t shmem = static_cast<size_t>(T) * 4;
-  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(nseq)), dim3(kTopkThreads), shmem, st,
-                     score, static_cast<int>(T), static_cast<int>(K), bos, idx_out, mask_out, status);
+  if (T <= kLdsKeys)
+    hipLaunchKernelGGL(topk_kernel<true>, dim3(static_cast<unsigned>(nseq)), dim3(kTopkThreads),
+                       static_cast<size_t>(T) * 4, st, score, static_cast<int>(T), static_cast<int>(K), bos,
+                       idx_out, mask_out, status);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(static_cast<unsigned>(nseq)), dim3(kTopkThreads), 0, st,
+                       score, static_cast<int>(T), static_cast<int>(K), bos, idx_out, mask_out, status);
   return launch_status();
 }
 

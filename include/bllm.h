@@ -287,7 +287,9 @@ int bllm_coding_rate_stream(const void* h, int dtype, int64_t nseq, int64_t W, i
  *   BLLM_S_NONFINITE); -0.0 equals +0.0.
  * score : fp32 [nseq x T].  idx_out : int32 [nseq x K] (positions inside the
  * sequence, idx_out[s*K] = 0).  mask_out : uint8 [nseq x T] or NULL.
- * Limits: 1 <= K <= T <= 16384 (the scores of one sequence live in LDS).
+ * Limits: 1 <= K <= T <= 65536 (BLLM_E_NOTSUP above).  Up to T = 16384 the
+ * keys of a sequence live in LDS; longer sequences re-read their scores from
+ * memory in every radix pass.
  */
 int bllm_topk_select(const float* score, int64_t nseq, int64_t T, int64_t K, int32_t* idx_out,
                      uint8_t* mask_out, int32_t* status, void* stream);

@@ -55,6 +55,24 @@ def test_topk_ties_specials_and_ragged_sizes(ops):
     assert int(to_np(st)[0]) & 2
 
 
+def test_topk_long_sequences_from_memory(ops):
+    """Past 16384 positions the keys are recomputed from the scores in every
+    radix pass (up to 64 positions per thread): ties, signed zeros, +-inf and
+    a NaN, then real-valued scores, at lengths across that switch."""
+    rng = np.random.default_rng(4)
+    for T in (16385, 32768, 40000, 65536):
+        sc = rng.integers(0, 7, size=(2, T)).astype(np.float32)
+        sc[0, ::7] = -0.0
+        sc[1, ::11] = np.inf
+        sc[1, 3::13] = -np.inf
+        for K in (1, 2, T // 4, T - 1, T):
+            _topk_check(ops, sc, K)
+    sc = rng.standard_normal((3, 65536)).astype(np.float32)
+    sc[2, 1000] = np.nan
+    st = _topk_check(ops, sc, 8192)
+    assert int(to_np(st)[0]) & 2
+
+
 def test_topk_full_size_c3_shape(ops):
     rng = np.random.default_rng(3)
     sc = rng.standard_normal((8, 8192)).astype(np.float32)
