@@ -173,6 +173,10 @@ class Workload:
         self.bf1 = torch.empty(N, dtype=torch.uint8, device=dev)
         self.tauf1 = torch.empty(1, device=dev)
         self.ws_routef = torch.empty(B.route_workspace(N), dtype=torch.uint8, device=dev)
+        # the unfused reference for it: the two projections through torch's
+        # library GEMM into q and k, then bllm_route on them
+        self.ql1 = torch.empty((N, 512), dtype=bf, device=dev)
+        self.kl1 = torch.empty((N, 512), dtype=bf, device=dev)
         # streaming chunker: the same byte streams arriving in windows of 1024
         # bytes, each its own dense buffer; the carried matrix is updated in place
         self.win = 1024
@@ -185,6 +189,7 @@ class Workload:
         self.ws_crw = torch.empty(B.coding_rate_workspace(self.nseq, self.win, 512), dtype=torch.uint8, device=dev)
         self._streaming_chunker()
         self._route_fused1()
+        self._route_library1()
         torch.cuda.synchronize()
         log(f"setup done: M1={self.M1} ({self.M1 / N:.3f} N), M2={self.M2} ({self.M2 / N:.3f} N)")
 
@@ -248,11 +253,20 @@ class Workload:
         self.B.route_fused(self.h1, self.wq1, self.wk1, self.off, quantile=0.75, p_out=self.pf1, b_out=self.bf1,
                            tau_out=self.tauf1, ws=self.ws_routef)
 
+    def _route_library1(self):
+        torch = self.torch
+        torch.matmul(self.h1, self.wq1, out=self.ql1)
+        torch.matmul(self.h1, self.wk1, out=self.kl1)
+        self.B.route(self.ql1, self.kl1, self.off, quantile=0.75, p_out=self.pf1, b_out=self.bf1,
+                     tau_out=self.tauf1, ws=self.ws_routef)
+
     def next_ops(self):
         """Rows past the hot path (fused projection, cosine chunker, EMA backward, streaming
-        chunker), timed on their own."""
+        chunker), timed on their own, and the unfused reference of the fused projection."""
         return [("cosine_chunker", self._cosine_chunker), ("dechunk_backward stage1", self._dechunk1_backward),
-                ("route_fused stage1", self._route_fused1), ("streaming_chunker", self._streaming_chunker)]
+                ("route_fused stage1", self._route_fused1),
+                ("library GEMM + route stage1", self._route_library1),
+                ("streaming_chunker", self._streaming_chunker)]
 
     def next_algorithmic(self):
         N, M1, nseq, K = self.N, self.M1, self.nseq, self.K
@@ -263,6 +277,9 @@ class Workload:
                 # h read once, Wq and Wk, p and b written; q = h Wq and k = h Wk on bf16 MFMA
                 "route_fused stage1": dict(bytes=N * (512 * e + 5) + 2 * 512 * 512 * e,
                                            flops=2 * N * 512 * 1024),
+                # the same work unfused: q and k written by the GEMMs and read back by the route
+                "library GEMM + route stage1": dict(bytes=N * (512 * e + 5) + 2 * 512 * 512 * e
+                                                    + 2 * 2 * N * 512 * e, flops=2 * N * 512 * 1024),
                 # every window: h read, Delta R written, the carried matrix read and written, the
                 # local selection; the same 3 T d^2 MFMA count as the whole-sequence coding rate
                 "streaming_chunker": dict(flops=3 * N * 512 * 512, peak_tflops=FP32_MFMA_PEAK_TFLOPS,
