@@ -78,66 +78,6 @@ __device__ inline int block_n(const CRGeom& g, int j) {
 
 // ------------------------------------------------------------------ Gram prefix
 
-template <int DT> struct GramLds;
-template <> struct GramLds<BLLM_BF16> { typedef uint16_t T; static constexpr int LD = 40; };
-template <> struct GramLds<BLLM_F32> { typedef float T; static constexpr int LD = 36; };
-
-// rows [r0, r0+32) (those < rend) of feature strip [f0, f0+64) -> s[feature][row]
-template <int DT>
-__device__ inline void stage_strip(const void* h, int64_t hrow0, int d, int r0, int rend, int f0,
-                                   typename GramLds<DT>::T* s) {
-  constexpr int LD = GramLds<DT>::LD;
-  const int t = threadIdx.x;
-  if (DT == BLLM_BF16) {
-    const int row = t >> 3, fc = (t & 7) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + row < rend && f0 + fc < d)
-      v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(h) + (hrow0 + r0 + row) * d + f0 + fc);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint16_t* sb = reinterpret_cast<uint16_t*>(s);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sb[(fc + 2 * e) * LD + row] = static_cast<uint16_t>(w[e] & 0xFFFFu);
-      sb[(fc + 2 * e + 1) * LD + row] = static_cast<uint16_t>(w[e] >> 16);
-    }
-  } else {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int row = (t >> 4) + 16 * hh, fc = (t & 15) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r0 + row < rend && f0 + fc < d)
-        v = *reinterpret_cast<const float4*>(static_cast<const float*>(h) + (hrow0 + r0 + row) * d + f0 + fc);
-      float* sf = reinterpret_cast<float*>(s);
-      sf[(fc + 0) * LD + row] = v.x;
-      sf[(fc + 1) * LD + row] = v.y;
-      sf[(fc + 2) * LD + row] = v.z;
-      sf[(fc + 3) * LD + row] = v.w;
-    }
-  }
-}
-
-template <int DT>
-__device__ inline floatx16 gram_chunk(const typename GramLds<DT>::T* sI, const typename GramLds<DT>::T* sJ,
-                                      int wm, int wn, int lane, floatx16 acc) {
-  constexpr int LD = GramLds<DT>::LD;
-  if (DT == BLLM_BF16) {
-#pragma unroll
-    for (int k0 = 0; k0 < 32; k0 += 16) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(sI) +
-                                                        (32 * wm + (lane & 31)) * LD + k0 + 8 * (lane >> 5));
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(sJ) +
-                                                        (32 * wn + (lane & 31)) * LD + k0 + 8 * (lane >> 5));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-    }
-  } else {
-    const float* pa = reinterpret_cast<const float*>(sI) + (32 * wm + (lane & 31)) * LD + 16 * (lane >> 5);
-    const float* pb = reinterpret_cast<const float*>(sJ) + (32 * wn + (lane & 31)) * LD + 16 * (lane >> 5);
-#pragma unroll
-    for (int st = 0; st < 16; ++st) acc = mfma32(pa[st], pb[st], acc);
-  }
-  return acc;
-}
-
 // The carried prefix matrix S of a stream (fp32 [d x d] per sequence, row
 // major) enters as the accumulator's start, (S - I) / alpha, so that
 // I + alpha acc is S before the window's first row (zero where there is no
@@ -175,25 +115,75 @@ __device__ inline void write_carry(float* sout, const CRGeom& g, int s, int r0, 
   }
 }
 
-// One 64x64 tile (I >= J) of A_j for all blocks j of one sequence; wave
-// (wm, wn) owns the 32x32 quadrant and keeps its running sum in registers.
-template <int DT>
-__global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h, float* __restrict__ ws,
-                                                      CRGeom g, float alpha, const float* sin, float* sout) {
-  typedef typename GramLds<DT>::T E;
-  constexpr int LD = GramLds<DT>::LD;
-  __shared__ __attribute__((aligned(16))) E sI[64 * LD];
-  __shared__ __attribute__((aligned(16))) E sJ[64 * LD];
+// One 64x64 tile (I >= J) of A_j for all blocks j of one sequence (fp32
+// input); wave (wm, wn) owns the 32x32 quadrant and keeps its running sum in
+// registers.  Rows go in steps of R = 128 (64 when c is not a multiple of
+// 128): registers hold the next step's rows while the current one, staged
+// transposed in LDS ([feature][row]), is multiplied 32 rows at a time on fp32
+// MFMA.  Rows past the sequence and features past d are loaded from row or
+// feature 0 and zeroed when stored to LDS.
+constexpr int kGR = 128;          // rows per step at most
+constexpr int kGLD = kGR + 4;     // LDS pitch (floats) of a staged [feature][row] strip
+__global__ __launch_bounds__(256) void cr_gram_prefix_f32(const float* __restrict__ h, float* __restrict__ ws,
+                                                          CRGeom g, float alpha, const float* sin, float* sout) {
+  __shared__ __attribute__((aligned(16))) float sI[64 * kGLD];
+  __shared__ __attribute__((aligned(16))) float sJ[64 * kGLD];
   int s, t;
   if (!gram_tile_of_block(g, s, t)) return;
   int I = 0;
   while (t > I) { t -= I + 1; ++I; }
   const int J = t;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool same = I == J;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int wm = w >> 1, wn = w & 1;
   const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
-  const int64_t hrow0 = static_cast<int64_t>(s) * g.T;
+  const int R = g.c % kGR == 0 ? kGR : 64;
+  const int spb = g.c / R;                         // steps per block
+  const int nq = (g.nblk - (sout ? 0 : 1)) * spb;  // steps that feed some prefix or the carry
+  // thread: rows lr + 16 e of a step, features fc .. fc + 3 of each strip
+  const int lr = tid >> 4, fc = (tid & 15) * 4;
+  const bool fiok = 64 * I + fc < g.d, fjok = 64 * J + fc < g.d;
+  const float* hI = h + static_cast<int64_t>(s) * g.T * g.d + (fiok ? 64 * I + fc : 0);
+  const float* hJ = h + static_cast<int64_t>(s) * g.T * g.d + (fjok ? 64 * J + fc : 0);
+  auto row_ok = [&](int q, int e) { return q * R + lr + 16 * e < g.T; };
+  float4 pI[kGR / 16], pJ[kGR / 16];
+  auto fetch = [&](int q) {
+#pragma unroll
+    for (int e = 0; e < kGR / 16; ++e) {
+      if (16 * e >= R) break;
+      const int64_t r = row_ok(q, e) ? q * R + lr + 16 * e : 0;
+      pI[e] = *reinterpret_cast<const float4*>(hI + r * g.d);
+      if (!same) pJ[e] = *reinterpret_cast<const float4*>(hJ + r * g.d);
+    }
+  };
+  auto put = [&](float* sd, const float4& v, bool ok, int row) {
+    sd[(fc + 0) * kGLD + row] = ok ? v.x : 0.f;
+    sd[(fc + 1) * kGLD + row] = ok ? v.y : 0.f;
+    sd[(fc + 2) * kGLD + row] = ok ? v.z : 0.f;
+    sd[(fc + 3) * kGLD + row] = ok ? v.w : 0.f;
+  };
+  auto stash = [&](int q) {
+#pragma unroll
+    for (int e = 0; e < kGR / 16; ++e) {
+      if (16 * e >= R) break;
+      const bool ok = row_ok(q, e);
+      put(sI, pI[e], ok && fiok, lr + 16 * e);
+      if (!same) put(sJ, pJ[e], ok && fjok, lr + 16 * e);
+    }
+  };
+  const float* sJr = same ? sI : sJ;
+  auto compute = [&](floatx16 acc) {
+    for (int r0 = 0; r0 < R; r0 += 32) {
+      const float* pa = sI + (32 * wm + (lane & 31)) * kGLD + r0 + 16 * (lane >> 5);
+      const float* pb = sJr + (32 * wn + (lane & 31)) * kGLD + r0 + 16 * (lane >> 5);
+#pragma unroll
+      for (int st = 0; st < 16; ++st) acc = mfma32(pa[st], pb[st], acc);
+    }
+    return acc;
+  };
   floatx16 acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
+  if (nq > 0) fetch(0);
+  int q = 0;
   for (int j = 0; j <= g.nblk; ++j) {
     if (j == g.nblk) {
       write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
@@ -206,13 +196,12 @@ __global__ __launch_bounds__(256) void cr_gram_prefix(const void* __restrict__ h
       Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
     }
     if (j == g.nblk - 1 && !sout) break;
-    const int rbeg = j * g.c, rend = min(rbeg + g.c, g.T);
-    for (int r0 = rbeg; r0 < rend; r0 += 32) {
+    for (int sq = 0; sq < spb; ++sq, ++q) {
       __syncthreads();
-      stage_strip<DT>(h, hrow0, g.d, r0, rend, 64 * I, sI);
-      if (I != J) stage_strip<DT>(h, hrow0, g.d, r0, rend, 64 * J, sJ);
+      stash(q);
       __syncthreads();
-      acc = gram_chunk<DT>(sI, I != J ? sJ : sI, wm, wn, lane, acc);
+      fetch(q + 1);  // past the last step: rows of the sequence, never staged
+      acc = compute(acc);
     }
   }
 }
@@ -261,31 +250,37 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
   const uint16_t* hI = h + static_cast<int64_t>(s) * g.T * g.d + 64 * I + lc;
   const uint16_t* hJ = h + static_cast<int64_t>(s) * g.T * g.d + 64 * J + lc;
   // one sub-chunk: rows q R + lr + 32 e; rows past the sequence or features
-  // past d read row 0 / feature 0 and are masked to zero (unconditional loads)
+  // past d read row 0 / feature 0 (unconditional loads) and are masked to
+  // zero when stored to LDS, a sub-chunk later: masked here, every load
+  // would wait for its data at once and the prefetch would not overlap the
+  // MFMAs
+  auto row_ok = [&](bool fok, int q, int e) { return fok && q * R + lr + 32 * e < g.T && lr + 32 * e < R; };
   auto ld = [&](const uint16_t* base, bool fok, int q, int e) {
     const int r = q * R + lr + 32 * e;
-    const bool ok = fok && r < g.T && lr + 32 * e < R;
-    uint4 v = *reinterpret_cast<const uint4*>(base - (fok ? 0 : lc) + static_cast<int64_t>(ok ? r : 0) * g.d);
+    return *reinterpret_cast<const uint4*>(base - (fok ? 0 : lc) +
+                                           static_cast<int64_t>(row_ok(fok, q, e) ? r : 0) * g.d);
+  };
+  auto msk = [&](const uint4& v, bool ok) {
     const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
-    v.x &= m; v.y &= m; v.z &= m; v.w &= m;
-    return v;
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
   };
   uint4 ai0, ai1, ai2, ai3, aj0, aj1, aj2, aj3;
   auto fetch_a = [&](int q) {
     ai0 = ld(hI, fiok, q, 0); ai1 = ld(hI, fiok, q, 1); ai2 = ld(hI, fiok, q, 2); ai3 = ld(hI, fiok, q, 3);
     if (!same) { aj0 = ld(hJ, fjok, q, 0); aj1 = ld(hJ, fjok, q, 1); aj2 = ld(hJ, fjok, q, 2); aj3 = ld(hJ, fjok, q, 3); }
   };
-  auto stash = [&](const uint4& x0, const uint4& x1, const uint4& x2, const uint4& x3, const uint4& y0,
+  // sub-chunk q's rows to LDS, zeroed where they fall past the sequence or d
+  auto stash = [&](int q, const uint4& x0, const uint4& x1, const uint4& x2, const uint4& x3, const uint4& y0,
                    const uint4& y1, const uint4& y2, const uint4& y3) {
-    *reinterpret_cast<uint4*>(sI + lr * GP + lc) = x0;
-    *reinterpret_cast<uint4*>(sI + (lr + 32) * GP + lc) = x1;
-    *reinterpret_cast<uint4*>(sI + (lr + 64) * GP + lc) = x2;
-    *reinterpret_cast<uint4*>(sI + (lr + 96) * GP + lc) = x3;
+    *reinterpret_cast<uint4*>(sI + lr * GP + lc) = msk(x0, row_ok(fiok, q, 0));
+    *reinterpret_cast<uint4*>(sI + (lr + 32) * GP + lc) = msk(x1, row_ok(fiok, q, 1));
+    *reinterpret_cast<uint4*>(sI + (lr + 64) * GP + lc) = msk(x2, row_ok(fiok, q, 2));
+    *reinterpret_cast<uint4*>(sI + (lr + 96) * GP + lc) = msk(x3, row_ok(fiok, q, 3));
     if (!same) {
-      *reinterpret_cast<uint4*>(sJ + lr * GP + lc) = y0;
-      *reinterpret_cast<uint4*>(sJ + (lr + 32) * GP + lc) = y1;
-      *reinterpret_cast<uint4*>(sJ + (lr + 64) * GP + lc) = y2;
-      *reinterpret_cast<uint4*>(sJ + (lr + 96) * GP + lc) = y3;
+      *reinterpret_cast<uint4*>(sJ + lr * GP + lc) = msk(y0, row_ok(fjok, q, 0));
+      *reinterpret_cast<uint4*>(sJ + (lr + 32) * GP + lc) = msk(y1, row_ok(fjok, q, 1));
+      *reinterpret_cast<uint4*>(sJ + (lr + 64) * GP + lc) = msk(y2, row_ok(fjok, q, 2));
+      *reinterpret_cast<uint4*>(sJ + (lr + 96) * GP + lc) = msk(y3, row_ok(fjok, q, 3));
     }
   };
   floatx16 acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
@@ -320,7 +315,7 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
     if (j == g.nblk - 1 && !sout) break;
     for (int sq = 0; sq < spb; ++sq, ++q) {
       lds_barrier();
-      stash(ai0, ai1, ai2, ai3, aj0, aj1, aj2, aj3);
+      stash(q, ai0, ai1, ai2, ai3, aj0, aj1, aj2, aj3);
       lds_barrier();
       fetch_a(q + 1);
       compute();
@@ -905,8 +900,8 @@ void cr_step(const CRCall& c, int i) {
       hipLaunchKernelGGL(cr_gram_prefix_bf16, dim3(ggrid), dim3(256), 0, c.st, static_cast<const uint16_t*>(c.h),
                          c.ws, g, static_cast<float>(c.alpha), c.sin, c.sout);
     else
-      hipLaunchKernelGGL(cr_gram_prefix<DT>, dim3(ggrid), dim3(256), 0, c.st, c.h, c.ws, g,
-                         static_cast<float>(c.alpha), c.sin, c.sout);
+      hipLaunchKernelGGL(cr_gram_prefix_f32, dim3(ggrid), dim3(256), 0, c.st, static_cast<const float*>(c.h),
+                         c.ws, g, static_cast<float>(c.alpha), c.sin, c.sout);
     return;
   }
   const int k = (i - 1) / 2, npan = g.ldm / NB;

@@ -275,25 +275,22 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
   const uint16_t* wb = W + static_cast<int64_t>(b) * g.dg * g.dl + min(n0 + nc, g.dl - 8);
   uint4 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;
   // Every load is issued (rows past the items read chunk 0's g row, whose
-  // results are not written); K past d_global, only in a last partial step,
-  // is masked to zero.
+  // results are not written; K past d_global, only in a last partial step,
+  // reads column or row 0).  The masks that zero that K range are applied when
+  // the registers are stored to LDS, a K step later: applied here, they would
+  // make every load wait for its data at once and the prefetch would not
+  // overlap the MFMAs.
   auto fetch = [&](int ko) {
-    const bool kin = ko + lc < g.dg;
-    const uint32_t ma = kin ? 0xFFFFFFFFu : 0u;
-    const int koa = kin ? ko : 0;
-    pa0 = and4(*reinterpret_cast<const uint4*>(ar0 + koa), ma);
-    pa1 = and4(*reinterpret_cast<const uint4*>(ar1 + koa), ma);
-    pa2 = and4(*reinterpret_cast<const uint4*>(ar2 + koa), ma);
-    pa3 = and4(*reinterpret_cast<const uint4*>(ar3 + koa), ma);
+    const int koa = ko + lc < g.dg ? ko : 0;
+    pa0 = *reinterpret_cast<const uint4*>(ar0 + koa);
+    pa1 = *reinterpret_cast<const uint4*>(ar1 + koa);
+    pa2 = *reinterpret_cast<const uint4*>(ar2 + koa);
+    pa3 = *reinterpret_cast<const uint4*>(ar3 + koa);
     const int k0 = ko + kr, k1 = k0 + 16, k2 = k0 + 32, k3 = k0 + 48;
-    pb0 = and4(*reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k0 < g.dg ? k0 : 0) * g.dl),
-               k0 < g.dg ? 0xFFFFFFFFu : 0u);
-    pb1 = and4(*reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k1 < g.dg ? k1 : 0) * g.dl),
-               k1 < g.dg ? 0xFFFFFFFFu : 0u);
-    pb2 = and4(*reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k2 < g.dg ? k2 : 0) * g.dl),
-               k2 < g.dg ? 0xFFFFFFFFu : 0u);
-    pb3 = and4(*reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k3 < g.dg ? k3 : 0) * g.dl),
-               k3 < g.dg ? 0xFFFFFFFFu : 0u);
+    pb0 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k0 < g.dg ? k0 : 0) * g.dl);
+    pb1 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k1 < g.dg ? k1 : 0) * g.dl);
+    pb2 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k2 < g.dg ? k2 : 0) * g.dl);
+    pb3 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k3 < g.dg ? k3 : 0) * g.dl);
   };
   const int j16 = lane & 15;
   const int frow = 8 * (lane >> 5) + (j16 >> 2);
@@ -301,15 +298,17 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
   fetch(0);
   const int nk = (g.dg + kBK - 1) / kBK;
   for (int kt = 0; kt < nk; ++kt) {
+    const int ko = kt * kBK;
+    const uint32_t ma = ko + lc < g.dg ? 0xFFFFFFFFu : 0u;
     __syncthreads();
-    *reinterpret_cast<uint4*>(sA + lr * kPA + lc) = pa0;
-    *reinterpret_cast<uint4*>(sA + (lr + 32) * kPA + lc) = pa1;
-    *reinterpret_cast<uint4*>(sA + (lr + 64) * kPA + lc) = pa2;
-    *reinterpret_cast<uint4*>(sA + (lr + 96) * kPA + lc) = pa3;
-    *reinterpret_cast<uint4*>(sB + kr * kPB + nc) = pb0;
-    *reinterpret_cast<uint4*>(sB + (kr + 16) * kPB + nc) = pb1;
-    *reinterpret_cast<uint4*>(sB + (kr + 32) * kPB + nc) = pb2;
-    *reinterpret_cast<uint4*>(sB + (kr + 48) * kPB + nc) = pb3;
+    *reinterpret_cast<uint4*>(sA + lr * kPA + lc) = and4(pa0, ma);
+    *reinterpret_cast<uint4*>(sA + (lr + 32) * kPA + lc) = and4(pa1, ma);
+    *reinterpret_cast<uint4*>(sA + (lr + 64) * kPA + lc) = and4(pa2, ma);
+    *reinterpret_cast<uint4*>(sA + (lr + 96) * kPA + lc) = and4(pa3, ma);
+    *reinterpret_cast<uint4*>(sB + kr * kPB + nc) = and4(pb0, ko + kr < g.dg ? 0xFFFFFFFFu : 0u);
+    *reinterpret_cast<uint4*>(sB + (kr + 16) * kPB + nc) = and4(pb1, ko + kr + 16 < g.dg ? 0xFFFFFFFFu : 0u);
+    *reinterpret_cast<uint4*>(sB + (kr + 32) * kPB + nc) = and4(pb2, ko + kr + 32 < g.dg ? 0xFFFFFFFFu : 0u);
+    *reinterpret_cast<uint4*>(sB + (kr + 48) * kPB + nc) = and4(pb3, ko + kr + 48 < g.dg ? 0xFFFFFFFFu : 0u);
     __syncthreads();
     if (kt + 1 < nk) fetch((kt + 1) * kBK);
 #pragma unroll
