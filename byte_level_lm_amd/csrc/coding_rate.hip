@@ -588,37 +588,69 @@ __device__ inline floatx16 mfma_split(const uint4* a, const uint4* b, floatx16 c
   return mfma_bf(a[0], b[0], c);
 }
 
-// elements (row, col .. col+3), col % 4 == 0; a group lies wholly in one part
+// C/D tile registers of one lane from the row segments orig(row, col0 + crow(q, lane)):
+// the Gram prefix in the A rows, sqrt(alpha) h in the S rows of the A columns
+// (zero past the block's rows and past d), the identity in the S block.  A
+// 32-column half lies wholly in one part and the rows of a 64-row tile in one
+// part, so the case is the same for every lane of a wave.  In two steps, so
+// that every load of a pass is in flight before any is used: orig_issue
+// loads (the S rows' values stay raw: bf16 pairs as bit patterns in the
+// first 8 registers, or unscaled fp32), orig_finish scales and masks them.
 template <int DT>
-__device__ inline float4 orig4(const void* h, const float* Mx, const CRGeom& g, int64_t hrow0, int cj,
-                               float salpha, int row, int col) {
-  if (col >= g.dp)
-    return make_float4(row == col ? 1.f : 0.f, row == col + 1 ? 1.f : 0.f, row == col + 2 ? 1.f : 0.f,
-                       row == col + 3 ? 1.f : 0.f);
-  if (row < g.dp) return *reinterpret_cast<const float4*>(Mx + static_cast<int64_t>(row) * g.ldm + col);
-  const int rr = row - g.dp;
-  if (rr >= cj || col >= g.d) return make_float4(0.f, 0.f, 0.f, 0.f);
-  const int64_t e = (hrow0 + rr) * g.d + col;
-  if (DT == BLLM_F32) {
-    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(h) + e);
-    return make_float4(salpha * v.x, salpha * v.y, salpha * v.z, salpha * v.w);
+__device__ inline floatx16 orig_issue(const void* h, const float* Mx, const CRGeom& g, int64_t hrow0, int cj,
+                                      int row, int col0, int hh) {
+  floatx16 a;
+  if (col0 >= g.dp) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) a[q] = row == col0 + 8 * (q >> 2) + 4 * hh + (q & 3) ? 1.f : 0.f;
+    return a;
   }
-  const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(h) + e);
-  return make_float4(salpha * bf16_to_f32(static_cast<uint16_t>(v.x & 0xFFFFu)),
-                     salpha * bf16_to_f32(static_cast<uint16_t>(v.x >> 16)),
-                     salpha * bf16_to_f32(static_cast<uint16_t>(v.y & 0xFFFFu)),
-                     salpha * bf16_to_f32(static_cast<uint16_t>(v.y >> 16)));
+  if (row < g.dp) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 v =
+          *reinterpret_cast<const float4*>(Mx + static_cast<int64_t>(row) * g.ldm + col0 + 8 * q4 + 4 * hh);
+      a[4 * q4] = v.x; a[4 * q4 + 1] = v.y; a[4 * q4 + 2] = v.z; a[4 * q4 + 3] = v.w;
+    }
+    return a;
+  }
+  const int rr = row - g.dp;
+  const int64_t rbase = (hrow0 + (rr < cj ? rr : 0)) * g.d;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int col = col0 + 8 * q4 + 4 * hh;
+    const int c = col < g.d ? col : 0;
+    if (DT == BLLM_F32) {
+      const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(h) + rbase + c);
+      a[4 * q4] = v.x; a[4 * q4 + 1] = v.y; a[4 * q4 + 2] = v.z; a[4 * q4 + 3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(h) + rbase + c);
+      a[2 * q4] = __uint_as_float(v.x);
+      a[2 * q4 + 1] = __uint_as_float(v.y);
+    }
+  }
+  return a;
 }
 
-// C/D tile registers of one lane from the row segments orig(row, col0 + crow(q, lane))
 template <int DT>
-__device__ inline floatx16 orig_tile_t(const void* h, const float* Mx, const CRGeom& g, int64_t hrow0,
-                                       int cj, float salpha, int row, int col0, int hh) {
+__device__ inline floatx16 orig_finish(const floatx16& r, const CRGeom& g, int cj, float salpha, int row,
+                                       int col0, int hh) {
+  if (col0 >= g.dp || row < g.dp) return r;
+  const bool rok = row - g.dp < cj;
   floatx16 a;
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
-    const float4 v = orig4<DT>(h, Mx, g, hrow0, cj, salpha, row, col0 + 8 * q4 + 4 * hh);
-    a[4 * q4] = v.x; a[4 * q4 + 1] = v.y; a[4 * q4 + 2] = v.z; a[4 * q4 + 3] = v.w;
+    const float sc = rok && col0 + 8 * q4 + 4 * hh < g.d ? salpha : 0.f;
+    if (DT == BLLM_F32) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[4 * q4 + e] = sc * r[4 * q4 + e];
+    } else {
+      const uint32_t x = __float_as_uint(r[2 * q4]), y = __float_as_uint(r[2 * q4 + 1]);
+      a[4 * q4] = sc * bf16_to_f32(static_cast<uint16_t>(x & 0xFFFFu));
+      a[4 * q4 + 1] = sc * bf16_to_f32(static_cast<uint16_t>(x >> 16));
+      a[4 * q4 + 2] = sc * bf16_to_f32(static_cast<uint16_t>(y & 0xFFFFu));
+      a[4 * q4 + 3] = sc * bf16_to_f32(static_cast<uint16_t>(y >> 16));
+    }
   }
   return a;
 }
@@ -667,16 +699,26 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
   const bool rowS1 = NB * (k + 1) >= g.dp;
   const int nch = NB * k / kChunk;
   {
+    // Linv_k to LDS: the four loads of a thread in flight together
     const float* Li = linv + static_cast<int64_t>(m) * NB * NB;
-    for (int e = tid; e < NB * NB / 4; e += 256) {
-      const int r = e >> 4, cc = (e & 15) * 4;
-      *reinterpret_cast<float4*>(sLi + r * kXP + cc) = *reinterpret_cast<const float4*>(Li + r * NB + cc);
+    float4 lv[NB * NB / 4 / 256];
+#pragma unroll
+    for (int i = 0; i < NB * NB / 4 / 256; ++i) {
+      const int e = tid + 256 * i;
+      lv[i] = *reinterpret_cast<const float4*>(Li + (e >> 4) * NB + (e & 15) * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < NB * NB / 4 / 256; ++i) {
+      const int e = tid + 256 * i;
+      *reinterpret_cast<float4*>(sLi + (e >> 4) * kXP + (e & 15) * 4) = lv[i];
     }
   }
+  // the lookahead tile and the first pass's tiles are loaded together and
+  // converted after one wait
   // lookahead tile, symmetric: read orig transposed for row-contiguous loads
+  const int rowD = NB * (k + 1) + 32 * dn + l32, colD = NB * (k + 1) + 32 * dm;
   floatx16 accD = zero16();
-  if (look)
-    accD = orig_tile_t<DT>(h, Mx, g, hrow0, cj, salpha, NB * (k + 1) + 32 * dn + l32, NB * (k + 1) + 32 * dm, hh);
+  if (look) accD = orig_issue<DT>(h, Mx, g, hrow0, cj, rowD, colD, hh);
   for (int t0 = tbeg; t0 < tend; t0 += kPassTiles) {
     const int npt = min(kPassTiles, nt - t0);
     const bool first = t0 == 0;
@@ -687,9 +729,9 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
       const int row = NB * (k + 1 + t0 + u) + 32 * wn + l32;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
-        acc[sl][mb] = u < npt ? orig_tile_t<DT>(h, Mx, g, hrow0, cj, salpha, row, NB * k + 32 * mb, hh)
-                              : zero16();
+        acc[sl][mb] = u < npt ? orig_issue<DT>(h, Mx, g, hrow0, cj, row, NB * k + 32 * mb, hh) : zero16();
     }
+
     // strip rows: the panel's 64 rows, then the pass tiles' rows.  Two sets of
     // named prefetch registers: chunk ch + 2 is loaded while chunk ch is
     // staged and multiplied.  Rows past the pass load a valid panel row
@@ -754,6 +796,15 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
     // the accumulators were loaded from memory: wait here once, so that the
     // loop's only outstanding loads are the prefetches
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (first) accD = orig_finish<DT>(accD, g, cj, salpha, rowD, colD, hh);
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) {
+      const int u = wp + 2 * sl;
+      const int row = NB * (k + 1 + t0 + u) + 32 * wn + l32;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        if (u < npt) acc[sl][mb] = orig_finish<DT>(acc[sl][mb], g, cj, salpha, row, NB * k + 32 * mb, hh);
+    }
     if (nch > 0) {
       fetch_a(0);
       fetch_b(1);
