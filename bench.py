@@ -665,7 +665,10 @@ def main():
         return
     wl = Workload()
     if args.profile_op:
-        f = wl.step if args.profile_op == "step" else dict(wl.ops() + wl.next_ops())[args.profile_op]
+        # the whole step with its ops queued in turn, so that each kernel's time
+        # under the profiler is its own and not shared with the H-Net stream
+        f = (lambda: wl.step(schedule="serial")) if args.profile_op == "step" else \
+            dict(wl.ops() + wl.next_ops())[args.profile_op]
         for _ in range(args.steps):
             f()
         torch.cuda.synchronize()
