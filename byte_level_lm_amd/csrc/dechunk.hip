@@ -261,9 +261,19 @@ __device__ inline float4 shfl_up4(float4 v, int off) {
 // through LDS.  Writes the carry into every tile (the scan value before it).
 // The tile values are read in batches of at most 16 (twice: for the group
 // fold and for the carries) to stay within 128 VGPRs at 1024 threads.
+// blockIdx.y = 1 scans a second set of aggregates (the backward's reverse
+// scan in the same launch as its forward one)
 __global__ __launch_bounds__(kCarryThreads) void ema_tile_carry(const float* __restrict__ Aagg,
                                                                 const float* __restrict__ Uagg, int d,
-                                                                float* __restrict__ carry) {
+                                                                float* __restrict__ carry,
+                                                                const float* __restrict__ Aagg2,
+                                                                const float* __restrict__ Uagg2,
+                                                                float* __restrict__ carry2) {
+  if (blockIdx.y == 1) {
+    Aagg = Aagg2;
+    Uagg = Uagg2;
+    carry = carry2;
+  }
   __shared__ float shA[kCarryThreads / kWave][kCarryCols];
   __shared__ float4 shU[kCarryThreads / kWave][kCarryCols];
   const int tid = threadIdx.x;
@@ -403,7 +413,7 @@ void launch_dechunk(const void* z, const float* P, int d, const int32_t* idx,
   hipLaunchKernelGGL(ema_tile_aggregate<DT>, dim3(kNT / 4 + nzero, nslices), dim3(256), 0, st, z, P, d,
                      idx, chunk_offsets, offsets, nseq, Aagg, Uagg, out);
   hipLaunchKernelGGL(ema_tile_carry, dim3((d + kCarryCols * 4 - 1) / (kCarryCols * 4)),
-                     dim3(kCarryThreads), 0, st, Aagg, Uagg, d, carry);
+                     dim3(kCarryThreads), 0, st, Aagg, Uagg, d, carry, nullptr, nullptr, nullptr);
   hipLaunchKernelGGL(ema_tile_expand<DT>, dim3(kNT / 4, nslices), dim3(256), 0, st, z, P, d, idx,
                      chunk_offsets, offsets, nseq, carry, out);
 }
@@ -426,9 +436,11 @@ void launch_dechunk(const void* z, const float* P, int d, const int32_t* idx,
 //   4. per tile, ascending: zbar from the forward carry; dz_c = P_c lam_c and
 //      one partial dot product per feature slice
 //   5. dP_c = the slice partials summed in slice order
+// (the two scans of 2 run in one launch, and 3 and 4 in one launch, each wave
+// rescanning its tile from the right and then from the left)
 // HBM: dout read once; z read twice; gbar/lam (M x d, the activations' type;
-// every sum and scan runs in fp32) written twice and read twice; dz written
-// once.
+// every sum and scan runs in fp32) written twice and read twice (the second
+// read mostly from the cache); dz written once.
 
 template <int DT>
 __global__ __launch_bounds__(256) void emab_aggregate(const void* __restrict__ z,
@@ -540,7 +552,7 @@ __global__ __launch_bounds__(256) void emab_aggregate(const void* __restrict__ z
 
 // 3. lam_c over the tile, last chunk first, written over gbar_c
 template <int DT>
-__global__ __launch_bounds__(256) void emab_reverse(const float* __restrict__ P, int d,
+__device__ inline void emab_reverse(const float* __restrict__ P, int d,
                                                     const int32_t* __restrict__ idx,
                                                     ChunkOffs chunk_offsets,
                                                     const int64_t* __restrict__ offsets, int nseq,
@@ -594,7 +606,7 @@ __global__ __launch_bounds__(256) void emab_reverse(const float* __restrict__ P,
 
 // 4. zbar from the forward carry, dz_c = P_c lam_c, and the slice's partial dP_c
 template <int DT>
-__global__ __launch_bounds__(256) void emab_forward(const void* __restrict__ z,
+__device__ inline void emab_forward(const void* __restrict__ z,
                                                     const float* __restrict__ P, int d,
                                                     const int32_t* __restrict__ idx,
                                                     ChunkOffs chunk_offsets,
@@ -657,6 +669,23 @@ __global__ __launch_bounds__(256) void emab_forward(const void* __restrict__ z,
   }
 }
 
+// 3 and 4 in one launch: each wave rescans its (tile, feature slice) from the
+// right and then from the left, so the lam_c it has just written are read
+// back from the cache instead of memory
+template <int DT>
+__global__ __launch_bounds__(256) void emab_rescan(const void* __restrict__ z, const float* __restrict__ P, int d,
+                                                   const int32_t* __restrict__ idx, ChunkOffs chunk_offsets,
+                                                   const int64_t* __restrict__ offsets, int nseq,
+                                                   const float* __restrict__ carry,
+                                                   const float* __restrict__ carry_rev, void* __restrict__ lam,
+                                                   void* __restrict__ dz, float* __restrict__ dPpart, int64_t mcap) {
+  emab_reverse<DT>(P, d, idx, chunk_offsets, offsets, nseq, carry_rev, lam);
+  // this wave's lam stores complete before its loads of the same words
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  emab_forward<DT>(z, P, d, idx, chunk_offsets, offsets, nseq, carry, lam, dz, dPpart, mcap);
+}
+
 __global__ __launch_bounds__(256) void emab_dp_reduce(const float* __restrict__ dPpart,
                                                       ChunkOffs chunk_offsets, int nseq,
                                                       int nslices, int64_t mcap, float* __restrict__ dP) {
@@ -704,12 +733,10 @@ void launch_dechunk_bwd(const void* z, const float* P, const void* dout, int d, 
   const dim3 cgrid((d + kCarryCols * 4 - 1) / (kCarryCols * 4));
   hipLaunchKernelGGL(emab_aggregate<DT>, grid, dim3(256), 0, st, z, P, dout, d, idx, chunk_offsets, offsets,
                      nseq, w.Aagg, w.Uf, w.Arev, w.Urev, w.lam);
-  hipLaunchKernelGGL(ema_tile_carry, cgrid, dim3(kCarryThreads), 0, st, w.Aagg, w.Uf, d, w.carry);
-  hipLaunchKernelGGL(ema_tile_carry, cgrid, dim3(kCarryThreads), 0, st, w.Arev, w.Urev, d, w.carry_rev);
-  hipLaunchKernelGGL(emab_reverse<DT>, grid, dim3(256), 0, st, P, d, idx, chunk_offsets, offsets, nseq,
-                     w.carry_rev, w.lam);
-  hipLaunchKernelGGL(emab_forward<DT>, grid, dim3(256), 0, st, z, P, d, idx, chunk_offsets, offsets, nseq,
-                     w.carry, w.lam, dz, w.dPpart, mcap);
+  hipLaunchKernelGGL(ema_tile_carry, dim3(cgrid.x, 2), dim3(kCarryThreads), 0, st, w.Aagg, w.Uf, d, w.carry,
+                     w.Arev, w.Urev, w.carry_rev);
+  hipLaunchKernelGGL(emab_rescan<DT>, grid, dim3(256), 0, st, z, P, d, idx, chunk_offsets, offsets, nseq,
+                     w.carry, w.carry_rev, w.lam, dz, w.dPpart, mcap);
   const unsigned rblocks = static_cast<unsigned>(std::min<int64_t>(ceil_div(mcap, 256), 1024));
   hipLaunchKernelGGL(emab_dp_reduce, dim3(rblocks > 0 ? rblocks : 1), dim3(256), 0, st, w.dPpart, chunk_offsets,
                      nseq, nslices, mcap, dP);
