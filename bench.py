@@ -715,7 +715,7 @@ def main():
     blended_peak = cr["flops"] / (ideal_ms * 1e-3) / 1e12
     roof = {
         "kernel": ("one bllm_coding_rate_split call (32 x 8192 x 512 bf16, two halves of 16 sequences on two "
-                   "streams): per half cr_gram_prefix_bf16 + 12 cr_diag + 11 cr_panel; Gram on bf16 MFMA, "
+                   "streams): per half cr_gram_prefix_bf16 + 1 cr_diag + 11 cr_panel (each factoring the next diagonal tile); Gram on bf16 MFMA, "
                    "factorization in fp32 arithmetic (strip products as exact three-part bf16 MFMA, diagonal and "
                    "TRSM on fp32 MFMA)"),
         "bound": "mfma",

@@ -501,11 +501,10 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
 }
 
 // ------------------------------------------------------------------ factorization
-// Left-looking by 64-column panels, two launches per panel over all block
-// matrices at once:
-//   cr_diag(k)   one wave per matrix factors the diagonal tile D_k (the Gram
-//                prefix for k = 0, else written by cr_panel(k-1)), stores
-//                Linv_k and, in the S part, the logs of the pivots
+// Left-looking by 64-column panels, one launch per panel over all block
+// matrices at once (plus one diagonal launch before the first):
+//   cr_diag(0)   one wave per matrix factors the first diagonal tile D_0 (the
+//                Gram prefix) and stores Linv_0
 //   cr_panel(k)  workgroups of each matrix build every tile below the diagonal
 //                of panel k, in passes of kPassTiles tiles (pp consecutive
 //                passes per workgroup; the passes are independent):
@@ -513,8 +512,15 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
 //                  L[i, k] = ACC_i Linv_k^T                            (TRSM)
 //                from row strips of L staged through LDS kChunk columns at a
 //                time (the panel's rows once per pass, every other strip row
-//                once), and the next diagonal tile
+//                once); the first pass's workgroup also builds the next
+//                diagonal tile
 //                  D_{k+1} = orig -/+ sum_{cols <= 64k+63} L[k+1, :] L[k+1, :]^T
+//                and factors it in LDS with one wave: Linv_{k+1} goes to the
+//                matrix's other inverse slot (the launch's other workgroups
+//                still read Linv_k from theirs) and, in the S part, the logs
+//                of its pivots to dR.  Those workgroups come first in the
+//                grid, so the factors overlap the rest of the launch instead
+//                of forming a serial launch of their own.
 // Waves hold ACC_i^T (panel columns x tile rows), so the TRSM is
 // Linv_k * ACC_i^T with the accumulator registers as the MFMA B operand: with
 // the k index of MFMA step st taken as crow(st, lane), register st of a C/D
@@ -530,6 +536,7 @@ constexpr int kXP = 68;                         // LDS row pitch of 64x64 tiles
 constexpr int kStripFloats = kStripRows * kSRow / 2 > 64 * kXP ? kStripRows * kSRow / 2 : 64 * kXP;
 constexpr int kPanelFloats = kStripFloats + 64 * kXP;
 static_assert(64 * kXP <= kStripFloats, "X staging must fit in the strip buffers");
+static_assert(64 * kXP + kFactorLds <= kPanelFloats, "D tile and factor scratch must fit");
 static_assert(kPassTiles == 2, "the strip loader below issues kPassTiles + 1 = 3 loads per set");
 
 // Strip products on bf16 MFMA: an fp32 value x is the exact sum of three
@@ -665,22 +672,34 @@ __global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __r
   const float* D = ws + static_cast<int64_t>(m) * g.ldm * g.ldm + static_cast<int64_t>(NB * k) * g.ldm + NB * k;
   float* dRb = NB * k >= g.dp ? dR + static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c : nullptr;
   // the last diagonal tile of a matrix has no rows below it: no inverse
-  factor64(D, g.ldm, sW, linv + static_cast<int64_t>(m) * NB * NB, NB, dRb, NB * k - g.dp,
+  factor64(D, g.ldm, sW, linv + static_cast<int64_t>(2 * m + (k & 1)) * NB * NB, NB, dRb, NB * k - g.dp,
            block_rows(g, j), status, NB * (k + 1) < block_n(g, j));
 }
 
 template <int DT>
 __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
-                                                   const float* __restrict__ linv, CRGeom g,
+                                                   float* __restrict__ linv, float* __restrict__ dR,
+                                                   int32_t* __restrict__ status, CRGeom g,
                                                    float salpha, int k, int pp) {
   __shared__ __attribute__((aligned(16))) float lds[kPanelFloats];
   float* sLi = lds + kStripFloats;      // Linv_k
   float* sX = lds;                      // X_{k+1} (over the strip buffers)
   uint16_t* sst = reinterpret_cast<uint16_t*>(lds);  // staged strip chunk, split into bf16 parts
-  // the workgroups of one matrix are consecutive on one XCD (block b runs on XCD b % 8)
   const int ngrp = (g.ldm / NB - k - 1 + kPassTiles * pp - 1) / (kPassTiles * pp);
-  const int bq = blockIdx.x >> 3, grp = bq % ngrp;
-  const int m = (bq / ngrp) * 8 + (blockIdx.x & 7);
+  // grid: first every matrix's lookahead workgroup (group 0, block m), so
+  // that the diagonal factors they finish with start early in the launch;
+  // then the other groups, those of one matrix consecutive on one XCD (block
+  // b runs on XCD b % 8) so that they share the panel's rows in its L2
+  const int nm8 = (g.nmat + 7) / 8 * 8;
+  int grp, m;
+  if (static_cast<int>(blockIdx.x) < nm8) {
+    grp = 0;
+    m = blockIdx.x;
+  } else {
+    const int b = blockIdx.x - nm8, bq = b >> 3;
+    grp = 1 + bq % (ngrp - 1);
+    m = (bq / (ngrp - 1)) * 8 + (b & 7);
+  }
   if (m >= g.nmat) return;
   const int s = m / g.nblk, j = m % g.nblk;
   const int npan = block_n(g, j) / NB;
@@ -700,7 +719,7 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
   const int nch = NB * k / kChunk;
   {
     // Linv_k to LDS: the four loads of a thread in flight together
-    const float* Li = linv + static_cast<int64_t>(m) * NB * NB;
+    const float* Li = linv + static_cast<int64_t>(2 * m + (k & 1)) * NB * NB;
     float4 lv[NB * NB / 4 / 256];
 #pragma unroll
     for (int i = 0; i < NB * NB / 4 / 256; ++i) {
@@ -889,10 +908,17 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
     __syncthreads();  // sX and the strip buffers are reused next
   }
   if (!look) return;
-  // D_{k+1} over the diagonal tile (k+1, k+1), whose original is consumed
-  float* Dt = Mx + static_cast<int64_t>(NB * (k + 1) + 32 * dm) * g.ldm + NB * (k + 1) + 32 * dn;
+  // D_{k+1} to LDS; one wave factors it (Linv_{k+1} to the other slot)
+  float* sD = lds;
+  float* sW = lds + 64 * kXP;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) Dt[static_cast<int64_t>(crow(q, lane)) * g.ldm + l32] = accD[q];
+  for (int q = 0; q < 16; ++q) sD[(32 * dm + crow(q, lane)) * kXP + 32 * dn + l32] = accD[q];
+  __syncthreads();
+  if (w != 0) return;
+  const int kd = k + 1;
+  float* dRb = NB * kd >= g.dp ? dR + static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c : nullptr;
+  factor64(sD, kXP, sW, linv + static_cast<int64_t>(2 * m + (kd & 1)) * NB * NB, NB, dRb, NB * kd - g.dp, cj,
+           status, NB * (kd + 1) < block_n(g, j));
 }
 
 CRGeom cr_geometry(int64_t nseq, int64_t T, int64_t d) {
@@ -912,7 +938,7 @@ CRGeom cr_geometry(int64_t nseq, int64_t T, int64_t d) {
 }
 
 size_t cr_ws_bytes(const CRGeom& g) {
-  return static_cast<size_t>(g.nmat) * (static_cast<size_t>(g.ldm) * g.ldm + NB * NB) * 4 + 256;
+  return static_cast<size_t>(g.nmat) * (static_cast<size_t>(g.ldm) * g.ldm + 2 * NB * NB) * 4 + 256;
 }
 
 // Passes of one panel launch per workgroup: one (a workgroup per pass, the
@@ -928,7 +954,7 @@ int passes_per_group(int nmat, int npass) {
 }
 
 // The launches of one factorization as numbered steps: 0 the Gram prefix,
-// then 2k + 1 the diagonal factor of panel k and 2k + 2 panel k.
+// 1 the first diagonal factor, then 2 + k panel k (which factors D_{k+1}).
 struct CRCall {
   const void* h;
   CRGeom g;
@@ -939,7 +965,7 @@ struct CRCall {
   hipStream_t st;
 };
 
-inline int cr_steps(const CRGeom& g) { return 2 * (g.ldm / NB); }  // gram + 12 diag + 11 panel at ldm 768
+inline int cr_steps(const CRGeom& g) { return g.ldm / NB + 1; }  // gram + diag 0 + 11 panels at ldm 768
 
 template <int DT>
 void cr_step(const CRCall& c, int i) {
@@ -955,14 +981,17 @@ void cr_step(const CRCall& c, int i) {
                          c.ws, g, static_cast<float>(c.alpha), c.sin, c.sout);
     return;
   }
-  const int k = (i - 1) / 2, npan = g.ldm / NB;
-  if (i % 2 == 1) {
-    hipLaunchKernelGGL(cr_diag, dim3(g.nmat), dim3(64), 0, c.st, c.ws, c.linv, c.dR, c.status, g, k);
-  } else if (k + 1 < npan) {
+  const int npan = g.ldm / NB;
+  if (i == 1) {
+    hipLaunchKernelGGL(cr_diag, dim3(g.nmat), dim3(64), 0, c.st, c.ws, c.linv, c.dR, c.status, g, 0);
+    return;
+  }
+  const int k = i - 2;
+  if (k + 1 < npan) {
     const int npass = (npan - k - 1 + kPassTiles - 1) / kPassTiles;
     const int pp = passes_per_group(g.nmat, npass);
     const int ngrp = (npass + pp - 1) / pp;
-    hipLaunchKernelGGL(cr_panel<DT>, dim3((g.nmat + 7) / 8 * 8 * ngrp), dim3(256), 0, c.st, c.h, c.ws, c.linv, g,
+    hipLaunchKernelGGL(cr_panel<DT>, dim3((g.nmat + 7) / 8 * 8 * ngrp), dim3(256), 0, c.st, c.h, c.ws, c.linv, c.dR, c.status, g,
                        static_cast<float>(std::sqrt(c.alpha)), k, pp);
   }
 }
@@ -1009,7 +1038,7 @@ static int coding_rate_entry(const void* h, int dtype, int64_t nseq, int64_t T, 
     c.alpha = alpha;
     c.dR = dR_out + s0 * T;
     c.ws = wsf + s0 * g.nblk * static_cast<int64_t>(g.ldm) * g.ldm;
-    c.linv = linv + s0 * g.nblk * static_cast<int64_t>(NB) * NB;
+    c.linv = linv + s0 * g.nblk * static_cast<int64_t>(2 * NB) * NB;
     c.sin = state_in ? state_in + s0 * d * d : nullptr;
     c.sout = state_out ? state_out + s0 * d * d : nullptr;
     c.status = status;

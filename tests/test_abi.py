@@ -47,7 +47,7 @@ def test_workspace_sizes(L):
     assert tiles >= 256 and w512 >= tiles * (1 + 2 * 512) * 4
     # d = 512: blocks of c = 256 rows, 32 blocks per sequence, block matrices of
     # (512 + 256)^2 fp32 plus a 64 x 64 inverse slot each
-    assert L.bllm_coding_rate_workspace(32, 8192, 512) == 32 * 32 * (768 * 768 + 64 * 64) * 4 + 256
+    assert L.bllm_coding_rate_workspace(32, 8192, 512) == 32 * 32 * (768 * 768 + 2 * 64 * 64) * 4 + 256
     assert L.bllm_coding_rate_workspace(0, 8192, 512) == 0
     # at most T + T/32 + 1 work items per sequence (one per present bin, one
     # more per 32 positions of a run), 16 bytes each
