@@ -26,8 +26,8 @@
 //                   bf16 MFMA with three-part splits, then X = acc L_kk^-T on
 //                   fp32 MFMA); the first workgroup also builds the next
 //                   diagonal tile
-// Workspace: nmat = nseq * nblk matrices of ldm^2 fp32 (ldm = d' + c), plus a
-// 64x64 inverse slot per matrix.
+// Workspace: nmat = nseq * nblk matrices of ldm^2 fp32 (ldm = d' + c) stored
+// as 64 x 16 tiles (mx_off), plus two 64x64 inverse slots per matrix.
 #include <algorithm>
 #include <cmath>
 
@@ -74,6 +74,14 @@ __device__ inline bool gram_tile_of_block(const CRGeom& g, int& s, int& t) {
 __device__ inline int block_rows(const CRGeom& g, int j) { return min(g.c, g.T - j * g.c); }
 __device__ inline int block_n(const CRGeom& g, int j) {
   return g.dp + ((block_rows(g, j) + NB - 1) / NB) * NB;
+}
+
+// A block matrix is stored as 64 x 16 fp32 tiles of 4 KB each, row-major
+// inside a tile and over the tiles: the 64 rows x 16 columns of a strip
+// chunk that a panel pass stages are one contiguous block of memory (rows of
+// the plain row-major form lie 3 KB apart, one 64-byte piece each).
+__device__ inline int mx_off(const CRGeom& g, int r, int c) {
+  return ((r >> 6) * (g.ldm >> 4) + (c >> 4)) * 1024 + (r & 63) * 16 + (c & 15);
 }
 
 // ------------------------------------------------------------------ Gram prefix
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_f32(const float* __restric
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
-      Mj[static_cast<int64_t>(row) * g.ldm + col] = (row == col ? 1.f : 0.f) + alpha * acc[r];
+      Mj[mx_off(g, row, col)] = (row == col ? 1.f : 0.f) + alpha * acc[r];
     }
     if (j == g.nblk - 1 && !sout) break;
     for (int sq = 0; sq < spb; ++sq, ++q) {
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       // streaming stores: the 600 MB of prefix tiles would otherwise push the
       // rows of h that the other tiles of the sequence still read out of L2
       __builtin_nontemporal_store((row == col ? 1.f : 0.f) + alpha * acc[r],
-                                  Mj + static_cast<int64_t>(row) * g.ldm + col);
+                                  Mj + mx_off(g, row, col));
     }
     if (j == g.nblk - 1 && !sout) break;
     for (int sq = 0; sq < spb; ++sq, ++q) {
@@ -537,6 +545,7 @@ constexpr int kStripFloats = kStripRows * kSRow / 2 > 64 * kXP ? kStripRows * kS
 constexpr int kPanelFloats = kStripFloats + 64 * kXP;
 static_assert(64 * kXP <= kStripFloats, "X staging must fit in the strip buffers");
 static_assert(64 * kXP + kFactorLds <= kPanelFloats, "D tile and factor scratch must fit");
+static_assert((NB / kChunk) % 2 == 0, "the strip loop takes chunks in pairs");
 static_assert(kPassTiles == 2, "the strip loader below issues kPassTiles + 1 = 3 loads per set");
 
 // Strip products on bf16 MFMA: an fp32 value x is the exact sum of three
@@ -616,7 +625,7 @@ __device__ inline floatx16 orig_issue(const void* h, const float* Mx, const CRGe
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const float4 v =
-          *reinterpret_cast<const float4*>(Mx + static_cast<int64_t>(row) * g.ldm + col0 + 8 * q4 + 4 * hh);
+          *reinterpret_cast<const float4*>(Mx + mx_off(g, row, col0 + 8 * q4 + 4 * hh));
       a[4 * q4] = v.x; a[4 * q4 + 1] = v.y; a[4 * q4 + 2] = v.z; a[4 * q4 + 3] = v.w;
     }
     return a;
@@ -666,13 +675,28 @@ __global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __r
                                               float* __restrict__ dR, int32_t* __restrict__ status,
                                               CRGeom g, int k) {
   __shared__ __attribute__((aligned(16))) float sW[kFactorLds];
+  __shared__ __attribute__((aligned(16))) float sD[64 * kXP];
   const int m = blockIdx.x;
   const int s = m / g.nblk, j = m % g.nblk;
   if (NB * k >= block_n(g, j)) return;
-  const float* D = ws + static_cast<int64_t>(m) * g.ldm * g.ldm + static_cast<int64_t>(NB * k) * g.ldm + NB * k;
+  // the tile (k, k) to LDS, row-major (all sixteen loads of a lane in flight together)
+  const float* Mx = ws + static_cast<int64_t>(m) * g.ldm * g.ldm;
+  const int lane = threadIdx.x;
+  float4 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = *reinterpret_cast<const float4*>(Mx + mx_off(g, NB * k + (e >> 4), NB * k + (e & 15) * 4));
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    *reinterpret_cast<float4*>(sD + (e >> 4) * kXP + (e & 15) * 4) = v[i];
+  }
+  wave_lds_sync();
   float* dRb = NB * k >= g.dp ? dR + static_cast<int64_t>(s) * g.T + static_cast<int64_t>(j) * g.c : nullptr;
   // the last diagonal tile of a matrix has no rows below it: no inverse
-  factor64(D, g.ldm, sW, linv + static_cast<int64_t>(2 * m + (k & 1)) * NB * NB, NB, dRb, NB * k - g.dp,
+  factor64(sD, kXP, sW, linv + static_cast<int64_t>(2 * m + (k & 1)) * NB * NB, NB, dRb, NB * k - g.dp,
            block_rows(g, j), status, NB * (k + 1) < block_n(g, j));
 }
 
@@ -764,17 +788,16 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
     for (int it = 0; it < 3; ++it) {
       const int r = lr + 64 * it;
       const int grow = r < NB ? NB * k + r : (r < nrows ? NB * (k + 1 + t0) + (r - NB) : NB * k + (r & 63));
-      go[it] = grow * g.ldm + lc;
+      go[it] = mx_off(g, grow, lc);
     }
     float4 qa0, qa1, qa2, qb0, qb1, qb2;
-    auto ldq = [&](int it, int co) { return *reinterpret_cast<const float4*>(Mx + go[it] + co); };
+    // chunk ch of a strip row is the row's piece of the ch-th 64 x 16 tile
+    auto ldq = [&](int it, int ch) { return *reinterpret_cast<const float4*>(Mx + go[it] + ch * 1024); };
     auto fetch_a = [&](int ch) {
-      const int co = ch * kChunk;
-      qa0 = ldq(0, co); qa1 = ldq(1, co); qa2 = ldq(2, co);
+      qa0 = ldq(0, ch); qa1 = ldq(1, ch); qa2 = ldq(2, ch);
     };
     auto fetch_b = [&](int ch) {
-      const int co = ch * kChunk;
-      qb0 = ldq(0, co); qb1 = ldq(1, co); qb2 = ldq(2, co);
+      qb0 = ldq(0, ch); qb1 = ldq(1, ch); qb2 = ldq(2, ch);
     };
     auto stash = [&](uint16_t* sb, const float4& v0, const float4& v1, const float4& v2) {
       stash_split(sb + lr * kSRow + lc, v0);
@@ -836,13 +859,13 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
       lds_barrier();
       fetch_a(ch + 2);
       compute(sst, ch);
-      if (ch + 1 < nch) {
-        lds_barrier();
-        stash(sst, qb0, qb1, qb2);
-        lds_barrier();
-        fetch_b(ch + 3);
-        compute(sst, ch + 1);
-      }
+      // nch is even (64 k / 16): no test here, so that the wait counts at
+      // both stashes leave the other set's prefetches in flight
+      lds_barrier();
+      stash(sst, qb0, qb1, qb2);
+      lds_barrier();
+      fetch_b(ch + 3);
+      compute(sst, ch + 1);
     }
     __syncthreads();  // strip buffers free (sX lives there); sLi staged
     // TRSM: X_u^T = Linv_k * ACC_u^T, written as rows of L
@@ -867,13 +890,12 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
           }
         }
         const int row = NB * (k + 1 + t0 + u) + 32 * wn + l32;
-        float* Lr = Mx + static_cast<int64_t>(row) * g.ldm + NB * k;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int kc = 8 * q4 + 4 * hh;
-          *reinterpret_cast<float4*>(Lr + kc) =
+          *reinterpret_cast<float4*>(Mx + mx_off(g, row, NB * k + kc)) =
               make_float4(x0[4 * q4], x0[4 * q4 + 1], x0[4 * q4 + 2], x0[4 * q4 + 3]);
-          *reinterpret_cast<float4*>(Lr + 32 + kc) =
+          *reinterpret_cast<float4*>(Mx + mx_off(g, row, NB * k + 32 + kc)) =
               make_float4(x1[4 * q4], x1[4 * q4 + 1], x1[4 * q4 + 2], x1[4 * q4 + 3]);
         }
         if (first && u == 0) {
