@@ -132,7 +132,7 @@ STEP_OPS = (("route_kernel", ("route+compact stage1", "route+compact stage2")),
             ("topk_kernel", ("topk_select",)),
             ("compact_count", ("gather",)),
             ("up_count", ("upsample_bins",)))
-STEP_KERNELS = 72  # dispatches of one step (coding rate at d 512 in two halves: 2 x (gram + 12 diag + 11 panel))
+STEP_KERNELS = 50  # dispatches of one step (coding rate at d 512 in two halves: 2 x (gram + 1 diag + 11 panel))
 MOPS_FLOPS = 512   # SQ_INSTS_VALU_MFMA_MOPS_* count MFMA work in units of 512 flops
 
 
