@@ -456,10 +456,14 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
   // sT holds L^T, so column p of L is the contiguous row p of sT.
   float x[32];
   {
-    const float* Tm = hi ? sT22 : sT11;
+    // the lane's own block as an offset computed from the lane index: as a
+    // choice between the two blocks' addresses, the compiler reads both
+    // blocks and selects per value
+    const int half32 = i >> 5;
+    const float* Tm = sT11 + half32 * (32 * kF);
     float ri[32];
 #pragma unroll
-    for (int p = 0; p < 32; p += 4) ld4(rinv + (hi ? 32 : 0) + p, ri + p);
+    for (int p = 0; p < 32; p += 4) ld4(rinv + 32 * half32 + p, ri + p);
 #pragma unroll
     for (int r = 0; r < 32; ++r) x[r] = r == ih ? 1.f : 0.f;
 #pragma unroll
@@ -474,7 +478,7 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
   wave_lds_sync();
   {
     // inverses to LDS (row-major, over the consumed transposes) and to Li
-    float* Tw = hi ? sT22 : sT11;
+    float* Tw = sT11 + (i >> 5) * (32 * kF);
 #pragma unroll
     for (int r = 0; r < 32; ++r) Tw[r * kF + ih] = x[r];
     if (!hi) {
