@@ -58,17 +58,49 @@ __device__ inline floatx16 zero16() {
 
 struct CRGeom {
   int T, d, dp, c, nblk, ldm, nmat, nseq;
+  int bps, nseg;  // Gram prefix segments: bps blocks each, nseg per sequence
 };
 
-// Gram tiles: 1-D grid of ceil(nseq/8)*8 * ntp blocks.  Block b runs on XCD
-// b % 8; every tile of one sequence lands on the same XCD so the rows of h
-// they all stream are fetched into that XCD's L2 once.
-__device__ inline bool gram_tile_of_block(const CRGeom& g, int& s, int& t) {
+// Gram tiles: 1-D grid of ceil(nseq/8)*8 * ntp * nseg blocks, one per
+// (sequence, 64x64 lower tile, segment of bps row blocks).  Block b runs on
+// XCD b % 8; every tile of one sequence lands on the same XCD, and the tiles
+// of one segment are consecutive there, so the rows of h they all stream are
+// fetched into that XCD's L2 once.
+__device__ inline bool gram_tile_of_block(const CRGeom& g, int& s, int& t, int& seg) {
   const int ntile = g.dp / 64, ntp = ntile * (ntile + 1) / 2;
   const int b = blockIdx.x, xcd = b & 7, q = b >> 3;
-  s = (q / ntp) * 8 + xcd;
-  t = q % ntp;
+  s = (q / (ntp * g.nseg)) * 8 + xcd;
+  const int u = q % (ntp * g.nseg);
+  seg = u / ntp;
+  t = u % ntp;
   return s < g.nseq;
+}
+
+// The Gram prefix runs in two launches over segments of bps row blocks, so
+// that no workgroup walks a whole sequence.  Pass 0: every segment but the
+// last sums its blocks' Gram tiles from zero and stores the total (fp32, in
+// the accumulator registers' own order: wave, register, lane).  Pass 1: a
+// segment starts from the stream's carried state plus the totals of the
+// segments before it, then stores the running prefix before each of its
+// blocks.
+__device__ inline float* seg_total(float* tot, const CRGeom& g, int s, int seg, int t) {
+  const int ntile = g.dp / 64, ntp = ntile * (ntile + 1) / 2;
+  return tot + ((static_cast<int64_t>(s) * g.nseg + seg) * ntp + t) * 4096;
+}
+__device__ inline floatx16 add_seg_totals(floatx16 acc, const float* tot, const CRGeom& g, int s, int seg, int t,
+                                          int w, int lane) {
+  for (int sp = 0; sp < seg; ++sp) {
+    const float* p = seg_total(const_cast<float*>(tot), g, s, sp, t) + w * 1024 + lane;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += p[r * 64];
+  }
+  return acc;
+}
+__device__ inline void store_seg_total(float* tot, const CRGeom& g, int s, int seg, int t, int w, int lane,
+                                       const floatx16& acc) {
+  float* p = seg_total(tot, g, s, seg, t) + w * 1024 + lane;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) p[r * 64] = acc[r];
 }
 
 __device__ inline int block_rows(const CRGeom& g, int j) { return min(g.c, g.T - j * g.c); }
@@ -132,12 +164,17 @@ __device__ inline void write_carry(float* sout, const CRGeom& g, int s, int r0, 
 // feature 0 and zeroed when stored to LDS.
 constexpr int kGR = 128;          // rows per step at most
 constexpr int kGLD = kGR + 4;     // LDS pitch (floats) of a staged [feature][row] strip
+template <int PASS>
 __global__ __launch_bounds__(256) void cr_gram_prefix_f32(const float* __restrict__ h, float* __restrict__ ws,
-                                                          CRGeom g, float alpha, const float* sin, float* sout) {
+                                                          CRGeom g, float alpha, const float* sin, float* sout,
+                                                          float* __restrict__ tot) {
   __shared__ __attribute__((aligned(16))) float sI[64 * kGLD];
   __shared__ __attribute__((aligned(16))) float sJ[64 * kGLD];
-  int s, t;
-  if (!gram_tile_of_block(g, s, t)) return;
+  int s, t, seg;
+  if (!gram_tile_of_block(g, s, t, seg)) return;
+  const bool lastseg = seg == g.nseg - 1;
+  if (PASS == 0 && lastseg) return;  // no later segment needs its total
+  const int tile = t;
   int I = 0;
   while (t > I) { t -= I + 1; ++I; }
   const int J = t;
@@ -147,7 +184,10 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_f32(const float* __restric
   const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
   const int R = g.c % kGR == 0 ? kGR : 64;
   const int spb = g.c / R;                         // steps per block
-  const int nq = (g.nblk - (sout ? 0 : 1)) * spb;  // steps that feed some prefix or the carry
+  const int b0 = seg * g.bps, b1 = min(g.nblk, b0 + g.bps);
+  // steps multiplied in: the segment's blocks (the sequence's last block only
+  // when its rows feed the carry)
+  const int nq = (lastseg && !sout ? g.nblk - 1 : b1) * spb;
   // thread: rows lr + 16 e of a step, features fc .. fc + 3 of each strip
   const int lr = tid >> 4, fc = (tid & 15) * 4;
   const bool fiok = 64 * I + fc < g.d, fjok = 64 * J + fc < g.d;
@@ -189,21 +229,28 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_f32(const float* __restric
     }
     return acc;
   };
-  floatx16 acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
-  if (nq > 0) fetch(0);
-  int q = 0;
-  for (int j = 0; j <= g.nblk; ++j) {
-    if (j == g.nblk) {
-      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
+  floatx16 acc = zero16();
+  if (PASS == 1) {
+    acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);  // every segment's start
+    acc = add_seg_totals(acc, tot, g, s, seg, tile, w, lane);
+  }
+  int q = b0 * spb;
+  if (q < nq) fetch(q);
+  for (int j = b0; j <= b1; ++j) {
+    if (j == b1) {
+      if (PASS == 0) store_seg_total(tot, g, s, seg, tile, w, lane, acc);
+      else if (lastseg) write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
       break;
     }
-    float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
+    if (PASS == 1) {
+      float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
-      Mj[mx_off(g, row, col)] = (row == col ? 1.f : 0.f) + alpha * acc[r];
+      for (int r = 0; r < 16; ++r) {
+        const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
+        Mj[mx_off(g, row, col)] = (row == col ? 1.f : 0.f) + alpha * acc[r];
+      }
     }
-    if (j == g.nblk - 1 && !sout) break;
+    if (q >= nq) break;
     for (int sq = 0; sq < spb; ++sq, ++q) {
       __syncthreads();
       stash(q);
@@ -235,14 +282,18 @@ __device__ inline bf16x8 tr_frag(const uint16_t* s, int row, int col, int pitch)
   return v;
 }
 
+template <int PASS>
 __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __restrict__ h,
                                                            float* __restrict__ ws, CRGeom g, float alpha,
-                                                           const float* sin, float* sout) {
+                                                           const float* sin, float* sout, float* __restrict__ tot) {
   constexpr int GP = 72;  // LDS pitch (bf16) of a staged row: 64 features + 8 pad
   __shared__ __attribute__((aligned(16))) uint16_t sI[128 * GP];
   __shared__ __attribute__((aligned(16))) uint16_t sJ[128 * GP];
-  int s, tt;
-  if (!gram_tile_of_block(g, s, tt)) return;
+  int s, tt, seg;
+  if (!gram_tile_of_block(g, s, tt, seg)) return;
+  const bool lastseg = seg == g.nseg - 1;
+  if (PASS == 0 && lastseg) return;  // no later segment needs its total
+  const int tile = tt;
   int I = 0;
   while (tt > I) { tt -= I + 1; ++I; }
   const int J = tt;
@@ -252,7 +303,10 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
   const int64_t mstride = static_cast<int64_t>(g.ldm) * g.ldm;
   const int R = g.c % 128 == 0 ? 128 : 64;
   const int spb = g.c / R;                // sub-chunks per block
-  const int nq = (g.nblk - (sout ? 0 : 1)) * spb;  // sub-chunks that feed some prefix or the carry
+  const int b0 = seg * g.bps, b1 = min(g.nblk, b0 + g.bps);
+  // sub-chunks multiplied in: the segment's blocks (the sequence's last block
+  // only when its rows feed the carry)
+  const int nq = (lastseg && !sout ? g.nblk - 1 : b1) * spb;
   const int lr = tid >> 3, lc = (tid & 7) * 8;  // rows lr + 32 q, features lc .. lc + 7
   const bool fiok = 64 * I + lc < g.d, fjok = 64 * J + lc < g.d;
   const uint16_t* hI = h + static_cast<int64_t>(s) * g.T * g.d + 64 * I + lc;
@@ -291,7 +345,11 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       *reinterpret_cast<uint4*>(sJ + (lr + 96) * GP + lc) = msk(y3, row_ok(fjok, q, 3));
     }
   };
-  floatx16 acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);
+  floatx16 acc = zero16();
+  if (PASS == 1) {
+    acc = carried_acc(sin, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, alpha);  // every segment's start
+    acc = add_seg_totals(acc, tot, g, s, seg, tile, w, lane);
+  }
   const uint16_t* sJr = same ? sI : sJ;
   const int j16 = lane & 15;
   const int frow = 8 * (lane >> 5) + (j16 >> 2);                  // + k0
@@ -304,23 +362,25 @@ __global__ __launch_bounds__(256) void cr_gram_prefix_bf16(const uint16_t* __res
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
     }
   };
-  if (nq > 0) fetch_a(0);
-  int q = 0;
-  for (int j = 0; j <= g.nblk; ++j) {
-    if (j == g.nblk) {
-      write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
+  int q = b0 * spb;
+  if (q < nq) fetch_a(q);
+  for (int j = b0; j <= b1; ++j) {
+    if (j == b1) {
+      if (PASS == 0) store_seg_total(tot, g, s, seg, tile, w, lane, acc);
+      else if (lastseg) write_carry(sout, g, s, 64 * I + 32 * wm, 64 * J + 32 * wn, lane, acc, alpha);
       break;
     }
-    float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
+    if (PASS == 1) {
+      float* Mj = ws + (static_cast<int64_t>(s) * g.nblk + j) * mstride;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
-      // streaming stores: the 600 MB of prefix tiles would otherwise push the
-      // rows of h that the other tiles of the sequence still read out of L2
-      __builtin_nontemporal_store((row == col ? 1.f : 0.f) + alpha * acc[r],
-                                  Mj + mx_off(g, row, col));
+      for (int r = 0; r < 16; ++r) {
+        const int row = 64 * I + 32 * wm + crow(r, lane), col = 64 * J + 32 * wn + (lane & 31);
+        // streaming stores: the 600 MB of prefix tiles would otherwise push the
+        // rows of h that the other tiles of the sequence still read out of L2
+        __builtin_nontemporal_store((row == col ? 1.f : 0.f) + alpha * acc[r], Mj + mx_off(g, row, col));
+      }
     }
-    if (j == g.nblk - 1 && !sout) break;
+    if (q >= nq) break;
     for (int sq = 0; sq < spb; ++sq, ++q) {
       lds_barrier();
       stash(q, ai0, ai1, ai2, ai3, aj0, aj1, aj2, aj3);
@@ -960,11 +1020,29 @@ CRGeom cr_geometry(int64_t nseq, int64_t T, int64_t d) {
   g.ldm = g.dp + c;
   g.nmat = static_cast<int>(nseq) * g.nblk;
   g.nseq = static_cast<int>(nseq);
+  // Gram prefix segments, chosen per sequence (never by the batch size, so a
+  // sequence's result does not depend on the batch it comes in): with few
+  // 64x64 tiles per sequence the chip idles while each tile's workgroup
+  // walks the whole sequence, so the blocks are cut into segments until a
+  // sequence has about 36 (tile, segment) workgroups (fp32 d 256: 10 tiles
+  // x 4 segments of 16 blocks); at d 512 (36 tiles) one segment, where a
+  // second launch and re-read rows cost more than they save.
+  const int ntile = g.dp / 64, ntp = ntile * (ntile + 1) / 2;
+  const int want = std::min(g.nblk, std::max(1, (36 + ntp - 1) / ntp));
+  g.bps = (g.nblk + want - 1) / want;
+  g.nseg = (g.nblk + g.bps - 1) / g.bps;
   return g;
 }
 
+// floats of the Gram prefix's segment totals
+size_t cr_tot_floats(const CRGeom& g) {
+  const size_t ntile = g.dp / 64, ntp = ntile * (ntile + 1) / 2;
+  return g.nseg > 1 ? static_cast<size_t>(g.nseq) * g.nseg * ntp * 4096 : 0;
+}
+
 size_t cr_ws_bytes(const CRGeom& g) {
-  return static_cast<size_t>(g.nmat) * (static_cast<size_t>(g.ldm) * g.ldm + 2 * NB * NB) * 4 + 256;
+  return (static_cast<size_t>(g.nmat) * (static_cast<size_t>(g.ldm) * g.ldm + 2 * NB * NB) + cr_tot_floats(g)) * 4 +
+         256;
 }
 
 // Passes of one panel launch per workgroup: one (a workgroup per pass, the
@@ -979,13 +1057,14 @@ int passes_per_group(int nmat, int npass) {
   return (npass + ngrp - 1) / ngrp;
 }
 
-// The launches of one factorization as numbered steps: 0 the Gram prefix,
-// 1 the first diagonal factor, then 2 + k panel k (which factors D_{k+1}).
+// The launches of one factorization as numbered steps: 0 the Gram prefix
+// (its segment totals, then the prefixes), 1 the first diagonal factor, then
+// 2 + k panel k (which factors D_{k+1}).
 struct CRCall {
   const void* h;
   CRGeom g;
   double alpha;
-  float *dR, *ws, *linv, *sout;
+  float *dR, *ws, *linv, *sout, *tot;
   const float* sin;
   int32_t* status;
   hipStream_t st;
@@ -998,13 +1077,23 @@ void cr_step(const CRCall& c, int i) {
   const CRGeom& g = c.g;
   if (i == 0) {
     const int nt = g.dp / NB;
-    const unsigned ggrid = static_cast<unsigned>((g.nseq + 7) / 8 * 8 * (nt * (nt + 1) / 2));
-    if (DT == BLLM_BF16)
-      hipLaunchKernelGGL(cr_gram_prefix_bf16, dim3(ggrid), dim3(256), 0, c.st, static_cast<const uint16_t*>(c.h),
-                         c.ws, g, static_cast<float>(c.alpha), c.sin, c.sout);
-    else
-      hipLaunchKernelGGL(cr_gram_prefix_f32, dim3(ggrid), dim3(256), 0, c.st, static_cast<const float*>(c.h),
-                         c.ws, g, static_cast<float>(c.alpha), c.sin, c.sout);
+    const unsigned ggrid = static_cast<unsigned>((g.nseq + 7) / 8 * 8 * (nt * (nt + 1) / 2) * g.nseg);
+    const float al = static_cast<float>(c.alpha);
+    if (DT == BLLM_BF16) {
+      const uint16_t* hb = static_cast<const uint16_t*>(c.h);
+      if (g.nseg > 1)
+        hipLaunchKernelGGL(cr_gram_prefix_bf16<0>, dim3(ggrid), dim3(256), 0, c.st, hb, c.ws, g, al, c.sin, c.sout,
+                           c.tot);
+      hipLaunchKernelGGL(cr_gram_prefix_bf16<1>, dim3(ggrid), dim3(256), 0, c.st, hb, c.ws, g, al, c.sin, c.sout,
+                         c.tot);
+    } else {
+      const float* hf = static_cast<const float*>(c.h);
+      if (g.nseg > 1)
+        hipLaunchKernelGGL(cr_gram_prefix_f32<0>, dim3(ggrid), dim3(256), 0, c.st, hf, c.ws, g, al, c.sin, c.sout,
+                           c.tot);
+      hipLaunchKernelGGL(cr_gram_prefix_f32<1>, dim3(ggrid), dim3(256), 0, c.st, hf, c.ws, g, al, c.sin, c.sout,
+                         c.tot);
+    }
     return;
   }
   const int npan = g.ldm / NB;
@@ -1065,6 +1154,8 @@ static int coding_rate_entry(const void* h, int dtype, int64_t nseq, int64_t T, 
     c.dR = dR_out + s0 * T;
     c.ws = wsf + s0 * g.nblk * static_cast<int64_t>(g.ldm) * g.ldm;
     c.linv = linv + s0 * g.nblk * static_cast<int64_t>(2 * NB) * NB;
+    c.tot = linv + static_cast<int64_t>(g.nmat) * 2 * NB * NB +
+            s0 * static_cast<int64_t>(cr_tot_floats(cr_geometry(1, T, d)));
     c.sin = state_in ? state_in + s0 * d * d : nullptr;
     c.sout = state_out ? state_out + s0 * d * d : nullptr;
     c.status = status;
