@@ -619,7 +619,7 @@ static_assert(kPassTiles == 2, "the strip loader below issues kPassTiles + 1 = 3
 // mid hi, hi lo, lo hi, mid mid), each exact in the fp32 accumulator, so the
 // sums keep fp32 accuracy at 6 x 32 instead of 8 x 64 MFMA cycles per 16 columns.
 // LDS strip row (kSRow bf16): [hi 0..15][mid 0..15][lo 0..15][pad 8].
-__device__ inline void stash_split(uint16_t* dst, const float4& v) {
+__device__ inline void stash_split(uint16_t* dst, const float4& v, uint32_t sgn = 0u) {
   const float x[4] = {v.x, v.y, v.z, v.w};
   uint32_t hw[4], mw[4], lw[4];
 #pragma unroll
@@ -634,11 +634,11 @@ __device__ inline void stash_split(uint16_t* dst, const float4& v) {
   // perm(s0, s1, sel): result low half = high half of s1, result high half = high half of s0
   const uint32_t sel = 0x07060302u;
   *reinterpret_cast<uint2*>(dst) =
-      make_uint2(__builtin_amdgcn_perm(hw[1], hw[0], sel), __builtin_amdgcn_perm(hw[3], hw[2], sel));
+      make_uint2(__builtin_amdgcn_perm(hw[1], hw[0], sel) ^ sgn, __builtin_amdgcn_perm(hw[3], hw[2], sel) ^ sgn);
   *reinterpret_cast<uint2*>(dst + 16) =
-      make_uint2(__builtin_amdgcn_perm(mw[1], mw[0], sel), __builtin_amdgcn_perm(mw[3], mw[2], sel));
+      make_uint2(__builtin_amdgcn_perm(mw[1], mw[0], sel) ^ sgn, __builtin_amdgcn_perm(mw[3], mw[2], sel) ^ sgn);
   *reinterpret_cast<uint2*>(dst + 32) =
-      make_uint2(__builtin_amdgcn_perm(lw[1], lw[0], sel), __builtin_amdgcn_perm(lw[3], lw[2], sel));
+      make_uint2(__builtin_amdgcn_perm(lw[1], lw[0], sel) ^ sgn, __builtin_amdgcn_perm(lw[3], lw[2], sel) ^ sgn);
 }
 
 // part p of the 8 columns 8 hh .. 8 hh + 7 of staged row r (16-byte LDS read)
@@ -863,19 +863,21 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
     auto fetch_b = [&](int ch) {
       qb0 = ldq(0, ch); qb1 = ldq(1, ch); qb2 = ldq(2, ch);
     };
-    auto stash = [&](uint16_t* sb, const float4& v0, const float4& v1, const float4& v2) {
-      stash_split(sb + lr * kSRow + lc, v0);
+    // the panel rows (rows 0..63 of the stage) are stored with the sign their
+    // products take in this chunk: negated unless an S panel meets A columns
+    auto stash = [&](uint16_t* sb, int ch, const float4& v0, const float4& v1, const float4& v2) {
+      const uint32_t sg = (panelS && ch * kChunk < g.dp) ? 0u : 0x80008000u;
+      stash_split(sb + lr * kSRow + lc, v0, sg);
       stash_split(sb + (lr + 64) * kSRow + lc, v1);
       stash_split(sb + (lr + 128) * kSRow + lc, v2);
     };
     auto compute = [&](const uint16_t* sb, int ch) {
       const bool chA = ch * kChunk < g.dp;
-      const uint32_t sg = (panelS && chA) ? 0u : 0x80008000u;  // sign flip of the panel rows
       uint4 a0[3], a1[3];
 #pragma unroll
       for (int p = 0; p < 3; ++p) {
-        a0[p] = xor4(frag(sb, l32, p, hh), sg);
-        a1[p] = xor4(frag(sb, 32 + l32, p, hh), sg);
+        a0[p] = frag(sb, l32, p, hh);
+        a1[p] = frag(sb, 32 + l32, p, hh);
       }
 #pragma unroll
       for (int sl = 0; sl < kSlots; ++sl) {
@@ -919,14 +921,14 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
     // flight across them)
     for (int ch = 0; ch < nch; ch += 2) {
       lds_barrier();
-      stash(sst, qa0, qa1, qa2);
+      stash(sst, ch, qa0, qa1, qa2);
       lds_barrier();
       fetch_a(ch + 2);
       compute(sst, ch);
       // nch is even (64 k / 16): no test here, so that the wait counts at
       // both stashes leave the other set's prefetches in flight
       lds_barrier();
-      stash(sst, qb0, qb1, qb2);
+      stash(sst, ch + 1, qb0, qb1, qb2);
       lds_barrier();
       fetch_b(ch + 3);
       compute(sst, ch + 1);

@@ -226,8 +226,9 @@ __device__ inline bf16x8 tr_frag(const uint16_t* s, int row, int col, int pitch)
 // row tile are given ids 8 apart inside a group of 8 * ncol consecutive ids.
 // They then run at about the same time on the same XCD and the gathered g
 // rows of the row tile come from HBM into that XCD's L2 once.
-__global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat,
-                                               const uint16_t* __restrict__ W,
+template <bool FULLK>
+__global__ __launch_bounds__(256, 3) void up_gemm(const uint16_t* gmat,
+                                               const uint16_t* W,
                                                const uint16_t* __restrict__ h, UpGeom g,
                                                const int32_t* __restrict__ bin_off,
                                                const int32_t* __restrict__ bin_cnt,
@@ -273,44 +274,59 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
   const uint16_t* ar2 = gmat + static_cast<int64_t>(sItem[lr + 64].x) * g.dg + lc;
   const uint16_t* ar3 = gmat + static_cast<int64_t>(sItem[lr + 96].x) * g.dg + lc;
   const uint16_t* wb = W + static_cast<int64_t>(b) * g.dg * g.dl + min(n0 + nc, g.dl - 8);
-  uint4 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;
+  // A rows (gathered g rows) are prefetched two K steps ahead in two named
+  // register sets used in turn (the loop takes steps in pairs, so every wait
+  // count is static and leaves the later set's loads in flight); W_b rows,
+  // which every row tile of the bin shares, one step ahead.
+  uint4 pa0, pa1, pa2, pa3, qa0, qa1, qa2, qa3, pb0, pb1, pb2, pb3;
   // Every load is issued (rows past the items read chunk 0's g row, whose
   // results are not written; K past d_global, only in a last partial step,
-  // reads column or row 0).  The masks that zero that K range are applied when
-  // the registers are stored to LDS, a K step later: applied here, they would
-  // make every load wait for its data at once and the prefetch would not
-  // overlap the MFMAs.
-  auto fetch = [&](int ko) {
-    const int koa = ko + lc < g.dg ? ko : 0;
-    pa0 = *reinterpret_cast<const uint4*>(ar0 + koa);
-    pa1 = *reinterpret_cast<const uint4*>(ar1 + koa);
-    pa2 = *reinterpret_cast<const uint4*>(ar2 + koa);
-    pa3 = *reinterpret_cast<const uint4*>(ar3 + koa);
+  // reads column or row 0; steps past the last reload it).  The masks that
+  // zero that K range are applied when the registers are stored to LDS: applied
+  // here, they would make every load wait for its data at once and the
+  // prefetch would not overlap the MFMAs.
+  const int nk = (g.dg + kBK - 1) / kBK;
+  auto fetch_a = [&](int kt, uint4& x0, uint4& x1, uint4& x2, uint4& x3) {
+    const int ko = min(kt, nk - 1) * kBK;
+    const int koa = FULLK || ko + lc < g.dg ? ko : 0;
+    x0 = *reinterpret_cast<const uint4*>(ar0 + koa);
+    x1 = *reinterpret_cast<const uint4*>(ar1 + koa);
+    x2 = *reinterpret_cast<const uint4*>(ar2 + koa);
+    x3 = *reinterpret_cast<const uint4*>(ar3 + koa);
+  };
+  auto fetch_b = [&](int kt) {
+    const int ko = min(kt, nk - 1) * kBK;
     const int k0 = ko + kr, k1 = k0 + 16, k2 = k0 + 32, k3 = k0 + 48;
-    pb0 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k0 < g.dg ? k0 : 0) * g.dl);
-    pb1 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k1 < g.dg ? k1 : 0) * g.dl);
-    pb2 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k2 < g.dg ? k2 : 0) * g.dl);
-    pb3 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(k3 < g.dg ? k3 : 0) * g.dl);
+    pb0 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(FULLK || k0 < g.dg ? k0 : 0) * g.dl);
+    pb1 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(FULLK || k1 < g.dg ? k1 : 0) * g.dl);
+    pb2 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(FULLK || k2 < g.dg ? k2 : 0) * g.dl);
+    pb3 = *reinterpret_cast<const uint4*>(wb + static_cast<int64_t>(FULLK || k3 < g.dg ? k3 : 0) * g.dl);
   };
   const int j16 = lane & 15;
   const int frow = 8 * (lane >> 5) + (j16 >> 2);
   const int fcol = 64 * wn + 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
-  fetch(0);
-  const int nk = (g.dg + kBK - 1) / kBK;
-  for (int kt = 0; kt < nk; ++kt) {
+  // one K step: stage A (from the given set) and B, then issue the next B and
+  // the A two steps ahead into the same set, then multiply
+  auto step = [&](int kt, uint4& x0, uint4& x1, uint4& x2, uint4& x3) {
     const int ko = kt * kBK;
-    const uint32_t ma = ko + lc < g.dg ? 0xFFFFFFFFu : 0u;
+    // with d_global a multiple of the K step every staged value is in range
+    const uint32_t ma = FULLK || ko + lc < g.dg ? 0xFFFFFFFFu : 0u;
+    auto mb = [&](int k) { return FULLK || ko + k < g.dg ? 0xFFFFFFFFu : 0u; };
     __syncthreads();
-    *reinterpret_cast<uint4*>(sA + lr * kPA + lc) = and4(pa0, ma);
-    *reinterpret_cast<uint4*>(sA + (lr + 32) * kPA + lc) = and4(pa1, ma);
-    *reinterpret_cast<uint4*>(sA + (lr + 64) * kPA + lc) = and4(pa2, ma);
-    *reinterpret_cast<uint4*>(sA + (lr + 96) * kPA + lc) = and4(pa3, ma);
-    *reinterpret_cast<uint4*>(sB + kr * kPB + nc) = and4(pb0, ko + kr < g.dg ? 0xFFFFFFFFu : 0u);
-    *reinterpret_cast<uint4*>(sB + (kr + 16) * kPB + nc) = and4(pb1, ko + kr + 16 < g.dg ? 0xFFFFFFFFu : 0u);
-    *reinterpret_cast<uint4*>(sB + (kr + 32) * kPB + nc) = and4(pb2, ko + kr + 32 < g.dg ? 0xFFFFFFFFu : 0u);
-    *reinterpret_cast<uint4*>(sB + (kr + 48) * kPB + nc) = and4(pb3, ko + kr + 48 < g.dg ? 0xFFFFFFFFu : 0u);
+    *reinterpret_cast<uint4*>(sA + lr * kPA + lc) = and4(x0, ma);
+    *reinterpret_cast<uint4*>(sA + (lr + 32) * kPA + lc) = and4(x1, ma);
+    *reinterpret_cast<uint4*>(sA + (lr + 64) * kPA + lc) = and4(x2, ma);
+    *reinterpret_cast<uint4*>(sA + (lr + 96) * kPA + lc) = and4(x3, ma);
+    *reinterpret_cast<uint4*>(sB + kr * kPB + nc) = and4(pb0, mb(kr));
+    *reinterpret_cast<uint4*>(sB + (kr + 16) * kPB + nc) = and4(pb1, mb(kr + 16));
+    *reinterpret_cast<uint4*>(sB + (kr + 32) * kPB + nc) = and4(pb2, mb(kr + 32));
+    *reinterpret_cast<uint4*>(sB + (kr + 48) * kPB + nc) = and4(pb3, mb(kr + 48));
     __syncthreads();
-    if (kt + 1 < nk) fetch((kt + 1) * kBK);
+    fetch_b(kt + 1);
+    // keeps the next B rows ahead of the A rows in issue order, so that the
+    // next step's wait for B leaves these A loads in flight
+    __asm__ volatile("" ::: "memory");
+    fetch_a(kt + 2, x0, x1, x2, x3);
 #pragma unroll
     for (int ks = 0; ks < kBK; ks += 16) {
       bf16x8 af[2], bfr[2];
@@ -325,7 +341,16 @@ __global__ __launch_bounds__(256) void up_gemm(const uint16_t* __restrict__ gmat
         for (int c = 0; c < 2; ++c)
           acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[c], acc[a][c], 0, 0, 0);
     }
+  };
+  fetch_b(0);
+  fetch_a(0, pa0, pa1, pa2, pa3);
+  fetch_a(1, qa0, qa1, qa2, qa3);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, pa0, pa1, pa2, pa3);
+    step(kt + 1, qa0, qa1, qa2, qa3);
   }
+  if (kt < nk) step(kt, pa0, pa1, pa2, pa3);
   // epilogue, one pass per row half p (rows 64p..64p+63, written by the waves
   // with wm == p): stage the fp32 accumulators in LDS, then add h and write
   // every position of each item's run with 16-byte accesses.
@@ -469,7 +494,13 @@ extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* 
   const int64_t max_tiles = ceil_div(static_cast<int64_t>(up_max_items(g)), kBM) + nbins;
   const int ncol = static_cast<int>(ceil_div(d_local, kBN));
   const int64_t nblocks = ceil_div(max_tiles, 8) * 8 * ncol;
-  hipLaunchKernelGGL(up_gemm, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, st,
+  if (g.dg % kBK == 0)
+    hipLaunchKernelGGL(up_gemm<true>, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(gm), static_cast<const uint16_t*>(W),
+                     static_cast<const uint16_t*>(h), g, u.bin_off,
+                     u.bin_cnt, u.tile_off, u.items, ncol, static_cast<uint16_t*>(s_out));
+  else
+    hipLaunchKernelGGL(up_gemm<false>, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(gm), static_cast<const uint16_t*>(W),
                      static_cast<const uint16_t*>(h), g, u.bin_off,
                      u.bin_cnt, u.tile_off, u.items, ncol, static_cast<uint16_t*>(s_out));
