@@ -354,6 +354,17 @@ __global__ __launch_bounds__(256, 3) void up_gemm(const uint16_t* gmat,
   // epilogue, one pass per row half p (rows 64p..64p+63, written by the waves
   // with wm == p): stage the fp32 accumulators in LDS, then add h and write
   // every position of each item's run with 16-byte accesses.
+  // The pass's work is cut into units of (4-position group of an item's run,
+  // 8-column chunk), so that a few long runs do not leave most threads idle:
+  // one wave numbers the groups of the pass's 64 items (an exclusive scan of
+  // ceil(run / 4)) into a group -> (item, group) map in LDS while the waves
+  // with wm == p stage their accumulators; then every thread takes units in
+  // steps of 256, kPairs of them with all their loads in flight together.
+  uint16_t* gmap = reinterpret_cast<uint16_t*>(sO + 64 * kOLD);  // [512]: item << 3 | group
+  __shared__ int sGroups;
+  static_assert(64 * kOLD * 4 + 512 * 2 <= (kBM * kPA + kBK * kPB) * 2, "epilogue staging and map must fit");
+  static_assert(kMaxRun <= 32, "at most 8 groups of 4 positions per item");
+  const int nchunk = min(kBN, g.dl - n0) / 8;
   for (int p = 0; p < 2; ++p) {
     __syncthreads();
     if (wm == p) {
@@ -364,30 +375,37 @@ __global__ __launch_bounds__(256, 3) void up_gemm(const uint16_t* gmat,
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             sO[(32 * a + crow_of(r, lane)) * kOLD + 64 * wn + 32 * c + (lane & 31)] = acc[a][c][r];
+    } else if (wn == 0) {
+      const int rows = min(64, max(0, mcount - 64 * p));
+      const int ng = lane < rows ? (sItem[64 * p + lane].z + 3) >> 2 : 0;
+      int x = ng;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+      }
+      const int g0 = x - ng;
+      for (int k = 0; k < ng; ++k) gmap[g0 + k] = static_cast<uint16_t>((lane << 3) | k);
+      if (lane == 63) sGroups = x;
     }
     __syncthreads();
-    // (item row, 8-column chunk) pairs, kPairs per thread and round: the
-    // first four positions of every pair's run are loaded before any is
-    // written (most runs are that short); longer runs continue four
-    // positions at a time
-    const int nchunk = min(kBN, g.dl - n0) / 8;
-    const int rows = min(64, max(0, mcount - 64 * p));
-    const int npairs = rows * nchunk;
-    for (int v0 = tid; v0 < npairs; v0 += kPairs * 256) {
-      int4 it[kPairs];
-      int so[kPairs];
+    const int nunits = sGroups * nchunk;
+    for (int v0 = tid; v0 < nunits; v0 += kPairs * 256) {
+      int np[kPairs], so[kPairs];
       int64_t o0[kPairs];
       uint4 hv[kPairs][4];
 #pragma unroll
       for (int j = 0; j < kPairs; ++j) {
         const int v = v0 + j * 256;
-        const int vv = v < npairs ? v : v0;
-        const int r = vv / nchunk, ch = vv - r * nchunk;
-        it[j] = sItem[64 * p + r];
-        if (v >= npairs) it[j].z = 0;
+        const int vv = v < nunits ? v : v0;
+        const int gi = vv / nchunk, ch = vv - gi * nchunk;
+        const int m = gmap[gi];
+        const int r = m >> 3, grp4 = 4 * (m & 7);
+        const int4 it = sItem[64 * p + r];
+        np[j] = v < nunits ? min(4, it.z - grp4) : 0;
         so[j] = r * kOLD + 8 * ch;
-        o0[j] = static_cast<int64_t>(it[j].y) * g.dl + n0 + 8 * ch;
-        const int last = max(it[j].z, 1) - 1;
+        o0[j] = (static_cast<int64_t>(it.y) + grp4) * g.dl + n0 + 8 * ch;
+        const int last = max(np[j], 1) - 1;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           hv[j][e] = *reinterpret_cast<const uint4*>(h + o0[j] + static_cast<int64_t>(min(e, last)) * g.dl);
@@ -397,26 +415,17 @@ __global__ __launch_bounds__(256, 3) void up_gemm(const uint16_t* gmat,
         float acc8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc8[e] = sO[so[j] + e];
-        for (int q0 = 0; q0 < it[j].z; q0 += 4) {
-          if (q0 > 0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int q = min(q0 + e, it[j].z - 1);  // past the run: reload its last position
-              hv[j][e] = *reinterpret_cast<const uint4*>(h + o0[j] + static_cast<int64_t>(q) * g.dl);
-            }
+        for (int e = 0; e < 4; ++e) {
+          if (e >= np[j]) break;
+          const uint32_t wv[4] = {hv[j][e].x, hv[j][e].y, hv[j][e].z, hv[j][e].w};
+          float sv[8];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            sv[2 * c] = acc8[2 * c] + bf16_to_f32(static_cast<uint16_t>(wv[c] & 0xFFFFu));
+            sv[2 * c + 1] = acc8[2 * c + 1] + bf16_to_f32(static_cast<uint16_t>(wv[c] >> 16));
           }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (q0 + e >= it[j].z) break;
-            const uint32_t wv[4] = {hv[j][e].x, hv[j][e].y, hv[j][e].z, hv[j][e].w};
-            float sv[8];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              sv[2 * c] = acc8[2 * c] + bf16_to_f32(static_cast<uint16_t>(wv[c] & 0xFFFFu));
-              sv[2 * c + 1] = acc8[2 * c + 1] + bf16_to_f32(static_cast<uint16_t>(wv[c] >> 16));
-            }
-            Vec<BLLM_BF16>::store(out, o0[j] + static_cast<int64_t>(q0 + e) * g.dl, sv);
-          }
+          Vec<BLLM_BF16>::store(out, o0[j] + static_cast<int64_t>(e) * g.dl, sv);
         }
       }
     }
