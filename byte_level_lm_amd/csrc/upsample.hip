@@ -10,8 +10,8 @@
 // items are the distinct (chunk, bin) pairs, each covering a run of
 // consecutive positions; runs longer than kMaxRun positions (long chunks) are
 // split into several items, so no GEMM tile's epilogue carries much more than
-// 128 * kMaxRun positions.  Items are bucketed by bin (counting sort with wave
-// ballots; a deterministic order), then one grouped GEMM per bin on bf16 MFMA
+// 128 * kMaxRun positions.  Items are bucketed by bin (counting sort with DPP
+// wave scans; a deterministic order), then one grouped GEMM per bin on bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16): A rows are gathered from g by chunk, B = W_b
 // as stored (read down its columns with the transposing LDS read), and the
 // epilogue adds h_t and writes every position of the item's run with 16-byte
@@ -63,28 +63,37 @@ __device__ inline int bin_pieces(int b, int L, int B) {
   return (bin_lo<BC>(b + 1, L, B) - bin_lo<BC>(b, L, B) + kMaxRun - 1) / kMaxRun;
 }
 
-// Wave sum and exclusive wave scan of small counts.  A lane holds at most one
-// item per bin unless its run exceeds kMaxRun positions, so the common case
-// is a ballot and a popcount (mbcnt); otherwise shuffles.
-__device__ inline int wave_sum_i(int v) {
-  if (__ballot(v > 1) == 0) return __popcll(__ballot(v == 1));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+// Wave scans of counts: an inclusive scan inside each row of 16 lanes by
+// four DPP row shifts (lanes with no source lane read 0), then the three
+// lower rows' totals by readlane.  No LDS round trip, so a scan costs a
+// dozen VALU instructions (the shuffle form waited on eight LDS permutes).
+// Every lane of the wave must be active.
+template <int N>
+__device__ inline int row_shr(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, true);
 }
 
-__device__ inline int wave_excl_i(int v, int lane) {
-  if (__ballot(v > 1) == 0) {
-    const uint64_t m = __ballot(v == 1);
-    return __popcll(m & ((uint64_t(1) << lane) - 1));
-  }
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
-  return x - v;
+__device__ inline int wave_incl_i(int v, int& total) {
+  v += row_shr<1>(v);
+  v += row_shr<2>(v);
+  v += row_shr<4>(v);
+  v += row_shr<8>(v);
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31);
+  const int t2 = __builtin_amdgcn_readlane(v, 47), t3 = __builtin_amdgcn_readlane(v, 63);
+  const int r = (threadIdx.x & 63) >> 4;
+  total = t0 + t1 + t2 + t3;
+  return v + (r > 0 ? t0 : 0) + (r > 1 ? t1 : 0) + (r > 2 ? t2 : 0);
+}
+
+__device__ inline int wave_sum_i(int v) {
+  int t;
+  wave_incl_i(v, t);
+  return t;
+}
+
+__device__ inline int wave_excl_i(int v) {
+  int t;
+  return wave_incl_i(v, t) - v;
 }
 
 // per-block, per-bin item counts
@@ -125,19 +134,16 @@ __global__ __launch_bounds__(kScanThreads) void up_scan(UpGeom g, int32_t* __res
     int tot = 0;
     for (int k0 = 0; k0 < g.nblk; k0 += 64) {
       const int k = k0 + lane;
-      int v = k < g.nblk ? counts[static_cast<int64_t>(k) * g.nbins + b] : 0;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-      tot += v;
+      tot += wave_sum_i(k < g.nblk ? counts[static_cast<int64_t>(k) * g.nbins + b] : 0);
     }
     if (lane == 0) sTot[b] = tot;
   }
   __syncthreads();
   if (w == 0) {
     const int tb = lane < g.nbins ? sTot[lane] : 0;
-    const int off = wave_excl_i(tb, lane);
+    const int off = wave_excl_i(tb);
     const int tc = (tb + kBM - 1) / kBM;
-    const int toff = wave_excl_i(tc, lane);
+    const int toff = wave_excl_i(tc);
     if (lane < g.nbins) {
       sOff[lane] = off;
       bin_off[lane] = off;
@@ -153,14 +159,10 @@ __global__ __launch_bounds__(kScanThreads) void up_scan(UpGeom g, int32_t* __res
       const int k = k0 + lane;
       int32_t* cp = counts + static_cast<int64_t>(k < g.nblk ? k : 0) * g.nbins + b;
       const int v = k < g.nblk ? *cp : 0;
-      int x = v;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-      }
+      int all;
+      const int x = wave_incl_i(v, all);
       if (k < g.nblk) *cp = run + x - v;
-      run += __shfl(x, 63, kWave);
+      run += all;
     }
   }
 }
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_items(const int32_t* __res
   const int64_t row0 = valid ? (cg / g.K) * g.T + idx[cg] : 0;
   for (int b = 0; b < g.nbins; ++b) {
     const int np = valid ? bin_pieces<BC>(b, L, g.nbins) : 0;
-    int slot = sBase[b] + wave_excl_i(np, lane);
+    int slot = sBase[b] + wave_excl_i(np);
     for (int q = 0; q < w; ++q) slot += wc[q][b];
     const int lo = bin_lo<BC>(b, L, g.nbins), hi = bin_lo<BC>(b + 1, L, g.nbins);
     for (int e = 0; e < np; ++e) {
@@ -378,15 +380,10 @@ __global__ __launch_bounds__(256, 3) void up_gemm(const uint16_t* gmat,
     } else if (wn == 0) {
       const int rows = min(64, max(0, mcount - 64 * p));
       const int ng = lane < rows ? (sItem[64 * p + lane].z + 3) >> 2 : 0;
-      int x = ng;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-      }
-      const int g0 = x - ng;
+      int total;
+      const int g0 = wave_incl_i(ng, total) - ng;
       for (int k = 0; k < ng; ++k) gmap[g0 + k] = static_cast<uint16_t>((lane << 3) | k);
-      if (lane == 63) sGroups = x;
+      if (lane == 0) sGroups = total;
     }
     __syncthreads();
     const int nunits = sGroups * nchunk;
