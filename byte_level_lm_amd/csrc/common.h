@@ -89,6 +89,27 @@ __device__ inline float load_elem(const void* base, int64_t i, int dtype) {
 
 // ---------------------------------------------------------------- wave helpers
 
+// Inclusive integer scan over the 64 lanes of a wave: an inclusive scan
+// inside each row of 16 lanes by four DPP row shifts (lanes with no source
+// lane read 0), then the three lower rows' totals added by readlane.  No LDS
+// round trip (a shuffle scan waits on six LDS permutes).  Every lane of the
+// wave must be active; `total` is the wave's sum, in every lane.
+template <int N>
+__device__ inline int dpp_row_shr(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, true);
+}
+__device__ inline int wave_incl_scan(int v, int& total) {
+  v += dpp_row_shr<1>(v);
+  v += dpp_row_shr<2>(v);
+  v += dpp_row_shr<4>(v);
+  v += dpp_row_shr<8>(v);
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31);
+  const int t2 = __builtin_amdgcn_readlane(v, 47), t3 = __builtin_amdgcn_readlane(v, 63);
+  const int r = (threadIdx.x & 63) >> 4;
+  total = t0 + t1 + t2 + t3;
+  return v + (r > 0 ? t0 : 0) + (r > 1 ? t1 : 0) + (r > 2 ? t2 : 0);
+}
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);

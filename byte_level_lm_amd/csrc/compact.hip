@@ -56,12 +56,8 @@ __device__ inline int lower_seq(const int64_t* a, int n, int64_t x) {
 // exclusive block scan of one int per thread (blockDim = 256); returns the block total in *tot
 __device__ inline int block_excl_scan256(int v, int* sh, int* tot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  int wt;
+  const int x = wave_incl_scan(v, wt);
   if (lane == 63) sh[w] = x;
   __syncthreads();
   int wbase = 0, all = 0;

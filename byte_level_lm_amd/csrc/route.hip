@@ -183,12 +183,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
       cnt[q] = q < per ? __hip_atomic_load(&gh[tid * per + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
       mine += cnt[q];
     }
-    uint32_t incl = mine;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t t = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += t;
-    }
+    int wall;  // at most 2^31 scores: the int scan is exact
+    uint32_t incl = static_cast<uint32_t>(wave_incl_scan(static_cast<int>(mine), wall));
     if (lane == kWave - 1) wtot[wv] = incl;
     __syncthreads();
     for (int w = 0; w < wv; ++w) incl += wtot[w];

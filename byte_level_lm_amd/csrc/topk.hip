@@ -35,22 +35,14 @@ __device__ inline uint32_t order_key(float x, bool* nan) {
 // exclusive scan over the 1024 threads of one int each
 __device__ inline int block_excl_scan1024(int v, int* sh, int* tot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  int wt;
+  const int x = wave_incl_scan(v, wt);
   if (lane == 63) sh[w] = x;
   __syncthreads();
   if (w == 0) {
-    int y = lane < 16 ? sh[lane] : 0;
-    int inc = y;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const int z = __shfl_up(inc, off, 64);
-      if (lane >= off) inc += z;
-    }
+    const int y = lane < 16 ? sh[lane] : 0;
+    int all;
+    const int inc = wave_incl_scan(y, all);
     if (lane < 16) sh[16 + lane] = inc - y;
     if (lane == 15) sh[32] = inc;
   }
@@ -108,7 +100,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
         const uint64_t am = __ballot(act);
         if (am == 0) continue;
         const int fl = __ffsll(static_cast<unsigned long long>(am)) - 1;
-        const uint32_t d0 = __shfl(dg, fl, 64);
+        const uint32_t d0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dg), fl));
         const uint64_t m0 = __ballot(act && dg == d0);
         if (lane == fl) atomicAdd(&hist[d0], static_cast<uint32_t>(__popcll(m0)));
         if (act && dg != d0) atomicAdd(&hist[dg], 1u);
@@ -120,12 +112,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
         uint32_t c[4], sum = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) { c[q] = hist[255 - 4 * l - q]; sum += c[q]; }
-        uint32_t inc = sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t z = __shfl_up(inc, off, 64);
-          if (l >= off) inc += z;
-        }
+        int all;  // counts of at most kMaxT keys: the int scan is exact
+        const uint32_t inc = static_cast<uint32_t>(wave_incl_scan(static_cast<int>(sum), all));
         const uint32_t want = sel_want;
         const uint32_t above = inc - sum;
         if (above < want && want <= inc) {

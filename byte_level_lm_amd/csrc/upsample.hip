@@ -63,37 +63,16 @@ __device__ inline int bin_pieces(int b, int L, int B) {
   return (bin_lo<BC>(b + 1, L, B) - bin_lo<BC>(b, L, B) + kMaxRun - 1) / kMaxRun;
 }
 
-// Wave scans of counts: an inclusive scan inside each row of 16 lanes by
-// four DPP row shifts (lanes with no source lane read 0), then the three
-// lower rows' totals by readlane.  No LDS round trip, so a scan costs a
-// dozen VALU instructions (the shuffle form waited on eight LDS permutes).
-// Every lane of the wave must be active.
-template <int N>
-__device__ inline int row_shr(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, true);
-}
-
-__device__ inline int wave_incl_i(int v, int& total) {
-  v += row_shr<1>(v);
-  v += row_shr<2>(v);
-  v += row_shr<4>(v);
-  v += row_shr<8>(v);
-  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31);
-  const int t2 = __builtin_amdgcn_readlane(v, 47), t3 = __builtin_amdgcn_readlane(v, 63);
-  const int r = (threadIdx.x & 63) >> 4;
-  total = t0 + t1 + t2 + t3;
-  return v + (r > 0 ? t0 : 0) + (r > 1 ? t1 : 0) + (r > 2 ? t2 : 0);
-}
-
+// Wave sums and exclusive wave scans of counts (DPP, no LDS round trip).
 __device__ inline int wave_sum_i(int v) {
   int t;
-  wave_incl_i(v, t);
+  wave_incl_scan(v, t);
   return t;
 }
 
 __device__ inline int wave_excl_i(int v) {
   int t;
-  return wave_incl_i(v, t) - v;
+  return wave_incl_scan(v, t) - v;
 }
 
 // per-block, per-bin item counts
@@ -160,7 +139,7 @@ __global__ __launch_bounds__(kScanThreads) void up_scan(UpGeom g, int32_t* __res
       int32_t* cp = counts + static_cast<int64_t>(k < g.nblk ? k : 0) * g.nbins + b;
       const int v = k < g.nblk ? *cp : 0;
       int all;
-      const int x = wave_incl_i(v, all);
+      const int x = wave_incl_scan(v, all);
       if (k < g.nblk) *cp = run + x - v;
       run += all;
     }
@@ -381,7 +360,7 @@ __global__ __launch_bounds__(256, 3) void up_gemm(const uint16_t* gmat,
       const int rows = min(64, max(0, mcount - 64 * p));
       const int ng = lane < rows ? (sItem[64 * p + lane].z + 3) >> 2 : 0;
       int total;
-      const int g0 = wave_incl_i(ng, total) - ng;
+      const int g0 = wave_incl_scan(ng, total) - ng;
       for (int k = 0; k < ng; ++k) gmap[g0 + k] = static_cast<uint16_t>((lane << 3) | k);
       if (lane == 0) sGroups = total;
     }
