@@ -38,13 +38,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--schedule", default="after_dr", choices=["after_dr", "with_dr", "serial"],
+    ap.add_argument("--schedule", default="after_dr", choices=["after_dr", "routes_with_dr", "with_dr", "serial"],
                     help="where the H-Net layer runs in a step: on a stream of its own beside Top-K, gather "
-                         "and upsample (after_dr, the default) or beside Delta R (with_dr), or every op on "
-                         "one stream in turn (serial); the other two are timed as well")
+                         "and upsample (after_dr, the default) or beside Delta R (with_dr), its routing beside "
+                         "Delta R and its dechunks after it (routes_with_dr), or every op on one stream in turn "
+                         "(serial); the others are timed as well")
     ap.add_argument("--profile-op", default=None,
-                    help="run only this op (or 'step': the whole step; 'copy': a 1 GiB device copy) "
-                         "--steps times after set-up, untimed (for rocprofv3)")
+                    help="run only this op (or 'step': the whole step with its ops queued in turn; "
+                         "'step-scheduled': the whole step in the --schedule order; 'copy': a 1 GiB device "
+                         "copy) --steps times after set-up, untimed (for rocprofv3)")
     return ap.parse_args()
 
 
@@ -305,22 +307,25 @@ class Workload:
         schedule "serial" queues every op on the current stream in turn; the
         others run the H-Net layer on a stream of its own, forked from the
         current stream at the start of the step ("with_dr") or once Delta R is
-        queued, beside Top-K, gather and upsample ("after_dr"), and joined back
-        before the step ends.  dom: a pair of events recorded around the coding
+        queued, beside Top-K, gather and upsample ("after_dr"), or its routing
+        and compaction beside Delta R and its dechunks after it
+        ("routes_with_dr"), and joined back before the step ends.  dom: a pair of events recorded around the coding
         rate on the current stream."""
         torch = self.torch
         cur = torch.cuda.current_stream()
 
-        def fork_hnet():
+        def fork_hnet(part=slice(None)):
             self.h_fork.record(cur)
             self.h_stream.wait_event(self.h_fork)
             with torch.cuda.stream(self.h_stream):
-                for _, f in self.hnet_ops():
+                for _, f in self.hnet_ops()[part]:
                     f()
                 self.h_join.record(self.h_stream)
 
         if schedule == "with_dr":
             fork_hnet()
+        elif schedule == "routes_with_dr":
+            fork_hnet(slice(0, 2))  # both stages' routing and compaction
         for name, f in (self.ops() if schedule == "serial" else self.byteflow_ops()):
             if dom is not None and name == "coding_rate":
                 dom[0].record(cur)
@@ -330,6 +335,8 @@ class Workload:
                 f()
             if name == "coding_rate" and schedule == "after_dr":
                 fork_hnet()
+            elif name == "coding_rate" and schedule == "routes_with_dr":
+                fork_hnet(slice(2, 4))  # the two dechunks, after the routing on the same stream
         if schedule != "serial":
             cur.wait_event(self.h_join)
 
@@ -501,6 +508,8 @@ def op_ideal_ms(name, a):
 
 
 SCHEDULES = {"after_dr": "H-Net layer on a stream of its own beside Top-K, gather and upsample",
+             "routes_with_dr": "H-Net routing and compaction (both stages) on a stream of its own beside Delta R, "
+                               "its two dechunks on that stream beside Top-K, gather and upsample",
              "with_dr": "H-Net layer on a stream of its own beside Delta R",
              "serial": "every op on one stream in turn"}
 
@@ -667,8 +676,12 @@ def main():
     if args.profile_op:
         # the whole step with its ops queued in turn, so that each kernel's time
         # under the profiler is its own and not shared with the H-Net stream
-        f = (lambda: wl.step(schedule="serial")) if args.profile_op == "step" else \
-            dict(wl.ops() + wl.next_ops())[args.profile_op]
+        if args.profile_op == "step":
+            f = lambda: wl.step(schedule="serial")
+        elif args.profile_op == "step-scheduled":
+            f = lambda: wl.step(schedule=args.schedule)  # the overlap of the two streams as timed
+        else:
+            f = dict(wl.ops() + wl.next_ops())[args.profile_op]
         for _ in range(args.steps):
             f()
         torch.cuda.synchronize()

@@ -240,9 +240,38 @@ def step_kernels(a):
     print("\n".join(lines))
 
 
+def step_timeline(a):
+    """Start and end of every kernel of the last traced step, per HIP queue
+    (stream), relative to the step's first kernel: how the streams of a
+    scheduled step overlap.  The step starts at its first Gram-prefix kernel."""
+    rows = list(csv.DictReader(open(_one(a.trace, "*kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    heads = [i for i, r in enumerate(rows) if _short(r["Kernel_Name"]).startswith("cr_gram_prefix")]
+    if len(heads) < 2:
+        raise ValueError(f"no whole step in {a.trace}")
+    step = rows[heads[-2]:]  # the coding rate's two halves open the last step
+    t0 = int(step[0]["Start_Timestamp"])
+    end = max(int(r["End_Timestamp"]) for r in step)
+    lines = [f"# rocprofv3 summary: {a.workload}", "", "Commands (run from the repository root on the GPU host):",
+             "", "```", a.cmd, "```", "",
+             f"The last traced step: {len(step)} kernels over {(end - t0) / 1e3:.1f} us (kernel trace, so each "
+             "kernel's span includes any time it shared the GPU with the other streams).  Times in us from the "
+             "step's first kernel; queue = the HIP queue (stream) it ran on.", "",
+             "| start | end | us | queue | kernel |", "|---|---|---|---|---|"]
+    for r in step:
+        s0 = (int(r["Start_Timestamp"]) - t0) / 1e3
+        s1 = (int(r["End_Timestamp"]) - t0) / 1e3
+        lines.append(f"| {s0:.1f} | {s1:.1f} | {s1 - s0:.1f} | {r['Queue_Id']} | {_short(r['Kernel_Name'])} |")
+    lines.append("")
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--op", required=True, choices=sorted(OPS) + ["step", "step-kernels"])
+    ap.add_argument("--op", required=True, choices=sorted(OPS) + ["step", "step-kernels", "step-timeline"])
     ap.add_argument("--mfma", help="--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 ... run")
     ap.add_argument("--trace-steps", type=int, default=3, help="steps in the kernel-trace run (step-kernels)")
     ap.add_argument("--step-kernels", type=int, default=STEP_KERNELS, help="dispatches per step (step-kernels)")
@@ -260,6 +289,9 @@ def main():
     ap.add_argument("--workload", required=True)
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.op == "step-timeline":
+        step_timeline(a)
+        return
     if a.op == "step-kernels":
         step_kernels(a)
         return
