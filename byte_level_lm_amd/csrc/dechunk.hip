@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kCarryThreads) void ema_tile_carry(const float* __r
   __shared__ float4 shU[kCarryThreads / kWave][kCarryCols];
   const int tid = threadIdx.x;
   const int col = tid & (kCarryCols - 1);
-  const int g = tid >> 3;
+  const int g = tid / kCarryCols;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   const int f = blockIdx.x * (kCarryCols * 4) + col * 4;
