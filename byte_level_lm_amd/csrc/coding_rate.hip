@@ -600,7 +600,10 @@ __device__ __forceinline__ void factor64(const float* __restrict__ D, int ldd, f
 constexpr int kChunk = 16;                      // columns per staged strip chunk
 constexpr int kWaitVmcnt0 = 0x0F70;             // s_waitcnt vmcnt(0), other counters unconstrained
 constexpr int kSRow = 56;                       // LDS row of a strip chunk: 3 x 16 bf16 parts + 8 pad
-constexpr int kPassTiles = 2;                   // tiles below the diagonal per pass
+#ifndef BLLM_CR_PASS_TILES
+#define BLLM_CR_PASS_TILES 2
+#endif
+constexpr int kPassTiles = BLLM_CR_PASS_TILES;  // tiles below the diagonal per pass
 constexpr int kSlots = kPassTiles / 2;          // pass tiles per wave
 constexpr int kStripRows = 64 * (kPassTiles + 1);
 constexpr int kXP = 68;                         // LDS row pitch of 64x64 tiles
@@ -610,7 +613,9 @@ constexpr int kPanelFloats = kStripFloats + 64 * kXP;
 static_assert(64 * kXP <= kStripFloats, "X staging must fit in the strip buffers");
 static_assert(64 * kXP + kFactorLds <= kPanelFloats, "D tile and factor scratch must fit");
 static_assert((NB / kChunk) % 2 == 0, "the strip loop takes chunks in pairs");
-static_assert(kPassTiles == 2, "the strip loader below issues kPassTiles + 1 = 3 loads per set");
+static_assert(kPassTiles % 2 == 0, "two waves share each pass tile");
+constexpr int kStripLoads = kPassTiles + 1;     // strip rows per thread per chunk (64 rows each)
+constexpr int kPanelWaves = kPassTiles == 2 ? 3 : 2;  // workgroups per CU the registers allow
 
 // Strip products on bf16 MFMA: an fp32 value x is the exact sum of three
 // bf16 parts, x = hi + mid + lo (hi = x with its low 16 bits cleared, mid the
@@ -765,7 +770,7 @@ __global__ __launch_bounds__(64) void cr_diag(float* __restrict__ ws, float* __r
 }
 
 template <int DT>
-__global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
+__global__ __launch_bounds__(256, kPanelWaves) void cr_panel(const void* __restrict__ h, float* __restrict__ ws,
                                                    float* __restrict__ linv, float* __restrict__ dR,
                                                    int32_t* __restrict__ status, CRGeom g,
                                                    float salpha, int k, int pp) {
@@ -847,29 +852,31 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
     // counts static.
     const int nrows = NB * (npt + 1);
     const int lr = tid >> 2, lc = (tid & 3) * 4;
-    int go[3];
+    int go[kStripLoads];
 #pragma unroll
-    for (int it = 0; it < 3; ++it) {
+    for (int it = 0; it < kStripLoads; ++it) {
       const int r = lr + 64 * it;
       const int grow = r < NB ? NB * k + r : (r < nrows ? NB * (k + 1 + t0) + (r - NB) : NB * k + (r & 63));
       go[it] = mx_off(g, grow, lc);
     }
-    float4 qa0, qa1, qa2, qb0, qb1, qb2;
+    float4 qa[kStripLoads], qb[kStripLoads];
     // chunk ch of a strip row is the row's piece of the ch-th 64 x 16 tile
     auto ldq = [&](int it, int ch) { return *reinterpret_cast<const float4*>(Mx + go[it] + ch * 1024); };
     auto fetch_a = [&](int ch) {
-      qa0 = ldq(0, ch); qa1 = ldq(1, ch); qa2 = ldq(2, ch);
+#pragma unroll
+      for (int it = 0; it < kStripLoads; ++it) qa[it] = ldq(it, ch);
     };
     auto fetch_b = [&](int ch) {
-      qb0 = ldq(0, ch); qb1 = ldq(1, ch); qb2 = ldq(2, ch);
+#pragma unroll
+      for (int it = 0; it < kStripLoads; ++it) qb[it] = ldq(it, ch);
     };
     // the panel rows (rows 0..63 of the stage) are stored with the sign their
     // products take in this chunk: negated unless an S panel meets A columns
-    auto stash = [&](uint16_t* sb, int ch, const float4& v0, const float4& v1, const float4& v2) {
+    auto stash = [&](uint16_t* sb, int ch, const float4 (&v)[kStripLoads]) {
       const uint32_t sg = (panelS && ch * kChunk < g.dp) ? 0u : 0x80008000u;
-      stash_split(sb + lr * kSRow + lc, v0, sg);
-      stash_split(sb + (lr + 64) * kSRow + lc, v1);
-      stash_split(sb + (lr + 128) * kSRow + lc, v2);
+      stash_split(sb + lr * kSRow + lc, v[0], sg);
+#pragma unroll
+      for (int it = 1; it < kStripLoads; ++it) stash_split(sb + (lr + 64 * it) * kSRow + lc, v[it]);
     };
     auto compute = [&](const uint16_t* sb, int ch) {
       const bool chA = ch * kChunk < g.dp;
@@ -921,14 +928,14 @@ __global__ __launch_bounds__(256, 3) void cr_panel(const void* __restrict__ h, f
     // flight across them)
     for (int ch = 0; ch < nch; ch += 2) {
       lds_barrier();
-      stash(sst, ch, qa0, qa1, qa2);
+      stash(sst, ch, qa);
       lds_barrier();
       fetch_a(ch + 2);
       compute(sst, ch);
       // nch is even (64 k / 16): no test here, so that the wait counts at
       // both stashes leave the other set's prefetches in flight
       lds_barrier();
-      stash(sst, ch + 1, qb0, qb1, qb2);
+      stash(sst, ch + 1, qb);
       lds_barrier();
       fetch_b(ch + 3);
       compute(sst, ch + 1);
