@@ -134,11 +134,7 @@ class Workload:
         self.h_fork, self.h_join = torch.cuda.Event(), torch.cuda.Event()
         self.ws_cr = torch.empty(B.coding_rate_workspace(self.nseq, T, 512), dtype=torch.uint8, device=dev)
         self.idx4 = torch.empty((self.nseq, self.K), dtype=torch.int32, device=dev)
-        self.mask4 = torch.empty((self.nseq, T), dtype=torch.uint8, device=dev)
-        self.gidx4 = torch.empty(self.nseq * self.K, dtype=torch.int32, device=dev)
-        self.coff4 = torch.empty(self.nseq + 1, dtype=torch.int64, device=dev)
         self.z4 = torch.empty((self.nseq * self.K, 512), dtype=bf, device=dev)
-        self.ws_compact4 = torch.empty(B.compact_workspace(self.N), dtype=torch.uint8, device=dev)
         self.W = torch.from_numpy(bfl["w_bin"]).to(dev, bf)
         self.s4 = torch.empty_like(self.h4)
         self.ws_up = torch.empty(B.upsample_workspace(self.nseq, T, self.K, 1536, 512, self.nbins),
@@ -225,12 +221,10 @@ class Workload:
                                  status=self.st, ws=self.ws_cr)
 
     def _topk(self):
-        self.B.topk_select(self.dR, self.K, idx_out=self.idx4, mask_out=self.mask4, status=self.st)
+        self.B.topk_select(self.dR, self.K, idx_out=self.idx4, status=self.st, want_mask=False)
 
     def _gather(self):
-        self.B.compact(self.mask4.view(-1), self.off4, rows=self.h4.view(-1, 512), capacity=self.nseq * self.K,
-                       idx_out=self.gidx4, chunk_offsets_out=self.coff4, rows_out=self.z4, status=self.st,
-                       ws=self.ws_compact4)
+        self.B.gather_topk(self.h4, self.idx4, z_out=self.z4.view(self.nseq, self.K, 512))
 
     def _upsample(self):
         self.B.upsample_bins(self.g4, self.W, self.idx4, self.h4, self.nbins, s_out=self.s4, ws=self.ws_up)
@@ -359,8 +353,8 @@ class Workload:
             "dechunk stage1": dict(bytes=M1 * (512 * e + 8) + N * 512 * e),
             "coding_rate": dict(flops=3 * T * 512 * 512 * nseq, bytes=N * 512 * e + N * 4,
                                 peak_tflops=FP32_MFMA_PEAK_TFLOPS),
-            "topk_select": dict(bytes=N * 4 + N + nseq * K * 4),
-            "gather": dict(bytes=N + nseq * K * (4 + 2 * 512 * e)),
+            "topk_select": dict(bytes=N * 4 + nseq * K * 4),
+            "gather": dict(bytes=nseq * K * (4 + 2 * 512 * e)),
             "upsample_bins": dict(flops=2 * 1536 * 512 * items, bytes=2 * N * 512 * e + nseq * K * 1536 * e),
         }
 

@@ -16,6 +16,8 @@
 // time order.  Up to kLdsKeys positions the keys are kept in LDS; longer
 // sequences (up to 64 positions per thread) recompute them from the scores,
 // which stay in L2, in every pass.
+#include <algorithm>
+
 #include "common.h"
 
 namespace bllm {
@@ -160,6 +162,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
 }
 
+// z = the hidden states at the selected positions, per sequence in time
+// order (the paper page's stage 2 gather, before the global model): one
+// group of G lanes per output row, 16-byte copies, grid-stride over rows.
+// An index outside [0, T) is clamped into it, so no read leaves h.
+__global__ __launch_bounds__(256) void gather_topk_kernel(const uint8_t* __restrict__ h, int64_t T, int64_t K,
+                                                          int64_t nrows, int row_bytes, int gshift,
+                                                          const int32_t* __restrict__ idx,
+                                                          uint8_t* __restrict__ z) {
+  const int G = 1 << gshift;
+  const int g = threadIdx.x & (G - 1);
+  const int64_t groups = static_cast<int64_t>(gridDim.x) * (blockDim.x >> gshift);
+  const int nvec = row_bytes / 16;
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> gshift) + (threadIdx.x >> gshift); r < nrows;
+       r += groups) {
+    const int64_t t = min(max(static_cast<int64_t>(idx[r]), int64_t(0)), T - 1);
+    const int64_t src = (r / K) * T + t;
+    const uint4* sp = reinterpret_cast<const uint4*>(h + src * row_bytes);
+    uint4* o = reinterpret_cast<uint4*>(z + r * row_bytes);
+    for (int v = g; v < nvec; v += G) o[v] = sp[v];
+  }
+}
+
 }  // namespace
 }  // namespace bllm
 
@@ -189,4 +213,24 @@ extern "C" int bllm_topk_select(const float* score, int64_t nseq, int64_t T, int
 extern "C" int bllm_topk_select_window(const float* score, int64_t nseq, int64_t W, int64_t K, int first,
                                        int32_t* idx_out, uint8_t* mask_out, int32_t* status, void* stream) {
   return topk_entry(score, nseq, W, K, first ? 1 : 0, idx_out, mask_out, status, stream);
+}
+
+extern "C" int bllm_gather_topk(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d, int64_t K,
+                                const int32_t* idx, void* z_out, void* stream) {
+  if (!h || !idx || !z_out || nseq < 1 || T < 1 || d < 1 || K < 1 || K > T) return BLLM_E_INVAL;
+  if (!valid_dtype(dtype)) return BLLM_E_NOTSUP;
+  const int64_t row_bytes = d * elem_size(dtype);
+  if (row_bytes % 16 != 0 || row_bytes > (int64_t(1) << 20) || !aligned16(h) || !aligned16(z_out))
+    return BLLM_E_NOTSUP;
+  if (nseq * T >= (int64_t(1) << 31)) return BLLM_E_NOTSUP;
+  const int nvec = static_cast<int>(row_bytes / 16);
+  int gshift = 0;
+  while ((1 << gshift) < nvec && gshift < 6) ++gshift;
+  const int64_t nrows = nseq * K;
+  const int rows_per_block = 256 >> gshift;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(ceil_div(nrows, rows_per_block), 16384));
+  hipLaunchKernelGGL(gather_topk_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(h), T, K, nrows, static_cast<int>(row_bytes), gshift, idx,
+                     static_cast<uint8_t*>(z_out));
+  return launch_status();
 }

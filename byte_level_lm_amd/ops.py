@@ -294,6 +294,20 @@ def topk_select(score, K: int, *, idx_out=None, mask_out=None, status=None, want
     return idx_out, mask_out, status
 
 
+def gather_topk(h, idx, *, z_out=None):
+    """z [nseq, K, d] = the rows of h [nseq, T, d] at the positions idx [nseq, K] (int32)."""
+    _dev(h, idx)
+    nseq, T, d = h.shape
+    K = idx.shape[1]
+    if idx.dtype != torch.int32 or idx.shape[0] != nseq:
+        raise ValueError("idx must be int32 [nseq, K]")
+    z_out = torch.empty((nseq, K, d), dtype=h.dtype, device=h.device) if z_out is None else z_out
+    rc = L.lib().bllm_gather_topk(h.data_ptr(), _dt(h), nseq, T, d, K, idx.data_ptr(), z_out.data_ptr(),
+                                  _stream())
+    L.check("bllm_gather_topk", rc)
+    return z_out
+
+
 def topk_select_window(score, K: int, first: bool, *, idx_out=None, mask_out=None, status=None, want_mask=True):
     """Local Top-K of one window [nseq, W] of a stream: the first window as
     ``topk_select`` (BOS + K-1), later windows their K largest scores."""

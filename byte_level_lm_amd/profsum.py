@@ -130,9 +130,9 @@ STEP_OPS = (("route_kernel", ("route+compact stage1", "route+compact stage2")),
             ("ema_tile_aggregate", ("dechunk stage2", "dechunk stage1")),
             ("cr_gram_prefix", ("coding_rate",)),
             ("topk_kernel", ("topk_select",)),
-            ("compact_count", ("gather",)),
+            ("gather_topk", ("gather",)),
             ("up_count", ("upsample_bins",)))
-STEP_KERNELS = 50  # dispatches of one step (coding rate at d 512 in two halves: 2 x (gram + 1 diag + 11 panel))
+STEP_KERNELS = 48  # dispatches of one step (coding rate at d 512 in two halves: 2 x (gram + 1 diag + 11 panel))
 MOPS_FLOPS = 512   # SQ_INSTS_VALU_MFMA_MOPS_* count MFMA work in units of 512 flops
 
 
@@ -147,8 +147,7 @@ def _label_step(names):
     labels, seen, cur = [], {}, None
     for n in names:
         for head, ops in STEP_OPS:
-            # compact_count opens the gather only after the Top-K kernel
-            if n.startswith(head) and (head != "compact_count" or cur == "topk_select"):
+            if n.startswith(head):
                 i = seen.get(head, 0)
                 cur = ops[min(i, len(ops) - 1)]
                 seen[head] = i + 1

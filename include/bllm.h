@@ -306,6 +306,25 @@ int bllm_topk_select_window(const float* score, int64_t nseq, int64_t W, int64_t
                             int32_t* idx_out, uint8_t* mask_out, int32_t* status, void* stream);
 
 /*
+ * bllm_gather_topk -- the chunk inputs z = [h_{s_1}, ..., h_{s_K}] of every
+ * sequence ([BF4] stage 2: the hidden states at the selected positions, in
+ * time order, before the global model), straight from the Top-K positions.
+ * h     : [nseq x T x d] rows of dtype (device).
+ * idx   : int32 [nseq x K] positions inside each sequence (device), e.g. the
+ *         idx_out of bllm_topk_select; an index outside [0, T) is clamped
+ *         into it (the library never reads outside h).
+ * z_out : [nseq x K x d] of dtype (device, caller-owned); row s*K + i is
+ *         h[s, idx[s*K + i]].
+ * The same rows as bllm_compact on the Top-K mask gives, without the mask's
+ * count and prefix passes.
+ * Errors : BLLM_E_INVAL for null pointers, nseq < 1, T < 1, d < 1, K < 1 or
+ *          K > T; BLLM_E_NOTSUP for a bad dtype, rows not a multiple of 16
+ *          bytes (or over 1 MB), unaligned h/z_out or nseq * T >= 2^31.
+ */
+int bllm_gather_topk(const void* h, int dtype, int64_t nseq, int64_t T, int64_t d, int64_t K,
+                     const int32_t* idx, void* z_out, void* stream);
+
+/*
  * bllm_upsample_bins -- multi-linear reconstruction with the large residual
  * ([BF4] stage 4, [BF2] key design 4):
  *   c(t)   = last i with idx[i] <= t,  L_c = idx[c+1] - idx[c] (idx[K] = T)
@@ -316,7 +335,8 @@ int bllm_topk_select_window(const float* score, int64_t nseq, int64_t W, int64_t
  * dtype must be BLLM_BF16 (bf16 MFMA, fp32 accumulate).
  * Limits: nbins <= 64, d_global % 8 == 0, d_local % 8 == 0, nseq * T < 2^31.
  * ws : bllm_upsample_workspace(nseq, T, K, d_global, d_local, nbins) bytes
- *      (bin-bucketed work items and a transposed copy of W).
+ *      (per-block counts, bin offsets and the bin-bucketed work items; W is
+ *      read as stored).
  */
 size_t bllm_upsample_workspace(int64_t nseq, int64_t T, int64_t K, int64_t d_global,
                                int64_t d_local, int64_t nbins);

@@ -505,6 +505,41 @@ def test_gather_via_compact_on_topk_mask(ops):
     assert np.array_equal(to_np(z)[:nseq * K], oracle.gather(h, to_np(idx)).reshape(-1, d))
 
 
+@pytest.mark.parametrize("dt,nseq,T,d,K", [("bf16", 3, 1000, 64, 100), ("f32", 2, 777, 8, 1), ("bf16", 2, 300, 512, 300),
+                                          ("f32", 5, 4096, 200, 1025), ("bf16", 1, 4096, 4096, 33)])
+def test_gather_topk_bitexact(ops, dt, nseq, T, d, K):
+    """z = h at the Top-K positions, row for row, against the oracle's gather
+    (K = 1, K = T, rows of 16 bytes to 8 KB); the same rows as the
+    compaction on the Top-K mask."""
+    torch = _torch()
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    rng = np.random.default_rng(nseq * 1000 + K)
+    h = rng.standard_normal((nseq, T, d)).astype(np.float32)
+    if dt == "bf16":
+        h = bf16_round(h)
+    sc = rng.standard_normal((nseq, T)).astype(np.float32)
+    idx, mask, _ = ops.topk_select(to_dev(sc), K)
+    hd = to_dev(h, tdt)
+    z = ops.gather_topk(hd, idx)
+    want = oracle.gather(h, to_np(idx))
+    assert np.array_equal(to_np(z.float()), want.astype(np.float32))
+    if nseq * T <= 20000:
+        off = np.arange(nseq + 1, dtype=np.int64) * T
+        _, _, zc, _, _ = ops.compact(mask.reshape(-1), to_dev(off), rows=hd.view(-1, d))
+        assert torch.equal(zc[:nseq * K].view(nseq, K, d), z)
+
+
+def test_gather_topk_clamps_indices(ops):
+    """Positions outside [0, T) read the nearest row of the sequence; the
+    library never reads outside h."""
+    torch = _torch()
+    h = np.arange(2 * 10 * 4, dtype=np.float32).reshape(2, 10, 4)
+    idx = np.array([[-5, 0, 9, 10], [3, 12, -1, 7]], np.int32)
+    z = ops.gather_topk(to_dev(h), to_dev(idx))
+    want = oracle.gather(h, np.clip(idx, 0, 9))
+    assert np.array_equal(to_np(z), want)
+
+
 def _random_idx(rng, nseq, T, K):
     return np.stack([np.sort(np.concatenate([[0], rng.choice(np.arange(1, T), K - 1, replace=False)]))
                      for _ in range(nseq)]).astype(np.int32)
