@@ -41,6 +41,7 @@ __device__ inline int crow_of(int r, int lane) { return 8 * (r >> 2) + 4 * (lane
 
 struct UpGeom {
   int nseq, T, K, dg, dl, nbins, nblk;
+  int cap;  // item slots of the workspace
 };
 
 // first position offset of bin b in a chunk of length L: ceil(b L / B);
@@ -51,10 +52,16 @@ __device__ inline int bin_lo(int b, int L, int B) {
   return (b * L + B - 1) / B;
 }
 
-__device__ inline int chunk_len(const int32_t* idx, const UpGeom& g, int64_t cg) {
+// first position of chunk cg inside its sequence and its length.  With the
+// positions ascending from 0 (as Top-K gives them) this is idx[cg] and
+// idx[cg + 1] - idx[cg]; any other input is clamped into [0, T) and an empty
+// or reversed chunk has length 0, so every position written lies inside its
+// sequence.
+__device__ inline int chunk_span(const int32_t* idx, const UpGeom& g, int64_t cg, int& start) {
   const int i = static_cast<int>(cg % g.K);
-  const int nxt = i + 1 < g.K ? idx[cg + 1] : g.T;
-  return nxt - idx[cg];
+  start = min(max(idx[cg], 0), g.T);
+  const int nxt = i + 1 < g.K ? min(max(idx[cg + 1], 0), g.T) : g.T;
+  return max(nxt - start, 0);
 }
 
 // items of bin b of a chunk of length L: its run split into pieces of at most kMaxRun
@@ -83,7 +90,8 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_count(const int32_t* __res
   const int64_t cg = static_cast<int64_t>(blockIdx.x) * kChunksPerBlock + threadIdx.x;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool valid = cg < static_cast<int64_t>(g.nseq) * g.K;
-  const int L = valid ? chunk_len(idx, g, cg) : 0;
+  int start = 0;
+  const int L = valid ? chunk_span(idx, g, cg, start) : 0;
   for (int b = 0; b < g.nbins; ++b) {
     const int n = wave_sum_i(valid ? bin_pieces<BC>(b, L, g.nbins) : 0);
     if (lane == 0) wc[w][b] = n;
@@ -106,41 +114,53 @@ __global__ __launch_bounds__(kScanThreads) void up_scan(UpGeom g, int32_t* __res
                                                         int32_t* __restrict__ bin_off,
                                                         int32_t* __restrict__ bin_cnt,
                                                         int32_t* __restrict__ tile_off) {
-  __shared__ int sTot[64], sOff[64];
+  // totals and offsets in 64 bits: with positions that are not ascending,
+  // chunks overlap and their items can outgrow the workspace (g.cap slots);
+  // the bins are then cut at g.cap and the items past it are not written
+  __shared__ int64_t sTot[64], sOff[64];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   constexpr int nw = kScanThreads / 64;
   for (int b = w; b < g.nbins; b += nw) {
-    int tot = 0;
+    int64_t tot = 0;
     for (int k0 = 0; k0 < g.nblk; k0 += 64) {
       const int k = k0 + lane;
-      tot += wave_sum_i(k < g.nblk ? counts[static_cast<int64_t>(k) * g.nbins + b] : 0);
+      tot += k < g.nblk ? counts[static_cast<int64_t>(k) * g.nbins + b] : 0;
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o, 64);
     if (lane == 0) sTot[b] = tot;
   }
   __syncthreads();
   if (w == 0) {
-    const int tb = lane < g.nbins ? sTot[lane] : 0;
-    const int off = wave_excl_i(tb);
-    const int tc = (tb + kBM - 1) / kBM;
+    const int64_t tb = lane < g.nbins ? sTot[lane] : 0;
+    int64_t off = tb;  // inclusive scan over the bins, then exclusive
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(off, o, 64);
+      if (lane >= o) off += y;
+    }
+    off -= tb;
+    const int cnt = static_cast<int>(min(max(static_cast<int64_t>(g.cap) - off, int64_t(0)), tb));
+    const int tc = (cnt + kBM - 1) / kBM;
     const int toff = wave_excl_i(tc);
     if (lane < g.nbins) {
       sOff[lane] = off;
-      bin_off[lane] = off;
-      bin_cnt[lane] = tb;
+      bin_off[lane] = static_cast<int>(min(off, static_cast<int64_t>(g.cap)));
+      bin_cnt[lane] = cnt;
       tile_off[lane] = toff;
     }
     if (lane == g.nbins - 1) tile_off[g.nbins] = toff + tc;
   }
   __syncthreads();
   for (int b = w; b < g.nbins; b += nw) {
-    int run = sOff[b];
+    int64_t run = sOff[b];
     for (int k0 = 0; k0 < g.nblk; k0 += 64) {
       const int k = k0 + lane;
       int32_t* cp = counts + static_cast<int64_t>(k < g.nblk ? k : 0) * g.nbins + b;
       const int v = k < g.nblk ? *cp : 0;
       int all;
-      const int x = wave_incl_scan(v, all);
-      if (k < g.nblk) *cp = run + x - v;
+      const int x = wave_incl_scan(v, all);  // at most 64 blocks of 256 chunks of 2^20 positions: fits
+      if (k < g.nblk) *cp = static_cast<int>(min(run + x - v, static_cast<int64_t>(g.cap)));
       run += all;
     }
   }
@@ -159,13 +179,14 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_items(const int32_t* __res
   if (tid < g.nbins) sBase[tid] = base[static_cast<int64_t>(blockIdx.x) * g.nbins + tid];
   const int64_t cg = static_cast<int64_t>(blockIdx.x) * kChunksPerBlock + tid;
   const bool valid = cg < static_cast<int64_t>(g.nseq) * g.K;
-  const int L = valid ? chunk_len(idx, g, cg) : 0;
+  int start = 0;
+  const int L = valid ? chunk_span(idx, g, cg, start) : 0;
   for (int b = 0; b < g.nbins; ++b) {
     const int n = wave_sum_i(valid ? bin_pieces<BC>(b, L, g.nbins) : 0);
     if (lane == 0) wc[w][b] = n;
   }
   __syncthreads();
-  const int64_t row0 = valid ? (cg / g.K) * g.T + idx[cg] : 0;
+  const int64_t row0 = valid ? (cg / g.K) * g.T + start : 0;
   for (int b = 0; b < g.nbins; ++b) {
     const int np = valid ? bin_pieces<BC>(b, L, g.nbins) : 0;
     int slot = sBase[b] + wave_excl_i(np);
@@ -173,7 +194,10 @@ __global__ __launch_bounds__(kChunksPerBlock) void up_items(const int32_t* __res
     const int lo = bin_lo<BC>(b, L, g.nbins), hi = bin_lo<BC>(b + 1, L, g.nbins);
     for (int e = 0; e < np; ++e) {
       const int a = lo + e * kMaxRun;
-      items[slot + e] = make_int4(static_cast<int>(cg), static_cast<int>(row0 + a), min(kMaxRun, hi - a), 0);
+      // only chunks that overlap (positions not ascending) can need more
+      // slots than the workspace holds; their extra items are dropped
+      if (slot + e < g.cap)
+        items[slot + e] = make_int4(static_cast<int>(cg), static_cast<int>(row0 + a), min(kMaxRun, hi - a), 0);
     }
   }
 }
@@ -446,7 +470,7 @@ extern "C" size_t bllm_upsample_workspace(int64_t nseq, int64_t T, int64_t K, in
   if (nseq < 1 || T < 1 || K < 1 || nbins < 1 || d_global < 1 || d_local < 1) return 0;
   UpGeom g{static_cast<int>(nseq), static_cast<int>(T), static_cast<int>(K), static_cast<int>(d_global),
            static_cast<int>(d_local), static_cast<int>(nbins),
-           static_cast<int>(ceil_div(nseq * K, kChunksPerBlock))};
+           static_cast<int>(ceil_div(nseq * K, kChunksPerBlock)), 0};
   return up_ws_bytes(g);
 }
 
@@ -459,11 +483,13 @@ extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* 
     return BLLM_E_INVAL;
   if (dtype != BLLM_BF16) return BLLM_E_NOTSUP;
   if (nbins > 64 || d_global % 8 != 0 || d_local % 8 != 0 || nseq * T >= (int64_t(1) << 31) ||
-      !aligned16(gm) || !aligned16(W) || !aligned16(h) || !aligned16(s_out))
+      T > (int64_t(1) << 20) || !aligned16(gm) || !aligned16(W) || !aligned16(h) || !aligned16(s_out))
     return BLLM_E_NOTSUP;
   UpGeom g{static_cast<int>(nseq), static_cast<int>(T), static_cast<int>(K), static_cast<int>(d_global),
            static_cast<int>(d_local), static_cast<int>(nbins),
-           static_cast<int>(ceil_div(nseq * K, kChunksPerBlock))};
+           static_cast<int>(ceil_div(nseq * K, kChunksPerBlock)), 0};
+  if (up_max_items(g) > static_cast<size_t>(INT32_MAX)) return BLLM_E_NOTSUP;
+  g.cap = static_cast<int>(up_max_items(g));
   if (!ws || ws_bytes < up_ws_bytes(g) || !aligned16(ws)) return BLLM_E_WS;
   hipStream_t st = static_cast<hipStream_t>(stream);
   UpWs u = up_carve(ws, g);

@@ -331,9 +331,14 @@ int bllm_gather_topk(const void* h, int dtype, int64_t nseq, int64_t T, int64_t 
  *   bin(t) = floor(nbins * (t - idx[c]) / L_c)          (relative position in chunk)
  *   s_t    = h_t + g_{c(t)} W_{bin(t)}                  (row vectors)
  * g : [nseq x K x d_global], W : [nbins x d_global x d_local],
- * idx : int32 [nseq x K] (ascending, idx[s*K] = 0), h, s_out : [nseq x T x d_local].
+ * idx : int32 [nseq x K] (ascending, idx[s*K] = 0, as bllm_topk_select gives
+ *       them), h, s_out : [nseq x T x d_local].  Other idx are clamped into
+ *       [0, T); then positions no chunk covers keep their contents and
+ *       overlapping chunks give unspecified rows, but no access leaves the
+ *       arguments or the workspace.
  * dtype must be BLLM_BF16 (bf16 MFMA, fp32 accumulate).
- * Limits: nbins <= 64, d_global % 8 == 0, d_local % 8 == 0, nseq * T < 2^31.
+ * Limits: nbins <= 64, d_global % 8 == 0, d_local % 8 == 0, nseq * T < 2^31,
+ *         T <= 2^20 (else BLLM_E_NOTSUP).
  * ws : bllm_upsample_workspace(nseq, T, K, d_global, d_local, nbins) bytes
  *      (per-block counts, bin offsets and the bin-bucketed work items; W is
  *      read as stored).

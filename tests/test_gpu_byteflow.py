@@ -545,6 +545,33 @@ def _random_idx(rng, nseq, T, K):
                      for _ in range(nseq)]).astype(np.int32)
 
 
+def test_upsample_positions_not_ascending_stay_in_bounds(ops):
+    """Positions that are not ascending or fall outside [0, T) (here chunks
+    that overlap, so their items outgrow the workspace's slots, and values
+    far outside the sequence) are clamped: the call succeeds and writes
+    nothing outside s_out (guard rows on both sides keep their contents)."""
+    torch = _torch()
+    rng = np.random.default_rng(5)
+    nseq, T, K, dg, dl, B = 5, 500, 400, 64, 32, 16
+    idx = _random_idx(rng, nseq, T, K)
+    idx[1] = np.where(np.arange(K) % 2 == 0, 0, T)  # [0, T, 0, T, ...]: 200 chunks of length T
+    idx[2] = idx[1]
+    idx[3] = np.where(np.arange(K) % 2 == 0, -50, T + 50)
+    idx[1, 7], idx[1, 9] = -7, 10 ** 6
+    idx[4] = rng.integers(-100, T + 100, K)
+    bf = torch.bfloat16
+    g = to_dev(bf16_round(rng.standard_normal((nseq, K, dg))), bf)
+    W = to_dev(bf16_round(rng.standard_normal((B, dg, dl)) / np.sqrt(dg)), bf)
+    h = to_dev(bf16_round(rng.standard_normal((nseq, T, dl))), bf)
+    G = 4096  # guard elements on each side (a multiple of 8: s_out stays 16-byte aligned)
+    n = nseq * T * dl
+    big = torch.full((n + 2 * G,), 7.0, dtype=bf, device="cuda")
+    s = big[G:G + n].view(nseq, T, dl)
+    ops.upsample_bins(g, W, to_dev(idx), h, B, s_out=s)
+    torch.cuda.synchronize()
+    assert bool((big[:G] == 7.0).all()) and bool((big[G + n:] == 7.0).all())
+
+
 @pytest.mark.parametrize("nseq,T,K,dg,dl,B", [(2, 300, 40, 64, 32, 16), (3, 1000, 37, 96, 136, 4),
                                               (1, 64, 64, 32, 8, 16), (2, 500, 1, 64, 64, 16),
                                               (4, 3000, 300, 200, 320, 16), (2, 2000, 20, 64, 64, 64)])
