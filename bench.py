@@ -38,11 +38,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--schedule", default="after_dr", choices=["after_dr", "routes_with_dr", "with_dr", "serial"],
+    ap.add_argument("--schedule", default="pipelined",
+                    choices=["pipelined", "after_dr", "routes_with_dr", "with_dr", "serial"],
                     help="where the H-Net layer runs in a step: on a stream of its own beside Top-K, gather "
-                         "and upsample (after_dr, the default) or beside Delta R (with_dr), its routing beside "
-                         "Delta R and its dechunks after it (routes_with_dr), or every op on one stream in turn "
-                         "(serial); the others are timed as well")
+                         "and upsample (after_dr), the same with that stream joined back only after the last "
+                         "step, so that it also runs beside the next step's Delta R (pipelined, the default), "
+                         "beside Delta R (with_dr), its routing beside Delta R and its dechunks after it "
+                         "(routes_with_dr), or every op on one stream in turn (serial); the others are timed "
+                         "as well")
     ap.add_argument("--profile-op", default=None,
                     help="run only this op (or 'step': the whole step with its ops queued in turn; "
                          "'step-scheduled': the whole step in the --schedule order; 'copy': a 1 GiB device "
@@ -294,7 +297,7 @@ class Workload:
     def byteflow_ops(self):
         return self.ops()[4:]
 
-    def step(self, dom=None, schedule="after_dr"):
+    def step(self, dom=None, schedule="after_dr", last=True):
         """One pass of the whole path.  The H-Net layer (stage 1 and 2 routing
         and compaction, both dechunks) and the ByteFlow chain (Delta R, Top-K,
         gather, upsample) take different inputs and share no buffer.
@@ -303,10 +306,18 @@ class Workload:
         current stream at the start of the step ("with_dr") or once Delta R is
         queued, beside Top-K, gather and upsample ("after_dr"), or its routing
         and compaction beside Delta R and its dechunks after it
-        ("routes_with_dr"), and joined back before the step ends.  dom: a pair of events recorded around the coding
-        rate on the current stream."""
+        ("routes_with_dr"), and joined back before the step ends.
+        "pipelined" is "after_dr" across steps: the H-Net stream is joined
+        back only after the last of a run of steps (last=True), so a step's
+        ByteFlow chain, from Delta R on, runs beside the previous step's
+        H-Net dechunks (the streams' own order keeps each layer's steps in
+        sequence; the two layers share no buffer).  dom: a pair of events
+        recorded around the coding rate on the current stream."""
         torch = self.torch
         cur = torch.cuda.current_stream()
+        join = last or schedule != "pipelined"
+        if schedule == "pipelined":
+            schedule = "after_dr"
 
         def fork_hnet(part=slice(None)):
             self.h_fork.record(cur)
@@ -331,7 +342,7 @@ class Workload:
                 fork_hnet()
             elif name == "coding_rate" and schedule == "routes_with_dr":
                 fork_hnet(slice(2, 4))  # the two dechunks, after the routing on the same stream
-        if schedule != "serial":
+        if schedule != "serial" and join:
             cur.wait_event(self.h_join)
 
     # ------------------------------------------------------------ algorithmic work
@@ -501,7 +512,9 @@ def op_ideal_ms(name, a):
     return max(t_hbm, t_mfma) * 1e3
 
 
-SCHEDULES = {"after_dr": "H-Net layer on a stream of its own beside Top-K, gather and upsample",
+SCHEDULES = {"pipelined": "H-Net layer on a stream of its own beside Top-K, gather and upsample and, across "
+                          "steps, beside the next step's Delta R (joined back after the last step)",
+             "after_dr": "H-Net layer on a stream of its own beside Top-K, gather and upsample",
              "routes_with_dr": "H-Net routing and compaction (both stages) on a stream of its own beside Delta R, "
                                "its two dechunks on that stream beside Top-K, gather and upsample",
              "with_dr": "H-Net layer on a stream of its own beside Delta R",
@@ -671,13 +684,14 @@ def main():
         # the whole step with its ops queued in turn, so that each kernel's time
         # under the profiler is its own and not shared with the H-Net stream
         if args.profile_op == "step":
-            f = lambda: wl.step(schedule="serial")
+            f = lambda last: wl.step(schedule="serial")
         elif args.profile_op == "step-scheduled":
-            f = lambda: wl.step(schedule=args.schedule)  # the overlap of the two streams as timed
+            f = lambda last: wl.step(schedule=args.schedule, last=last)  # the streams' overlap as timed
         else:
-            f = dict(wl.ops() + wl.next_ops())[args.profile_op]
-        for _ in range(args.steps):
-            f()
+            op = dict(wl.ops() + wl.next_ops())[args.profile_op]
+            f = lambda last: op()
+        for i in range(args.steps):
+            f(i == args.steps - 1)
         torch.cuda.synchronize()
         log("profiled", args.profile_op, args.steps, "launches")
         return
@@ -699,7 +713,7 @@ def main():
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record()
         for i in range(args.steps):
-            wl.step(dom=dom_ev[i], schedule=schedule)
+            wl.step(dom=dom_ev[i], schedule=schedule, last=i == args.steps - 1)
         ev1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -735,6 +749,10 @@ def main():
     }
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["op_ms"] = round(dom_ms, 4)
+    if "after_dr" in others:
+        # the same op's live time in the steps where it has the chip to itself
+        roof["op_ms_alone"] = round(others["after_dr"][1], 4)
+        roof["frac_alone"] = round(ideal_ms / others["after_dr"][1], 4)
     roof["ideal_ms"] = round(ideal_ms, 4)
     roof["fp32_only_frac"] = round(roof["achieved"] / FP32_MFMA_PEAK_TFLOPS, 4)
     hnet_ms = sum(per_op[n] for n in ("route+compact stage1", "route+compact stage2", "dechunk stage2", "dechunk stage1"))
