@@ -248,14 +248,16 @@ def step_timeline(a):
     heads = [i for i, r in enumerate(rows) if _short(r["Kernel_Name"]).startswith("cr_gram_prefix")]
     if len(heads) < 2:
         raise ValueError(f"no whole step in {a.trace}")
-    step = rows[heads[-2]:]  # the coding rate's two halves open the last step
-    t0 = int(step[0]["Start_Timestamp"])
+    t0 = int(rows[heads[-2]]["Start_Timestamp"])  # the coding rate's two halves open the last step
+    # with the steps overlapped, kernels of the step before may still run at its start
+    step = [r for r in rows[:heads[-2]] if int(r["End_Timestamp"]) > t0] + rows[heads[-2]:]
     end = max(int(r["End_Timestamp"]) for r in step)
     lines = [f"# rocprofv3 summary: {a.workload}", "", "Commands (run from the repository root on the GPU host):",
              "", "```", a.cmd, "```", "",
              f"The last traced step: {len(step)} kernels over {(end - t0) / 1e3:.1f} us (kernel trace, so each "
              "kernel's span includes any time it shared the GPU with the other streams).  Times in us from the "
-             "step's first kernel; queue = the HIP queue (stream) it ran on.", "",
+             "step's first kernel (negative: a kernel of the step before, still running); queue = the HIP queue "
+             "(stream) it ran on.", "",
              "| start | end | us | queue | kernel |", "|---|---|---|---|---|"]
     for r in step:
         s0 = (int(r["Start_Timestamp"]) - t0) / 1e3
