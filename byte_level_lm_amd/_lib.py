@@ -47,6 +47,9 @@ _SIGS = {
     "bllm_topk_select_window": (C.c_int, [_p, _i64, _i64, _i64, C.c_int, _p, _p, _p, _p]),
     "bllm_gather_topk": (C.c_int, [_p, C.c_int, _i64, _i64, _i64, _i64, _p, _p, _p]),
     "bllm_upsample_workspace": (C.c_size_t, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "bllm_upsample_plan": (C.c_int, [_p, _i64, _i64, _i64, _i64, _p, C.c_size_t, _p]),
+    "bllm_upsample_apply": (C.c_int, [_p, _p, _p, C.c_int, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p,
+                                      C.c_size_t, _p]),
     "bllm_upsample_bins": (C.c_int, [_p, _p, _p, _p, C.c_int, _i64, _i64, _i64, _i64, _i64, _i64,
                                      _p, _p, C.c_size_t, _p]),
 }

@@ -474,26 +474,23 @@ extern "C" size_t bllm_upsample_workspace(int64_t nseq, int64_t T, int64_t K, in
   return up_ws_bytes(g);
 }
 
-extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* idx, const void* h,
-                                  int dtype, int64_t nseq, int64_t T, int64_t K, int64_t d_global,
-                                  int64_t d_local, int64_t nbins, void* s_out, void* ws,
-                                  size_t ws_bytes, void* stream) {
-  if (!gm || !W || !idx || !h || !s_out || nseq < 1 || T < 1 || K < 1 || K > T || d_global < 1 ||
-      d_local < 1 || nbins < 1)
-    return BLLM_E_INVAL;
-  if (dtype != BLLM_BF16) return BLLM_E_NOTSUP;
-  if (nbins > 64 || d_global % 8 != 0 || d_local % 8 != 0 || nseq * T >= (int64_t(1) << 31) ||
-      T > (int64_t(1) << 20) || !aligned16(gm) || !aligned16(W) || !aligned16(h) || !aligned16(s_out))
-    return BLLM_E_NOTSUP;
-  UpGeom g{static_cast<int>(nseq), static_cast<int>(T), static_cast<int>(K), static_cast<int>(d_global),
-           static_cast<int>(d_local), static_cast<int>(nbins),
+// Shapes and the workspace of an upsample: BLLM_OK and the geometry, or the
+// error the entry points return.
+static int up_setup(int64_t nseq, int64_t T, int64_t K, int64_t nbins, const void* ws, size_t ws_bytes,
+                    UpGeom* out) {
+  if (nseq < 1 || T < 1 || K < 1 || K > T || nbins < 1) return BLLM_E_INVAL;
+  if (nbins > 64 || nseq * T >= (int64_t(1) << 31) || T > (int64_t(1) << 20)) return BLLM_E_NOTSUP;
+  UpGeom g{static_cast<int>(nseq), static_cast<int>(T), static_cast<int>(K), 0, 0, static_cast<int>(nbins),
            static_cast<int>(ceil_div(nseq * K, kChunksPerBlock)), 0};
   if (up_max_items(g) > static_cast<size_t>(INT32_MAX)) return BLLM_E_NOTSUP;
   g.cap = static_cast<int>(up_max_items(g));
   if (!ws || ws_bytes < up_ws_bytes(g) || !aligned16(ws)) return BLLM_E_WS;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  UpWs u = up_carve(ws, g);
-  if (nbins == 16) {
+  *out = g;
+  return BLLM_OK;
+}
+
+static void up_plan_launch(const int32_t* idx, const UpGeom& g, const UpWs& u, hipStream_t st) {
+  if (g.nbins == 16) {
     hipLaunchKernelGGL(up_count<16>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts);
     hipLaunchKernelGGL(up_scan, dim3(1), dim3(kScanThreads), 0, st, g, u.counts, u.bin_off, u.bin_cnt, u.tile_off);
     hipLaunchKernelGGL(up_items<16>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts, u.items);
@@ -502,8 +499,12 @@ extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* 
     hipLaunchKernelGGL(up_scan, dim3(1), dim3(kScanThreads), 0, st, g, u.counts, u.bin_off, u.bin_cnt, u.tile_off);
     hipLaunchKernelGGL(up_items<0>, dim3(g.nblk), dim3(kChunksPerBlock), 0, st, idx, g, u.counts, u.items);
   }
-  const int64_t max_tiles = ceil_div(static_cast<int64_t>(up_max_items(g)), kBM) + nbins;
-  const int ncol = static_cast<int>(ceil_div(d_local, kBN));
+}
+
+static void up_apply_launch(const void* gm, const void* W, const void* h, const UpGeom& g, const UpWs& u,
+                            void* s_out, hipStream_t st) {
+  const int64_t max_tiles = ceil_div(static_cast<int64_t>(up_max_items(g)), kBM) + g.nbins;
+  const int ncol = static_cast<int>(ceil_div(g.dl, kBN));
   const int64_t nblocks = ceil_div(max_tiles, 8) * 8 * ncol;
   if (g.dg % kBK == 0)
     hipLaunchKernelGGL(up_gemm<true>, dim3(static_cast<unsigned>(nblocks)), dim3(256), 0, st,
@@ -515,5 +516,61 @@ extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* 
                      static_cast<const uint16_t*>(gm), static_cast<const uint16_t*>(W),
                      static_cast<const uint16_t*>(h), g, u.bin_off,
                      u.bin_cnt, u.tile_off, u.items, ncol, static_cast<uint16_t*>(s_out));
+}
+
+// the apply's own arguments: every BLLM_E_INVAL condition of the call is
+// checked before any BLLM_E_NOTSUP one
+static int up_apply_args(const void* gm, const void* W, const void* h, int dtype, int64_t nseq, int64_t T,
+                         int64_t K, int64_t d_global, int64_t d_local, int64_t nbins, void* s_out) {
+  if (!gm || !W || !h || !s_out || d_global < 1 || d_local < 1 || nseq < 1 || T < 1 || K < 1 || K > T ||
+      nbins < 1)
+    return BLLM_E_INVAL;
+  if (dtype != BLLM_BF16) return BLLM_E_NOTSUP;
+  if (d_global % 8 != 0 || d_local % 8 != 0 || d_global >= (int64_t(1) << 20) || d_local >= (int64_t(1) << 20) ||
+      !aligned16(gm) || !aligned16(W) || !aligned16(h) || !aligned16(s_out))
+    return BLLM_E_NOTSUP;
+  return BLLM_OK;
+}
+
+extern "C" int bllm_upsample_plan(const int32_t* idx, int64_t nseq, int64_t T, int64_t K, int64_t nbins,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  if (!idx) return BLLM_E_INVAL;
+  UpGeom g{};
+  const int rc = up_setup(nseq, T, K, nbins, ws, ws_bytes, &g);
+  if (rc != BLLM_OK) return rc;
+  up_plan_launch(idx, g, up_carve(ws, g), static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+extern "C" int bllm_upsample_apply(const void* gm, const void* W, const void* h, int dtype, int64_t nseq,
+                                   int64_t T, int64_t K, int64_t d_global, int64_t d_local, int64_t nbins,
+                                   void* s_out, const void* ws, size_t ws_bytes, void* stream) {
+  int rc = up_apply_args(gm, W, h, dtype, nseq, T, K, d_global, d_local, nbins, s_out);
+  if (rc != BLLM_OK) return rc;
+  UpGeom g{};
+  rc = up_setup(nseq, T, K, nbins, ws, ws_bytes, &g);
+  if (rc != BLLM_OK) return rc;
+  g.dg = static_cast<int>(d_global);
+  g.dl = static_cast<int>(d_local);
+  up_apply_launch(gm, W, h, g, up_carve(const_cast<void*>(ws), g), s_out, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+extern "C" int bllm_upsample_bins(const void* gm, const void* W, const int32_t* idx, const void* h,
+                                  int dtype, int64_t nseq, int64_t T, int64_t K, int64_t d_global,
+                                  int64_t d_local, int64_t nbins, void* s_out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  if (!idx) return BLLM_E_INVAL;
+  int rc = up_apply_args(gm, W, h, dtype, nseq, T, K, d_global, d_local, nbins, s_out);
+  if (rc != BLLM_OK) return rc;
+  UpGeom g{};
+  rc = up_setup(nseq, T, K, nbins, ws, ws_bytes, &g);
+  if (rc != BLLM_OK) return rc;
+  g.dg = static_cast<int>(d_global);
+  g.dl = static_cast<int>(d_local);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const UpWs u = up_carve(ws, g);
+  up_plan_launch(idx, g, u, st);
+  up_apply_launch(gm, W, h, g, u, s_out, st);
   return launch_status();
 }

@@ -325,6 +325,30 @@ def topk_select_window(score, K: int, first: bool, *, idx_out=None, mask_out=Non
     return idx_out, mask_out, status
 
 
+def upsample_plan(idx, T: int, nbins: int, *, ws=None, d_global: int = 8, d_local: int = 8):
+    """The upsample's work items from the chunk starts idx int32 [nseq, K] into a
+    workspace (returned; pass it to ``upsample_apply``)."""
+    _dev(idx)
+    nseq, K = idx.shape
+    w = _ws(upsample_workspace(nseq, T, K, d_global, d_local, nbins), ws, idx.device)
+    rc = L.lib().bllm_upsample_plan(idx.data_ptr(), nseq, int(T), K, int(nbins), w.data_ptr(), _nbytes(w),
+                                    _stream())
+    L.check("bllm_upsample_plan", rc)
+    return w
+
+
+def upsample_apply(g, W, h, nbins: int, ws, *, s_out=None):
+    """s_t = h_t + g_{c(t)} W_{bin(t)} from a plan made by ``upsample_plan`` in ws."""
+    _dev(g, W, h, ws)
+    nseq, K, dg = g.shape
+    T, dl = h.shape[1], h.shape[2]
+    s_out = torch.empty_like(h) if s_out is None else s_out
+    rc = L.lib().bllm_upsample_apply(g.data_ptr(), W.data_ptr(), h.data_ptr(), _dt(h), nseq, T, K, dg, dl,
+                                     int(nbins), s_out.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream())
+    L.check("bllm_upsample_apply", rc)
+    return s_out
+
+
 def upsample_bins(g, W, idx, h, nbins: int, *, s_out=None, ws=None):
     """s_t = h_t + g_{c(t)} W_{bin(t)}; g [nseq,K,dg], W [nbins,dg,dl], idx int32 [nseq,K], h [nseq,T,dl]."""
     _dev(g, W, idx, h)

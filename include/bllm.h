@@ -349,6 +349,25 @@ int bllm_upsample_bins(const void* g, const void* W, const int32_t* idx, const v
                        int64_t nseq, int64_t T, int64_t K, int64_t d_global, int64_t d_local,
                        int64_t nbins, void* s_out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * bllm_upsample_plan / bllm_upsample_apply -- bllm_upsample_bins in its two
+ * parts ([BF4] stage 4).  The plan needs only the chunk starts: it buckets
+ * every (chunk, bin) run of positions into the workspace (its kernels read
+ * idx, nothing else), so it can run as soon as Top-K is done, beside the
+ * gather and the global model; the apply is the binned GEMM with the
+ * residual, from that plan.  plan followed by apply (same nseq, T, K, nbins
+ * and ws; the apply queued after the plan on one stream, or ordered after it
+ * by the caller's events) gives bit for bit the result of bllm_upsample_bins.
+ * Arguments, layouts, limits and errors as bllm_upsample_bins (the plan's
+ * ws as bllm_upsample_workspace sizes it: it does not depend on d_global or
+ * d_local).  The workspace holds the plan until the next plan into it.
+ */
+int bllm_upsample_plan(const int32_t* idx, int64_t nseq, int64_t T, int64_t K, int64_t nbins, void* ws,
+                       size_t ws_bytes, void* stream);
+int bllm_upsample_apply(const void* g, const void* W, const void* h, int dtype, int64_t nseq, int64_t T,
+                        int64_t K, int64_t d_global, int64_t d_local, int64_t nbins, void* s_out,
+                        const void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -545,6 +545,32 @@ def _random_idx(rng, nseq, T, K):
                      for _ in range(nseq)]).astype(np.int32)
 
 
+@pytest.mark.parametrize("nseq,T,K,dg,dl,B", [(3, 1000, 37, 96, 136, 4), (4, 3000, 300, 200, 320, 16)])
+def test_upsample_plan_then_apply_equals_one_call(ops, nseq, T, K, dg, dl, B):
+    """The plan on a second stream (ordered before the apply by an event),
+    then the apply, gives bit for bit the one-call result; a second plan into
+    the same workspace (other chunk starts) replaces the first."""
+    torch = _torch()
+    rng = np.random.default_rng(nseq * T + K)
+    bf = torch.bfloat16
+    g = to_dev(bf16_round(rng.standard_normal((nseq, K, dg))), bf)
+    W = to_dev(bf16_round(rng.standard_normal((B, dg, dl)) / np.sqrt(dg)), bf)
+    h = to_dev(bf16_round(rng.standard_normal((nseq, T, dl))), bf)
+    ws = None
+    for rep in range(2):
+        idx = to_dev(_random_idx(rng, nseq, T, K))
+        want = ops.upsample_bins(g, W, idx, h, B)
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            ws = ops.upsample_plan(idx, T, B, ws=ws)
+            done = torch.cuda.Event()
+            done.record(s2)
+        torch.cuda.current_stream().wait_event(done)
+        got = ops.upsample_apply(g, W, h, B, ws)
+        assert torch.equal(got, want), rep
+
+
 def test_upsample_positions_not_ascending_stay_in_bounds(ops):
     """Positions that are not ascending or fall outside [0, T) (here chunks
     that overlap, so their items outgrow the workspace's slots, and values
