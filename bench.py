@@ -232,7 +232,6 @@ class Workload:
     def _upsample(self):
         self.B.upsample_bins(self.g4, self.W, self.idx4, self.h4, self.nbins, s_out=self.s4, ws=self.ws_up)
 
-
     def _cosine_chunker(self):
         self.B.route(self.q4, self.k4, self.off4, threshold=0.5, p_out=self.p4, b_out=self.b4)
         self.B.topk_select(self.p4.view(self.nseq, -1), self.K, idx_out=self.idx5, mask_out=self.mask5,
