@@ -92,6 +92,20 @@ def test_argument_errors_return_before_any_launch(L):
     # upsample: fp32 unsupported, nbins < 1
     assert L.bllm_upsample_bins(dummy, dummy, dummy, dummy, 0, 1, 64, 4, 64, 32, 16, dummy, dummy, 1 << 30, None) == -2
     assert L.bllm_upsample_bins(dummy, dummy, dummy, dummy, 1, 1, 64, 4, 64, 32, 0, dummy, dummy, 1 << 30, None) == -1
+    # upsample plan / apply: K > T, null idx, fp32 unsupported, workspace too small
+    assert L.bllm_upsample_plan(dummy, 1, 64, 65, 16, dummy, 1 << 30, None) == -1
+    assert L.bllm_upsample_plan(None, 1, 64, 4, 16, dummy, 1 << 30, None) == -1
+    assert L.bllm_upsample_plan(dummy, 1, 64, 4, 16, dummy, 16, None) == -3
+    assert L.bllm_upsample_apply(dummy, dummy, dummy, 0, 1, 64, 4, 64, 32, 16, dummy, dummy, 1 << 30, None) == -2
+    assert L.bllm_upsample_apply(dummy, dummy, None, 1, 1, 64, 4, 64, 32, 16, dummy, dummy, 1 << 30, None) == -1
+    assert L.bllm_upsample_apply(dummy, dummy, dummy, 1, 1, 64, 4, 64, 32, 16, dummy, dummy, 16, None) == -3
+    # an invalid argument is reported before an unsupported one (K > T with an fp32 dtype)
+    assert L.bllm_upsample_bins(dummy, dummy, dummy, dummy, 0, 1, 64, 65, 64, 32, 16, dummy, dummy, 1 << 30,
+                                None) == -1
+    # Top-K gather: K > T, null idx, rows not a multiple of 16 bytes
+    assert L.bllm_gather_topk(dummy, 0, 1, 10, 8, 11, dummy, dummy, None) == -1
+    assert L.bllm_gather_topk(dummy, 0, 1, 10, 8, 4, None, dummy, None) == -1
+    assert L.bllm_gather_topk(dummy, 1, 1, 10, 4, 4, dummy, dummy, None) == -2
     # compact without a workspace: more positions than its scratch holds (checked before any HIP call)
     assert L.bllm_compact_noalloc(dummy, None, None, 0, 0, dummy, 1, (1 << 27) + 1, 5, dummy, dummy, None, None,
                                   None, None) == -3

@@ -135,3 +135,33 @@ def test_profsum_calls_split_over_two_streams(tmp_path):
     block = json.loads(out.read_text().split("```json\n")[-1].split("\n```")[0])
     assert block["us_per_call"] == pytest.approx(0.32) and block["parts"] == 2
     assert block["kernel_us_per_call"] == pytest.approx((100 + 105 + 20 + 15 + 180 + 195) / 1e3, abs=0.01)
+
+
+def test_profsum_step_timeline_keeps_kernels_still_running(tmp_path):
+    """The timeline of the last step starts at its first Gram-prefix kernel
+    and keeps a kernel of the step before that still runs at that time
+    (negative start), but not one that ended before it."""
+    gram = "bllm::(anonymous namespace)::cr_gram_prefix_bf16(unsigned short const*)"
+    expand = "void bllm::(anonymous namespace)::ema_tile_expand<1>(void const*)"
+    topk = "void bllm::(anonymous namespace)::topk_kernel<true>(float const*)"
+    ks = [(gram, 0, 100), (gram, 5, 110), (expand, 900, 950), (expand, 960, 1030),
+          (gram, 1000, 1100), (gram, 1005, 1120), (topk, 1200, 1230)]
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "x_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Queue_Id"])
+        w.writeheader()
+        for name, s0, s1 in ks:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": s0, "End_Timestamp": s1, "Queue_Id": 1})
+    out = tmp_path / "tl.md"
+    sys_argv = sys.argv
+    try:
+        sys.argv = ["profsum", "--op", "step-timeline", "--trace", str(d), "--cmd", "c", "--workload", "w",
+                    "--out", str(out)]
+        profsum.main()
+    finally:
+        sys.argv = sys_argv
+    rows = [ln for ln in out.read_text().splitlines() if ln.startswith("| ") and "kernel |" not in ln]
+    assert len(rows) == 4  # the still-running expand, both Grams, Top-K
+    assert rows[0].startswith("| -0.0") and "ema_tile_expand" in rows[0]
+    assert "topk_kernel" in rows[-1]
