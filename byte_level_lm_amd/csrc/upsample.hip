@@ -252,12 +252,25 @@ __global__ __launch_bounds__(256, 3) void up_gemm(const uint16_t* gmat,
   if (tau_f >= tile_off[g.nbins]) return;
   const int tau = tile_off[g.nbins] - 1 - tau_f;  // last bins first: they hold the longest runs
   int b = 0;
-  while (tile_off[b + 1] <= tau) ++b;
-  const int first = (tau - tile_off[b]) * kBM;
-  const int mcount = min(kBM, bin_cnt[b] - first);
+  while (b + 1 < g.nbins && tile_off[b + 1] <= tau) ++b;
+  const int64_t first = (static_cast<int64_t>(tau) - tile_off[b]) * kBM;
+  const int mcount = static_cast<int>(
+      min(static_cast<int64_t>(kBM), max(static_cast<int64_t>(bin_cnt[b]) - first, int64_t(0))));
   const int n0 = (rem >> 3) * kBN;
   const int tid = threadIdx.x;
-  if (tid < kBM) sItem[tid] = tid < mcount ? items[bin_off[b] + first + tid] : make_int4(0, 0, 0, 0);
+  if (tid < kBM) {
+    // a plan made by the plan kernels always passes these bounds; they keep a
+    // workspace that holds no plan (bllm_upsample_apply alone) in bounds too
+    int4 it = make_int4(0, 0, 0, 0);
+    const int64_t slot = static_cast<int64_t>(bin_off[b]) + first + tid;
+    if (tid < mcount && slot >= 0 && slot < g.cap) {
+      it = items[slot];
+      it.x = min(max(it.x, 0), g.nseq * g.K - 1);
+      it.y = min(max(it.y, 0), g.nseq * g.T - 1);
+      it.z = min(max(it.z, 0), min(kMaxRun, g.nseq * g.T - it.y));
+    }
+    sItem[tid] = it;
+  }
   __syncthreads();
   const int w = tid >> 6, lane = tid & 63;
   const int wm = w >> 1, wn = w & 1;

@@ -360,7 +360,9 @@ int bllm_upsample_bins(const void* g, const void* W, const int32_t* idx, const v
  * by the caller's events) gives bit for bit the result of bllm_upsample_bins.
  * Arguments, layouts, limits and errors as bllm_upsample_bins (the plan's
  * ws as bllm_upsample_workspace sizes it: it does not depend on d_global or
- * d_local).  The workspace holds the plan until the next plan into it.
+ * d_local).  The workspace holds the plan until the next plan into it; an
+ * apply from a workspace that holds no plan for these shapes gives
+ * unspecified rows, but no access leaves the arguments or the workspace.
  */
 int bllm_upsample_plan(const int32_t* idx, int64_t nseq, int64_t T, int64_t K, int64_t nbins, void* ws,
                        size_t ws_bytes, void* stream);
